@@ -1,0 +1,239 @@
+"""MiniMax Sparse Attention (MSA) decode path with NVFP4 caches for AMD MI355X (gfx950).
+
+Thin Python binding of libmsa.so (C ABI in include/msa.h). Every step of the path runs in the
+library's HIP kernels; this module only marshals torch tensors (device memory) and the current
+HIP stream into the C calls, with the same names:
+
+    msa_kv_insert_nvfp4(cache, slots, k, v, ik)
+    msa_indexer_score(cache, batch, q_idx, block_scores)
+    msa_block_topk(block_scores, batch, topk, block_ids)
+    msa_sparse_attn_workspace_bytes(batch)
+    msa_sparse_attn_decode(cache, batch, q, block_ids, softmax_scale, out, workspace)
+
+A non-zero status raises MSAError. There is no fallback: importing fails loudly when the
+library has not been built (python -m block_sparse_attention_nvfp4_amd.build).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmsa.so")
+
+BLOCK = 128
+HEAD_DIM = 128
+KV_HEADS = 4
+Q_HEADS = 64
+TOPK = 16
+HEAD_PAGE_BYTES = 9216
+
+MSA_OK = 0
+MSA_ERR_INVALID_ARG = -1
+MSA_ERR_UNSUPPORTED = -2
+MSA_ERR_WORKSPACE = -3
+MSA_ERR_HIP = -4
+
+EXPORTED = ("msa_page_bytes", "msa_kv_insert_nvfp4", "msa_indexer_score", "msa_block_topk",
+            "msa_sparse_attn_workspace_bytes", "msa_sparse_attn_decode", "msa_last_error",
+            "msa_version")
+
+
+class MSAError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[{code}] {message}")
+        self.code = code
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("ik", ctypes.c_void_p),
+                ("num_pages", ctypes.c_int64)]
+
+
+class _Batch(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("ctx_lens", ctypes.c_void_p),
+                ("batch", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+                ("q_len", ctypes.c_int32)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m block_sparse_attention_nvfp4_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    L.msa_page_bytes.restype, L.msa_page_bytes.argtypes = sz, [ctypes.c_int]
+    L.msa_kv_insert_nvfp4.restype = ctypes.c_int
+    L.msa_kv_insert_nvfp4.argtypes = [ctypes.POINTER(_Cache), vp, vp, vp, vp, i32, vp]
+    L.msa_indexer_score.restype = ctypes.c_int
+    L.msa_indexer_score.argtypes = [ctypes.POINTER(_Cache), ctypes.POINTER(_Batch), vp, vp, vp]
+    L.msa_block_topk.restype = ctypes.c_int
+    L.msa_block_topk.argtypes = [vp, ctypes.POINTER(_Batch), i32, vp, vp]
+    L.msa_sparse_attn_workspace_bytes.restype = sz
+    L.msa_sparse_attn_workspace_bytes.argtypes = [ctypes.POINTER(_Batch)]
+    L.msa_sparse_attn_decode.restype = ctypes.c_int
+    L.msa_sparse_attn_decode.argtypes = [ctypes.POINTER(_Cache), ctypes.POINTER(_Batch), vp, vp,
+                                         ctypes.c_float, vp, vp, sz, vp]
+    L.msa_last_error.restype, L.msa_last_error.argtypes = ctypes.c_char_p, []
+    L.msa_version.restype, L.msa_version.argtypes = ctypes.c_char_p, []
+    return L
+
+
+lib = _load()
+
+
+def _check(rc: int) -> None:
+    if rc != MSA_OK:
+        raise MSAError(rc, lib.msa_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor], dtype: torch.dtype, name: str):
+    if t is None:
+        return None
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+class Cache:
+    """Paged NVFP4 pools (K, V, index keys) as device uint8 tensors; see include/msa.h."""
+
+    def __init__(self, k: torch.Tensor, v: torch.Tensor, ik: torch.Tensor):
+        self.k, self.v, self.ik = k, v, ik
+        self.num_pages = int(ik.shape[0])
+        self._c = _Cache(_ptr(k, torch.uint8, "k"), _ptr(v, torch.uint8, "v"),
+                         _ptr(ik, torch.uint8, "ik"), self.num_pages)
+
+    @classmethod
+    def allocate(cls, num_pages: int, device="cuda") -> "Cache":
+        """Zero-initialized pools for `num_pages` pages."""
+        shape = (num_pages, KV_HEADS, HEAD_PAGE_BYTES)
+        return cls(torch.zeros(shape, dtype=torch.uint8, device=device),
+                   torch.zeros(shape, dtype=torch.uint8, device=device),
+                   torch.zeros((num_pages, HEAD_PAGE_BYTES), dtype=torch.uint8, device=device))
+
+
+class Batch:
+    """Block table (int32 [batch][max_blocks]), context lengths (int32 [batch]) and q_len."""
+
+    def __init__(self, block_table: torch.Tensor, ctx_lens: torch.Tensor, q_len: int):
+        if block_table.dim() != 2 or ctx_lens.dim() != 1 or ctx_lens.shape[0] != block_table.shape[0]:
+            raise ValueError("block_table must be [batch][max_blocks] and ctx_lens [batch]")
+        self.block_table, self.ctx_lens, self.q_len = block_table, ctx_lens, int(q_len)
+        self.batch, self.max_blocks = int(block_table.shape[0]), int(block_table.shape[1])
+        self._c = _Batch(_ptr(block_table, torch.int32, "block_table"),
+                         _ptr(ctx_lens, torch.int32, "ctx_lens"), self.batch, self.max_blocks,
+                         self.q_len)
+
+    @property
+    def rows(self) -> int:
+        return self.batch * self.q_len
+
+
+def msa_page_bytes(which: int) -> int:
+    return int(lib.msa_page_bytes(int(which)))
+
+
+def msa_version() -> str:
+    return lib.msa_version().decode()
+
+
+def msa_last_error() -> str:
+    return lib.msa_last_error().decode()
+
+
+def msa_kv_insert_nvfp4(cache: Cache, slots: torch.Tensor, k: Optional[torch.Tensor],
+                        v: Optional[torch.Tensor], ik: Optional[torch.Tensor], stream=None) -> None:
+    n = int(slots.shape[0])
+    for name, t, tail in (("k", k, (KV_HEADS, HEAD_DIM)), ("v", v, (KV_HEADS, HEAD_DIM)),
+                          ("ik", ik, (HEAD_DIM,))):
+        if t is not None and tuple(t.shape) != (n, *tail):
+            raise ValueError(f"{name}: expected shape {(n, *tail)}, got {tuple(t.shape)}")
+    _check(lib.msa_kv_insert_nvfp4(ctypes.byref(cache._c), _ptr(slots, torch.int64, "slots"),
+                                   _ptr(k, torch.float32, "k"), _ptr(v, torch.float32, "v"),
+                                   _ptr(ik, torch.float32, "ik"), n, _stream(stream)))
+
+
+def msa_indexer_score(cache: Cache, batch: Batch, q_idx: torch.Tensor, block_scores: torch.Tensor,
+                      stream=None) -> None:
+    if tuple(q_idx.shape) != (batch.rows, KV_HEADS, HEAD_DIM):
+        raise ValueError(f"q_idx: expected {(batch.rows, KV_HEADS, HEAD_DIM)}, got {tuple(q_idx.shape)}")
+    if tuple(block_scores.shape) != (batch.rows, KV_HEADS, batch.max_blocks):
+        raise ValueError("block_scores: expected [batch*q_len][4][max_blocks]")
+    _check(lib.msa_indexer_score(ctypes.byref(cache._c), ctypes.byref(batch._c),
+                                 _ptr(q_idx, torch.bfloat16, "q_idx"),
+                                 _ptr(block_scores, torch.float32, "block_scores"), _stream(stream)))
+
+
+def msa_block_topk(block_scores: torch.Tensor, batch: Batch, topk: int, block_ids: torch.Tensor,
+                   stream=None) -> None:
+    if tuple(block_scores.shape) != (batch.rows, KV_HEADS, batch.max_blocks):
+        raise ValueError("block_scores: expected [batch*q_len][4][max_blocks]")
+    if tuple(block_ids.shape) != (batch.rows, KV_HEADS, int(topk)):
+        raise ValueError("block_ids: expected [batch*q_len][4][topk]")
+    _check(lib.msa_block_topk(_ptr(block_scores, torch.float32, "block_scores"),
+                              ctypes.byref(batch._c), int(topk),
+                              _ptr(block_ids, torch.int32, "block_ids"), _stream(stream)))
+
+
+def msa_sparse_attn_workspace_bytes(batch: Batch) -> int:
+    return int(lib.msa_sparse_attn_workspace_bytes(ctypes.byref(batch._c)))
+
+
+def msa_sparse_attn_decode(cache: Cache, batch: Batch, q: torch.Tensor, block_ids: torch.Tensor,
+                           softmax_scale: float, out: torch.Tensor,
+                           workspace: Optional[torch.Tensor], stream=None) -> None:
+    if tuple(q.shape) != (batch.rows, Q_HEADS, HEAD_DIM) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q and out: expected [batch*q_len][64][128]")
+    if tuple(block_ids.shape) != (batch.rows, KV_HEADS, TOPK):
+        raise ValueError("block_ids: expected [batch*q_len][4][16]")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _ptr(workspace, workspace.dtype, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.msa_sparse_attn_decode(ctypes.byref(cache._c), ctypes.byref(batch._c),
+                                      _ptr(q, torch.bfloat16, "q"),
+                                      _ptr(block_ids, torch.int32, "block_ids"),
+                                      float(softmax_scale), _ptr(out, torch.bfloat16, "out"),
+                                      ws_ptr, ws_bytes, _stream(stream)))
+
+
+def default_softmax_scale() -> float:
+    return 1.0 / math.sqrt(HEAD_DIM)
+
+
+class DecodeStep:
+    """Buffers and the four calls of one MSA decode step for a fixed batch shape."""
+
+    def __init__(self, cache: Cache, batch: Batch, device="cuda"):
+        self.cache, self.batch = cache, batch
+        rows = batch.rows
+        self.block_scores = torch.empty((rows, KV_HEADS, batch.max_blocks), dtype=torch.float32,
+                                        device=device)
+        self.block_ids = torch.empty((rows, KV_HEADS, TOPK), dtype=torch.int32, device=device)
+        self.out = torch.empty((rows, Q_HEADS, HEAD_DIM), dtype=torch.bfloat16, device=device)
+        ws = msa_sparse_attn_workspace_bytes(batch)
+        self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device) if ws else None
+
+    def run(self, slots, k, v, ik, q_idx, q, softmax_scale=None, stream=None):
+        scale = default_softmax_scale() if softmax_scale is None else softmax_scale
+        msa_kv_insert_nvfp4(self.cache, slots, k, v, ik, stream)
+        msa_indexer_score(self.cache, self.batch, q_idx, self.block_scores, stream)
+        msa_block_topk(self.block_scores, self.batch, TOPK, self.block_ids, stream)
+        msa_sparse_attn_decode(self.cache, self.batch, q, self.block_ids, scale, self.out,
+                               self.workspace, stream)
+        return self.out

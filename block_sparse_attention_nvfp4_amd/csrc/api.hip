@@ -1,0 +1,149 @@
+// C entry points of libmsa.so (declared and documented in include/msa.h): host-side argument
+// checks, then asynchronous launches on the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/msa.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_last_error[0] = '\0';
+    return MSA_OK;
+}
+
+int hip_status(hipError_t err, const char* what) {
+    if (err != hipSuccess) return fail(MSA_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+    return ok();
+}
+
+int check_batch(const msa_batch_t* batch, const char* fn) {
+    if (!batch) return fail(MSA_ERR_INVALID_ARG, "%s: batch is NULL", fn);
+    if (!batch->block_table || !batch->ctx_lens)
+        return fail(MSA_ERR_INVALID_ARG, "%s: block_table or ctx_lens is NULL", fn);
+    if (batch->batch < 1 || batch->max_blocks < 1 || batch->q_len < 1)
+        return fail(MSA_ERR_INVALID_ARG, "%s: batch=%d max_blocks=%d q_len=%d must all be >= 1", fn,
+                    batch->batch, batch->max_blocks, batch->q_len);
+    if (batch->batch > 65535)
+        return fail(MSA_ERR_INVALID_ARG, "%s: batch=%d exceeds 65535", fn, batch->batch);
+    if ((int64_t)batch->max_blocks * MSA_BLOCK > INT32_MAX / 2)
+        return fail(MSA_ERR_INVALID_ARG, "%s: max_blocks=%d too large", fn, batch->max_blocks);
+    const int64_t rows = (int64_t)batch->batch * batch->q_len * MSA_KV_HEADS;
+    if (rows > INT32_MAX / 64)
+        return fail(MSA_ERR_INVALID_ARG, "%s: batch*q_len=%lld too large", fn,
+                    (long long)batch->batch * batch->q_len);
+    return MSA_OK;
+}
+
+int check_cache(const msa_cache_t* cache, const char* fn, bool need_kv, bool need_ik) {
+    if (!cache) return fail(MSA_ERR_INVALID_ARG, "%s: cache is NULL", fn);
+    if (cache->num_pages < 1) return fail(MSA_ERR_INVALID_ARG, "%s: num_pages must be >= 1", fn);
+    if (need_kv && (!cache->k || !cache->v))
+        return fail(MSA_ERR_INVALID_ARG, "%s: K or V pool is NULL", fn);
+    if (need_ik && !cache->ik) return fail(MSA_ERR_INVALID_ARG, "%s: index-key pool is NULL", fn);
+    return MSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t msa_page_bytes(int which) {
+    switch (which) {
+        case 0:
+        case 1:
+            return MSA_KV_PAGE_BYTES;
+        case 2:
+            return MSA_IK_PAGE_BYTES;
+        default:
+            return 0;
+    }
+}
+
+const char* msa_last_error(void) { return g_last_error; }
+
+const char* msa_version(void) { return "msa-mi355x 0.1 (gfx950)"; }
+
+int msa_kv_insert_nvfp4(const msa_cache_t* cache, const int64_t* slots, const float* k,
+                        const float* v, const float* ik, int32_t n, void* stream) {
+    static const char* fn = "msa_kv_insert_nvfp4";
+    if (!cache) return fail(MSA_ERR_INVALID_ARG, "%s: cache is NULL", fn);
+    if (!slots) return fail(MSA_ERR_INVALID_ARG, "%s: slots is NULL", fn);
+    if (n < 0) return fail(MSA_ERR_INVALID_ARG, "%s: n=%d < 0", fn, n);
+    if (!k && !v && !ik) return fail(MSA_ERR_INVALID_ARG, "%s: k, v and ik are all NULL", fn);
+    if (cache->num_pages < 1) return fail(MSA_ERR_INVALID_ARG, "%s: num_pages must be >= 1", fn);
+    if ((k && !cache->k) || (v && !cache->v) || (ik && !cache->ik))
+        return fail(MSA_ERR_INVALID_ARG, "%s: a pool for supplied values is NULL", fn);
+    if (n == 0) return ok();
+    return hip_status(msa::launch_insert(cache->k, cache->v, cache->ik, cache->num_pages, slots, k,
+                                         v, ik, n, (hipStream_t)stream),
+                      fn);
+}
+
+int msa_indexer_score(const msa_cache_t* cache, const msa_batch_t* batch, const uint16_t* q_idx,
+                      float* block_scores, void* stream) {
+    static const char* fn = "msa_indexer_score";
+    int rc = check_cache(cache, fn, false, true);
+    if (rc) return rc;
+    if ((rc = check_batch(batch, fn))) return rc;
+    if (!q_idx || !block_scores) return fail(MSA_ERR_INVALID_ARG, "%s: q_idx or block_scores is NULL", fn);
+    return hip_status(msa::launch_indexer(cache->ik, cache->num_pages, batch->block_table,
+                                          batch->ctx_lens, batch->batch, batch->max_blocks,
+                                          batch->q_len, q_idx, block_scores, (hipStream_t)stream),
+                      fn);
+}
+
+int msa_block_topk(const float* block_scores, const msa_batch_t* batch, int32_t topk,
+                   int32_t* block_ids, void* stream) {
+    static const char* fn = "msa_block_topk";
+    int rc = check_batch(batch, fn);
+    if (rc) return rc;
+    if (!block_scores || !block_ids)
+        return fail(MSA_ERR_INVALID_ARG, "%s: block_scores or block_ids is NULL", fn);
+    if (topk != MSA_TOPK) return fail(MSA_ERR_UNSUPPORTED, "%s: topk=%d (only 16 is built)", fn, topk);
+    return hip_status(msa::launch_topk(block_scores, batch->ctx_lens, batch->batch,
+                                       batch->max_blocks, batch->q_len, block_ids,
+                                       (hipStream_t)stream),
+                      fn);
+}
+
+size_t msa_sparse_attn_workspace_bytes(const msa_batch_t* batch) {
+    if (!batch || batch->batch < 1 || batch->q_len < 1) return 0;
+    return msa::attn_workspace_bytes(batch->batch, batch->q_len);
+}
+
+int msa_sparse_attn_decode(const msa_cache_t* cache, const msa_batch_t* batch, const uint16_t* q,
+                           const int32_t* block_ids, float softmax_scale, uint16_t* out,
+                           void* workspace, size_t ws_bytes, void* stream) {
+    static const char* fn = "msa_sparse_attn_decode";
+    int rc = check_cache(cache, fn, true, false);
+    if (rc) return rc;
+    if ((rc = check_batch(batch, fn))) return rc;
+    if (!q || !block_ids || !out)
+        return fail(MSA_ERR_INVALID_ARG, "%s: q, block_ids or out is NULL", fn);
+    const size_t need = msa::attn_workspace_bytes(batch->batch, batch->q_len);
+    if (need > 0 && (!workspace || ws_bytes < need))
+        return fail(MSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                    workspace ? ws_bytes : (size_t)0);
+    if (need > 0 && ((uintptr_t)workspace & 255u))
+        return fail(MSA_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+    return hip_status(msa::launch_attention(cache->k, cache->v, cache->num_pages,
+                                            batch->block_table, batch->ctx_lens, batch->batch,
+                                            batch->max_blocks, batch->q_len, q, block_ids,
+                                            softmax_scale, out, (float*)workspace,
+                                            (hipStream_t)stream),
+                      fn);
+}
+
+}  // extern "C"

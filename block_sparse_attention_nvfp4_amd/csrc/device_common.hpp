@@ -1,0 +1,127 @@
+// Device-side building blocks of the MSA decode kernels for gfx950 (CDNA4).
+//
+// Page layouts follow include/msa.h. Matrix-core operand layouts (64-lane wavefront, lane l,
+// n = l % 16, c = l / 16), as used throughout:
+//   v_mfma_f32_16x16x32_bf16 : A[m][k] in lane (m, c) holds k = 8c..8c+7;  B[k][n] in lane
+//                              (n, c) holds k = 8c..8c+7;  D[m][n] in lane (n, c) holds
+//                              m = 4c..4c+3.
+//   v_mfma_f32_16x16x16_f16  : the same with k = 4c..4c+3.
+// The reduction index k may be permuted freely as long as A and B agree; the page layouts
+// pick the permutation that makes every operand a single 16-byte load per lane.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+constexpr int kBlock = 128;        // tokens per block / page
+constexpr int kDim = 128;          // head dim = index dim
+constexpr int kKvHeads = 4;
+constexpr int kQHeads = 64;
+constexpr int kGroupHeads = 16;
+constexpr int kTopk = 16;
+constexpr int kCodeBytes = 8192;   // E2M1 codes of one head page
+constexpr int kHeadPageBytes = 9216;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- page layouts (msa.h)
+// K / index-key pages: 16-byte code chunk (token t, elements 32c..32c+31).
+__device__ __forceinline__ int row_chunk_offset(int t, int c) {
+    return ((t & 31) >> 2) * 1024 + (16 * c + 4 * (t >> 5) + (t & 3)) * 16;
+}
+// K / index-key pages: scale byte of (token t, group g).
+__device__ __forceinline__ int row_scale_offset(int t, int g) {
+    return kCodeBytes + (g >> 1) * 256 + (t >> 5) * 64 + (t & 3) * 16 + ((t & 31) >> 2) * 2 + (g & 1);
+}
+// V pages: byte holding tokens (t & ~1, t | 1) of element e; scale byte of (token t, group g).
+__device__ __forceinline__ int col_code_byte(int e, int t) { return e * 64 + (t >> 1); }
+__device__ __forceinline__ int col_scale_offset(int t, int g) { return kCodeBytes + g * 128 + t; }
+
+// ---------------------------------------------------------------- loads
+__device__ __forceinline__ u32x4 load16(const uint8_t* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+// ---------------------------------------------------------------- NVFP4 dequantization
+// Two E4M3 scale bytes (byte pair HI of `w`) -> two fp32 values (exact).
+template <bool HI>
+__device__ __forceinline__ f32x2 e4m3_pair_f32(uint32_t w) {
+    return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+}
+
+// Eight E2M1 codes (one 32-bit word, element 2i in the low nibble of byte i) times the fp32
+// scale s -> eight bf16 values. The conversion instruction yields the unscaled E2M1 value
+// exactly (its scale operand only carries a power of two, so 1.0 is passed) and the E4M3
+// scale is applied by an fp32 multiply; every product E2M1 x E4M3 is exact in fp32 and in bf16.
+__device__ __forceinline__ bf16x8 dequant8_bf16(uint32_t w, float s) {
+    const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    bf16x8 r;
+    r[0] = (__bf16)(p0[0] * s);
+    r[1] = (__bf16)(p0[1] * s);
+    r[2] = (__bf16)(p1[0] * s);
+    r[3] = (__bf16)(p1[1] * s);
+    r[4] = (__bf16)(p2[0] * s);
+    r[5] = (__bf16)(p2[1] * s);
+    r[6] = (__bf16)(p3[0] * s);
+    r[7] = (__bf16)(p3[1] * s);
+    return r;
+}
+
+// Four E2M1 codes (bytes SEL, SEL+1 of `w`) times four per-code E4M3 scales (the four bytes
+// of `sw`) -> four fp16 values, exact: E2M1 and E4M3 values are exact in fp16 and so is their
+// product (at most 6 significant bits, magnitude within [2^-10, 2688]).
+template <int SEL>
+__device__ __forceinline__ f16x4 dequant4_f16_percode(uint32_t w, uint32_t sw) {
+    const f16x2 v01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+    const f16x2 v23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL + 1);
+    const f32x2 s01 = __builtin_amdgcn_cvt_pk_f32_fp8(sw, false);
+    const f32x2 s23 = __builtin_amdgcn_cvt_pk_f32_fp8(sw, true);
+    f16x2 h01, h23;
+    h01[0] = (_Float16)s01[0];
+    h01[1] = (_Float16)s01[1];
+    h23[0] = (_Float16)s23[0];
+    h23[1] = (_Float16)s23[1];
+    const f16x2 a = v01 * h01;
+    const f16x2 b = v23 * h23;
+    f16x4 r;
+    r[0] = a[0];
+    r[1] = a[1];
+    r[2] = b[0];
+    r[3] = b[1];
+    return r;
+}
+
+// ---------------------------------------------------------------- matrix cores
+__device__ __forceinline__ f32x4 mfma_bf16_k32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f16_k16(const f16x4& a, const f16x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- cross-lane
+__device__ __forceinline__ float max_over_c(float x) {
+    x = fmaxf(x, __shfl_xor(x, 16, 64));
+    return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+__device__ __forceinline__ float sum_over_c(float x) {
+    x += __shfl_xor(x, 16, 64);
+    return x + __shfl_xor(x, 32, 64);
+}
+
+__device__ __forceinline__ int clamp_ctx(int T, int max_blocks) {
+    const int cap = max_blocks * kBlock;
+    return T < 0 ? 0 : (T > cap ? cap : T);
+}
+
+}  // namespace msa

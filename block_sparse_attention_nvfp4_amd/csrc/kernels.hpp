@@ -1,0 +1,32 @@
+// Host-side launchers of the MSA kernels (internal to libmsa.so). Arguments are already
+// validated by the C entry points in api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace msa {
+
+hipError_t launch_insert(uint8_t* k_pool, uint8_t* v_pool, uint8_t* ik_pool, int64_t num_pages,
+                         const int64_t* slots, const float* k, const float* v, const float* ik,
+                         int n, hipStream_t stream);
+
+hipError_t launch_indexer(const uint8_t* ik_pool, int64_t num_pages, const int32_t* block_table,
+                          const int32_t* ctx_lens, int batch, int max_blocks, int q_len,
+                          const uint16_t* q_idx, float* scores, hipStream_t stream);
+
+hipError_t launch_topk(const float* scores, const int32_t* ctx_lens, int batch, int max_blocks,
+                       int q_len, int32_t* ids, hipStream_t stream);
+
+// Split of the 16 selected blocks of a (sequence, token, group) row over workgroups.
+int attn_num_splits(int batch, int q_len);
+size_t attn_workspace_bytes(int batch, int q_len);
+
+hipError_t launch_attention(const uint8_t* k_pool, const uint8_t* v_pool, int64_t num_pages,
+                            const int32_t* block_table, const int32_t* ctx_lens, int batch,
+                            int max_blocks, int q_len, const uint16_t* q, const int32_t* ids,
+                            float softmax_scale, uint16_t* out, float* workspace,
+                            hipStream_t stream);
+
+}  // namespace msa

@@ -1,0 +1,205 @@
+/*
+ * msa.h - C ABI of libmsa.so: the MiniMax Sparse Attention (MSA) decode path with NVFP4 caches
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources are web pages, cited by title and section):
+ *   "vLLM day-0 support for MiniMax-M3.1-Flash", section "MSA primer": the KV cache is split
+ *   into 128-token blocks; a light indexer scores every cached key with one index query per GQA
+ *   group against one shared index-key head and max-pools the scores to one score per block;
+ *   exact attention then runs over the 16 best blocks only, the most recent block always kept,
+ *   so a query reads at most 2,048 keys.
+ *   "MiniMax-M3.1-Flash serving notes", section "The capacity numbers": both caches are NVFP4,
+ *   4-bit E2M1 values with one E4M3 scale per 16 values (4.5 bits per element).
+ *   "MiniMax M3 on vLLM", sections "MSA mechanism", "Decode execution" and "Speculative
+ *   decoding in the decode kernels": blocks are the 128-token pages of the paged cache, main
+ *   KV and index-key caches are tracked separately through the same block table, the partial
+ *   last block and the causal boundary are masked, and several query tokens per request
+ *   (uniform decode_query_len) are flattened request-major, each with its own causal position.
+ *
+ * A decode step is four calls on one stream, in this order:
+ *   msa_kv_insert_nvfp4 -> msa_indexer_score -> msa_block_topk -> msa_sparse_attn_decode
+ *
+ * Conventions for every entry point
+ *   - All tensor arguments are device pointers owned by the caller. The library allocates
+ *     nothing and keeps no state besides a thread-local error message.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Every call only enqueues work on it
+ *     and returns; nothing synchronizes. Launch shapes depend only on the scalar arguments,
+ *     so a step can be captured in a HIP graph.
+ *   - Return value: MSA_OK or a negative MSA_ERR_* code; nothing is launched on an error.
+ *     msa_last_error() then describes the failure. Arguments are checked on the host only
+ *     where that costs nothing (pointers, sizes, constants). Values that live in device
+ *     memory (context lengths, block-table entries, selected ids, slots) are not checked on
+ *     the host; the kernels stay in bounds for any value: a page id outside [0, num_pages)
+ *     or a negative slot is treated as an absent page or token, and context lengths are
+ *     clamped to [0, max_blocks * 128].
+ *
+ * Shapes (notation): B = batch, q = query tokens per sequence (uniform), T_b = context length
+ * of sequence b counting its q query tokens, which are already inserted; query token j of
+ * sequence b sits at position p = T_b - q + j. 64 query heads, 4 KV heads, head h belongs to
+ * KV group h / 16. head_dim = index dim = 128. bf16 tensors are passed as uint16_t bit patterns.
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSA_BLOCK 128       /* tokens per block = tokens per cache page */
+#define MSA_HEAD_DIM 128    /* head_dim of K/V and dimension of index keys/queries */
+#define MSA_KV_HEADS 4      /* KV heads = GQA groups = index queries per query token */
+#define MSA_Q_HEADS 64      /* query heads, 16 per group */
+#define MSA_TOPK 16         /* blocks kept per (query token, group) */
+
+/* NVFP4 page of one head: 128 tokens x 128 elements. 8,192 code bytes + 1,024 scale bytes
+ * = 9,216 B (72 B per 128-element vector, 4.5 bits per element). */
+#define MSA_HEAD_PAGE_BYTES 9216
+#define MSA_KV_PAGE_BYTES (MSA_KV_HEADS * MSA_HEAD_PAGE_BYTES) /* 36,864 B per page of K or V */
+#define MSA_IK_PAGE_BYTES MSA_HEAD_PAGE_BYTES                  /* 9,216 B per index-key page */
+
+/* Status codes */
+#define MSA_OK 0
+#define MSA_ERR_INVALID_ARG (-1) /* null pointer, size out of range */
+#define MSA_ERR_UNSUPPORTED (-2) /* a value this build does not implement (e.g. topk != 16) */
+#define MSA_ERR_WORKSPACE (-3)   /* workspace pointer null or smaller than required */
+#define MSA_ERR_HIP (-4)         /* the HIP runtime reported an error at launch */
+
+/*
+ * Paged NVFP4 caches. One page id addresses the same 128 tokens in all three pools.
+ *   k  : [num_pages][4 heads][9,216 B]   keys
+ *   v  : [num_pages][4 heads][9,216 B]   values
+ *   ik : [num_pages][9,216 B]            index keys (one shared head)
+ *
+ * Within a 9,216 B head page, bytes [0, 8192) hold E2M1 codes (sign bit 3, magnitude bits
+ * 2..0: 0, 0.5, 1, 1.5, 2, 3, 4, 6) and bytes [8192, 9216) hold one E4M3 (OCP "FN") scale
+ * per 16 consecutive elements of a token's 128-element vector (scale group g = elements
+ * 16g..16g+15). A value is E2M1(code) * E4M3(scale). Token t = 0..127 of the page, element
+ * e = 0..127, group g = e / 16:
+ *
+ *   K and index-key pages ("row-operand" layout, a token's elements run along a row):
+ *     code byte holding elements e and e+1 (e even; e in the low nibble):
+ *         ((t % 32) / 4) * 1024 + 256 * (e / 32) + 64 * (t / 32) + 16 * (t % 4) + (e % 32) / 2
+ *       i.e. the 16-byte chunk (t, c = e / 32) starts at
+ *         ((t % 32) / 4) * 1024 + (16 c + 4 (t / 32) + t % 4) * 16
+ *     scale byte: 8192 + (g / 2) * 256 + (t / 32) * 64 + (t % 4) * 16 + ((t % 32) / 4) * 2 + g % 2
+ *
+ *   V pages ("column-operand" layout, one element runs along the tokens):
+ *     code byte holding tokens t and t+1 (t even; t in the low nibble) of element e:
+ *         e * 64 + t / 2
+ *     scale byte: 8192 + g * 128 + t
+ *
+ * These orders let each 64-lane wavefront load, with single 16-byte loads, exactly the
+ * operands of its matrix-core instructions. Bytes of a page that no insert touched are left
+ * as the caller initialized them (zero-initialize pools to read absent tokens as 0).
+ */
+typedef struct {
+    uint8_t *k;
+    uint8_t *v;
+    uint8_t *ik;
+    int64_t num_pages;
+} msa_cache_t;
+
+/*
+ * A decode batch.
+ *   block_table : device int32 [batch][max_blocks]; entry (b, i) = page id of logical block i
+ *                 of sequence b (entries past the sequence are never read; use -1).
+ *   ctx_lens    : device int32 [batch]; T_b (tokens in the cache, query tokens included).
+ *   q_len       : query tokens per sequence, uniform across the batch (1 for plain decode,
+ *                 the draft length for speculative verify, the chunk length for prefill).
+ */
+typedef struct {
+    const int32_t *block_table;
+    const int32_t *ctx_lens;
+    int32_t batch;
+    int32_t max_blocks;
+    int32_t q_len;
+} msa_batch_t;
+
+/* Bytes of one page of pool `which` (0 = K, 1 = V, 2 = index keys). 0 for other values. */
+size_t msa_page_bytes(int which);
+
+/*
+ * NVFP4-quantize n tokens and write them into their cache slots. ("vLLM day-0 support for
+ * MiniMax-M3.1-Flash", section "QKV GEMM + norm + RoPE + KV insert fusion": K, V and the
+ * index key are quantized to NVFP4 as they are written to their caches.)
+ *   slots : device int64 [n]; slot = page * 128 + token offset in the page. A negative slot or
+ *           one whose page is outside [0, num_pages) skips that token. Slots must be distinct
+ *           within one call (two tokens in one slot race).
+ *   k, v  : device fp32 [n][4][128]; ik : device fp32 [n][128]. Any of the three may be NULL
+ *           to leave that pool untouched.
+ * Quantization of each 16-element group x[0..15] (bit-exact, fp32 as stated):
+ *   s32 = max|x| / 6 (IEEE fp32 division); scale = E4M3 round-to-nearest-even of s32,
+ *   saturating at 448; s = value of scale; magnitude of x_i = E2M1 nearest-even of the fp32
+ *   quotient |x_i| / s (0 if s == 0, saturating at 6); sign bit = sign bit of x_i.
+ *   Non-finite inputs give unspecified codes.
+ * n == 0 is a no-op. Errors: MSA_ERR_INVALID_ARG (cache or slots NULL, n < 0,
+ * num_pages < 1, all three value pointers NULL).
+ */
+int msa_kv_insert_nvfp4(const msa_cache_t *cache, const int64_t *slots, const float *k,
+                        const float *v, const float *ik, int32_t n, void *stream);
+
+/*
+ * Indexer: block scores ("vLLM day-0 support for MiniMax-M3.1-Flash", section "MSA primer";
+ * "MiniMax M3 on vLLM", section "Decode indexer score kernel").
+ *   q_idx        : device bf16 [batch * q_len][4][128]; row (b * q_len + j, g) is the index
+ *                  query of group g for query token j of sequence b.
+ *   block_scores : device fp32 [batch * q_len][4][max_blocks], written in full:
+ *                  score(b, j, g, i) = max over tokens t of block i with t <= p and t < T_b of
+ *                  sum_d q_idx[d] * ik_t[d] (exact NVFP4 values, fp32 accumulation);
+ *                  -inf when the block holds no such token or its page id is out of range.
+ * Errors: MSA_ERR_INVALID_ARG (NULL pointers, batch/max_blocks/q_len < 1).
+ */
+int msa_indexer_score(const msa_cache_t *cache, const msa_batch_t *batch, const uint16_t *q_idx,
+                      float *block_scores, void *stream);
+
+/*
+ * Block selection ("vLLM day-0 support for MiniMax-M3.1-Flash", section "MSA primer"; "MiniMax
+ * M3 on vLLM", section "MSA mechanism": local_blocks = 1, init_blocks = 0, the local block is
+ * not counted twice). For each row (b, j, g): the eligible blocks are 0..f with
+ * f = min(p / 128, max_blocks - 1); block f (the block of the query token) is always kept.
+ * If at most `topk` blocks are eligible, all are kept; otherwise f and the best topk - 1 of
+ * blocks 0..f-1 by (score descending, block index ascending).
+ *   block_ids : device int32 [batch * q_len][4][topk], ascending block ids, padded with -1.
+ * Scores must not be NaN. Rows whose token has p < 0 get all -1.
+ * Errors: MSA_ERR_INVALID_ARG (NULL pointers, sizes < 1), MSA_ERR_UNSUPPORTED (topk != 16).
+ */
+int msa_block_topk(const float *block_scores, const msa_batch_t *batch, int32_t topk,
+                   int32_t *block_ids, void *stream);
+
+/* Workspace bytes msa_sparse_attn_decode needs for this batch shape (may be 0). */
+size_t msa_sparse_attn_workspace_bytes(const msa_batch_t *batch);
+
+/*
+ * Sparse GQA attention over the selected blocks ("vLLM day-0 support for MiniMax-M3.1-Flash",
+ * section "MSA primer" and its Figure 1; "MiniMax M3 on vLLM", sections "MiniMax sparse
+ * attention backend" (the decode GQA kernel reads the selected pages and merges partial
+ * outputs) and "Prefill execution" (the result equals dense attention restricted to the
+ * selected set)).
+ *   q         : device bf16 [batch * q_len][64][128]
+ *   block_ids : device int32 [batch * q_len][4][16] as msa_block_topk writes them (-1 skipped)
+ *   out       : device bf16 [batch * q_len][64][128]:
+ *               out(b, j, h) = sum_t softmax_t(softmax_scale * q . k_t) v_t over the tokens t of
+ *               the selected blocks of (b, j, h / 16) with t <= p, t < T_b (exact NVFP4 values;
+ *               fp32 softmax and accumulation); 0 when no key is valid.
+ *   workspace : device scratch of at least msa_sparse_attn_workspace_bytes(batch) bytes
+ *               (may be NULL when that is 0), 256-byte aligned.
+ * Errors: MSA_ERR_INVALID_ARG (NULL pointers, sizes < 1), MSA_ERR_WORKSPACE.
+ */
+int msa_sparse_attn_decode(const msa_cache_t *cache, const msa_batch_t *batch, const uint16_t *q,
+                           const int32_t *block_ids, float softmax_scale, uint16_t *out,
+                           void *workspace, size_t ws_bytes, void *stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *msa_last_error(void);
+
+/* Library version string. */
+const char *msa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H */

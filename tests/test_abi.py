@@ -1,0 +1,97 @@
+"""Host checks of the C ABI: libmsa.so loads without a GPU, exports every entry point that
+include/msa.h declares, and rejects invalid arguments before launching anything."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+LIB = os.path.join(ROOT, "block_sparse_attention_nvfp4_amd", "libmsa.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def msa():
+    if not os.path.exists(LIB):
+        from block_sparse_attention_nvfp4_amd import build
+        build.build()
+    import block_sparse_attention_nvfp4_amd as m
+    return m
+
+
+def test_header_declares_the_path(msa):
+    fns = declared_functions()
+    for f in ("msa_kv_insert_nvfp4", "msa_indexer_score", "msa_block_topk", "msa_sparse_attn_decode"):
+        assert f in fns
+    assert set(fns) == set(msa.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(msa):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (msa_[a-z0-9_]+)$", out, flags=re.M))
+    missing = set(declared_functions()) - exported
+    assert not missing, missing
+    for f in declared_functions():
+        assert hasattr(msa.lib, f)
+
+
+def test_constants_and_version(msa):
+    assert msa.msa_page_bytes(0) == 4 * 9216 == msa.msa_page_bytes(1)
+    assert msa.msa_page_bytes(2) == 9216 and msa.msa_page_bytes(7) == 0
+    assert "gfx950" in msa.msa_version()
+    # 72 B per 128-element vector: 4.5 bits per element
+    assert 9216 / 128 == 72 and 72 * 8 / 128 == 4.5
+
+
+def _cache(k=1, v=1, ik=1, pages=4):
+    import block_sparse_attention_nvfp4_amd as m
+    return m._Cache(k, v, ik, pages)
+
+
+def _batch(bt=1, cl=1, b=1, mb=1, q=1):
+    import block_sparse_attention_nvfp4_amd as m
+    return m._Batch(bt, cl, b, mb, q)
+
+
+def test_invalid_arguments_return_codes_without_launch(msa):
+    L = msa.lib
+    by = ctypes.byref
+    # insert
+    assert L.msa_kv_insert_nvfp4(None, 1, 1, 1, 1, 1, None) == msa.MSA_ERR_INVALID_ARG
+    assert L.msa_kv_insert_nvfp4(by(_cache()), None, 1, 1, 1, 1, None) == msa.MSA_ERR_INVALID_ARG
+    assert L.msa_kv_insert_nvfp4(by(_cache()), 1, None, None, None, 1, None) == msa.MSA_ERR_INVALID_ARG
+    assert L.msa_kv_insert_nvfp4(by(_cache()), 1, 1, 1, 1, -1, None) == msa.MSA_ERR_INVALID_ARG
+    assert L.msa_kv_insert_nvfp4(by(_cache(pages=0)), 1, 1, 1, 1, 1, None) == msa.MSA_ERR_INVALID_ARG
+    assert L.msa_kv_insert_nvfp4(by(_cache(k=None)), 1, 1, None, None, 1, None) == msa.MSA_ERR_INVALID_ARG
+    assert "NULL" in msa.msa_last_error()
+    assert L.msa_kv_insert_nvfp4(by(_cache()), 1, 1, 1, 1, 0, None) == msa.MSA_OK  # n = 0: no-op
+    # indexer
+    assert L.msa_indexer_score(by(_cache(ik=None)), by(_batch()), 1, 1, None) == msa.MSA_ERR_INVALID_ARG
+    assert L.msa_indexer_score(by(_cache()), by(_batch(q=0)), 1, 1, None) == msa.MSA_ERR_INVALID_ARG
+    assert L.msa_indexer_score(by(_cache()), by(_batch(bt=None)), 1, 1, None) == msa.MSA_ERR_INVALID_ARG
+    assert L.msa_indexer_score(by(_cache()), by(_batch()), None, 1, None) == msa.MSA_ERR_INVALID_ARG
+    assert L.msa_indexer_score(by(_cache()), by(_batch(b=70000)), 1, 1, None) == msa.MSA_ERR_INVALID_ARG
+    # top-k
+    assert L.msa_block_topk(1, by(_batch()), 8, 1, None) == msa.MSA_ERR_UNSUPPORTED
+    assert "topk" in msa.msa_last_error()
+    assert L.msa_block_topk(None, by(_batch()), 16, 1, None) == msa.MSA_ERR_INVALID_ARG
+    assert L.msa_block_topk(1, by(_batch(mb=0)), 16, 1, None) == msa.MSA_ERR_INVALID_ARG
+    # attention
+    small = by(_batch(b=1, q=1))
+    need = L.msa_sparse_attn_workspace_bytes(small)
+    assert need > 0
+    assert L.msa_sparse_attn_decode(by(_cache()), small, 1, 1, 0.1, 1, None, 0, None) == msa.MSA_ERR_WORKSPACE
+    assert L.msa_sparse_attn_decode(by(_cache()), small, 1, 1, 0.1, 1, 256, need - 1, None) == msa.MSA_ERR_WORKSPACE
+    assert L.msa_sparse_attn_decode(by(_cache()), small, 1, 1, 0.1, 1, 257, need, None) == msa.MSA_ERR_WORKSPACE
+    assert L.msa_sparse_attn_decode(by(_cache(v=None)), small, 1, 1, 0.1, 1, 256, need, None) == msa.MSA_ERR_INVALID_ARG
+    assert L.msa_sparse_attn_decode(by(_cache()), small, None, 1, 0.1, 1, 256, need, None) == msa.MSA_ERR_INVALID_ARG
+    # large batches need no workspace (one workgroup per row group covers the chip)
+    assert L.msa_sparse_attn_workspace_bytes(by(_batch(b=256, q=1))) == 0
