@@ -1,0 +1,313 @@
+"""MSA decode benchmark on one MI355X: query-tokens/s per layer at 128K context.
+
+Workload (the headline configuration): batch 8, context 131,072 tokens (1,024 blocks of 128),
+4 query tokens per sequence (speculative verify, causal within the last block), 64 query heads,
+4 KV heads, head_dim 128, NVFP4 K/V/index-key caches in 128-token pages under a random page
+permutation, top-16 selection. Synthetic, seeded data (msa_inputs, recipe 3).
+
+A step is one layer's whole decode path: NVFP4 insert of the step's 32 new tokens, indexer over
+the full context, block top-16, sparse attention (+ split-K combine). Each step runs on the next
+of L layers whose caches live in separate memory, so the index-key working set (L x 75.5 MB)
+exceeds the 256 MB Infinity Cache and the scan streams from HBM, as a multi-layer decode does.
+Each layer's step is captured once in a HIP graph; the timed region replays K steps.
+
+Kernel durations for the roofline come from HIP events around graphs of L back-to-back launches
+of one kernel (one per layer), recorded on the stream the kernels run on.
+
+Output: one JSON line (see the keys below). --gpus N > 1 exits: this build runs on one GPU.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+METRIC = "MSA decode query-tokens/s per layer at 128K ctx; achieved HBM GB/s vs peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--kernel-reps", type=int, default=20, help="graph replays per kernel timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle CPU time")
+    ap.add_argument("--only", default="", help="profiling aid: run only this kernel in a loop "
+                                               "(insert|indexer|topk|attention) and exit")
+    return ap.parse_args()
+
+
+def source_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "block_sparse_attention_nvfp4_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, digest):
+    """HBM bytes per launch measured with rocprofv3 counters for this exact kernel source, if any."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_spec128k_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the MSA decode path "
+              "here is single-GPU, see DESIGN.md for how it would shard.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_nvfp4_amd as msa
+    import msa_inputs as mi
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    w = mi.make_workload(3)
+    B, q, T = w.batch, w.q_len, w.ctx_lens[0]
+    L = args.layers
+    t_setup = time.time()
+
+    # ---------------------------------------------------------------- caches (layer 0 built
+    # from the generator through the insert kernel; layers 1..L-1 are copies in their own memory)
+    cache0 = msa.Cache.allocate(w.num_pages, dev)
+    chunk = 1 << 15
+    for b in range(B):
+        for t0 in range(0, T - q, chunk):
+            t1 = min(T - q, t0 + chunk)
+            slots = torch.from_numpy(w.slots(b, t0, t1)).to(dev)
+            msa.msa_kv_insert_nvfp4(cache0, slots, w.kv_rows("k", b, t0, t1, dev),
+                                    w.kv_rows("v", b, t0, t1, dev), w.ik_rows(b, t0, t1, dev))
+    caches = [cache0] + [msa.Cache(cache0.k.clone(), cache0.v.clone(), cache0.ik.clone())
+                         for _ in range(L - 1)]
+    table = torch.from_numpy(w.block_table).to(dev)
+    ctx = torch.tensor(w.ctx_lens, dtype=torch.int32, device=dev)
+    batch = msa.Batch(table, ctx, q)
+    toks = [(b, T - q, T) for b in range(B)]
+    new_slots = torch.from_numpy(np.concatenate([w.slots(b, t0, t1) for b, t0, t1 in toks])).to(dev)
+    new_k = torch.cat([w.kv_rows("k", b, t0, t1, dev) for b, t0, t1 in toks])
+    new_v = torch.cat([w.kv_rows("v", b, t0, t1, dev) for b, t0, t1 in toks])
+    new_ik = torch.cat([w.ik_rows(b, t0, t1, dev) for b, t0, t1 in toks])
+    q_idx, qq = w.q_idx.to(dev), w.q.to(dev)
+    steps = [msa.DecodeStep(c, batch, dev) for c in caches]
+    scale = msa.default_softmax_scale()
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+    print(f"# setup {setup_s:.1f}s: {L} layers x {w.num_pages} pages, "
+          f"{torch.cuda.memory_allocated() / 2**30:.2f} GiB allocated", file=sys.stderr, flush=True)
+
+    calls = {
+        "insert": lambda s: msa.msa_kv_insert_nvfp4(s.cache, new_slots, new_k, new_v, new_ik),
+        "indexer": lambda s: msa.msa_indexer_score(s.cache, batch, q_idx, s.block_scores),
+        "topk": lambda s: msa.msa_block_topk(s.block_scores, batch, 16, s.block_ids),
+        "attention": lambda s: msa.msa_sparse_attn_decode(s.cache, batch, qq, s.block_ids, scale,
+                                                          s.out, s.workspace),
+    }
+
+    def full_step(s):
+        for name in ("insert", "indexer", "topk", "attention"):
+            calls[name](s)
+
+    # eager warmup (also fills every layer's scores/ids used by single-kernel timings)
+    for s in steps:
+        full_step(s)
+    torch.cuda.synchronize()
+
+    if args.only:
+        # profiling aid: the chosen kernel alone, L launches per round, no graphs
+        for _ in range(args.kernel_reps):
+            for s in steps:
+                calls[args.only](s)
+        torch.cuda.synchronize()
+        print(f"# ran {args.kernel_reps * L} launches of {args.only}", file=sys.stderr)
+        return
+
+    stream = torch.cuda.Stream()
+    # ---------------------------------------------------------------- graphs
+    with torch.cuda.stream(stream):
+        graphs = []
+        for s in steps:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                full_step(s)
+            graphs.append(g)
+        kgraphs = {}
+        for name in calls:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for s in steps:
+                    calls[name](s)
+            kgraphs[name] = g
+    torch.cuda.synchronize()
+
+    # ---------------------------------------------------------------- timed steps
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            graphs[i % L].replay()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for i in range(args.steps):
+            graphs[i % L].replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        dev_ms = ev0.elapsed_time(ev1)
+
+        # per-kernel durations: graphs of L back-to-back launches, HIP events around each replay
+        kernel_us = {}
+        for name, g in kgraphs.items():
+            g.replay()
+            torch.cuda.synchronize()
+            es, ee = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            es.record(stream)
+            for _ in range(args.kernel_reps):
+                g.replay()
+            ee.record(stream)
+            torch.cuda.synchronize()
+            kernel_us[name] = es.elapsed_time(ee) * 1e3 / (args.kernel_reps * L)
+
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_per_step = B * q
+    value = tokens_per_step / (ms_per_step * 1e-3)
+
+    # algorithmic bytes per launch of the indexer (the dominant kernel): every index-key byte of
+    # the context (72 B per token), the index queries, and the block scores it writes
+    sum_T = sum(w.ctx_lens)
+    idx_bytes = sum_T * 72 + B * q * 4 * 128 * 2 + B * q * 4 * w.max_blocks * 4
+    idx_gbs = idx_bytes / (kernel_us["indexer"] * 1e-6) / 1e9
+    digest = source_digest("indexer.hip", "device_common.hpp")
+    traffic = load_traffic("indexer", digest)
+
+    # gather bytes of the attention: K+V of each selected (sequence, group, block) once per
+    # distinct block over the 4 draft tokens (144 B per valid token), queries and outputs
+    ids = steps[0].block_ids.cpu().numpy().reshape(B, q, 4, 16)
+    gathered_tokens = 0
+    for b in range(B):
+        for g in range(4):
+            for blk in set(int(x) for x in ids[b, :, g].ravel() if x >= 0):
+                gathered_tokens += min(128, T - blk * 128)
+    attn_bytes = gathered_tokens * 144 + 2 * B * q * 64 * 128 * 2 + B * q * 4 * 16 * 4
+    attn_gbs = attn_bytes / (kernel_us["attention"] * 1e-6) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "spec128k: batch 8 x context 131072 tokens, 4 query tokens each "
+                        "(speculative verify), 64 q heads / 4 kv heads / head_dim 128, "
+                        "NVFP4 K/V/index caches, 128-token pages, top-16",
+            "batch": B, "context": T, "query_tokens": q, "cache_dtype": "nvfp4",
+            "layers_rotated": L, "step_graph": True,
+            "device_ms_per_step": round(dev_ms / args.steps, 5),
+        },
+        "kernels_us": {k: round(v, 3) for k, v in kernel_us.items()},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "indexer",
+            "achieved": round(idx_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(idx_gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes": idx_bytes,
+        },
+        "attention_gather": {"achieved_gbs": round(attn_gbs, 1), "frac": round(attn_gbs / PEAK_HBM_GBS, 4),
+                             "algorithmic_bytes": attn_bytes},
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, target_seconds):
+    """The oracle (single-threaded, fp64) on whole sequences of the same workload: quantize the
+    step's new tokens, score every index key, select, attend. Cache quantization of the
+    already-cached context is setup and untimed."""
+    import numpy as np
+
+    import msa_inputs as mi
+    import oracle
+
+    q = w.q_len
+    done_tokens, spent, seqs = 0, 0.0, 0
+    for b in range(w.batch):
+        T = w.ctx_lens[b]
+        ik = w.ik_rows(b, 0, T).numpy()
+        ikc, iks = oracle.quantize(ik[:T - q])
+        qi = mi.bf16_bits(w.q_idx[b * q:(b + 1) * q])
+        qb = mi.bf16_bits(w.q[b * q:(b + 1) * q])
+        # untimed: which K/V blocks the attention will read, quantized ahead as cache contents
+        pre_c, pre_s = oracle.quantize(ik[T - q:])
+        ids0, _ = oracle.select_sequence(
+            oracle.index_scores(qi, np.concatenate([ikc, pre_c]), np.concatenate([iks, pre_s]),
+                                T, q, w.max_blocks), T, q)
+        blocks = sorted(set(int(x) for x in ids0.ravel() if x >= 0))
+        kc = np.zeros((T, 4, 64), np.uint8)
+        ks = np.zeros((T, 4, 8), np.uint8)
+        vc, vs = np.zeros_like(kc), np.zeros_like(ks)
+        for blk in blocks:
+            t0, t1 = blk * 128, min(T - q, blk * 128 + 128)
+            if t1 > t0:
+                kc[t0:t1], ks[t0:t1] = oracle.quantize(w.kv_rows("k", b, t0, t1).numpy())
+                vc[t0:t1], vs[t0:t1] = oracle.quantize(w.kv_rows("v", b, t0, t1).numpy())
+        new_ik = ik[T - q:]
+        new_k = w.kv_rows("k", b, T - q, T).numpy()
+        new_v = w.kv_rows("v", b, T - q, T).numpy()
+        t0 = time.perf_counter()
+        c, s = oracle.quantize(new_ik)                                        # insert
+        kc[T - q:], ks[T - q:] = oracle.quantize(new_k)
+        vc[T - q:], vs[T - q:] = oracle.quantize(new_v)
+        full_c, full_s = np.concatenate([ikc, c]), np.concatenate([iks, s])
+        scores = oracle.index_scores(qi, full_c, full_s, T, q, w.max_blocks)  # indexer
+        ids, _ = oracle.select_sequence(scores, T, q)                          # top-k
+        for j in range(q):                                                    # attention
+            oracle.sparse_attention_token(qb[j], kc, ks, vc, vs, T, ids[j], T - q + j,
+                                          oracle.default_scale())
+        spent += time.perf_counter() - t0
+        done_tokens += q
+        seqs += 1
+        if spent >= target_seconds:
+            break
+    return {
+        "value": round(done_tokens / spent, 3),
+        "unit": "query-tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{seqs} of {w.batch} sequences of the same workload (full 131072-token context, "
+                  f"{q} query tokens each); {spent:.1f} s single-threaded; cache quantization of "
+                  "the context untimed",
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -25,6 +25,7 @@ constexpr int kCodeBytes = 8192;   // E2M1 codes of one head page
 constexpr int kHeadPageBytes = 9216;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -101,9 +102,71 @@ __device__ __forceinline__ f16x4 dequant4_f16_percode(uint32_t w, uint32_t sw) {
     return r;
 }
 
+// Eight E2M1 codes (one 32-bit word) times the scale pair {s, s} -> eight fp16 values, exact
+// (see dequant4_f16_percode): the conversion gives the unscaled E2M1 values, one packed fp16
+// multiply per pair applies the E4M3 scale.
+__device__ __forceinline__ f16x8 dequant8_f16(uint32_t w, f16x2 ss) {
+    const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
+    const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
+    const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
+    const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
+    return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// Two E4M3 scale bytes (byte pair HI of `w`) -> fp16 pairs {s0, s0} and {s1, s1} (exact).
+template <bool HI>
+__device__ __forceinline__ void e4m3_pair_f16(uint32_t w, f16x2& s0, f16x2& s1) {
+    const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+    const _Float16 a = (_Float16)f[0], b = (_Float16)f[1];
+    s0 = f16x2{a, a};
+    s1 = f16x2{b, b};
+}
+
+// Query operands in fp16. A query row (one index query, or one attention head) of 128 bf16
+// values is spread over the four lanes n, n+16, n+32, n+48 (32 values each, as 4 x bf16x8).
+// Multiplying the row by 2^k (k chosen so the row's largest magnitude lands in [2^14, 2^15))
+// keeps every value of a usual row exactly representable in fp16; the caller then divides the
+// fp32 result by 2^k, which is exact. Returns false on any lane whose values did not convert
+// exactly (the caller keeps the bf16 path for that wavefront).
+__device__ __forceinline__ bool query_to_f16(const bf16x8 (&qb)[4], f16x8 (&qh)[4], float& inv_scale) {
+    float mx = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; m++)
+#pragma unroll
+        for (int i = 0; i < 8; i++) mx = fmaxf(mx, fabsf((float)qb[m][i]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    int e = 0;
+    if (mx > 0.f) (void)frexpf(mx, &e);  // mx in [2^(e-1), 2^e)
+    const int k = 15 - e;
+    inv_scale = ldexpf(1.0f, -k);
+    bool exact = inv_scale > 0.f;  // k beyond the fp32 range: keep the bf16 path
+#pragma unroll
+    for (int m = 0; m < 4; m++)
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const float f = ldexpf((float)qb[m][i], k);  // exact: no intermediate 2^k
+            const _Float16 h = (_Float16)f;
+            exact = exact && ((float)h == f);
+            qh[m][i] = h;
+        }
+    return exact;
+}
+
+// Exact fp16 -> bf16 of eight dequantized values (E2M1 x E4M3 products fit both formats).
+__device__ __forceinline__ bf16x8 f16x8_to_bf16x8(const f16x8& h) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; i++) r[i] = (__bf16)(float)h[i];
+    return r;
+}
+
 // ---------------------------------------------------------------- matrix cores
 __device__ __forceinline__ f32x4 mfma_bf16_k32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f16_k32(const f16x8& a, const f16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 mfma_f16_k16(const f16x4& a, const f16x4& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
