@@ -8,16 +8,22 @@
 // kernel consumes the selected block pages and merges partial attention outputs; section
 // "Prefill execution": the result equals dense attention restricted to the selected set.
 //
-// Per workgroup: one row group (sequence b, query token j, KV group g) = 16 query heads, and a
-// share of its 16 selected blocks; 4 wavefronts, each takes whole blocks.
+// Work: a row group is (sequence b, query token j, KV group g) = 16 query heads with its 16
+// selected blocks. Each workgroup (4 wavefronts) takes 16 / n_split of them; each wavefront
+// streams whole blocks: the K and V pages of a block are copied into the wavefront's LDS
+// buffer with direct global->LDS loads (the next block's while the current one computes).
 // Per block and wavefront (lane l, n = l % 16, c = l / 16):
-//   S^T = K Q^T on bf16 matrix cores (A = keys, exact dequantized; B = the 16 heads), so lane
-//   (n, c) holds the logits of head n for tokens 32c + 4s + i (slab s, i = 0..3);
-//   fp32 online softmax per head (running max and sum), probabilities in fp16;
-//   O^T += V^T P^T on fp16 matrix cores: P^T in the same lanes is already the B operand, V^T
+//   S^T = K Q^T on the matrix cores (A = keys dequantized exactly to fp16, B = the 16 heads as
+//   fp16 after a per-head power-of-two scaling, or bf16 when a head does not convert exactly),
+//   so lane (n, c) holds the logits of head n for tokens 32c + 4s + i (slab s, i = 0..3);
+//   fp32 online softmax per head, probabilities in fp16;
+//   O^T += V^T P^T on fp16 matrix cores: P^T in the same lanes is already the B operand and V^T
 //   (A operand, dims x tokens) is the exact fp16 dequantization of the column-layout V page.
-// The 4 wavefronts merge through LDS; with one split the workgroup writes bf16 output,
-// otherwise it writes an fp32 partial (max, sum, output) that the combine kernel merges.
+// The wavefronts merge through LDS. With one split the workgroup writes the bf16 output;
+// otherwise it writes an fp32 partial (max, sum, output) and a second kernel merges the splits
+// of each row group. Workgroup ids of both kernels map all work of one (sequence, group) pair
+// to one XCD, so the blocks that the query tokens of a pair share are read from HBM once and
+// then hit that XCD's L2, and the merge finds the partials in the same L2.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -26,124 +32,236 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kPartStride = 132;  // floats per (row group, split, head): m, l, 2 pad, 128 out
+constexpr int kBlockBytes = 2 * kHeadPageBytes;  // K page then V page of one (block, group)
+constexpr int kMergeStride = kDim + 4;           // LDS row of the wavefront merge
+constexpr int kNonTemporal = 2;                  // cache-policy bits of the page loads
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ uint16_t bf16_bits_rne(float x) {
     const __bf16 h = (__bf16)x;
     return __builtin_bit_cast(uint16_t, h);
 }
 
+// Copy the K and V pages of one (block, group) into an LDS buffer: 18 direct 16-byte loads.
+__device__ __forceinline__ void block_to_lds(const uint8_t* kp, const uint8_t* vp, uint8_t* buf,
+                                             int lane) {
+#pragma unroll
+    for (int s = 0; s < 9; s++)
+        __builtin_amdgcn_global_load_lds(kp + s * 1024 + lane * 16, (lds_void*)(buf + s * 1024), 16,
+                                         0, kNonTemporal);
+#pragma unroll
+    for (int s = 0; s < 9; s++)
+        __builtin_amdgcn_global_load_lds(vp + s * 1024 + lane * 16,
+                                         (lds_void*)(buf + kHeadPageBytes + s * 1024), 16, 0,
+                                         kNonTemporal);
+}
+
+// LDS reads as explicit instructions: the compiler would otherwise wait for every page load in
+// flight before any LDS read. The waits below make the results available.
+__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+template <typename T>
+__device__ __forceinline__ void lds_wait(T& v) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v));
+}
+
+// One block of one wavefront: logits, online-softmax update, output accumulation.
+template <bool F16>
+__device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c, int tok0, int p,
+                                             const u32x4 (&qop)[4], float logit_scale,
+                                             float& m_run, float& l_run, f32x4 (&o)[8]) {
+    const uint32_t kbase = (uint32_t)(uintptr_t)buf;
+    const uint32_t vbase = kbase + kHeadPageBytes;
+    // ---- logits S^T (log2 domain)
+    u32x4 kc[8];
+#pragma unroll
+    for (int s = 0; s < 8; s++) kc[s] = lds_read16(kbase + s * 1024 + lane * 16);
+    u32x4 ksc = lds_read16(kbase + kCodeBytes + lane * 16);
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(kc[0]), "+v"(kc[1]), "+v"(kc[2]), "+v"(kc[3]), "+v"(kc[4]), "+v"(kc[5]),
+                   "+v"(kc[6]), "+v"(kc[7]), "+v"(ksc));
+    f32x4 sv[8];
+#pragma unroll
+    for (int s = 0; s < 8; s++) {
+        const u32x4 code = kc[s];
+        f16x2 s0, s1;
+        if (s & 1) e4m3_pair_f16<true>(ksc[s >> 1], s0, s1);
+        else e4m3_pair_f16<false>(ksc[s >> 1], s0, s1);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 4; m++) {
+            const f16x8 a = dequant8_f16(code[m], m < 2 ? s0 : s1);
+            if constexpr (F16)
+                acc = mfma_f16_k32(a, __builtin_bit_cast(f16x8, qop[m]), acc);
+            else
+                acc = mfma_bf16_k32(f16x8_to_bf16x8(a), __builtin_bit_cast(bf16x8, qop[m]), acc);
+        }
+        sv[s] = acc * logit_scale;
+    }
+    const bool full = tok0 + kBlock - 1 <= p;
+    float mb = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < 8; s++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            if (!full && tok0 + 32 * c + 4 * s + i > p) sv[s][i] = -INFINITY;
+            mb = fmaxf(mb, sv[s][i]);
+        }
+    mb = max_over_c(mb);  // finite: token tok0 <= p is valid
+    const float m_new = fmaxf(m_run, mb);
+    const float alpha = exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++) o[dt] *= alpha;
+    float ls = 0.f;
+    f16x4 pt[8];
+#pragma unroll
+    for (int s = 0; s < 8; s++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float e = exp2f(sv[s][i] - m_new);
+            ls += e;
+            pt[s][i] = (_Float16)e;
+        }
+    l_run += sum_over_c(ls);
+    m_run = m_new;
+
+    // ---- O^T += V^T P^T, one 16-dim tile (= one scale group) at a time
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++) {
+        const int d = 16 * dt + (lane & 15);
+        u32x4 vc = lds_read16(vbase + d * 64 + 16 * c);                    // tokens 32c..32c+31
+        u32x4 vs0 = lds_read16(vbase + kCodeBytes + dt * 128 + 32 * c);       // scales, tokens 32c..+15
+        u32x4 vs1 = lds_read16(vbase + kCodeBytes + dt * 128 + 32 * c + 16);  // tokens 32c+16..+31
+        lds_wait(vc);
+        lds_wait(vs0);
+        lds_wait(vs1);
+#pragma unroll
+        for (int s = 0; s < 8; s++) {
+            const uint32_t sw = s < 4 ? vs0[s] : vs1[s - 4];  // tokens 32c + 4s .. +3
+            const f16x4 a = (s & 1) ? dequant4_f16_percode<2>(vc[s >> 1], sw)
+                                    : dequant4_f16_percode<0>(vc[s >> 1], sw);
+            o[dt] = mfma_f16_k16(a, pt[s], o[dt]);
+        }
+    }
+}
+
 template <int BPW>
 __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
     const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool, int64_t num_pages,
-    const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens, int max_blocks,
-    int q_len, const uint16_t* __restrict__ q, const int32_t* __restrict__ block_ids,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens, int batch,
+    int max_blocks, int q_len, const uint16_t* __restrict__ q, const int32_t* __restrict__ block_ids,
     float scale_log2, int n_split, uint16_t* __restrict__ out, float* __restrict__ partials) {
-    __shared__ float sh_o[kWaves][kGroupHeads][kDim + 4];
+    constexpr int kBufs = BPW > 1 ? 2 : 1;
+    static_assert(kWaves * kBufs * kBlockBytes >= kWaves * kGroupHeads * kMergeStride * 4,
+                  "merge area must fit in the page buffers");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves][kBufs][kBlockBytes];
     __shared__ float sh_m[kWaves][kGroupHeads];
     __shared__ float sh_l[kWaves][kGroupHeads];
+    __shared__ int sh_ids[kWaves][BPW];
+    __shared__ int sh_pages[kWaves][BPW];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int n = lane & 15;
     const int c = lane >> 4;
-    const int rg = blockIdx.x / n_split;  // row group ((b * q_len + j) * 4 + g)
-    const int split = blockIdx.x - rg * n_split;
-    const int g = rg & 3;
-    const int bq = rg >> 2;
-    const int b = bq / q_len;
-    const int j = bq - b * q_len;
+    // XCD-aware work mapping: pair = (b, g) -> XCD pair % 8
+    const int per_pair = q_len * n_split;
+    const int local = blockIdx.x >> 3;
+    const int pair = (local / per_pair) * 8 + (blockIdx.x & 7);
+    if (pair >= batch * kKvHeads) return;
+    const int within = local - (local / per_pair) * per_pair;
+    const int j = within / n_split;
+    const int split = within - j * n_split;
+    const int b = pair >> 2;
+    const int g = pair & 3;
+    const int bq = b * q_len + j;
+    const int rg = bq * kKvHeads + g;  // row group
     const int T = clamp_ctx(ctx_lens[b], max_blocks);
     const int p = T - q_len + j;
 
-    // B operand of S^T: head 16g + n, dims 32c + 8m .. +7
-    bf16x8 qop[4];
-    {
-        const uint16_t* qp = q + ((int64_t)bq * kQHeads + kGroupHeads * g + n) * kDim + 32 * c;
-#pragma unroll
-        for (int m = 0; m < 4; m++) qop[m] = *reinterpret_cast<const bf16x8*>(qp + 8 * m);
+    // this wavefront's blocks (id and page, or -1 when the id is not selected, has no visible
+    // token or maps to a page out of range), read once: a table load issued between page loads
+    // would make the in-order memory counter wait for every page in flight
+    const int32_t* my_ids = block_ids + (int64_t)rg * kTopk + (split * kWaves + wave) * BPW;
+    if (lane < BPW) {
+        const int id = my_ids[lane];
+        int page = -1;
+        if (id >= 0 && id < max_blocks && id * kBlock <= p) {
+            const int pg = block_table[(int64_t)b * max_blocks + id];
+            page = (pg >= 0 && pg < num_pages) ? pg : -1;
+        }
+        sh_ids[wave][lane] = page >= 0 ? id : -1;
+        sh_pages[wave][lane] = page;
     }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 
     float m_run = -INFINITY, l_run = 0.f;
     f32x4 o[8];
 #pragma unroll
     for (int dt = 0; dt < 8; dt++) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int32_t* my_ids = block_ids + (int64_t)rg * kTopk + (split * kWaves + wave) * BPW;
-    for (int kb = 0; kb < BPW; kb++) {
-        const int id = my_ids[kb];
-        if (id < 0 || id >= max_blocks || id * kBlock > p) continue;
-        const int page = block_table[(int64_t)b * max_blocks + id];
-        if (page < 0 || page >= num_pages) continue;
-        const uint8_t* kp = k_pool + ((int64_t)page * kKvHeads + g) * kHeadPageBytes;
-        const uint8_t* vp = v_pool + ((int64_t)page * kKvHeads + g) * kHeadPageBytes;
-
-        // ---- logits S^T (log2 domain)
-        u32x4 kc[8];
-#pragma unroll
-        for (int s = 0; s < 8; s++) kc[s] = load16(kp + s * 1024 + lane * 16);
-        const u32x4 ksc = load16(kp + kCodeBytes + lane * 16);
-        f32x4 sv[8];
-#pragma unroll
-        for (int s = 0; s < 8; s++) {
-            const f32x2 s2 = (s & 1) ? e4m3_pair_f32<true>(ksc[s >> 1])
-                                     : e4m3_pair_f32<false>(ksc[s >> 1]);
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int m = 0; m < 4; m++)
-                acc = mfma_bf16_k32(dequant8_bf16(kc[s][m], s2[m >> 1]), qop[m], acc);
-            sv[s] = acc * scale_log2;
-        }
-        const int tok0 = id * kBlock;
-        const bool full = tok0 + kBlock - 1 <= p;
-        float mb = -INFINITY;
-#pragma unroll
-        for (int s = 0; s < 8; s++)
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                if (!full && tok0 + 32 * c + 4 * s + i > p) sv[s][i] = -INFINITY;
-                mb = fmaxf(mb, sv[s][i]);
-            }
-        mb = max_over_c(mb);  // finite: token tok0 <= p is valid
-        const float m_new = fmaxf(m_run, mb);
-        const float alpha = exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 8; dt++) o[dt] *= alpha;
-        float ls = 0.f;
-        f16x4 pt[8];
-#pragma unroll
-        for (int s = 0; s < 8; s++)
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const float e = exp2f(sv[s][i] - m_new);
-                ls += e;
-                pt[s][i] = (_Float16)e;
-            }
-        l_run += sum_over_c(ls);
-        m_run = m_new;
-
-        // ---- O^T += V^T P^T, one 16-dim tile (= one scale group) at a time
-#pragma unroll
-        for (int dt = 0; dt < 8; dt++) {
-            const int d = 16 * dt + n;
-            const u32x4 vc = load16(vp + d * 64 + 16 * c);            // tokens 32c..32c+31
-            const u32x4 vs0 = load16(vp + kCodeBytes + dt * 128 + 32 * c);
-            const u32x4 vs1 = load16(vp + kCodeBytes + dt * 128 + 32 * c + 16);
-#pragma unroll
-            for (int s = 0; s < 8; s++) {
-                const uint32_t sw = s < 4 ? vs0[s] : vs1[s - 4];       // tokens 32c+4s..+3
-                const f16x4 a = (s & 1) ? dequant4_f16_percode<2>(vc[s >> 1], sw)
-                                        : dequant4_f16_percode<0>(vc[s >> 1], sw);
-                o[dt] = mfma_f16_k16(a, pt[s], o[dt]);
-            }
-        }
+    const uint8_t* kg = k_pool + (int64_t)g * kHeadPageBytes;
+    const uint8_t* vg = v_pool + (int64_t)g * kHeadPageBytes;
+    constexpr int64_t kPageStride = (int64_t)kKvHeads * kHeadPageBytes;
+    int cur_id = __builtin_amdgcn_readfirstlane(sh_ids[wave][0]);
+    if (cur_id >= 0) {
+        const int pg = __builtin_amdgcn_readfirstlane(sh_pages[wave][0]);
+        block_to_lds(kg + pg * kPageStride, vg + pg * kPageStride, lds[wave][0], lane);
     }
+    // B operand of S^T (prepared while the first block streams in): head 16g + n, dims 32c + 8m .. +7
+    bf16x8 qb[4];
+    {
+        const uint16_t* qp = q + ((int64_t)bq * kQHeads + kGroupHeads * g + n) * kDim + 32 * c;
+#pragma unroll
+        for (int m = 0; m < 4; m++) qb[m] = *reinterpret_cast<const bf16x8*>(qp + 8 * m);
+    }
+    f16x8 qh[4];
+    float q_unscale;
+    const bool f16 = __all(query_to_f16(qb, qh, q_unscale));
+    u32x4 qop[4];
+#pragma unroll
+    for (int m = 0; m < 4; m++)
+        qop[m] = f16 ? __builtin_bit_cast(u32x4, qh[m]) : __builtin_bit_cast(u32x4, qb[m]);
+    const float logit_scale = scale_log2 * (f16 ? q_unscale : 1.0f);
+
+#pragma unroll
+    for (int kb = 0; kb < BPW; kb++) {
+        int nxt_id = -1;
+        if (kb + 1 < BPW) {
+            nxt_id = __builtin_amdgcn_readfirstlane(sh_ids[wave][kb + 1]);
+            if (nxt_id >= 0) {
+                const int pg = __builtin_amdgcn_readfirstlane(sh_pages[wave][kb + 1]);
+                block_to_lds(kg + pg * kPageStride, vg + pg * kPageStride,
+                             lds[wave][(kb + 1) % kBufs], lane);
+            }
+        }
+        if (cur_id >= 0) {
+            if (nxt_id >= 0) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            if (f16)
+                attend_block<true>(lds[wave][kb % kBufs], lane, c, cur_id * kBlock, p, qop,
+                                   logit_scale, m_run, l_run, o);
+            else
+                attend_block<false>(lds[wave][kb % kBufs], lane, c, cur_id * kBlock, p, qop,
+                                    logit_scale, m_run, l_run, o);
+        }
+        cur_id = nxt_id;
+    }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __syncthreads();  // all page buffers are free: reuse them for the merge
 
     // ---- merge the 4 wavefronts: lane (n, c) holds o[dt][i] = out(head n, dim 16dt + 4c + i)
+    float* sh_o = reinterpret_cast<float*>(&lds[0][0][0]);  // [kWaves][16][kMergeStride]
 #pragma unroll
     for (int dt = 0; dt < 8; dt++)
 #pragma unroll
-        for (int i = 0; i < 4; i++) sh_o[wave][n][16 * dt + 4 * c + i] = o[dt][i];
+        for (int i = 0; i < 4; i++)
+            sh_o[(wave * kGroupHeads + n) * kMergeStride + 16 * dt + 4 * c + i] = o[dt][i];
     if (c == 0) {
         sh_m[wave][n] = m_run;
         sh_l[wave][n] = l_run;
@@ -154,30 +272,23 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; w++) M = fmaxf(M, sh_m[w][h]);
-    float wt[kWaves], L = 0.f;
+    float L = 0.f, acc[8];
+    {
+        float wt[kWaves];
 #pragma unroll
-    for (int w = 0; w < kWaves; w++) {
-        wt[w] = (sh_m[w][h] == -INFINITY) ? 0.f : exp2f(sh_m[w][h] - M);
-        L += wt[w] * sh_l[w][h];
+        for (int w = 0; w < kWaves; w++) {
+            wt[w] = (sh_m[w][h] == -INFINITY) ? 0.f : exp2f(sh_m[w][h] - M);
+            L += wt[w] * sh_l[w][h];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            float x = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; w++) x += wt[w] * sh_o[(w * kGroupHeads + h) * kMergeStride + d0 + e];
+            acc[e] = x;
+        }
     }
-    float acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; e++) {
-        float x = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; w++) x += wt[w] * sh_o[w][h][d0 + e];
-        acc[e] = x;
-    }
-    if (n_split == 1) {
-        const float inv = L > 0.f ? 1.f / L : 0.f;
-        uint16_t* op = out + ((int64_t)bq * kQHeads + kGroupHeads * g + h) * kDim + d0;
-        uint32_t packed[4];
-#pragma unroll
-        for (int e = 0; e < 4; e++)
-            packed[e] = (uint32_t)bf16_bits_rne(acc[2 * e] * inv) |
-                        ((uint32_t)bf16_bits_rne(acc[2 * e + 1] * inv) << 16);
-        *reinterpret_cast<u32x4*>(op) = u32x4{packed[0], packed[1], packed[2], packed[3]};
-    } else {
+    if (n_split > 1) {
         float* pp = partials + (((int64_t)rg * n_split + split) * kGroupHeads + h) * kPartStride;
         if (d0 == 0) {
             pp[0] = M;
@@ -185,15 +296,31 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
         }
         *reinterpret_cast<f32x4*>(pp + 4 + d0) = f32x4{acc[0], acc[1], acc[2], acc[3]};
         *reinterpret_cast<f32x4*>(pp + 8 + d0) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+        return;
     }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    uint32_t packed[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++)
+        packed[e] = (uint32_t)bf16_bits_rne(acc[2 * e] * inv) |
+                    ((uint32_t)bf16_bits_rne(acc[2 * e + 1] * inv) << 16);
+    uint16_t* op = out + ((int64_t)bq * kQHeads + kGroupHeads * g + h) * kDim + d0;
+    *reinterpret_cast<u32x4*>(op) = u32x4{packed[0], packed[1], packed[2], packed[3]};
 }
 
-// One workgroup per row group: merge its n_split partials per head into bf16 output.
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ partials,
-                                                     int n_split, uint16_t* __restrict__ out) {
-    const int rg = blockIdx.x;
-    const int g = rg & 3;
-    const int bq = rg >> 2;
+// Merge the n_split partials of a row group into bf16 output; the same pair -> XCD mapping as
+// the attention kernel, so the partials are read from the L2 they were written to.
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ partials, int batch,
+                                                     int q_len, int n_split,
+                                                     uint16_t* __restrict__ out) {
+    const int local = blockIdx.x >> 3;
+    const int pair = (local / q_len) * 8 + (blockIdx.x & 7);
+    if (pair >= batch * kKvHeads) return;
+    const int j = local - (local / q_len) * q_len;
+    const int b = pair >> 2;
+    const int g = pair & 3;
+    const int bq = b * q_len + j;
+    const int rg = bq * kKvHeads + g;
     const int h = threadIdx.x >> 4;
     const int d0 = (threadIdx.x & 15) * 8;
     const float* base = partials + ((int64_t)rg * n_split * kGroupHeads + h) * kPartStride;
@@ -245,29 +372,31 @@ hipError_t launch_attention(const uint8_t* k_pool, const uint8_t* v_pool, int64_
                             float softmax_scale, uint16_t* out, float* workspace,
                             hipStream_t stream) {
     const int ns = attn_num_splits(batch, q_len);
-    const int rows = batch * q_len * kKvHeads;
+    const int pairs = batch * kKvHeads;
+    const int pair_slots = 8 * ((pairs + 7) / 8);
     const float scale_log2 = softmax_scale * 1.4426950408889634f;
-    const dim3 grid(rows * ns), block(kWaves * 64);
+    const dim3 grid(pair_slots * q_len * ns), block(kWaves * 64);
     switch (ns) {
         case 1:
             hipLaunchKernelGGL(attention_kernel<4>, grid, block, 0, stream, k_pool, v_pool,
-                               num_pages, block_table, ctx_lens, max_blocks, q_len, q, ids,
+                               num_pages, block_table, ctx_lens, batch, max_blocks, q_len, q, ids,
                                scale_log2, ns, out, workspace);
             break;
         case 2:
             hipLaunchKernelGGL(attention_kernel<2>, grid, block, 0, stream, k_pool, v_pool,
-                               num_pages, block_table, ctx_lens, max_blocks, q_len, q, ids,
+                               num_pages, block_table, ctx_lens, batch, max_blocks, q_len, q, ids,
                                scale_log2, ns, out, workspace);
             break;
         default:
             hipLaunchKernelGGL(attention_kernel<1>, grid, block, 0, stream, k_pool, v_pool,
-                               num_pages, block_table, ctx_lens, max_blocks, q_len, q, ids,
+                               num_pages, block_table, ctx_lens, batch, max_blocks, q_len, q, ids,
                                scale_log2, ns, out, workspace);
             break;
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || ns == 1) return err;
-    hipLaunchKernelGGL(combine_kernel, dim3(rows), dim3(256), 0, stream, workspace, ns, out);
+    hipLaunchKernelGGL(combine_kernel, dim3(pair_slots * q_len), dim3(256), 0, stream, workspace,
+                       batch, q_len, ns, out);
     return hipGetLastError();
 }
 

@@ -80,26 +80,18 @@ __device__ __forceinline__ bf16x8 dequant8_bf16(uint32_t w, float s) {
 
 // Four E2M1 codes (bytes SEL, SEL+1 of `w`) times four per-code E4M3 scales (the four bytes
 // of `sw`) -> four fp16 values, exact: E2M1 and E4M3 values are exact in fp16 and so is their
-// product (at most 6 significant bits, magnitude within [2^-10, 2688]).
+// product (at most 6 significant bits, magnitude within [2^-10, 2688]). The conversions carry a
+// power-of-two scale operand only, so 1.0 is passed and the E4M3 scale is applied by one packed
+// fp16 multiply per pair.
 template <int SEL>
 __device__ __forceinline__ f16x4 dequant4_f16_percode(uint32_t w, uint32_t sw) {
     const f16x2 v01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
     const f16x2 v23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL + 1);
-    const f32x2 s01 = __builtin_amdgcn_cvt_pk_f32_fp8(sw, false);
-    const f32x2 s23 = __builtin_amdgcn_cvt_pk_f32_fp8(sw, true);
-    f16x2 h01, h23;
-    h01[0] = (_Float16)s01[0];
-    h01[1] = (_Float16)s01[1];
-    h23[0] = (_Float16)s23[0];
-    h23[1] = (_Float16)s23[1];
-    const f16x2 a = v01 * h01;
-    const f16x2 b = v23 * h23;
-    f16x4 r;
-    r[0] = a[0];
-    r[1] = a[1];
-    r[2] = b[0];
-    r[3] = b[1];
-    return r;
+    const f16x2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
+    const f16x2 s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, true);
+    const f16x2 a = v01 * s01;
+    const f16x2 b = v23 * s23;
+    return f16x4{a[0], a[1], b[0], b[1]};
 }
 
 // Eight E2M1 codes (one 32-bit word) times the scale pair {s, s} -> eight fp16 values, exact
@@ -116,10 +108,9 @@ __device__ __forceinline__ f16x8 dequant8_f16(uint32_t w, f16x2 ss) {
 // Two E4M3 scale bytes (byte pair HI of `w`) -> fp16 pairs {s0, s0} and {s1, s1} (exact).
 template <bool HI>
 __device__ __forceinline__ void e4m3_pair_f16(uint32_t w, f16x2& s0, f16x2& s1) {
-    const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
-    const _Float16 a = (_Float16)f[0], b = (_Float16)f[1];
-    s0 = f16x2{a, a};
-    s1 = f16x2{b, b};
+    const f16x2 s = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
+    s0 = f16x2{s[0], s[0]};
+    s1 = f16x2{s[1], s[1]};
 }
 
 // Query operands in fp16. A query row (one index query, or one attention head) of 128 bf16

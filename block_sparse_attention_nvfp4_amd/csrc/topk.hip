@@ -7,9 +7,17 @@
 // counted twice; section "Decode indexer score kernel": the top-k boundary stays close to the
 // scores. Ties go to the lower block index.
 //
-// One 256-thread workgroup per row. The 15th-largest score key is found by a 4-pass radix
-// select (8-bit digits, most significant first) over order-preserving integer keys; all keys
-// above it are kept and the keys equal to it are taken in ascending block order until 15.
+// Rows of up to 4,096 candidate blocks: one 64-lane wavefront per row, no atomics. The row's
+// scores become order-preserving integer keys in registers (candidate i in lane i % 64). The
+// 15th-largest of the 64 per-lane maxima, found by a bitwise search with ballot counts, is a lower
+// bound of the 15th-largest key (at least 15 keys reach it), so the selection lies among the keys
+// at or above it. Those few candidates are compacted into LDS in ascending block order and each
+// is ranked exactly against the others by (key, block index); the 15 best, already in ascending
+// block order, are written with the forced block last. When more than 64 candidates reach the
+// bound (heavy ties), the wavefront extracts the 15 best one by one instead.
+// Longer rows: one 256-thread workgroup per row with a 4-pass radix select (8-bit digits, LDS
+// histograms) on the keys, then keys above the found key are kept and keys equal to it are taken
+// in ascending block order.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -17,6 +25,7 @@ namespace msa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kPerThread = 16;  // keys held in registers: rows of up to 4,096 candidates
 
 // Order-preserving map of a non-NaN float to uint32 (larger float -> larger key); -0 == +0.
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -35,16 +44,74 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x, int lane) {
     return x;
 }
 
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
+    return x;
+}
+
+struct Shared {
+    uint32_t hist[256];
+    uint32_t digit_prefix, need;
+    uint32_t wave_tot[kThreads / 64];
+    int sel[kTopk];
+    int sel_count;
+};
+
+// Radix-select the key of the `need`-th largest candidate among m (REG: keys from registers).
+template <bool REG>
+__device__ __forceinline__ void radix_select(Shared& sh, const uint32_t (&keys)[kPerThread],
+                                             const float* s, int m, int tid, int lane, int wave,
+                                             uint32_t& prefix, uint32_t& need) {
+    uint32_t prefix_mask = 0;
+    for (int pass = 0; pass < 4; pass++) {
+        const int shift = 24 - 8 * pass;
+        sh.hist[tid] = 0;
+        __syncthreads();
+        if constexpr (REG) {
+#pragma unroll
+            for (int j = 0; j < kPerThread; j++) {
+                const int i = tid + j * kThreads;
+                if (i < m && (keys[j] & prefix_mask) == prefix)
+                    atomicAdd(&sh.hist[(keys[j] >> shift) & 255u], 1u);
+            }
+        } else {
+            for (int i = tid; i < m; i += kThreads) {
+                const uint32_t key = order_key(s[i]);
+                if ((key & prefix_mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // lane L covers digits 255-4L .. 252-4L (descending): the scan counts from the top
+            uint32_t cnt[4], tot = 0;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                cnt[i] = sh.hist[255 - 4 * lane - i];
+                tot += cnt[i];
+            }
+            uint32_t before = wave_inclusive_scan(tot, lane) - tot;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                if (before < need && before + cnt[i] >= need) {
+                    sh.digit_prefix = prefix | ((uint32_t)(255 - 4 * lane - i) << shift);
+                    sh.need = need - before;
+                }
+                before += cnt[i];
+            }
+        }
+        __syncthreads();
+        prefix = sh.digit_prefix;
+        need = sh.need;
+        prefix_mask |= 255u << shift;
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ scores,
                                                        const int32_t* __restrict__ ctx_lens,
                                                        int max_blocks, int q_len,
                                                        int32_t* __restrict__ ids) {
-    __shared__ uint32_t hist[256];
-    __shared__ uint32_t sh_digit_prefix, sh_need;
-    __shared__ uint32_t wave_tot[kThreads / 64];
-    __shared__ int sel[kTopk];
-    __shared__ int sel_count;
-
+    __shared__ Shared sh;
     const int row = blockIdx.x;  // ((b * q_len + j) * 4 + g)
     const int bq = row >> 2;
     const int b = bq / q_len;
@@ -67,75 +134,210 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     }
     const float* s = scores + (int64_t)row * max_blocks;
     const int m = n - 1;  // candidates 0..m-1 compete for kTopk - 1 places
-    uint32_t prefix = 0, prefix_mask = 0, need = kTopk - 1;
-
-    for (int pass = 0; pass < 4; pass++) {
-        const int shift = 24 - 8 * pass;
-        hist[tid] = 0;
-        __syncthreads();
-        for (int i = tid; i < m; i += kThreads) {
-            const uint32_t key = order_key(s[i]);
-            if ((key & prefix_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-        }
-        __syncthreads();
-        if (wave == 0) {
-            // lane L covers digits 255-4L .. 252-4L (descending), so the scan counts keys from the top
-            uint32_t cnt[4], tot = 0;
+    const bool in_regs = m <= kThreads * kPerThread;
+    uint32_t keys[kPerThread];
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                cnt[i] = hist[255 - 4 * lane - i];
-                tot += cnt[i];
-            }
-            uint32_t before = wave_inclusive_scan(tot, lane) - tot;
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                if (before < need && before + cnt[i] >= need) {
-                    sh_digit_prefix = prefix | ((uint32_t)(255 - 4 * lane - i) << shift);
-                    sh_need = need - before;
-                }
-                before += cnt[i];
-            }
-        }
-        __syncthreads();
-        prefix = sh_digit_prefix;
-        need = sh_need;
-        prefix_mask |= 255u << shift;
+    for (int q = 0; q < kPerThread; q++) {
+        const int i = tid + q * kThreads;
+        keys[q] = (in_regs && i < m) ? order_key(s[i]) : 0u;
     }
-    // prefix = key of the 15th largest candidate; `need` of the candidates equal to it are kept
-    // (the lowest block ids), every candidate above it is kept.
-    if (tid == 0) sel_count = 0;
-    const int chunk = (m + kThreads - 1) / kThreads;
-    const int lo = tid * chunk;
-    const int hi = min(lo + chunk, m);
+    uint32_t prefix = 0, need = kTopk - 1;
+    if (in_regs) radix_select<true>(sh, keys, s, m, tid, lane, wave, prefix, need);
+    else radix_select<false>(sh, keys, s, m, tid, lane, wave, prefix, need);
+    // prefix = key of the 15th largest candidate; every candidate above it is kept, and `need`
+    // of the candidates equal to it (the lowest block ids).
+    if (tid == 0) sh.sel_count = 0;
     uint32_t eq = 0;
-    for (int i = lo; i < hi; i++) eq += (order_key(s[i]) == prefix);
-    const uint32_t incl = wave_inclusive_scan(eq, lane);
-    if (lane == 63) wave_tot[wave] = incl;
+    if (in_regs) {
+#pragma unroll
+        for (int q = 0; q < kPerThread; q++) eq += (tid + q * kThreads < m) && keys[q] == prefix;
+    } else {
+        for (int i = tid; i < m; i += kThreads) eq += order_key(s[i]) == prefix;
+    }
+    const uint32_t eq_w = wave_sum(eq);
+    if (lane == 0) sh.wave_tot[wave] = eq_w;
     __syncthreads();
-    uint32_t rank = incl - eq;
-    for (int w = 0; w < wave; w++) rank += wave_tot[w];
-    for (int i = lo; i < hi; i++) {
-        const uint32_t key = order_key(s[i]);
-        bool take = key > prefix;
-        if (key == prefix) {
-            take = rank < need;
-            rank++;
+    const uint32_t total_eq = sh.wave_tot[0] + sh.wave_tot[1] + sh.wave_tot[2] + sh.wave_tot[3];
+    if (total_eq == need) {
+        // no tie straddles the boundary: keep every key >= prefix
+        if (in_regs) {
+#pragma unroll
+            for (int q = 0; q < kPerThread; q++) {
+                const int i = tid + q * kThreads;
+                if (i < m && keys[q] >= prefix) {
+                    const int slot = atomicAdd(&sh.sel_count, 1);
+                    if (slot < kTopk - 1) sh.sel[slot] = i;
+                }
+            }
+        } else {
+            for (int i = tid; i < m; i += kThreads) {
+                if (order_key(s[i]) >= prefix) {
+                    const int slot = atomicAdd(&sh.sel_count, 1);
+                    if (slot < kTopk - 1) sh.sel[slot] = i;
+                }
+            }
         }
-        if (take) {
-            const int slot = atomicAdd(&sel_count, 1);
-            if (slot < kTopk - 1) sel[slot] = i;
+    } else {
+        // ties at the boundary: rank equal keys in ascending block order over contiguous chunks
+        const int chunk = (m + kThreads - 1) / kThreads;
+        const int lo = tid * chunk;
+        const int hi = min(lo + chunk, m);
+        uint32_t e = 0;
+        for (int i = lo; i < hi; i++) e += order_key(s[i]) == prefix;
+        const uint32_t incl = wave_inclusive_scan(e, lane);
+        __syncthreads();
+        if (lane == 63) sh.wave_tot[wave] = incl;
+        __syncthreads();
+        uint32_t rank = incl - e;
+        for (int w = 0; w < wave; w++) rank += sh.wave_tot[w];
+        for (int i = lo; i < hi; i++) {
+            const uint32_t key = order_key(s[i]);
+            bool take = key > prefix;
+            if (key == prefix) {
+                take = rank < need;
+                rank++;
+            }
+            if (take) {
+                const int slot = atomicAdd(&sh.sel_count, 1);
+                if (slot < kTopk - 1) sh.sel[slot] = i;
+            }
         }
     }
     __syncthreads();
-    if (tid == 0) sel[kTopk - 1] = m;  // the forced block of the query token
+    if (tid == 0) sh.sel[kTopk - 1] = m;  // the forced block of the query token
     __syncthreads();
     if (tid < kTopk) {
-        const int v = sel[tid];
+        const int v = sh.sel[tid];
         int pos = 0;
 #pragma unroll
-        for (int k = 0; k < kTopk; k++) pos += sel[k] < v;
+        for (int k = 0; k < kTopk; k++) pos += sh.sel[k] < v;
         out[pos] = v;
     }
+}
+
+// ---------------------------------------------------------------- one wavefront per row
+constexpr int kRowsPerWg = 4;
+
+__device__ __forceinline__ int popc64(uint64_t x) { return __popcll(x); }
+
+// Number of lanes before this one whose bit is set.
+__device__ __forceinline__ int lanes_before(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+}
+
+template <int KPL>  // keys per lane: rows of up to 64 * KPL candidates
+__global__ __launch_bounds__(kRowsPerWg * 64) void topk_wave_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ ctx_lens, int max_blocks,
+    int q_len, int rows, int32_t* __restrict__ ids) {
+    __shared__ uint32_t cand_key[kRowsPerWg][64];
+    __shared__ int cand_idx[kRowsPerWg][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int row = blockIdx.x * kRowsPerWg + wave;  // ((b * q_len + j) * 4 + g)
+    if (row >= rows) return;
+    const int bq = row >> 2;
+    const int b = bq / q_len;
+    const int j = bq - b * q_len;
+    int32_t* out = ids + (int64_t)row * kTopk;
+    const int T = clamp_ctx(ctx_lens[b], max_blocks);
+    const int p = T - q_len + j;
+    if (p < 0) {
+        if (lane < kTopk) out[lane] = -1;
+        return;
+    }
+    const int n = min(p / kBlock + 1, max_blocks);  // eligible blocks 0..n-1, forced n-1
+    if (n <= kTopk) {
+        if (lane < kTopk) out[lane] = lane < n ? lane : -1;
+        return;
+    }
+    const int m = n - 1;  // candidates 0..m-1 compete for 15 places
+    const float* s = scores + (int64_t)row * max_blocks;
+    uint32_t key[KPL];  // 0 marks "no candidate": every real key is above it
+    uint32_t lmax = 0;
+#pragma unroll
+    for (int k = 0; k < KPL; k++) {
+        const int i = lane + 64 * k;
+        key[k] = i < m ? order_key(s[i]) : 0u;
+        lmax = max(lmax, key[k]);
+    }
+    // bound: the 15th-largest per-lane maximum (bitwise search, most significant bit first)
+    uint32_t bound = 0;
+    for (int bit = 31; bit >= 0; bit--) {
+        const uint32_t cand = bound | (1u << bit);
+        if (popc64(__ballot(lmax >= cand)) >= kTopk - 1) bound = cand;
+    }
+    int count = 0;
+#pragma unroll
+    for (int k = 0; k < KPL; k++) count += popc64(__ballot(key[k] >= bound));
+    if (count <= 64) {
+        // compact the candidates in ascending block order (k-major, lane-minor), then rank them
+        int base = 0;
+#pragma unroll
+        for (int k = 0; k < KPL; k++) {
+            const bool c = key[k] >= bound;
+            const uint64_t mask = __ballot(c);
+            if (c) {
+                const int pos = base + lanes_before(mask);
+                cand_key[wave][pos] = key[k];
+                cand_idx[wave][pos] = lane + 64 * k;
+            }
+            base += popc64(mask);
+        }
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        bool sel = false;
+        int my_idx = 0;
+        if (lane < count) {
+            const uint32_t mk = cand_key[wave][lane];
+            my_idx = cand_idx[wave][lane];
+            int rank = 0;
+            for (int t = 0; t < count; t++) {
+                const uint32_t ok = cand_key[wave][t];
+                rank += (ok > mk) || (ok == mk && t < lane);  // same key: lower block first
+            }
+            sel = rank < kTopk - 1;
+        }
+        const uint64_t smask = __ballot(sel);
+        if (sel) out[lanes_before(smask)] = my_idx;
+    } else {
+        // heavy ties: take the best remaining (key, lowest index) 15 times
+        uint32_t taken[(KPL + 31) / 32] = {};
+        for (int r = 0; r < kTopk - 1; r++) {
+            uint32_t bk = 0;
+            int bi = 0x7fffffff;
+#pragma unroll
+            for (int k = 0; k < KPL; k++) {
+                const int i = lane + 64 * k;
+                const bool avail = !((taken[k >> 5] >> (k & 31)) & 1u) && key[k] != 0u;
+                if (avail && (key[k] > bk || (key[k] == bk && i < bi))) {
+                    bk = key[k];
+                    bi = i;
+                }
+            }
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) {
+                const uint32_t ok = __shfl_xor(bk, d, 64);
+                const int oi = __shfl_xor(bi, d, 64);
+                if (ok > bk || (ok == bk && oi < bi)) {
+                    bk = ok;
+                    bi = oi;
+                }
+            }
+            if ((bi & 63) == lane) {
+                const int k = bi >> 6;
+                taken[k >> 5] |= 1u << (k & 31);
+            }
+        }
+        int base = 0;
+#pragma unroll
+        for (int k = 0; k < KPL; k++) {
+            const bool sel = (taken[k >> 5] >> (k & 31)) & 1u;
+            const uint64_t mask = __ballot(sel);
+            if (sel) out[base + lanes_before(mask)] = lane + 64 * k;
+            base += popc64(mask);
+        }
+    }
+    if (lane == 0) out[kTopk - 1] = m;  // the forced block of the query token, the largest id
 }
 
 }  // namespace
@@ -143,8 +345,16 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
 hipError_t launch_topk(const float* scores, const int32_t* ctx_lens, int batch, int max_blocks,
                        int q_len, int32_t* ids, hipStream_t stream) {
     const int rows = batch * q_len * kKvHeads;
-    hipLaunchKernelGGL(topk_kernel, dim3(rows), dim3(kThreads), 0, stream, scores, ctx_lens,
-                       max_blocks, q_len, ids);
+    const dim3 wgrid((rows + kRowsPerWg - 1) / kRowsPerWg), wblock(kRowsPerWg * 64);
+    if (max_blocks <= 64 * 16 + 1)
+        hipLaunchKernelGGL(topk_wave_kernel<16>, wgrid, wblock, 0, stream, scores, ctx_lens,
+                           max_blocks, q_len, rows, ids);
+    else if (max_blocks <= 64 * 64 + 1)
+        hipLaunchKernelGGL(topk_wave_kernel<64>, wgrid, wblock, 0, stream, scores, ctx_lens,
+                           max_blocks, q_len, rows, ids);
+    else
+        hipLaunchKernelGGL(topk_kernel, dim3(rows), dim3(kThreads), 0, stream, scores, ctx_lens,
+                           max_blocks, q_len, ids);
     return hipGetLastError();
 }
 

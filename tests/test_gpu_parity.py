@@ -28,6 +28,8 @@ CASES = {
     "prefill_small": (5, dict(batch=1, ctx=2048 + 128, q_len=128)),
     "short_context": (2, dict(batch=2, ctx_lens=[1000, 2048], q_len=1)),
     "spec_at_block_edge": (3, dict(batch=2, ctx_lens=[2 * 128 + 2, 20 * 128 + 3], q_len=4)),
+    # 1,024 row groups: one workgroup per row group, no split partials
+    "prefill_q256": (5, dict(batch=1, ctx=2048 + 256, q_len=256)),
 }
 
 
@@ -117,3 +119,4 @@ def test_step_is_deterministic(run):
     again = g.run()
     assert torch.equal(ids, g.step.block_ids)
     assert torch.equal(first, again)
+
