@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+COPY_BYTES = 512 << 20  # calibration copy for the HBM traffic counters (read and written once)
 METRIC = "MSA decode query-tokens/s per layer at 128K ctx; achieved HBM GB/s vs peak"
 
 
@@ -40,8 +41,12 @@ def parse():
     ap.add_argument("--kernel-reps", type=int, default=20, help="graph replays per kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle CPU time")
-    ap.add_argument("--only", default="", help="profiling aid: run only this kernel in a loop "
-                                               "(insert|indexer|topk|attention) and exit")
+    ap.add_argument("--only", default="", help="profiling aid: run a calibration copy of "
+                    f"{COPY_BYTES >> 20} MiB, then only this kernel in a loop "
+                    "(insert|indexer|topk|attention), and exit")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter CSVs of '--only indexer' (FETCH_SIZE, "
+                         "WRITE_SIZE) into profiles/indexer_spec128k_traffic.json and exit")
     return ap.parse_args()
 
 
@@ -65,8 +70,49 @@ def load_traffic(kernel, digest):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _counter_means(path):
+    """Mean counter value per kernel name of a rocprofv3 counter-collection CSV."""
+    import collections
+    import csv
+    acc = collections.defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def traffic_from(fetch_csv, write_csv):
+    """HBM bytes per indexer launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled
+    by what the same counter reads for the calibration copy (COPY_BYTES read, COPY_BYTES
+    written)."""
+    rec = {"source_digest": source_digest("indexer.hip", "device_common.hpp"),
+           "copy_bytes": COPY_BYTES}
+    total = 0.0
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        means = _counter_means(path)
+        idx = [k for k in means if "indexer_kernel" in k]
+        other = [k for k in means if "msa::" not in k]
+        assert len(idx) == 1 and other, (counter, list(means))
+        copy_name = max(other, key=lambda k: means[k])
+        factor = means[copy_name] * 1024.0 / COPY_BYTES
+        raw = means[idx[0]] * 1024.0
+        rec[counter] = {"indexer_kib_per_dispatch": means[idx[0]],
+                        "copy_kib_per_dispatch": means[copy_name], "copy_kernel": copy_name[:80],
+                        "factor": factor, "indexer_bytes_scaled": raw / factor}
+        total += raw / factor
+    rec["hbm_bytes_per_launch"] = total
+    path = os.path.join(ROOT, "profiles", "indexer_spec128k_traffic.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
+
+
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the MSA decode path "
               "here is single-GPU, see DESIGN.md for how it would shard.", file=sys.stderr)
@@ -80,7 +126,7 @@ def main():
 
     dev = "cuda"
     torch.cuda.set_device(0)
-    w = mi.make_workload(3)
+    w = mi.full_workload(3)
     B, q, T = w.batch, w.q_len, w.ctx_lens[0]
     L = args.layers
     t_setup = time.time()
@@ -131,7 +177,14 @@ def main():
     torch.cuda.synchronize()
 
     if args.only:
-        # profiling aid: the chosen kernel alone, L launches per round, no graphs
+        # profiling aid: a plain copy of known size (counter calibration), then the chosen
+        # kernel alone, L launches per round, no graphs
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
         for _ in range(args.kernel_reps):
             for s in steps:
                 calls[args.only](s)

@@ -33,7 +33,9 @@ chosen block, in fp32, before quantization.
 from __future__ import annotations
 
 import dataclasses
+import json
 import math
+import os
 from typing import Dict, List, Optional, Tuple
 
 import numpy as np
@@ -257,6 +259,22 @@ def make_workload(cfg: int, batch: Optional[int] = None, ctx: Optional[int] = No
                     ik_kind="t3" if cfg == 4 else "normal", plants=plants,
                     plant_dir=plant_dir.astype(np.float32), q_idx=qi.contiguous(), q=Q.contiguous(),
                     retries=retries)
+
+
+RETRIES_FILE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                            "tests", "golden", "retries.json")
+
+
+def full_workload(cfg: int) -> Workload:
+    """Workload `cfg` at its stated size, with the margin-enforcing retry counters that
+    tests/golden/make_retries.py found with the oracle (every selection row then has a margin
+    of at least 1e-3). Without that file, every counter is 0."""
+    retries = {}
+    if os.path.exists(RETRIES_FILE):
+        with open(RETRIES_FILE) as f:
+            doc = json.load(f)
+        retries = {int(b): int(r) for b, r in doc.get(str(cfg), {}).get("retries", {}).items()}
+    return make_workload(cfg, retries=retries)
 
 
 def bf16_bits(x: torch.Tensor) -> np.ndarray:

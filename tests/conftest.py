@@ -15,4 +15,4 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests that create large inputs run last so a failure in a small case shows first.
-    items.sort(key=lambda it: 1 if it.get_closest_marker("gpu") and "full" in it.name else 0)
+    items.sort(key=lambda it: 1 if it.module.__name__.endswith("test_gpu_full") else 0)

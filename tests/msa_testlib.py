@@ -140,6 +140,64 @@ def oracle_sequence(w: mi.Workload, b: int, attention_tokens: Optional[Sequence[
     return res
 
 
+def oracle_rows(w: mi.Workload, b: int, rows: Sequence[int], ids_override: Optional[np.ndarray] = None,
+                attention: bool = True):
+    """Oracle reference for chosen query tokens j of sequence b, each scored on its own causal
+    prefix (tokens 0..p), so that a few rows of a long prefill cost a few prefix scans.
+    Returns scores [n][4][max_blocks], ids [n][4][16], margins [n][4] and, if asked,
+    attention [n][64][128] over ids_override[n] (else over the oracle's own ids)."""
+    import oracle
+    T, q = w.ctx_lens[b], w.q_len
+    rows = list(rows)
+    last = T - q + max(rows) + 1
+    ikc, iks = oracle.quantize(w.ik_rows(b, 0, last).numpy())
+    qi = mi.bf16_bits(w.q_idx[b * q:(b + 1) * q])
+    scores = np.empty((len(rows), 4, w.max_blocks))
+    ids = np.empty((len(rows), 4, 16), np.int32)
+    margins = np.empty((len(rows), 4))
+    for i, j in enumerate(rows):
+        p = T - q + j
+        scores[i] = oracle.index_scores(qi[j:j + 1], ikc[:p + 1], iks[:p + 1], p + 1, 1, w.max_blocks)[0]
+        sid, m = oracle.select_sequence(scores[i:i + 1], p + 1, 1)
+        ids[i], margins[i] = sid[0], m[0]
+    res = dict(scores=scores, ids=ids, margins=margins, ik=(ikc, iks))
+    if not attention:
+        return res
+    use_ids = ids if ids_override is None else np.asarray(ids_override)
+    blocks = sorted(set(int(x) for x in use_ids.ravel() if x >= 0))
+    kc = np.zeros((last, 4, 64), np.uint8)
+    ks = np.zeros((last, 4, 8), np.uint8)
+    vc, vs = np.zeros_like(kc), np.zeros_like(ks)
+    for blk in blocks:
+        t0, t1 = blk * BLOCK, min(last, blk * BLOCK + BLOCK)
+        kc[t0:t1], ks[t0:t1] = oracle.quantize(w.kv_rows("k", b, t0, t1).numpy())
+        vc[t0:t1], vs[t0:t1] = oracle.quantize(w.kv_rows("v", b, t0, t1).numpy())
+    qb = mi.bf16_bits(w.q[b * q:(b + 1) * q])
+    res["attention"] = np.stack([
+        oracle.sparse_attention_token(qb[j], kc, ks, vc, vs, last, use_ids[i], T - q + j,
+                                      oracle.default_scale()) for i, j in enumerate(rows)])
+    return res
+
+
+def gpu_block_caches(cache, w: mi.Workload, b: int, blocks: Sequence[int]):
+    """Logical (codes, scales) of the given blocks of sequence b read back from the GPU pools,
+    concatenated in the order given: ik [n*128][64]/[..][8], k and v [n*128][4][64]/[..][4][8]."""
+    pages = torch.from_numpy(w.block_table[b, list(blocks)].astype(np.int64))
+    out = {}
+    ikp = cache.ik[pages.to(cache.ik.device)].cpu().numpy()
+    c, s = zip(*[unpack_row_page(pg) for pg in ikp])
+    out["ik"] = (np.concatenate(c), np.concatenate(s))
+    for name, pool, fn in (("k", cache.k, unpack_row_page), ("v", cache.v, unpack_col_page)):
+        pp = pool[pages.to(pool.device)].cpu().numpy()
+        cs, ss = [], []
+        for pg in pp:
+            per_head = [fn(pg[h]) for h in range(4)]
+            cs.append(np.stack([x[0] for x in per_head], axis=1))
+            ss.append(np.stack([x[1] for x in per_head], axis=1))
+        out[name] = (np.concatenate(cs), np.concatenate(ss))
+    return out
+
+
 # ------------------------------------------------------------------ comparisons
 def score_tolerance(qi_bits: np.ndarray, ik_codes: np.ndarray, ik_scales: np.ndarray) -> np.ndarray:
     """fp32-accumulation bound per (row): 128 * 2^-24 * ||q|| * max_t ||k_t|| (Cauchy-Schwarz)."""
