@@ -70,37 +70,35 @@ def load_traffic(kernel, digest):
     return rec.get("hbm_bytes_per_launch")
 
 
-def _counter_means(path):
-    """Mean counter value per kernel name of a rocprofv3 counter-collection CSV."""
-    import collections
+def _counter_rows(path):
+    """(kernel name, counter value) per dispatch of a rocprofv3 counter-collection CSV."""
     import csv
-    acc = collections.defaultdict(list)
     with open(path) as f:
-        for r in csv.DictReader(f):
-            acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
-    return {k: sum(v) / len(v) for k, v in acc.items()}
+        return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in csv.DictReader(f)]
 
 
 def traffic_from(fetch_csv, write_csv):
     """HBM bytes per indexer launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled
-    by what the same counter reads for the calibration copy (COPY_BYTES read, COPY_BYTES
-    written)."""
+    by what the same counter reads for the calibration copy: the largest runtime copy-kernel
+    dispatch of the run, which moves COPY_BYTES in and COPY_BYTES out."""
     rec = {"source_digest": source_digest("indexer.hip", "device_common.hpp"),
            "copy_bytes": COPY_BYTES}
     total = 0.0
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
-        means = _counter_means(path)
-        idx = [k for k in means if "indexer_kernel" in k]
-        other = [k for k in means if "msa::" not in k]
-        assert len(idx) == 1 and other, (counter, list(means))
-        copy_name = max(other, key=lambda k: means[k])
-        factor = means[copy_name] * 1024.0 / COPY_BYTES
-        raw = means[idx[0]] * 1024.0
-        rec[counter] = {"indexer_kib_per_dispatch": means[idx[0]],
-                        "copy_kib_per_dispatch": means[copy_name], "copy_kernel": copy_name[:80],
-                        "factor": factor, "indexer_bytes_scaled": raw / factor}
-        total += raw / factor
-    rec["hbm_bytes_per_launch"] = total
+        rows = _counter_rows(path)
+        idx = [v for k, v in rows if "indexer_kernel" in k]
+        copies = [v for k, v in rows if "copyBuffer" in k]
+        assert idx and copies, (counter, sorted(set(k for k, _ in rows))[:20])
+        copy_kib = max(copies)
+        factor = copy_kib * 1024.0 / COPY_BYTES
+        assert 0.25 <= factor <= 4.0, (counter, copy_kib)
+        mean_kib = sum(idx) / len(idx)
+        scaled = mean_kib * 1024.0 / factor
+        rec[counter] = {"indexer_kib_per_dispatch": round(mean_kib, 1), "indexer_dispatches": len(idx),
+                        "copy_kib": copy_kib, "factor": round(factor, 5),
+                        "indexer_bytes_scaled": round(scaled)}
+        total += scaled
+    rec["hbm_bytes_per_launch"] = round(total)
     path = os.path.join(ROOT, "profiles", "indexer_spec128k_traffic.json")
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
