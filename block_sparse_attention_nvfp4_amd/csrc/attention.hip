@@ -32,9 +32,18 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kPartStride = 132;  // floats per (row group, split, head): m, l, 2 pad, 128 out
+constexpr int kMaxSplits = 4;     // attn_num_splits returns 1, 2 or 4
 constexpr int kBlockBytes = 2 * kHeadPageBytes;  // K page then V page of one (block, group)
 constexpr int kMergeStride = kDim + 4;           // LDS row of the wavefront merge
 constexpr int kNonTemporal = 2;                  // cache-policy bits of the page loads
+// Lazy rescaling: a row keeps its running maximum until a block's maximum exceeds it by more
+// than this (log2 units); probabilities then stay below 2^kTau, well inside fp16, and the
+// accumulators are rescaled only when the maximum jumps.
+constexpr float kTau = 8.0f;
+
+// 2^x by the hardware instruction (results below 2^-126 flush to zero, which a softmax weight
+// next to a weight of at least 1 cannot notice).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -112,23 +121,25 @@ __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c
             mb = fmaxf(mb, sv[s][i]);
         }
     mb = max_over_c(mb);  // finite: token tok0 <= p is valid
-    const float m_new = fmaxf(m_run, mb);
-    const float alpha = exp2f(m_run - m_new);
-    l_run *= alpha;
+    const float m_new = (mb > m_run + kTau) ? mb : m_run;  // m_run = -inf -> m_new = mb
+    if (__any(m_new != m_run)) {
+        const float alpha = fast_exp2(m_run - m_new);  // 0 when m_run = -inf (o, l are 0)
+        l_run *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < 8; dt++) o[dt] *= alpha;
+        for (int dt = 0; dt < 8; dt++) o[dt] *= alpha;
+        m_run = m_new;
+    }
     float ls = 0.f;
     f16x4 pt[8];
 #pragma unroll
     for (int s = 0; s < 8; s++)
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            const float e = exp2f(sv[s][i] - m_new);
+            const float e = fast_exp2(sv[s][i] - m_new);
             ls += e;
             pt[s][i] = (_Float16)e;
         }
     l_run += sum_over_c(ls);
-    m_run = m_new;
 
     // ---- O^T += V^T P^T, one 16-dim tile (= one scale group) at a time
 #pragma unroll
@@ -277,7 +288,7 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
         float wt[kWaves];
 #pragma unroll
         for (int w = 0; w < kWaves; w++) {
-            wt[w] = (sh_m[w][h] == -INFINITY) ? 0.f : exp2f(sh_m[w][h] - M);
+            wt[w] = (sh_m[w][h] == -INFINITY) ? 0.f : fast_exp2(sh_m[w][h] - M);
             L += wt[w] * sh_l[w][h];
         }
 #pragma unroll
@@ -325,19 +336,35 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const int d0 = (threadIdx.x & 15) * 8;
     const float* base = partials + ((int64_t)rg * n_split * kGroupHeads + h) * kPartStride;
     const int stride = kGroupHeads * kPartStride;
+    // every split's (max, sum, 8 outputs) requested before any is used: one memory round trip
+    float mv[kMaxSplits], lv[kMaxSplits];
+    f32x4 av[kMaxSplits], bv[kMaxSplits];
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; sp++) {
+        if (sp < n_split) {
+            const float* pp = base + sp * stride;
+            mv[sp] = pp[0];
+            lv[sp] = pp[1];
+            av[sp] = *reinterpret_cast<const f32x4*>(pp + 4 + d0);
+            bv[sp] = *reinterpret_cast<const f32x4*>(pp + 8 + d0);
+        } else {
+            mv[sp] = -INFINITY;
+            lv[sp] = 0.f;
+            av[sp] = bv[sp] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
     float M = -INFINITY;
-    for (int sp = 0; sp < n_split; sp++) M = fmaxf(M, base[sp * stride]);
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; sp++) M = fmaxf(M, mv[sp]);
     float L = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int sp = 0; sp < n_split; sp++) {
-        const float* pp = base + sp * stride;
-        const float w = (pp[0] == -INFINITY) ? 0.f : exp2f(pp[0] - M);
-        L += w * pp[1];
-        const f32x4 a = *reinterpret_cast<const f32x4*>(pp + 4 + d0);
-        const f32x4 bb = *reinterpret_cast<const f32x4*>(pp + 8 + d0);
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; sp++) {
+        const float w = (mv[sp] == -INFINITY) ? 0.f : fast_exp2(mv[sp] - M);
+        L += w * lv[sp];
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-            acc[e] += w * a[e];
-            acc[4 + e] += w * bb[e];
+            acc[e] += w * av[sp][e];
+            acc[4 + e] += w * bv[sp][e];
         }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;

@@ -30,6 +30,13 @@ CASES = {
     "spec_at_block_edge": (3, dict(batch=2, ctx_lens=[2 * 128 + 2, 20 * 128 + 3], q_len=4)),
     # 1,024 row groups: one workgroup per row group, no split partials
     "prefill_q256": (5, dict(batch=1, ctx=2048 + 256, q_len=256)),
+    # speculative verify with 2, 3, 8 and 16 draft tokens (token tiles of 2 and 4, a partial
+    # tile, several tiles), and 17 (the per-token path above 16)
+    "spec_q2": (3, dict(batch=2, ctx=5000, q_len=2)),
+    "spec_q3": (3, dict(batch=3, ctx_lens=[3000, 4097, 5000], q_len=3)),
+    "spec_q8": (3, dict(batch=2, ctx_lens=[4000, 7000], q_len=8)),
+    "spec_q16": (3, dict(batch=1, ctx=6000, q_len=16)),
+    "spec_q17": (3, dict(batch=1, ctx=6000, q_len=17)),
 }
 
 
