@@ -136,10 +136,19 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     const int m = n - 1;  // candidates 0..m-1 compete for kTopk - 1 places
     const bool in_regs = m <= kThreads * kPerThread;
     uint32_t keys[kPerThread];
+    {
+        // every load goes out before any is used (one memory round trip; an index past the row
+        // reads its last score and is discarded)
+        float v[kPerThread] = {};
+        if (in_regs) {
 #pragma unroll
-    for (int q = 0; q < kPerThread; q++) {
-        const int i = tid + q * kThreads;
-        keys[q] = (in_regs && i < m) ? order_key(s[i]) : 0u;
+            for (int q = 0; q < kPerThread; q++) v[q] = s[min(tid + q * kThreads, max_blocks - 1)];
+        }
+#pragma unroll
+        for (int q = 0; q < kPerThread; q++) {
+            const int i = tid + q * kThreads;
+            keys[q] = (in_regs && i < m) ? order_key(v[q]) : 0u;
+        }
     }
     uint32_t prefix = 0, need = kTopk - 1;
     if (in_regs) radix_select<true>(sh, keys, s, m, tid, lane, wave, prefix, need);
@@ -239,7 +248,19 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void topk_wave_kernel(
     const int b = bq / q_len;
     const int j = bq - b * q_len;
     int32_t* out = ids + (int64_t)row * kTopk;
-    const int T = clamp_ctx(ctx_lens[b], max_blocks);
+    // the row's scores are requested together with the context length, before anything waits
+    // for either: one memory round trip (an index past the row reads its last score and is
+    // discarded)
+    const float* s = scores + (int64_t)row * max_blocks;
+    float v[KPL];
+#pragma unroll
+    for (int k = 0; k < KPL; k++) v[k] = s[min(lane + 64 * k, max_blocks - 1)];
+    int T_raw = ctx_lens[b];
+    // both loads are needed here, so the compiler issues all of them before its single wait
+#pragma unroll
+    for (int k = 0; k < KPL; k++) asm volatile("" : "+v"(v[k]));
+    asm volatile("" : "+v"(T_raw));
+    const int T = clamp_ctx(T_raw, max_blocks);
     const int p = T - q_len + j;
     if (p < 0) {
         if (lane < kTopk) out[lane] = -1;
@@ -251,13 +272,12 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void topk_wave_kernel(
         return;
     }
     const int m = n - 1;  // candidates 0..m-1 compete for 15 places
-    const float* s = scores + (int64_t)row * max_blocks;
     uint32_t key[KPL];  // 0 marks "no candidate": every real key is above it
     uint32_t lmax = 0;
 #pragma unroll
     for (int k = 0; k < KPL; k++) {
         const int i = lane + 64 * k;
-        key[k] = i < m ? order_key(s[i]) : 0u;
+        key[k] = i < m ? order_key(v[k]) : 0u;
         lmax = max(lmax, key[k]);
     }
     // bound: the 15th-largest per-lane maximum (bitwise search, most significant bit first)
@@ -285,18 +305,16 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void topk_wave_kernel(
         }
         __builtin_amdgcn_wave_barrier();
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        bool sel = false;
-        int my_idx = 0;
-        if (lane < count) {
-            const uint32_t mk = cand_key[wave][lane];
-            my_idx = cand_idx[wave][lane];
-            int rank = 0;
-            for (int t = 0; t < count; t++) {
-                const uint32_t ok = cand_key[wave][t];
-                rank += (ok > mk) || (ok == mk && t < lane);  // same key: lower block first
-            }
-            sel = rank < kTopk - 1;
+        // lane t holds candidate t; each compares itself with all others through register
+        // broadcasts (no LDS round trip per comparison)
+        const uint32_t mk = lane < count ? cand_key[wave][lane] : 0u;
+        const int my_idx = lane < count ? cand_idx[wave][lane] : 0;
+        int rank = 0;
+        for (int t = 0; t < count; t++) {
+            const uint32_t ok = __builtin_amdgcn_readlane(mk, t);
+            rank += (ok > mk) || (ok == mk && t < lane);  // same key: lower block first
         }
+        const bool sel = lane < count && rank < kTopk - 1;
         const uint64_t smask = __ballot(sel);
         if (sel) out[lanes_before(smask)] = my_idx;
     } else {
