@@ -192,15 +192,17 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
     const int g = pair & 3;
     const int bq = b * q_len + j;
     const int rg = bq * kKvHeads + g;  // row group
-    const int T = clamp_ctx(ctx_lens[b], max_blocks);
-    const int p = T - q_len + j;
-
     // this wavefront's blocks (id and page, or -1 when the id is not selected, has no visible
     // token or maps to a page out of range), read once: a table load issued between page loads
-    // would make the in-order memory counter wait for every page in flight
+    // would make the in-order memory counter wait for every page in flight. The ids and the
+    // context length are requested together, then the table entries of the ids in range.
     const int32_t* my_ids = block_ids + (int64_t)rg * kTopk + (split * kWaves + wave) * BPW;
+    int id = lane < BPW ? my_ids[lane] : -1;
+    int T_raw = ctx_lens[b];
+    asm volatile("" : "+v"(id), "+v"(T_raw));
+    const int T = clamp_ctx(T_raw, max_blocks);
+    const int p = T - q_len + j;
     if (lane < BPW) {
-        const int id = my_ids[lane];
         int page = -1;
         if (id >= 0 && id < max_blocks && id * kBlock <= p) {
             const int pg = block_table[(int64_t)b * max_blocks + id];

@@ -130,11 +130,6 @@ __device__ __forceinline__ float half_max(const HalfRegs& hr, const u32x4 (&qop)
     return best;
 }
 
-__device__ __forceinline__ int page_of(const int32_t* table, int blk, int n_blocks,
-                                       int64_t num_pages) {
-    const int pid = blk < n_blocks ? table[blk] : -1;
-    return (pid >= 0 && pid < num_pages) ? pid : -1;
-}
 
 __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
     const uint8_t* __restrict__ ik_pool, int64_t num_pages, const int32_t* __restrict__ block_table,
@@ -153,17 +148,24 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
     const int blk0 = (blockIdx.x * kPairs + pair) * kPagesPerPair;
     // a pair past the end still takes part in the workgroup barriers below
     const bool active = blk0 < max_blocks;
-    const int T = clamp_ctx(ctx_lens[b], max_blocks);
+    const int32_t* table = block_table + (int64_t)b * max_blocks;
+    // the pair's block-table entries and the context length are requested together (the
+    // entries do not depend on it): one memory round trip before the first page load
+    int pid_raw = -1;
+    if (lane < kPagesPerPair && blk0 + lane < max_blocks) pid_raw = table[blk0 + lane];
+    int T_raw = ctx_lens[b];
+    asm volatile("" : "+v"(pid_raw), "+v"(T_raw));
+    const int T = clamp_ctx(T_raw, max_blocks);
     const int rows = 4 * q_len;
     const int64_t row_base = (int64_t)b * rows;
-    const int32_t* table = block_table + (int64_t)b * max_blocks;
     const int blk_end = active ? min(blk0 + kPagesPerPair, max_blocks) : blk0;
     // blocks past the last query position hold no visible key and are never loaded
     const int n_blocks = T > 0 ? min(max_blocks, (T - 1) / kBlock + 1) : 0;
     // page ids of the pair's blocks, read once into LDS: a block-table load issued between page
     // loads would make the in-order memory counter wait for every page in flight
     if (lane < kPagesPerPair)
-        page_ids[wave][lane] = active ? page_of(table, blk0 + lane, n_blocks, num_pages) : -1;
+        page_ids[wave][lane] = (active && blk0 + lane < n_blocks && pid_raw >= 0 &&
+                                pid_raw < num_pages) ? pid_raw : -1;
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 
     for (int rt = 0; rt < rows; rt += 16) {

@@ -72,30 +72,35 @@ __global__ __launch_bounds__(576) void insert_kernel(uint8_t* __restrict__ k_poo
     const int token = blockIdx.x;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int64_t slot = slots[token];
+    const float* src;
+    if (wave < 4) {
+        if (!k) return;
+        src = k + ((int64_t)token * kKvHeads + wave) * kDim;
+    } else if (wave < 8) {
+        if (!v) return;
+        src = v + ((int64_t)token * kKvHeads + (wave - 4)) * kDim;
+    } else {
+        if (!ik) return;
+        src = ik + (int64_t)token * kDim;
+    }
+    // the values and the slot are requested together: one memory round trip before quantizing
+    f32x2 x = *reinterpret_cast<const f32x2*>(src + 2 * lane);
+    int64_t slot = slots[token];
+    asm volatile("" : "+v"(x));
     if (slot < 0) return;
     const int64_t page = slot >> 7;
     const int t = (int)(slot & 127);
     if (page >= num_pages) return;
-
-    const float* src;
     uint8_t* dst;
     bool column_layout = false;
     if (wave < 4) {
-        if (!k) return;
-        src = k + ((int64_t)token * kKvHeads + wave) * kDim;
         dst = k_pool + (page * kKvHeads + wave) * kHeadPageBytes;
     } else if (wave < 8) {
-        if (!v) return;
-        src = v + ((int64_t)token * kKvHeads + (wave - 4)) * kDim;
         dst = v_pool + (page * kKvHeads + (wave - 4)) * kHeadPageBytes;
         column_layout = true;
     } else {
-        if (!ik) return;
-        src = ik + (int64_t)token * kDim;
         dst = ik_pool + page * kHeadPageBytes;
     }
-    const f32x2 x = *reinterpret_cast<const f32x2*>(src + 2 * lane);
     uint32_t byte, scale;
     quantize_pair(x[0], x[1], byte, scale);
     const int e = 2 * lane;   // first of the lane's two elements
