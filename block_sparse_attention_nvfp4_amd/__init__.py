@@ -227,7 +227,8 @@ class DecodeStep:
         self.block_ids = torch.empty((rows, KV_HEADS, TOPK), dtype=torch.int32, device=device)
         self.out = torch.empty((rows, Q_HEADS, HEAD_DIM), dtype=torch.bfloat16, device=device)
         ws = msa_sparse_attn_workspace_bytes(batch)
-        self.workspace = torch.empty(ws, dtype=torch.uint8, device=device) if ws else None
+        # zero-filled once: the attention leaves its counters at zero after every call
+        self.workspace = torch.zeros(ws, dtype=torch.uint8, device=device) if ws else None
 
     def run(self, slots, k, v, ik, q_idx, q, softmax_scale=None, stream=None):
         scale = default_softmax_scale() if softmax_scale is None else softmax_scale

@@ -141,7 +141,7 @@ int msa_sparse_attn_decode(const msa_cache_t* cache, const msa_batch_t* batch, c
     return hip_status(msa::launch_attention(cache->k, cache->v, cache->num_pages,
                                             batch->block_table, batch->ctx_lens, batch->batch,
                                             batch->max_blocks, batch->q_len, q, block_ids,
-                                            softmax_scale, out, (float*)workspace,
+                                            softmax_scale, out, workspace,
                                             (hipStream_t)stream),
                       fn);
 }

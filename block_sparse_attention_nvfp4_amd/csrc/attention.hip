@@ -20,10 +20,12 @@
 //   O^T += V^T P^T on fp16 matrix cores: P^T in the same lanes is already the B operand and V^T
 //   (A operand, dims x tokens) is the exact fp16 dequantization of the column-layout V page.
 // The wavefronts merge through LDS. With one split the workgroup writes the bf16 output;
-// otherwise it writes an fp32 partial (max, sum, output) and a second kernel merges the splits
-// of each row group. Workgroup ids of both kernels map all work of one (sequence, group) pair
+// otherwise it writes an fp32 partial (max, sum, output) with agent-coherent stores and counts
+// itself finished on the row group's counter; the split that finishes last reads the others'
+// partials, merges them by log-sum-exp and writes the output, so no second launch (and no
+// second kernel boundary) is needed. Workgroup ids map all work of one (sequence, group) pair
 // to one XCD, so the blocks that the query tokens of a pair share are read from HBM once and
-// then hit that XCD's L2, and the merge finds the partials in the same L2.
+// then hit that XCD's L2.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -64,6 +66,19 @@ __device__ __forceinline__ void block_to_lds(const uint8_t* kp, const uint8_t* v
         __builtin_amdgcn_global_load_lds(vp + s * 1024 + lane * 16,
                                          (lds_void*)(buf + kHeadPageBytes + s * 1024), 16, 0,
                                          kNonTemporal);
+}
+
+// Agent-coherent 16-byte store and load (cache policy sc1): written through to, and read from,
+// the point where every XCD sees the same data, without flushing or invalidating the whole L2
+// as a device-scope fence would. Used only for the split partials that one workgroup hands to
+// another within a launch.
+__device__ __forceinline__ void store16_coherent(float* p, const f32x4& v) {
+    asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ f32x4 load16_coherent(const float* p) {
+    f32x4 v;
+    asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(v) : "v"(p) : "memory");
+    return v;
 }
 
 // LDS reads as explicit instructions: the compiler would otherwise wait for every page load in
@@ -166,7 +181,8 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
     const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool, int64_t num_pages,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens, int batch,
     int max_blocks, int q_len, const uint16_t* __restrict__ q, const int32_t* __restrict__ block_ids,
-    float scale_log2, int n_split, uint16_t* __restrict__ out, float* __restrict__ partials) {
+    float scale_log2, int n_split, uint16_t* __restrict__ out, int32_t* __restrict__ counters,
+    float* __restrict__ partials) {
     constexpr int kBufs = BPW > 1 ? 2 : 1;
     static_assert(kWaves * kBufs * kBlockBytes >= kWaves * kGroupHeads * kMergeStride * 4,
                   "merge area must fit in the page buffers");
@@ -175,6 +191,7 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
     __shared__ float sh_l[kWaves][kGroupHeads];
     __shared__ int sh_ids[kWaves][BPW];
     __shared__ int sh_pages[kWaves][BPW];
+    __shared__ int sh_last;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -302,71 +319,56 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
         }
     }
     if (n_split > 1) {
-        float* pp = partials + (((int64_t)rg * n_split + split) * kGroupHeads + h) * kPartStride;
-        if (d0 == 0) {
-            pp[0] = M;
-            pp[1] = L;
+        // hand this split's (max, sum, output) over; the split that finishes last merges all of
+        // them and writes the output (the counter of the row group counts finished splits and is
+        // left at zero again for the next launch)
+        const int64_t part_base = (int64_t)rg * n_split * kGroupHeads;
+        float* pp = partials + ((part_base + (int64_t)split * kGroupHeads) + h) * kPartStride;
+        if (d0 == 0) store16_coherent(pp, f32x4{M, L, 0.f, 0.f});
+        store16_coherent(pp + 4 + d0, f32x4{acc[0], acc[1], acc[2], acc[3]});
+        store16_coherent(pp + 8 + d0, f32x4{acc[4], acc[5], acc[6], acc[7]});
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // stores complete, agent-wide
+        __syncthreads();
+        if (threadIdx.x == 0)
+            sh_last = __hip_atomic_fetch_add(&counters[rg], 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT) == n_split - 1;
+        __syncthreads();
+        if (!sh_last) return;
+        // every other split's values requested before any is used: one memory round trip
+        f32x4 ml[kMaxSplits], a0[kMaxSplits], a1[kMaxSplits];
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplits; sp++) {
+            if (sp < n_split && sp != split) {
+                const float* qp = partials + ((part_base + (int64_t)sp * kGroupHeads) + h) * kPartStride;
+                ml[sp] = load16_coherent(qp);
+                a0[sp] = load16_coherent(qp + 4 + d0);
+                a1[sp] = load16_coherent(qp + 8 + d0);
+            } else {
+                ml[sp] = f32x4{sp == split ? M : -INFINITY, sp == split ? L : 0.f, 0.f, 0.f};
+                a0[sp] = sp == split ? f32x4{acc[0], acc[1], acc[2], acc[3]} : f32x4{0.f, 0.f, 0.f, 0.f};
+                a1[sp] = sp == split ? f32x4{acc[4], acc[5], acc[6], acc[7]} : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         }
-        *reinterpret_cast<f32x4*>(pp + 4 + d0) = f32x4{acc[0], acc[1], acc[2], acc[3]};
-        *reinterpret_cast<f32x4*>(pp + 8 + d0) = f32x4{acc[4], acc[5], acc[6], acc[7]};
-        return;
-    }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    uint32_t packed[4];
+        asm volatile("s_waitcnt vmcnt(0)"
+                     : "+v"(ml[0]), "+v"(ml[1]), "+v"(ml[2]), "+v"(ml[3]), "+v"(a0[0]), "+v"(a0[1]),
+                       "+v"(a0[2]), "+v"(a0[3]), "+v"(a1[0]), "+v"(a1[1]), "+v"(a1[2]), "+v"(a1[3]));
+        if (threadIdx.x == 0)
+            __hip_atomic_store(&counters[rg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        M = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 4; e++)
-        packed[e] = (uint32_t)bf16_bits_rne(acc[2 * e] * inv) |
-                    ((uint32_t)bf16_bits_rne(acc[2 * e + 1] * inv) << 16);
-    uint16_t* op = out + ((int64_t)bq * kQHeads + kGroupHeads * g + h) * kDim + d0;
-    *reinterpret_cast<u32x4*>(op) = u32x4{packed[0], packed[1], packed[2], packed[3]};
-}
-
-// Merge the n_split partials of a row group into bf16 output; the same pair -> XCD mapping as
-// the attention kernel, so the partials are read from the L2 they were written to.
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ partials, int batch,
-                                                     int q_len, int n_split,
-                                                     uint16_t* __restrict__ out) {
-    const int local = blockIdx.x >> 3;
-    const int pair = (local / q_len) * 8 + (blockIdx.x & 7);
-    if (pair >= batch * kKvHeads) return;
-    const int j = local - (local / q_len) * q_len;
-    const int b = pair >> 2;
-    const int g = pair & 3;
-    const int bq = b * q_len + j;
-    const int rg = bq * kKvHeads + g;
-    const int h = threadIdx.x >> 4;
-    const int d0 = (threadIdx.x & 15) * 8;
-    const float* base = partials + ((int64_t)rg * n_split * kGroupHeads + h) * kPartStride;
-    const int stride = kGroupHeads * kPartStride;
-    // every split's (max, sum, 8 outputs) requested before any is used: one memory round trip
-    float mv[kMaxSplits], lv[kMaxSplits];
-    f32x4 av[kMaxSplits], bv[kMaxSplits];
+        for (int sp = 0; sp < kMaxSplits; sp++) M = fmaxf(M, ml[sp][0]);
+        L = 0.f;
 #pragma unroll
-    for (int sp = 0; sp < kMaxSplits; sp++) {
-        if (sp < n_split) {
-            const float* pp = base + sp * stride;
-            mv[sp] = pp[0];
-            lv[sp] = pp[1];
-            av[sp] = *reinterpret_cast<const f32x4*>(pp + 4 + d0);
-            bv[sp] = *reinterpret_cast<const f32x4*>(pp + 8 + d0);
-        } else {
-            mv[sp] = -INFINITY;
-            lv[sp] = 0.f;
-            av[sp] = bv[sp] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-    }
-    float M = -INFINITY;
+        for (int e = 0; e < 8; e++) acc[e] = 0.f;
 #pragma unroll
-    for (int sp = 0; sp < kMaxSplits; sp++) M = fmaxf(M, mv[sp]);
-    float L = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int sp = 0; sp < kMaxSplits; sp++) {
+            const float w = ml[sp][0] == -INFINITY ? 0.f : fast_exp2(ml[sp][0] - M);
+            L += w * ml[sp][1];
 #pragma unroll
-    for (int sp = 0; sp < kMaxSplits; sp++) {
-        const float w = (mv[sp] == -INFINITY) ? 0.f : fast_exp2(mv[sp] - M);
-        L += w * lv[sp];
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            acc[e] += w * av[sp][e];
-            acc[4 + e] += w * bv[sp][e];
+            for (int e = 0; e < 4; e++) {
+                acc[e] += w * a0[sp][e];
+                acc[4 + e] += w * a1[sp][e];
+            }
         }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -389,43 +391,53 @@ int attn_num_splits(int batch, int q_len) {
     return 4;
 }
 
+// Workspace with split partials: one int32 counter per row group (zero between launches),
+// padded to 256 bytes, then the partials.
+static size_t attn_counter_bytes(int batch, int q_len) {
+    return ((size_t)batch * q_len * kKvHeads * sizeof(int32_t) + 255) / 256 * 256;
+}
+
 size_t attn_workspace_bytes(int batch, int q_len) {
     const int ns = attn_num_splits(batch, q_len);
     if (ns == 1) return 0;
-    return (size_t)batch * q_len * kKvHeads * ns * kGroupHeads * kPartStride * sizeof(float);
+    return attn_counter_bytes(batch, q_len) +
+           (size_t)batch * q_len * kKvHeads * ns * kGroupHeads * kPartStride * sizeof(float);
 }
 
 hipError_t launch_attention(const uint8_t* k_pool, const uint8_t* v_pool, int64_t num_pages,
                             const int32_t* block_table, const int32_t* ctx_lens, int batch,
                             int max_blocks, int q_len, const uint16_t* q, const int32_t* ids,
-                            float softmax_scale, uint16_t* out, float* workspace,
+                            float softmax_scale, uint16_t* out, void* workspace,
                             hipStream_t stream) {
     const int ns = attn_num_splits(batch, q_len);
     const int pairs = batch * kKvHeads;
     const int pair_slots = 8 * ((pairs + 7) / 8);
     const float scale_log2 = softmax_scale * 1.4426950408889634f;
     const dim3 grid(pair_slots * q_len * ns), block(kWaves * 64);
+    int32_t* counters = nullptr;
+    float* partials = nullptr;
+    if (ns > 1) {
+        counters = static_cast<int32_t*>(workspace);
+        partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                            attn_counter_bytes(batch, q_len));
+    }
     switch (ns) {
         case 1:
             hipLaunchKernelGGL(attention_kernel<4>, grid, block, 0, stream, k_pool, v_pool,
                                num_pages, block_table, ctx_lens, batch, max_blocks, q_len, q, ids,
-                               scale_log2, ns, out, workspace);
+                               scale_log2, ns, out, counters, partials);
             break;
         case 2:
             hipLaunchKernelGGL(attention_kernel<2>, grid, block, 0, stream, k_pool, v_pool,
                                num_pages, block_table, ctx_lens, batch, max_blocks, q_len, q, ids,
-                               scale_log2, ns, out, workspace);
+                               scale_log2, ns, out, counters, partials);
             break;
         default:
             hipLaunchKernelGGL(attention_kernel<1>, grid, block, 0, stream, k_pool, v_pool,
                                num_pages, block_table, ctx_lens, batch, max_blocks, q_len, q, ids,
-                               scale_log2, ns, out, workspace);
+                               scale_log2, ns, out, counters, partials);
             break;
     }
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess || ns == 1) return err;
-    hipLaunchKernelGGL(combine_kernel, dim3(pair_slots * q_len), dim3(256), 0, stream, workspace,
-                       batch, q_len, ns, out);
     return hipGetLastError();
 }
 

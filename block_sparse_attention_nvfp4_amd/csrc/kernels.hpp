@@ -26,7 +26,7 @@ size_t attn_workspace_bytes(int batch, int q_len);
 hipError_t launch_attention(const uint8_t* k_pool, const uint8_t* v_pool, int64_t num_pages,
                             const int32_t* block_table, const int32_t* ctx_lens, int batch,
                             int max_blocks, int q_len, const uint16_t* q, const int32_t* ids,
-                            float softmax_scale, uint16_t* out, float* workspace,
+                            float softmax_scale, uint16_t* out, void* workspace,
                             hipStream_t stream);
 
 }  // namespace msa

@@ -185,9 +185,12 @@ size_t msa_sparse_attn_workspace_bytes(const msa_batch_t *batch);
  *               the selected blocks of (b, j, h / 16) with t <= p, t < T_b (exact NVFP4 values;
  *               fp32 softmax and accumulation); 0 when no key is valid.
  *   workspace : device scratch of at least msa_sparse_attn_workspace_bytes(batch) bytes
- *               (may be NULL when that is 0), 256-byte aligned. It holds the split partial
- *               results between the attention and merge launches; calls that share a workspace
- *               must not overlap in time (same stream, or ordered).
+ *               (may be NULL when that is 0), 256-byte aligned, ZERO-FILLED before its first
+ *               use; every call leaves it zero-filled again where it must be (the per-row-group
+ *               counters at its start), so one zero fill at allocation serves all later calls.
+ *               It holds the split partial results that the workgroups of one call hand to each
+ *               other; calls that share a workspace must not overlap in time (same stream, or
+ *               ordered).
  * Errors: MSA_ERR_INVALID_ARG (NULL pointers, sizes < 1), MSA_ERR_WORKSPACE.
  */
 int msa_sparse_attn_decode(const msa_cache_t *cache, const msa_batch_t *batch, const uint16_t *q,
