@@ -9,10 +9,11 @@
 //
 // Rows of up to 4,096 candidate blocks: one 64-lane wavefront per row, no atomics. The row's
 // scores become order-preserving integer keys in registers (candidate i in lane i % 64). The
-// 15th-largest of the 64 per-lane maxima, found by a bitwise search with ballot counts, is a lower
-// bound of the 15th-largest key (at least 15 keys reach it), so the selection lies among the keys
-// at or above it. Those few candidates are compacted into LDS in ascending block order and each
-// is ranked exactly against the others by (key, block index); the 15 best, already in ascending
+// 15th-largest of the 64 per-lane maxima, found by a bitwise search with ballot counts (two bits
+// per step), is a lower bound of the 15th-largest key (at least 15 keys reach it), so the
+// selection lies among the keys at or above it. Those few candidates are compacted into LDS in
+// ascending block order as (key, inverted block index) composites and each is ranked exactly
+// against the others by reading them back as LDS broadcasts; the 15 best, already in ascending
 // block order, are written with the forced block last. When more than 64 candidates reach the
 // bound (heavy ties), the wavefront extracts the 15 best one by one instead.
 // Longer rows: one 256-thread workgroup per row with a 4-pass radix select (8-bit digits, LDS
@@ -238,8 +239,7 @@ template <int KPL>  // keys per lane: rows of up to 64 * KPL candidates
 __global__ __launch_bounds__(kRowsPerWg * 64) void topk_wave_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ ctx_lens, int max_blocks,
     int q_len, int rows, int32_t* __restrict__ ids) {
-    __shared__ uint32_t cand_key[kRowsPerWg][64];
-    __shared__ int cand_idx[kRowsPerWg][64];
+    __shared__ uint64_t cand[kRowsPerWg][128];  // 64 candidates + one spare entry per lane
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int row = blockIdx.x * kRowsPerWg + wave;  // ((b * q_len + j) * 4 + g)
@@ -280,43 +280,51 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void topk_wave_kernel(
         key[k] = i < m ? order_key(v[k]) : 0u;
         lmax = max(lmax, key[k]);
     }
-    // bound: the 15th-largest per-lane maximum (bitwise search, most significant bit first)
+    // bound: the 15th-largest per-lane maximum (bitwise search, most significant bits first, two
+    // bits per step: the three candidate values of a step are tested by independent ballots, and
+    // the count of maxima at or above a value falls as the value grows)
     uint32_t bound = 0;
-    for (int bit = 31; bit >= 0; bit--) {
-        const uint32_t cand = bound | (1u << bit);
-        if (popc64(__ballot(lmax >= cand)) >= kTopk - 1) bound = cand;
+#pragma unroll
+    for (int bit = 30; bit >= 0; bit -= 2) {
+        const uint32_t c3 = bound | (3u << bit), c2 = bound | (2u << bit), c1 = bound | (1u << bit);
+        const int n3 = popc64(__ballot(lmax >= c3));
+        const int n2 = popc64(__ballot(lmax >= c2));
+        const int n1 = popc64(__ballot(lmax >= c1));
+        bound = n3 >= kTopk - 1 ? c3 : (n2 >= kTopk - 1 ? c2 : (n1 >= kTopk - 1 ? c1 : bound));
     }
+    // candidates: the keys at or above the bound
     int count = 0;
 #pragma unroll
     for (int k = 0; k < KPL; k++) count += popc64(__ballot(key[k] >= bound));
     if (count <= 64) {
-        // compact the candidates in ascending block order (k-major, lane-minor), then rank them
+        // compact the candidates in ascending block order (k-major, lane-minor) as composites
+        // (key, inverted block index): a larger composite ranks first, and equal keys rank by
+        // the lower block. Lanes without a candidate in slot k write a spare entry instead of
+        // branching.
         int base = 0;
 #pragma unroll
         for (int k = 0; k < KPL; k++) {
             const bool c = key[k] >= bound;
             const uint64_t mask = __ballot(c);
-            if (c) {
-                const int pos = base + lanes_before(mask);
-                cand_key[wave][pos] = key[k];
-                cand_idx[wave][pos] = lane + 64 * k;
-            }
+            const int pos = c ? base + lanes_before(mask) : 64 + lane;
+            cand[wave][pos] = ((uint64_t)key[k] << 32) | (uint32_t)~(uint32_t)(lane + 64 * k);
             base += popc64(mask);
         }
         __builtin_amdgcn_wave_barrier();
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        // lane t holds candidate t; each compares itself with all others through register
-        // broadcasts (no LDS round trip per comparison)
-        const uint32_t mk = lane < count ? cand_key[wave][lane] : 0u;
-        const int my_idx = lane < count ? cand_idx[wave][lane] : 0;
+        // candidate t of lane t counts the candidates ranked before it, reading them eight at a
+        // time as LDS broadcasts
+        const uint64_t mine = lane < count ? cand[wave][lane] : 0u;
         int rank = 0;
-        for (int t = 0; t < count; t++) {
-            const uint32_t ok = __builtin_amdgcn_readlane(mk, t);
-            rank += (ok > mk) || (ok == mk && t < lane);  // same key: lower block first
+        for (int t0 = 0; t0 < count; t0 += 8) {
+            uint64_t o[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++) o[i] = cand[wave][t0 + i];
+#pragma unroll
+            for (int i = 0; i < 8; i++) rank += (t0 + i < count) && o[i] > mine;
         }
         const bool sel = lane < count && rank < kTopk - 1;
         const uint64_t smask = __ballot(sel);
-        if (sel) out[lanes_before(smask)] = my_idx;
+        if (sel) out[lanes_before(smask)] = (int)~(uint32_t)mine;
     } else {
         // heavy ties: take the best remaining (key, lowest index) 15 times
         uint32_t taken[(KPL + 31) / 32] = {};
