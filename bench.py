@@ -6,7 +6,9 @@ Workload (the headline configuration): batch 8, context 131,072 tokens (1,024 bl
 permutation, top-16 selection. Synthetic, seeded data (msa_inputs, recipe 3).
 
 A step is one layer's whole decode path: NVFP4 insert of the step's 32 new tokens, indexer over
-the full context, block top-16, sparse attention (+ split-K combine). Each step runs on the next
+the full context, block top-16 and sparse attention (selection, attention and the split merge in
+one launch, msa_select_attn_decode; the same step as four calls is timed too and reported as
+config.ms_per_step_four_calls). Each step runs on the next
 of L layers whose caches live in separate memory, so the index-key working set (L x 75.5 MB)
 exceeds the 256 MB Infinity Cache and the scan streams from HBM, as a multi-layer decode does.
 Each layer's step is captured once in a HIP graph; the timed region replays K steps.
@@ -43,7 +45,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle CPU time")
     ap.add_argument("--only", default="", help="profiling aid: run a calibration copy of "
                     f"{COPY_BYTES >> 20} MiB, then only this kernel in a loop "
-                    "(insert|indexer|topk|attention), and exit")
+                    "(insert|indexer|topk|attention|select_attention), and exit")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs of '--only indexer' (FETCH_SIZE, "
                          "WRITE_SIZE) into profiles/indexer_spec128k_traffic.json and exit")
@@ -163,10 +165,15 @@ def main():
         "topk": lambda s: msa.msa_block_topk(s.block_scores, batch, 16, s.block_ids),
         "attention": lambda s: msa.msa_sparse_attn_decode(s.cache, batch, qq, s.block_ids, scale,
                                                           s.out, s.workspace),
+        "select_attention": lambda s: msa.msa_select_attn_decode(s.cache, batch, s.block_scores, 16,
+                                                                 s.block_ids, qq, scale, s.out,
+                                                                 s.workspace),
     }
+    STEP = ("insert", "indexer", "select_attention")          # the timed step: three launches
+    FOUR_CALLS = ("insert", "indexer", "topk", "attention")   # the same step as four calls
 
-    def full_step(s):
-        for name in ("insert", "indexer", "topk", "attention"):
+    def full_step(s, names=STEP):
+        for name in names:
             calls[name](s)
 
     # eager warmup (also fills every layer's scores/ids used by single-kernel timings)
@@ -198,6 +205,10 @@ def main():
         with torch.cuda.graph(layers_graph, stream=stream):
             for s in steps:
                 full_step(s)
+        four_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(four_graph, stream=stream):
+            for s in steps:
+                full_step(s, FOUR_CALLS)
         graphs = []  # single-layer steps for a step count that is not a multiple of L
         for s in steps:
             g = torch.cuda.CUDAGraph()
@@ -229,6 +240,17 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         dev_ms = ev0.elapsed_time(ev1)
+
+        # the same steps as four calls (selection and attention as two launches)
+        four_graph.replay()
+        torch.cuda.synchronize()
+        e4s, e4e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e4s.record(stream)
+        for _ in range(max(1, args.steps // L)):
+            four_graph.replay()
+        e4e.record(stream)
+        torch.cuda.synchronize()
+        four_ms = e4s.elapsed_time(e4e) / (max(1, args.steps // L) * L)
 
         # per-kernel durations: graphs of L back-to-back launches, HIP events around each replay
         kernel_us = {}
@@ -264,7 +286,7 @@ def main():
             for blk in set(int(x) for x in ids[b, :, g].ravel() if x >= 0):
                 gathered_tokens += min(128, T - blk * 128)
     attn_bytes = gathered_tokens * 144 + 2 * B * q * 64 * 128 * 2 + B * q * 4 * 16 * 4
-    attn_gbs = attn_bytes / (kernel_us["attention"] * 1e-6) / 1e9
+    attn_gbs = attn_bytes / (kernel_us["select_attention"] * 1e-6) / 1e9
 
     result = {
         "metric": METRIC,
@@ -286,6 +308,8 @@ def main():
             "batch": B, "context": T, "query_tokens": q, "cache_dtype": "nvfp4",
             "layers_rotated": L, "graph": f"{L} layer steps per graph replay",
             "device_ms_per_step": round(dev_ms / args.steps, 5),
+            "step_calls": "msa_kv_insert_nvfp4, msa_indexer_score, msa_select_attn_decode",
+            "ms_per_step_four_calls": round(four_ms, 5),
         },
         "kernels_us": {k: round(v, 3) for k, v in kernel_us.items()},
         "roofline": {

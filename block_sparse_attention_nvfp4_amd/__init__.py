@@ -9,9 +9,11 @@ HIP stream into the C calls, with the same names:
     msa_block_topk(block_scores, batch, topk, block_ids)
     msa_sparse_attn_workspace_bytes(batch)
     msa_sparse_attn_decode(cache, batch, q, block_ids, softmax_scale, out, workspace)
+    msa_select_attn_decode(cache, batch, block_scores, topk, block_ids, q, softmax_scale, out,
+                           workspace)        # the last two in one launch
 
 A non-zero status raises MSAError. There is no fallback: importing fails loudly when the
-library has not been built (python -m block_sparse_attention_nvfp4_amd.build).
+library has not been built (python block_sparse_attention_nvfp4_amd/build.py).
 """
 from __future__ import annotations
 
@@ -39,8 +41,8 @@ MSA_ERR_WORKSPACE = -3
 MSA_ERR_HIP = -4
 
 EXPORTED = ("msa_page_bytes", "msa_kv_insert_nvfp4", "msa_indexer_score", "msa_block_topk",
-            "msa_sparse_attn_workspace_bytes", "msa_sparse_attn_decode", "msa_last_error",
-            "msa_version")
+            "msa_sparse_attn_workspace_bytes", "msa_sparse_attn_decode", "msa_select_attn_decode",
+            "msa_last_error", "msa_version")
 
 
 class MSAError(RuntimeError):
@@ -63,7 +65,7 @@ class _Batch(ctypes.Structure):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m block_sparse_attention_nvfp4_amd.build` (hipcc, gfx950)")
+                          "`python block_sparse_attention_nvfp4_amd/build.py` (hipcc, gfx950)")
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     L.msa_page_bytes.restype, L.msa_page_bytes.argtypes = sz, [ctypes.c_int]
@@ -78,6 +80,9 @@ def _load() -> ctypes.CDLL:
     L.msa_sparse_attn_decode.restype = ctypes.c_int
     L.msa_sparse_attn_decode.argtypes = [ctypes.POINTER(_Cache), ctypes.POINTER(_Batch), vp, vp,
                                          ctypes.c_float, vp, vp, sz, vp]
+    L.msa_select_attn_decode.restype = ctypes.c_int
+    L.msa_select_attn_decode.argtypes = [ctypes.POINTER(_Cache), ctypes.POINTER(_Batch), vp, i32,
+                                         vp, vp, ctypes.c_float, vp, vp, sz, vp]
     L.msa_last_error.restype, L.msa_last_error.argtypes = ctypes.c_char_p, []
     L.msa_version.restype, L.msa_version.argtypes = ctypes.c_char_p, []
     return L
@@ -212,15 +217,38 @@ def msa_sparse_attn_decode(cache: Cache, batch: Batch, q: torch.Tensor, block_id
                                       ws_ptr, ws_bytes, _stream(stream)))
 
 
+def msa_select_attn_decode(cache: Cache, batch: Batch, block_scores: torch.Tensor, topk: int,
+                           block_ids: torch.Tensor, q: torch.Tensor, softmax_scale: float,
+                           out: torch.Tensor, workspace: Optional[torch.Tensor],
+                           stream=None) -> None:
+    if tuple(block_scores.shape) != (batch.rows, KV_HEADS, batch.max_blocks):
+        raise ValueError("block_scores: expected [batch*q_len][4][max_blocks]")
+    if tuple(block_ids.shape) != (batch.rows, KV_HEADS, int(topk)):
+        raise ValueError("block_ids: expected [batch*q_len][4][topk]")
+    if tuple(q.shape) != (batch.rows, Q_HEADS, HEAD_DIM) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q and out: expected [batch*q_len][64][128]")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _ptr(workspace, workspace.dtype, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.msa_select_attn_decode(ctypes.byref(cache._c), ctypes.byref(batch._c),
+                                      _ptr(block_scores, torch.float32, "block_scores"), int(topk),
+                                      _ptr(block_ids, torch.int32, "block_ids"),
+                                      _ptr(q, torch.bfloat16, "q"), float(softmax_scale),
+                                      _ptr(out, torch.bfloat16, "out"), ws_ptr, ws_bytes,
+                                      _stream(stream)))
+
+
 def default_softmax_scale() -> float:
     return 1.0 / math.sqrt(HEAD_DIM)
 
 
 class DecodeStep:
-    """Buffers and the four calls of one MSA decode step for a fixed batch shape."""
+    """Buffers and the calls of one MSA decode step for a fixed batch shape: insert, indexer, then
+    selection and attention in one launch (fused=True) or as two calls (fused=False)."""
 
-    def __init__(self, cache: Cache, batch: Batch, device="cuda"):
-        self.cache, self.batch = cache, batch
+    def __init__(self, cache: Cache, batch: Batch, device="cuda", fused: bool = True):
+        self.cache, self.batch, self.fused = cache, batch, fused
         rows = batch.rows
         self.block_scores = torch.empty((rows, KV_HEADS, batch.max_blocks), dtype=torch.float32,
                                         device=device)
@@ -234,7 +262,11 @@ class DecodeStep:
         scale = default_softmax_scale() if softmax_scale is None else softmax_scale
         msa_kv_insert_nvfp4(self.cache, slots, k, v, ik, stream)
         msa_indexer_score(self.cache, self.batch, q_idx, self.block_scores, stream)
-        msa_block_topk(self.block_scores, self.batch, TOPK, self.block_ids, stream)
-        msa_sparse_attn_decode(self.cache, self.batch, q, self.block_ids, scale, self.out,
-                               self.workspace, stream)
+        if self.fused:
+            msa_select_attn_decode(self.cache, self.batch, self.block_scores, TOPK, self.block_ids,
+                                   q, scale, self.out, self.workspace, stream)
+        else:
+            msa_block_topk(self.block_scores, self.batch, TOPK, self.block_ids, stream)
+            msa_sparse_attn_decode(self.cache, self.batch, q, self.block_ids, scale, self.out,
+                                   self.workspace, stream)
         return self.out

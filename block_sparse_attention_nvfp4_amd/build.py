@@ -1,6 +1,8 @@
 """Build libmsa.so (the HIP kernels and the C ABI of include/msa.h) in-tree for gfx950.
 
-    python -m block_sparse_attention_nvfp4_amd.build      # or build() from Python
+    python block_sparse_attention_nvfp4_amd/build.py      # or build() of __graft_entry__
+
+(run as a file: importing the package loads the library this builds)
 
 Each .hip file under csrc/ is compiled by hipcc to an object and the objects are linked into
 block_sparse_attention_nvfp4_amd/libmsa.so. Packed-fp32 instructions are disabled for all

@@ -123,6 +123,17 @@ size_t msa_sparse_attn_workspace_bytes(const msa_batch_t* batch) {
     return msa::attn_workspace_bytes(batch->batch, batch->q_len);
 }
 
+static int check_workspace(const msa_batch_t* batch, void* workspace, size_t ws_bytes,
+                           const char* fn) {
+    const size_t need = msa::attn_workspace_bytes(batch->batch, batch->q_len);
+    if (need > 0 && (!workspace || ws_bytes < need))
+        return fail(MSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                    workspace ? ws_bytes : (size_t)0);
+    if (need > 0 && ((uintptr_t)workspace & 255u))
+        return fail(MSA_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+    return MSA_OK;
+}
+
 int msa_sparse_attn_decode(const msa_cache_t* cache, const msa_batch_t* batch, const uint16_t* q,
                            const int32_t* block_ids, float softmax_scale, uint16_t* out,
                            void* workspace, size_t ws_bytes, void* stream) {
@@ -132,17 +143,32 @@ int msa_sparse_attn_decode(const msa_cache_t* cache, const msa_batch_t* batch, c
     if ((rc = check_batch(batch, fn))) return rc;
     if (!q || !block_ids || !out)
         return fail(MSA_ERR_INVALID_ARG, "%s: q, block_ids or out is NULL", fn);
-    const size_t need = msa::attn_workspace_bytes(batch->batch, batch->q_len);
-    if (need > 0 && (!workspace || ws_bytes < need))
-        return fail(MSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
-                    workspace ? ws_bytes : (size_t)0);
-    if (need > 0 && ((uintptr_t)workspace & 255u))
-        return fail(MSA_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+    if ((rc = check_workspace(batch, workspace, ws_bytes, fn))) return rc;
     return hip_status(msa::launch_attention(cache->k, cache->v, cache->num_pages,
                                             batch->block_table, batch->ctx_lens, batch->batch,
                                             batch->max_blocks, batch->q_len, q, block_ids,
                                             softmax_scale, out, workspace,
                                             (hipStream_t)stream),
+                      fn);
+}
+
+int msa_select_attn_decode(const msa_cache_t* cache, const msa_batch_t* batch,
+                           const float* block_scores, int32_t topk, int32_t* block_ids,
+                           const uint16_t* q, float softmax_scale, uint16_t* out,
+                           void* workspace, size_t ws_bytes, void* stream) {
+    static const char* fn = "msa_select_attn_decode";
+    int rc = check_cache(cache, fn, true, false);
+    if (rc) return rc;
+    if ((rc = check_batch(batch, fn))) return rc;
+    if (!block_scores || !block_ids || !q || !out)
+        return fail(MSA_ERR_INVALID_ARG, "%s: block_scores, block_ids, q or out is NULL", fn);
+    if (topk != MSA_TOPK) return fail(MSA_ERR_UNSUPPORTED, "%s: topk=%d (only 16 is built)", fn, topk);
+    if ((rc = check_workspace(batch, workspace, ws_bytes, fn))) return rc;
+    return hip_status(msa::launch_select_attention(cache->k, cache->v, cache->num_pages,
+                                                   batch->block_table, batch->ctx_lens,
+                                                   batch->batch, batch->max_blocks, batch->q_len,
+                                                   block_scores, block_ids, q, softmax_scale, out,
+                                                   workspace, (hipStream_t)stream),
                       fn);
 }
 

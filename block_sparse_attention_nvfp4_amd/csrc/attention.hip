@@ -28,6 +28,7 @@
 // then hit that XCD's L2.
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "select_wave.hpp"
 
 namespace msa {
 namespace {
@@ -176,13 +177,16 @@ __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c
     }
 }
 
-template <int BPW>
+// SELECT: the row's blocks are selected here from its block scores (wavefront 0 of every
+// workgroup of the row; the first split also writes them to block_ids) instead of being read
+// from block_ids.
+template <int BPW, bool SELECT>
 __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
     const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool, int64_t num_pages,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens, int batch,
-    int max_blocks, int q_len, const uint16_t* __restrict__ q, const int32_t* __restrict__ block_ids,
-    float scale_log2, int n_split, uint16_t* __restrict__ out, int32_t* __restrict__ counters,
-    float* __restrict__ partials) {
+    int max_blocks, int q_len, const uint16_t* __restrict__ q, int32_t* __restrict__ block_ids,
+    const float* __restrict__ scores, float scale_log2, int n_split, uint16_t* __restrict__ out,
+    int32_t* __restrict__ counters, float* __restrict__ partials) {
     constexpr int kBufs = BPW > 1 ? 2 : 1;
     static_assert(kWaves * kBufs * kBlockBytes >= kWaves * kGroupHeads * kMergeStride * 4,
                   "merge area must fit in the page buffers");
@@ -192,6 +196,9 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
     __shared__ int sh_ids[kWaves][BPW];
     __shared__ int sh_pages[kWaves][BPW];
     __shared__ int sh_last;
+    __shared__ int sh_sel[SELECT ? kTopk : 1];
+    __shared__ uint64_t sel_cand[SELECT ? kSelectScratch : 1];
+    __shared__ int sh_tbl[SELECT ? kSelectFusedMaxBlocks : 1];  // the sequence's block table
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -213,16 +220,50 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
     // token or maps to a page out of range), read once: a table load issued between page loads
     // would make the in-order memory counter wait for every page in flight. The ids and the
     // context length are requested together, then the table entries of the ids in range.
-    const int32_t* my_ids = block_ids + (int64_t)rg * kTopk + (split * kWaves + wave) * BPW;
-    int id = lane < BPW ? my_ids[lane] : -1;
-    int T_raw = ctx_lens[b];
-    asm volatile("" : "+v"(id), "+v"(T_raw));
+    int id, T_raw;
+    if constexpr (SELECT) {
+        if (wave == 0) {
+            // the row's scores and the context length in one memory round trip, then the
+            // selection, exactly as msa_block_topk makes it
+            float sv[16];
+            load_row_scores<16>(scores + (int64_t)rg * max_blocks, max_blocks, lane, sv);
+            int t_sel = ctx_lens[b];
+#pragma unroll
+            for (int k = 0; k < 16; k++) asm volatile("" : "+v"(sv[k]));
+            asm volatile("" : "+v"(t_sel));
+            const int p_sel = clamp_ctx(t_sel, max_blocks) - q_len + j;
+            select_row<16>(sv, eligible_blocks(p_sel, max_blocks), lane, sel_cand, sh_sel);
+            if (split == 0 && lane < kTopk) block_ids[(int64_t)rg * kTopk + lane] = sh_sel[lane];
+        } else {
+            // meanwhile the other wavefronts copy the sequence's block-table row into LDS (all
+            // loads issued before any is stored), so the selected blocks' pages need no further
+            // memory round trip
+            constexpr int kThr = (kWaves - 1) * 64;
+            constexpr int kPer = (kSelectFusedMaxBlocks + kThr - 1) / kThr;
+            const int t0 = threadIdx.x - 64;
+            const int32_t* trow = block_table + (int64_t)b * max_blocks;
+            int tv[kPer];
+#pragma unroll
+            for (int r = 0; r < kPer; r++) tv[r] = trow[min(t0 + r * kThr, max_blocks - 1)];
+#pragma unroll
+            for (int r = 0; r < kPer; r++)
+                if (t0 + r * kThr < max_blocks) sh_tbl[t0 + r * kThr] = tv[r];
+        }
+        __syncthreads();
+        id = lane < BPW ? sh_sel[(split * kWaves + wave) * BPW + lane] : -1;
+        T_raw = ctx_lens[b];
+    } else {
+        const int32_t* my_ids = block_ids + (int64_t)rg * kTopk + (split * kWaves + wave) * BPW;
+        id = lane < BPW ? my_ids[lane] : -1;
+        T_raw = ctx_lens[b];
+        asm volatile("" : "+v"(id), "+v"(T_raw));
+    }
     const int T = clamp_ctx(T_raw, max_blocks);
     const int p = T - q_len + j;
     if (lane < BPW) {
         int page = -1;
         if (id >= 0 && id < max_blocks && id * kBlock <= p) {
-            const int pg = block_table[(int64_t)b * max_blocks + id];
+            const int pg = SELECT ? sh_tbl[id] : block_table[(int64_t)b * max_blocks + id];
             page = (pg >= 0 && pg < num_pages) ? pg : -1;
         }
         sh_ids[wave][lane] = page >= 0 ? id : -1;
@@ -404,11 +445,14 @@ size_t attn_workspace_bytes(int batch, int q_len) {
            (size_t)batch * q_len * kKvHeads * ns * kGroupHeads * kPartStride * sizeof(float);
 }
 
-hipError_t launch_attention(const uint8_t* k_pool, const uint8_t* v_pool, int64_t num_pages,
-                            const int32_t* block_table, const int32_t* ctx_lens, int batch,
-                            int max_blocks, int q_len, const uint16_t* q, const int32_t* ids,
-                            float softmax_scale, uint16_t* out, void* workspace,
-                            hipStream_t stream) {
+namespace {
+
+template <bool SELECT>
+hipError_t launch_attention_t(const uint8_t* k_pool, const uint8_t* v_pool, int64_t num_pages,
+                              const int32_t* block_table, const int32_t* ctx_lens, int batch,
+                              int max_blocks, int q_len, const uint16_t* q, int32_t* ids,
+                              const float* scores, float softmax_scale, uint16_t* out,
+                              void* workspace, hipStream_t stream) {
     const int ns = attn_num_splits(batch, q_len);
     const int pairs = batch * kKvHeads;
     const int pair_slots = 8 * ((pairs + 7) / 8);
@@ -421,24 +465,46 @@ hipError_t launch_attention(const uint8_t* k_pool, const uint8_t* v_pool, int64_
         partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
                                             attn_counter_bytes(batch, q_len));
     }
+#define MSA_LAUNCH_ATTN(BPW_)                                                                    \
+    hipLaunchKernelGGL((attention_kernel<BPW_, SELECT>), grid, block, 0, stream, k_pool, v_pool, \
+                       num_pages, block_table, ctx_lens, batch, max_blocks, q_len, q, ids,       \
+                       scores, scale_log2, ns, out, counters, partials)
     switch (ns) {
-        case 1:
-            hipLaunchKernelGGL(attention_kernel<4>, grid, block, 0, stream, k_pool, v_pool,
-                               num_pages, block_table, ctx_lens, batch, max_blocks, q_len, q, ids,
-                               scale_log2, ns, out, counters, partials);
-            break;
-        case 2:
-            hipLaunchKernelGGL(attention_kernel<2>, grid, block, 0, stream, k_pool, v_pool,
-                               num_pages, block_table, ctx_lens, batch, max_blocks, q_len, q, ids,
-                               scale_log2, ns, out, counters, partials);
-            break;
-        default:
-            hipLaunchKernelGGL(attention_kernel<1>, grid, block, 0, stream, k_pool, v_pool,
-                               num_pages, block_table, ctx_lens, batch, max_blocks, q_len, q, ids,
-                               scale_log2, ns, out, counters, partials);
-            break;
+        case 1: MSA_LAUNCH_ATTN(4); break;
+        case 2: MSA_LAUNCH_ATTN(2); break;
+        default: MSA_LAUNCH_ATTN(1); break;
     }
+#undef MSA_LAUNCH_ATTN
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention(const uint8_t* k_pool, const uint8_t* v_pool, int64_t num_pages,
+                            const int32_t* block_table, const int32_t* ctx_lens, int batch,
+                            int max_blocks, int q_len, const uint16_t* q, const int32_t* ids,
+                            float softmax_scale, uint16_t* out, void* workspace,
+                            hipStream_t stream) {
+    return launch_attention_t<false>(k_pool, v_pool, num_pages, block_table, ctx_lens, batch,
+                                     max_blocks, q_len, q, const_cast<int32_t*>(ids), nullptr,
+                                     softmax_scale, out, workspace, stream);
+}
+
+hipError_t launch_select_attention(const uint8_t* k_pool, const uint8_t* v_pool, int64_t num_pages,
+                                   const int32_t* block_table, const int32_t* ctx_lens, int batch,
+                                   int max_blocks, int q_len, const float* scores, int32_t* ids,
+                                   const uint16_t* q, float softmax_scale, uint16_t* out,
+                                   void* workspace, hipStream_t stream) {
+    if (max_blocks > kSelectFusedMaxBlocks) {
+        // long rows: the selection kernel for them, then the attention reading its ids
+        const hipError_t err = launch_topk(scores, ctx_lens, batch, max_blocks, q_len, ids, stream);
+        if (err != hipSuccess) return err;
+        return launch_attention(k_pool, v_pool, num_pages, block_table, ctx_lens, batch,
+                                max_blocks, q_len, q, ids, softmax_scale, out, workspace, stream);
+    }
+    return launch_attention_t<true>(k_pool, v_pool, num_pages, block_table, ctx_lens, batch,
+                                    max_blocks, q_len, q, ids, scores, softmax_scale, out,
+                                    workspace, stream);
 }
 
 }  // namespace msa

@@ -21,6 +21,7 @@
 // in ascending block order.
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "select_wave.hpp"
 
 namespace msa {
 namespace {
@@ -28,12 +29,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kPerThread = 16;  // keys held in registers: rows of up to 4,096 candidates
 
-// Order-preserving map of a non-NaN float to uint32 (larger float -> larger key); -0 == +0.
-__device__ __forceinline__ uint32_t order_key(float f) {
-    if (f == 0.0f) f = 0.0f;
-    const uint32_t u = __float_as_uint(f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 
 // Inclusive prefix sum over a 64-lane wavefront.
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x, int lane) {
@@ -228,18 +223,11 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
 // ---------------------------------------------------------------- one wavefront per row
 constexpr int kRowsPerWg = 4;
 
-__device__ __forceinline__ int popc64(uint64_t x) { return __popcll(x); }
-
-// Number of lanes before this one whose bit is set.
-__device__ __forceinline__ int lanes_before(uint64_t mask) {
-    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
-}
-
 template <int KPL>  // keys per lane: rows of up to 64 * KPL candidates
 __global__ __launch_bounds__(kRowsPerWg * 64) void topk_wave_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ ctx_lens, int max_blocks,
     int q_len, int rows, int32_t* __restrict__ ids) {
-    __shared__ uint64_t cand[kRowsPerWg][128];  // 64 candidates + one spare entry per lane
+    __shared__ uint64_t cand[kRowsPerWg][kSelectScratch];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int row = blockIdx.x * kRowsPerWg + wave;  // ((b * q_len + j) * 4 + g)
@@ -247,123 +235,17 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void topk_wave_kernel(
     const int bq = row >> 2;
     const int b = bq / q_len;
     const int j = bq - b * q_len;
-    int32_t* out = ids + (int64_t)row * kTopk;
     // the row's scores are requested together with the context length, before anything waits
-    // for either: one memory round trip (an index past the row reads its last score and is
-    // discarded)
-    const float* s = scores + (int64_t)row * max_blocks;
+    // for either: one memory round trip
     float v[KPL];
-#pragma unroll
-    for (int k = 0; k < KPL; k++) v[k] = s[min(lane + 64 * k, max_blocks - 1)];
+    load_row_scores<KPL>(scores + (int64_t)row * max_blocks, max_blocks, lane, v);
     int T_raw = ctx_lens[b];
     // both loads are needed here, so the compiler issues all of them before its single wait
 #pragma unroll
     for (int k = 0; k < KPL; k++) asm volatile("" : "+v"(v[k]));
     asm volatile("" : "+v"(T_raw));
-    const int T = clamp_ctx(T_raw, max_blocks);
-    const int p = T - q_len + j;
-    if (p < 0) {
-        if (lane < kTopk) out[lane] = -1;
-        return;
-    }
-    const int n = min(p / kBlock + 1, max_blocks);  // eligible blocks 0..n-1, forced n-1
-    if (n <= kTopk) {
-        if (lane < kTopk) out[lane] = lane < n ? lane : -1;
-        return;
-    }
-    const int m = n - 1;  // candidates 0..m-1 compete for 15 places
-    uint32_t key[KPL];  // 0 marks "no candidate": every real key is above it
-    uint32_t lmax = 0;
-#pragma unroll
-    for (int k = 0; k < KPL; k++) {
-        const int i = lane + 64 * k;
-        key[k] = i < m ? order_key(v[k]) : 0u;
-        lmax = max(lmax, key[k]);
-    }
-    // bound: the 15th-largest per-lane maximum (bitwise search, most significant bits first, two
-    // bits per step: the three candidate values of a step are tested by independent ballots, and
-    // the count of maxima at or above a value falls as the value grows)
-    uint32_t bound = 0;
-#pragma unroll
-    for (int bit = 30; bit >= 0; bit -= 2) {
-        const uint32_t c3 = bound | (3u << bit), c2 = bound | (2u << bit), c1 = bound | (1u << bit);
-        const int n3 = popc64(__ballot(lmax >= c3));
-        const int n2 = popc64(__ballot(lmax >= c2));
-        const int n1 = popc64(__ballot(lmax >= c1));
-        bound = n3 >= kTopk - 1 ? c3 : (n2 >= kTopk - 1 ? c2 : (n1 >= kTopk - 1 ? c1 : bound));
-    }
-    // candidates: the keys at or above the bound
-    int count = 0;
-#pragma unroll
-    for (int k = 0; k < KPL; k++) count += popc64(__ballot(key[k] >= bound));
-    if (count <= 64) {
-        // compact the candidates in ascending block order (k-major, lane-minor) as composites
-        // (key, inverted block index): a larger composite ranks first, and equal keys rank by
-        // the lower block. Lanes without a candidate in slot k write a spare entry instead of
-        // branching.
-        int base = 0;
-#pragma unroll
-        for (int k = 0; k < KPL; k++) {
-            const bool c = key[k] >= bound;
-            const uint64_t mask = __ballot(c);
-            const int pos = c ? base + lanes_before(mask) : 64 + lane;
-            cand[wave][pos] = ((uint64_t)key[k] << 32) | (uint32_t)~(uint32_t)(lane + 64 * k);
-            base += popc64(mask);
-        }
-        __builtin_amdgcn_wave_barrier();
-        // candidate t of lane t counts the candidates ranked before it, reading them eight at a
-        // time as LDS broadcasts
-        const uint64_t mine = lane < count ? cand[wave][lane] : 0u;
-        int rank = 0;
-        for (int t0 = 0; t0 < count; t0 += 8) {
-            uint64_t o[8];
-#pragma unroll
-            for (int i = 0; i < 8; i++) o[i] = cand[wave][t0 + i];
-#pragma unroll
-            for (int i = 0; i < 8; i++) rank += (t0 + i < count) && o[i] > mine;
-        }
-        const bool sel = lane < count && rank < kTopk - 1;
-        const uint64_t smask = __ballot(sel);
-        if (sel) out[lanes_before(smask)] = (int)~(uint32_t)mine;
-    } else {
-        // heavy ties: take the best remaining (key, lowest index) 15 times
-        uint32_t taken[(KPL + 31) / 32] = {};
-        for (int r = 0; r < kTopk - 1; r++) {
-            uint32_t bk = 0;
-            int bi = 0x7fffffff;
-#pragma unroll
-            for (int k = 0; k < KPL; k++) {
-                const int i = lane + 64 * k;
-                const bool avail = !((taken[k >> 5] >> (k & 31)) & 1u) && key[k] != 0u;
-                if (avail && (key[k] > bk || (key[k] == bk && i < bi))) {
-                    bk = key[k];
-                    bi = i;
-                }
-            }
-#pragma unroll
-            for (int d = 32; d >= 1; d >>= 1) {
-                const uint32_t ok = __shfl_xor(bk, d, 64);
-                const int oi = __shfl_xor(bi, d, 64);
-                if (ok > bk || (ok == bk && oi < bi)) {
-                    bk = ok;
-                    bi = oi;
-                }
-            }
-            if ((bi & 63) == lane) {
-                const int k = bi >> 6;
-                taken[k >> 5] |= 1u << (k & 31);
-            }
-        }
-        int base = 0;
-#pragma unroll
-        for (int k = 0; k < KPL; k++) {
-            const bool sel = (taken[k >> 5] >> (k & 31)) & 1u;
-            const uint64_t mask = __ballot(sel);
-            if (sel) out[base + lanes_before(mask)] = lane + 64 * k;
-            base += popc64(mask);
-        }
-    }
-    if (lane == 0) out[kTopk - 1] = m;  // the forced block of the query token, the largest id
+    const int p = clamp_ctx(T_raw, max_blocks) - q_len + j;
+    select_row<KPL>(v, eligible_blocks(p, max_blocks), lane, cand[wave], ids + (int64_t)row * kTopk);
 }
 
 }  // namespace

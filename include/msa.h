@@ -18,6 +18,8 @@
  *
  * A decode step is four calls on one stream, in this order:
  *   msa_kv_insert_nvfp4 -> msa_indexer_score -> msa_block_topk -> msa_sparse_attn_decode
+ * or three, with the last two fused:
+ *   msa_kv_insert_nvfp4 -> msa_indexer_score -> msa_select_attn_decode
  *
  * Conventions for every entry point
  *   - All tensor arguments are device pointers owned by the caller. The library allocates
@@ -195,6 +197,21 @@ size_t msa_sparse_attn_workspace_bytes(const msa_batch_t *batch);
  */
 int msa_sparse_attn_decode(const msa_cache_t *cache, const msa_batch_t *batch, const uint16_t *q,
                            const int32_t *block_ids, float softmax_scale, uint16_t *out,
+                           void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Selection and attention in one launch: the effect of msa_block_topk(block_scores, batch, topk,
+ * block_ids) followed by msa_sparse_attn_decode(cache, batch, q, block_ids, softmax_scale, out,
+ * workspace, ws_bytes), with the same results bit for bit (block_ids is written as well), but
+ * each attention workgroup selects its row's blocks itself from the scores, so the selection
+ * needs no launch of its own and its ids no round trip through memory ("MiniMax M3 on vLLM",
+ * section "Decode indexer score kernel": the top-k boundary stays close to the scores). Rows of
+ * more than 1,025 blocks (max_blocks > 1025) run the two steps as two launches.
+ * Arguments and workspace as for the two calls. Errors: as for the two calls.
+ */
+int msa_select_attn_decode(const msa_cache_t *cache, const msa_batch_t *batch,
+                           const float *block_scores, int32_t topk, int32_t *block_ids,
+                           const uint16_t *q, float softmax_scale, uint16_t *out,
                            void *workspace, size_t ws_bytes, void *stream);
 
 /* Message of the last failed call on this thread ("" if none). */

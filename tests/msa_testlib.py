@@ -69,7 +69,8 @@ def gpu_sequence_caches(cache, w: mi.Workload, b: int):
 
 # ------------------------------------------------------------------ GPU side
 class GpuRun:
-    def __init__(self, w: mi.Workload, device: str = "cuda", chunk: int = 1 << 15):
+    def __init__(self, w: mi.Workload, device: str = "cuda", chunk: int = 1 << 15,
+                 fused: bool = True):
         import block_sparse_attention_nvfp4_amd as msa
         self.msa = msa
         self.w = w
@@ -92,7 +93,7 @@ class GpuRun:
         self.new_ik = torch.cat([w.ik_rows(b, t0, t1, device) for b, t0, t1 in toks])
         self.q_idx = w.q_idx.to(device)
         self.q = w.q.to(device)
-        self.step = msa.DecodeStep(self.cache, self.batch, device)
+        self.step = msa.DecodeStep(self.cache, self.batch, device, fused=fused)
 
     def insert(self, b: int, t0: int, t1: int):
         w, dev = self.w, self.cache.ik.device

@@ -21,7 +21,11 @@ def declared_functions():
 @pytest.fixture(scope="module")
 def msa():
     if not os.path.exists(LIB):
-        from block_sparse_attention_nvfp4_amd import build
+        import importlib.util
+        path = os.path.join(os.path.dirname(LIB), "build.py")
+        spec = importlib.util.spec_from_file_location("msa_build", path)
+        build = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(build)
         build.build()
     import block_sparse_attention_nvfp4_amd as m
     return m
@@ -95,3 +99,11 @@ def test_invalid_arguments_return_codes_without_launch(msa):
     assert L.msa_sparse_attn_decode(by(_cache()), small, None, 1, 0.1, 1, 256, need, None) == msa.MSA_ERR_INVALID_ARG
     # large batches need no workspace (one workgroup per row group covers the chip)
     assert L.msa_sparse_attn_workspace_bytes(by(_batch(b=256, q=1))) == 0
+    # selection + attention in one launch: the checks of both calls
+    sel = L.msa_select_attn_decode
+    assert sel(by(_cache()), small, 1, 8, 1, 1, 0.1, 1, 256, need, None) == msa.MSA_ERR_UNSUPPORTED
+    assert sel(by(_cache()), small, None, 16, 1, 1, 0.1, 1, 256, need, None) == msa.MSA_ERR_INVALID_ARG
+    assert sel(by(_cache()), small, 1, 16, None, 1, 0.1, 1, 256, need, None) == msa.MSA_ERR_INVALID_ARG
+    assert sel(by(_cache(k=None)), small, 1, 16, 1, 1, 0.1, 1, 256, need, None) == msa.MSA_ERR_INVALID_ARG
+    assert sel(by(_cache()), small, 1, 16, 1, 1, 0.1, 1, None, 0, None) == msa.MSA_ERR_WORKSPACE
+    assert sel(by(_cache()), small, 1, 16, 1, 1, 0.1, 1, 257, need, None) == msa.MSA_ERR_WORKSPACE

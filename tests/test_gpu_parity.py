@@ -127,3 +127,16 @@ def test_step_is_deterministic(run):
     assert torch.equal(ids, g.step.block_ids)
     assert torch.equal(first, again)
 
+
+def test_fused_selection_matches_separate_launches(run):
+    """msa_select_attn_decode (the fixture's step) equals msa_block_topk + msa_sparse_attn_decode
+    bit for bit, ids and outputs."""
+    import block_sparse_attention_nvfp4_amd as msa
+    name, w, g, _ = run
+    fused_ids = g.step.block_ids.clone()
+    fused_out = g.step.out.clone()
+    sep = msa.DecodeStep(g.cache, g.batch, "cuda", fused=False)
+    sep.run(g.new_slots, g.new_k, g.new_v, g.new_ik, g.q_idx, g.q)
+    torch.cuda.synchronize()
+    assert torch.equal(sep.block_ids, fused_ids), name
+    assert torch.equal(sep.out, fused_out), name
