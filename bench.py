@@ -6,9 +6,11 @@ Workload (the headline configuration): batch 8, context 131,072 tokens (1,024 bl
 permutation, top-16 selection. Synthetic, seeded data (msa_inputs, recipe 3).
 
 A step is one layer's whole decode path: NVFP4 insert of the step's 32 new tokens, indexer over
-the full context, block top-16 and sparse attention (selection, attention and the split merge in
-one launch, msa_select_attn_decode; the same step as four calls is timed too and reported as
-config.ms_per_step_four_calls). Each step runs on the next
+the full context, block top-16 and sparse attention, as two launches: insert and indexer
+(msa_insert_indexer_score), then selection, attention and the split merge
+(msa_select_attn_decode). The same step as three calls (insert, indexer, selection + attention)
+and as four is timed too (config.ms_per_step_three_calls, config.ms_per_step_four_calls).
+Each step runs on the next
 of L layers whose caches live in separate memory, so the index-key working set (L x 75.5 MB)
 exceeds the 256 MB Infinity Cache and the scan streams from HBM, as a multi-layer decode does.
 Each layer's step is captured once in a HIP graph; the timed region replays K steps.
@@ -45,10 +47,11 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle CPU time")
     ap.add_argument("--only", default="", help="profiling aid: run a calibration copy of "
                     f"{COPY_BYTES >> 20} MiB, then only this kernel in a loop "
-                    "(insert|indexer|topk|attention|select_attention), and exit")
+                    "(insert|indexer|insert_indexer|topk|attention|select_attention), and exit")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="turn two rocprofv3 --pmc counter CSVs of '--only indexer' (FETCH_SIZE, "
-                         "WRITE_SIZE) into profiles/indexer_spec128k_traffic.json and exit")
+                    help="turn two rocprofv3 --pmc counter CSVs of '--only insert_indexer' "
+                         "(FETCH_SIZE, WRITE_SIZE) into "
+                         "profiles/insert_indexer_spec128k_traffic.json and exit")
     return ap.parse_args()
 
 
@@ -79,16 +82,22 @@ def _counter_rows(path):
         return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in csv.DictReader(f)]
 
 
+# the dominant kernel of the step (insert + indexer launch), its sources and its dispatch name
+ROOF_KERNEL = "insert_indexer"
+ROOF_SOURCES = ("indexer.hip", "nvfp4_quant.hpp", "device_common.hpp")
+ROOF_DISPATCH = "indexer_kernel<true>"
+
+
 def traffic_from(fetch_csv, write_csv):
-    """HBM bytes per indexer launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled
-    by what the same counter reads for the calibration copy: the largest runtime copy-kernel
-    dispatch of the run, which moves COPY_BYTES in and COPY_BYTES out."""
-    rec = {"source_digest": source_digest("indexer.hip", "device_common.hpp"),
-           "copy_bytes": COPY_BYTES}
+    """HBM bytes per insert + indexer launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by what the same counter reads for the calibration copy: the largest runtime
+    copy-kernel dispatch of the run, which moves COPY_BYTES in and COPY_BYTES out."""
+    rec = {"source_digest": source_digest(*ROOF_SOURCES), "copy_bytes": COPY_BYTES,
+           "kernel": ROOF_DISPATCH}
     total = 0.0
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = _counter_rows(path)
-        idx = [v for k, v in rows if "indexer_kernel" in k]
+        idx = [v for k, v in rows if ROOF_DISPATCH in k]
         copies = [v for k, v in rows if "copyBuffer" in k]
         assert idx and copies, (counter, sorted(set(k for k, _ in rows))[:20])
         copy_kib = max(copies)
@@ -96,12 +105,12 @@ def traffic_from(fetch_csv, write_csv):
         assert 0.25 <= factor <= 4.0, (counter, copy_kib)
         mean_kib = sum(idx) / len(idx)
         scaled = mean_kib * 1024.0 / factor
-        rec[counter] = {"indexer_kib_per_dispatch": round(mean_kib, 1), "indexer_dispatches": len(idx),
+        rec[counter] = {"kib_per_dispatch": round(mean_kib, 1), "dispatches": len(idx),
                         "copy_kib": copy_kib, "factor": round(factor, 5),
-                        "indexer_bytes_scaled": round(scaled)}
+                        "bytes_scaled": round(scaled)}
         total += scaled
     rec["hbm_bytes_per_launch"] = round(total)
-    path = os.path.join(ROOT, "profiles", "indexer_spec128k_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{ROOF_KERNEL}_spec128k_traffic.json")
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
@@ -162,6 +171,8 @@ def main():
     calls = {
         "insert": lambda s: msa.msa_kv_insert_nvfp4(s.cache, new_slots, new_k, new_v, new_ik),
         "indexer": lambda s: msa.msa_indexer_score(s.cache, batch, q_idx, s.block_scores),
+        "insert_indexer": lambda s: msa.msa_insert_indexer_score(s.cache, batch, new_k, new_v,
+                                                                 new_ik, q_idx, s.block_scores),
         "topk": lambda s: msa.msa_block_topk(s.block_scores, batch, 16, s.block_ids),
         "attention": lambda s: msa.msa_sparse_attn_decode(s.cache, batch, qq, s.block_ids, scale,
                                                           s.out, s.workspace),
@@ -169,8 +180,9 @@ def main():
                                                                  s.block_ids, qq, scale, s.out,
                                                                  s.workspace),
     }
-    STEP = ("insert", "indexer", "select_attention")          # the timed step: three launches
-    FOUR_CALLS = ("insert", "indexer", "topk", "attention")   # the same step as four calls
+    STEP = ("insert_indexer", "select_attention")               # the timed step: two launches
+    THREE_CALLS = ("insert", "indexer", "select_attention")     # the same step as three calls
+    FOUR_CALLS = ("insert", "indexer", "topk", "attention")     # and as four
 
     def full_step(s, names=STEP):
         for name in names:
@@ -205,10 +217,13 @@ def main():
         with torch.cuda.graph(layers_graph, stream=stream):
             for s in steps:
                 full_step(s)
-        four_graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(four_graph, stream=stream):
-            for s in steps:
-                full_step(s, FOUR_CALLS)
+        alt_graphs = {}
+        for key, names in (("three", THREE_CALLS), ("four", FOUR_CALLS)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for s in steps:
+                    full_step(s, names)
+            alt_graphs[key] = g
         graphs = []  # single-layer steps for a step count that is not a multiple of L
         for s in steps:
             g = torch.cuda.CUDAGraph()
@@ -241,16 +256,18 @@ def main():
         wall = time.perf_counter() - t0
         dev_ms = ev0.elapsed_time(ev1)
 
-        # the same steps as four calls (selection and attention as two launches)
-        four_graph.replay()
-        torch.cuda.synchronize()
-        e4s, e4e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e4s.record(stream)
-        for _ in range(max(1, args.steps // L)):
-            four_graph.replay()
-        e4e.record(stream)
-        torch.cuda.synchronize()
-        four_ms = e4s.elapsed_time(e4e) / (max(1, args.steps // L) * L)
+        # the same steps as three and as four calls
+        alt_ms = {}
+        for key, g in alt_graphs.items():
+            g.replay()
+            torch.cuda.synchronize()
+            e4s, e4e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e4s.record(stream)
+            for _ in range(max(1, args.steps // L)):
+                g.replay()
+            e4e.record(stream)
+            torch.cuda.synchronize()
+            alt_ms[key] = e4s.elapsed_time(e4e) / (max(1, args.steps // L) * L)
 
         # per-kernel durations: graphs of L back-to-back launches, HIP events around each replay
         kernel_us = {}
@@ -269,13 +286,16 @@ def main():
     tokens_per_step = B * q
     value = tokens_per_step / (ms_per_step * 1e-3)
 
-    # algorithmic bytes per launch of the indexer (the dominant kernel): every index-key byte of
-    # the context (72 B per token), the index queries, and the block scores it writes
+    # algorithmic bytes per launch of the insert + indexer kernel (the dominant one): every
+    # index-key byte of the context (72 B per token), the index queries, the block scores it
+    # writes, and the insert's fp32 inputs (9 vectors of 128 per new token) and NVFP4 outputs
     sum_T = sum(w.ctx_lens)
     idx_bytes = sum_T * 72 + B * q * 4 * 128 * 2 + B * q * 4 * w.max_blocks * 4
+    ins_bytes = B * q * 9 * (128 * 4 + 72)
+    roof_bytes = idx_bytes + ins_bytes
+    roof_gbs = roof_bytes / (kernel_us[ROOF_KERNEL] * 1e-6) / 1e9
     idx_gbs = idx_bytes / (kernel_us["indexer"] * 1e-6) / 1e9
-    digest = source_digest("indexer.hip", "device_common.hpp")
-    traffic = load_traffic("indexer", digest)
+    traffic = load_traffic(ROOF_KERNEL, source_digest(*ROOF_SOURCES))
 
     # gather bytes of the attention: K+V of each selected (sequence, group, block) once per
     # distinct block over the 4 draft tokens (144 B per valid token), queries and outputs
@@ -308,20 +328,23 @@ def main():
             "batch": B, "context": T, "query_tokens": q, "cache_dtype": "nvfp4",
             "layers_rotated": L, "graph": f"{L} layer steps per graph replay",
             "device_ms_per_step": round(dev_ms / args.steps, 5),
-            "step_calls": "msa_kv_insert_nvfp4, msa_indexer_score, msa_select_attn_decode",
-            "ms_per_step_four_calls": round(four_ms, 5),
+            "step_calls": "msa_insert_indexer_score, msa_select_attn_decode",
+            "ms_per_step_three_calls": round(alt_ms["three"], 5),
+            "ms_per_step_four_calls": round(alt_ms["four"], 5),
         },
         "kernels_us": {k: round(v, 3) for k, v in kernel_us.items()},
         "roofline": {
             "bound": "hbm",
-            "kernel": "indexer",
-            "achieved": round(idx_gbs, 1),
+            "kernel": ROOF_KERNEL,
+            "achieved": round(roof_gbs, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
-            "frac": round(idx_gbs / PEAK_HBM_GBS, 4),
+            "frac": round(roof_gbs / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "algorithmic_bytes": idx_bytes,
+            "algorithmic_bytes": roof_bytes,
         },
+        "indexer_alone": {"achieved_gbs": round(idx_gbs, 1), "frac": round(idx_gbs / PEAK_HBM_GBS, 4),
+                          "algorithmic_bytes": idx_bytes},
         "attention_gather": {"achieved_gbs": round(attn_gbs, 1), "frac": round(attn_gbs / PEAK_HBM_GBS, 4),
                              "algorithmic_bytes": attn_bytes},
     }

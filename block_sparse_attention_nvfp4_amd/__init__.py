@@ -11,6 +11,9 @@ HIP stream into the C calls, with the same names:
     msa_sparse_attn_decode(cache, batch, q, block_ids, softmax_scale, out, workspace)
     msa_select_attn_decode(cache, batch, block_scores, topk, block_ids, q, softmax_scale, out,
                            workspace)        # the last two in one launch
+    msa_insert_indexer_score(cache, batch, k, v, ik, q_idx, block_scores)  # insert + indexer
+    msa_decode_step(cache, batch, k, v, ik, q_idx, q, topk, softmax_scale, block_scores,
+                    block_ids, out, workspace)   # the two launches above and below in one call
 
 A non-zero status raises MSAError. There is no fallback: importing fails loudly when the
 library has not been built (python block_sparse_attention_nvfp4_amd/build.py).
@@ -42,7 +45,7 @@ MSA_ERR_HIP = -4
 
 EXPORTED = ("msa_page_bytes", "msa_kv_insert_nvfp4", "msa_indexer_score", "msa_block_topk",
             "msa_sparse_attn_workspace_bytes", "msa_sparse_attn_decode", "msa_select_attn_decode",
-            "msa_last_error", "msa_version")
+            "msa_insert_indexer_score", "msa_decode_step", "msa_last_error", "msa_version")
 
 
 class MSAError(RuntimeError):
@@ -83,6 +86,12 @@ def _load() -> ctypes.CDLL:
     L.msa_select_attn_decode.restype = ctypes.c_int
     L.msa_select_attn_decode.argtypes = [ctypes.POINTER(_Cache), ctypes.POINTER(_Batch), vp, i32,
                                          vp, vp, ctypes.c_float, vp, vp, sz, vp]
+    L.msa_insert_indexer_score.restype = ctypes.c_int
+    L.msa_insert_indexer_score.argtypes = [ctypes.POINTER(_Cache), ctypes.POINTER(_Batch), vp, vp,
+                                           vp, vp, vp, vp]
+    L.msa_decode_step.restype = ctypes.c_int
+    L.msa_decode_step.argtypes = [ctypes.POINTER(_Cache), ctypes.POINTER(_Batch), vp, vp, vp, vp,
+                                  vp, i32, ctypes.c_float, vp, vp, vp, vp, sz, vp]
     L.msa_last_error.restype, L.msa_last_error.argtypes = ctypes.c_char_p, []
     L.msa_version.restype, L.msa_version.argtypes = ctypes.c_char_p, []
     return L
@@ -239,16 +248,65 @@ def msa_select_attn_decode(cache: Cache, batch: Batch, block_scores: torch.Tenso
                                       _stream(stream)))
 
 
+def _check_step_shapes(batch: Batch, **tensors) -> None:
+    n = batch.rows
+    tails = dict(k=(KV_HEADS, HEAD_DIM), v=(KV_HEADS, HEAD_DIM), ik=(HEAD_DIM,),
+                 q_idx=(KV_HEADS, HEAD_DIM), q=(Q_HEADS, HEAD_DIM), out=(Q_HEADS, HEAD_DIM),
+                 block_scores=(KV_HEADS, batch.max_blocks), block_ids=(KV_HEADS, TOPK))
+    for name, t in tensors.items():
+        if tuple(t.shape) != (n, *tails[name]):
+            raise ValueError(f"{name}: expected shape {(n, *tails[name])}, got {tuple(t.shape)}")
+
+
+def msa_insert_indexer_score(cache: Cache, batch: Batch, k: torch.Tensor, v: torch.Tensor,
+                             ik: torch.Tensor, q_idx: torch.Tensor, block_scores: torch.Tensor,
+                             stream=None) -> None:
+    _check_step_shapes(batch, k=k, v=v, ik=ik, q_idx=q_idx, block_scores=block_scores)
+    _check(lib.msa_insert_indexer_score(ctypes.byref(cache._c), ctypes.byref(batch._c),
+                                        _ptr(k, torch.float32, "k"), _ptr(v, torch.float32, "v"),
+                                        _ptr(ik, torch.float32, "ik"),
+                                        _ptr(q_idx, torch.bfloat16, "q_idx"),
+                                        _ptr(block_scores, torch.float32, "block_scores"),
+                                        _stream(stream)))
+
+
+def msa_decode_step(cache: Cache, batch: Batch, k: torch.Tensor, v: torch.Tensor,
+                    ik: torch.Tensor, q_idx: torch.Tensor, q: torch.Tensor, topk: int,
+                    softmax_scale: float, block_scores: torch.Tensor, block_ids: torch.Tensor,
+                    out: torch.Tensor, workspace: Optional[torch.Tensor], stream=None) -> None:
+    _check_step_shapes(batch, k=k, v=v, ik=ik, q_idx=q_idx, q=q, out=out,
+                       block_scores=block_scores)
+    if tuple(block_ids.shape) != (batch.rows, KV_HEADS, int(topk)):
+        raise ValueError("block_ids: expected [batch*q_len][4][topk]")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _ptr(workspace, workspace.dtype, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.msa_decode_step(ctypes.byref(cache._c), ctypes.byref(batch._c),
+                               _ptr(k, torch.float32, "k"), _ptr(v, torch.float32, "v"),
+                               _ptr(ik, torch.float32, "ik"), _ptr(q_idx, torch.bfloat16, "q_idx"),
+                               _ptr(q, torch.bfloat16, "q"), int(topk), float(softmax_scale),
+                               _ptr(block_scores, torch.float32, "block_scores"),
+                               _ptr(block_ids, torch.int32, "block_ids"),
+                               _ptr(out, torch.bfloat16, "out"), ws_ptr, ws_bytes,
+                               _stream(stream)))
+
+
 def default_softmax_scale() -> float:
     return 1.0 / math.sqrt(HEAD_DIM)
 
 
 class DecodeStep:
-    """Buffers and the calls of one MSA decode step for a fixed batch shape: insert, indexer, then
-    selection and attention in one launch (fused=True) or as two calls (fused=False)."""
+    """Buffers and the calls of one MSA decode step for a fixed batch shape. mode "step": one
+    msa_decode_step call (two launches); "select": insert, indexer, then selection and attention
+    in one launch; "separate": the four calls. All three give the same bytes."""
 
-    def __init__(self, cache: Cache, batch: Batch, device="cuda", fused: bool = True):
-        self.cache, self.batch, self.fused = cache, batch, fused
+    MODES = ("step", "select", "separate")
+
+    def __init__(self, cache: Cache, batch: Batch, device="cuda", mode: str = "step"):
+        if mode not in self.MODES:
+            raise ValueError(f"mode must be one of {self.MODES}")
+        self.cache, self.batch, self.mode = cache, batch, mode
         rows = batch.rows
         self.block_scores = torch.empty((rows, KV_HEADS, batch.max_blocks), dtype=torch.float32,
                                         device=device)
@@ -259,10 +317,17 @@ class DecodeStep:
         self.workspace = torch.zeros(ws, dtype=torch.uint8, device=device) if ws else None
 
     def run(self, slots, k, v, ik, q_idx, q, softmax_scale=None, stream=None):
+        """slots: the new tokens' cache slots (page * 128 + token), used by the modes that call
+        msa_kv_insert_nvfp4; they must be the slots of positions T_b - q_len + j, which
+        msa_decode_step derives itself."""
         scale = default_softmax_scale() if softmax_scale is None else softmax_scale
+        if self.mode == "step":
+            msa_decode_step(self.cache, self.batch, k, v, ik, q_idx, q, TOPK, scale,
+                            self.block_scores, self.block_ids, self.out, self.workspace, stream)
+            return self.out
         msa_kv_insert_nvfp4(self.cache, slots, k, v, ik, stream)
         msa_indexer_score(self.cache, self.batch, q_idx, self.block_scores, stream)
-        if self.fused:
+        if self.mode == "select":
             msa_select_attn_decode(self.cache, self.batch, self.block_scores, TOPK, self.block_ids,
                                    q, scale, self.out, self.workspace, stream)
         else:

@@ -172,4 +172,54 @@ int msa_select_attn_decode(const msa_cache_t* cache, const msa_batch_t* batch,
                       fn);
 }
 
+static int check_insert_indexer(const msa_cache_t* cache, const msa_batch_t* batch,
+                                const float* k, const float* v, const float* ik,
+                                const uint16_t* q_idx, const float* block_scores, const char* fn) {
+    int rc = check_cache(cache, fn, true, true);
+    if (rc) return rc;
+    if ((rc = check_batch(batch, fn))) return rc;
+    if (!k || !v || !ik || !q_idx || !block_scores)
+        return fail(MSA_ERR_INVALID_ARG, "%s: k, v, ik, q_idx or block_scores is NULL", fn);
+    return MSA_OK;
+}
+
+int msa_insert_indexer_score(const msa_cache_t* cache, const msa_batch_t* batch, const float* k,
+                             const float* v, const float* ik, const uint16_t* q_idx,
+                             float* block_scores, void* stream) {
+    static const char* fn = "msa_insert_indexer_score";
+    const int rc = check_insert_indexer(cache, batch, k, v, ik, q_idx, block_scores, fn);
+    if (rc) return rc;
+    return hip_status(msa::launch_insert_indexer(cache->k, cache->v, cache->ik, cache->num_pages,
+                                                 batch->block_table, batch->ctx_lens,
+                                                 batch->batch, batch->max_blocks, batch->q_len, k,
+                                                 v, ik, q_idx, block_scores, (hipStream_t)stream),
+                      fn);
+}
+
+int msa_decode_step(const msa_cache_t* cache, const msa_batch_t* batch, const float* k,
+                    const float* v, const float* ik, const uint16_t* q_idx, const uint16_t* q,
+                    int32_t topk, float softmax_scale, float* block_scores, int32_t* block_ids,
+                    uint16_t* out, void* workspace, size_t ws_bytes, void* stream) {
+    static const char* fn = "msa_decode_step";
+    int rc = check_insert_indexer(cache, batch, k, v, ik, q_idx, block_scores, fn);
+    if (rc) return rc;
+    if (!q || !block_ids || !out)
+        return fail(MSA_ERR_INVALID_ARG, "%s: q, block_ids or out is NULL", fn);
+    if (topk != MSA_TOPK) return fail(MSA_ERR_UNSUPPORTED, "%s: topk=%d (only 16 is built)", fn, topk);
+    if ((rc = check_workspace(batch, workspace, ws_bytes, fn))) return rc;
+    const hipStream_t s = (hipStream_t)stream;
+    rc = hip_status(msa::launch_insert_indexer(cache->k, cache->v, cache->ik, cache->num_pages,
+                                               batch->block_table, batch->ctx_lens, batch->batch,
+                                               batch->max_blocks, batch->q_len, k, v, ik, q_idx,
+                                               block_scores, s),
+                    fn);
+    if (rc) return rc;
+    return hip_status(msa::launch_select_attention(cache->k, cache->v, cache->num_pages,
+                                                   batch->block_table, batch->ctx_lens,
+                                                   batch->batch, batch->max_blocks, batch->q_len,
+                                                   block_scores, block_ids, q, softmax_scale, out,
+                                                   workspace, s),
+                      fn);
+}
+
 }  // extern "C"

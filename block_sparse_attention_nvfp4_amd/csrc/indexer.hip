@@ -25,10 +25,12 @@
 // Rows beyond 16 (q_len > 4) loop over row tiles.
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "nvfp4_quant.hpp"
 
 namespace msa {
 namespace {
 
+constexpr int kFusedMaxNew = 8;    // new tokens per sequence the fused step's patch stages
 constexpr int kPairs = 4;            // wavefront pairs per workgroup; a pair shares its blocks
 constexpr int kWaves = 2 * kPairs;   // wavefront h of a pair scores the tokens of half h of each page
 constexpr int kBufs = 2;             // LDS buffers per wavefront (half pages in flight: kBufs - 1)
@@ -67,12 +69,14 @@ static_assert(kBufs <= 3, "wait_halves covers at most two half pages in flight")
 
 // The same wait for loads issued before `after` half pages, and the registers those loads
 // write: the asm operands keep every use of `v` after the wait.
-__device__ __forceinline__ void wait_halves_then(int after, u32x4 (&v)[4]) {
+__device__ __forceinline__ void wait_halves_then(int after, u32x4 (&v)[4], int& w) {
+#define MSA_WAIT(n) asm volatile("s_waitcnt vmcnt(" #n ")" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(w) :: "memory")
     switch (after) {
-        case 0: asm volatile("s_waitcnt vmcnt(0)" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]) :: "memory"); break;
-        case 1: asm volatile("s_waitcnt vmcnt(5)" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]) :: "memory"); break;
-        default: asm volatile("s_waitcnt vmcnt(10)" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]) :: "memory"); break;
+        case 0: MSA_WAIT(0); break;
+        case 1: MSA_WAIT(5); break;
+        default: MSA_WAIT(10); break;
     }
+#undef MSA_WAIT
 }
 
 // This lane's four 16-byte code chunks and the two scale words of its slabs, read from LDS
@@ -131,21 +135,118 @@ __device__ __forceinline__ float half_max(const HalfRegs& hr, const u32x4 (&qop)
 }
 
 
+// Fused decode step: the step's new tokens (positions T - q_len .. T - 1) are written to the
+// caches by other wavefronts of the same launch, so a page of new tokens may still hold their
+// old bytes when it streams in. The wavefront scoring half h of such a page writes the NVFP4
+// bytes of those of the new index keys that fall in its half into its LDS copy of the page,
+// exactly where the insert writes them in memory (the token's code chunks of the half and its
+// scale bytes, which only this half reads). Every wavefront copies the sequence's new index keys
+// (fp32) into its own staging area `pq` at start-up, token j at pq + 512 j (no workgroup barrier:
+// only the wavefront itself reads them); prepare_patch_token quantizes one of its tokens (one
+// per page while the pages stream in, every remaining one at the first page that holds new
+// tokens) and overwrites the token's first 72 bytes with the result: the code byte of lane l's
+// elements 2l, 2l+1 at pq + 512 j + l, scale g at pq + 512 j + 64 + g.
+constexpr int kStageBytes = kDim * 4;
+
+__device__ __forceinline__ bool is_patch_token(int j, int blk0, int blk_end, int T, int q_len,
+                                               int h) {
+    const int pos = T - q_len + j;
+    return pos >= 0 && (pos >> 7) >= blk0 && (pos >> 7) < blk_end && ((pos & 31) >> 4) == h;
+}
+
+__device__ __forceinline__ void prepare_patch_token(uint8_t* pq, int j, int lane) {
+    const uint32_t a = (uint32_t)(uintptr_t)(pq + kStageBytes * j);
+    f32x2 x;
+    asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(x) : "v"(a + 8 * lane)
+                 : "memory");
+    uint32_t byte, scale;
+    quantize_pair(x[0], x[1], byte, scale);
+    asm volatile("ds_write_b8 %0, %1" ::"v"(a + lane), "v"(byte) : "memory");
+    if ((lane & 7) == 0)
+        asm volatile("ds_write_b8 %0, %1" ::"v"(a + 64 + (lane >> 3)), "v"(scale) : "memory");
+}
+
+__device__ __forceinline__ void patch_new_tokens(const uint8_t* buf, int tok0, int T, int q_len,
+                                                 int h, int lane, const uint8_t* pq) {
+    const int first = max(T - q_len, tok0), last = min(T - 1, tok0 + kBlock - 1);
+    for (int pos = first; pos <= last; pos++) {
+        const int t = pos - tok0;
+        if (((t & 31) >> 4) != h) continue;
+        const uint32_t a = (uint32_t)(uintptr_t)(pq + kStageBytes * (pos - (T - q_len)));
+        uint32_t byte, scale;
+        asm volatile("ds_read_u8 %0, %2\n\tds_read_u8 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(byte), "=&v"(scale) : "v"(a + lane), "v"(a + 64 + (lane >> 3))
+                     : "memory");
+        const int sl = ((t & 31) >> 2) - 4 * h;  // the token's code slab within the half
+        const uint32_t cb = (uint32_t)(uintptr_t)buf + sl * 1024 +
+                            (16 * (lane >> 4) + 4 * (t >> 5) + (t & 3)) * 16 + (lane & 15);
+        asm volatile("ds_write_b8 %0, %1" ::"v"(cb), "v"(byte) : "memory");
+        if ((lane & 7) == 0) {
+            const int g = lane >> 3;
+            const uint32_t sb = (uint32_t)(uintptr_t)buf + 4096 + (g >> 1) * 256 + (t >> 5) * 64 +
+                                (t & 3) * 16 + ((t & 31) >> 2) * 2 + (g & 1);
+            asm volatile("ds_write_b8 %0, %1" ::"v"(sb), "v"(scale) : "memory");
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// Source of insert item i = 9 j + vec of sequence b: new token j, head vector vec (K heads
+// 0-3, V heads 4-7, the index key 8).
+__device__ __forceinline__ const float* item_source(int item, int b, int q_len,
+                                                    const float* new_k, const float* new_v,
+                                                    const float* new_ik) {
+    const int j = item / 9, vec = item - 9 * (item / 9);
+    const int64_t token = (int64_t)b * q_len + j;
+    return vec < 4   ? new_k + (token * kKvHeads + vec) * kDim
+           : vec < 8 ? new_v + (token * kKvHeads + vec - 4) * kDim
+                     : new_ik + token * kDim;
+}
+
+// Store insert item i of sequence b (quantized to byte / scale by this wavefront) at position
+// T - q_len + j, on page `page` (the block-table entry of that position).
+__device__ __forceinline__ void store_item(int item, int64_t page, int pos, int64_t num_pages,
+                                           uint32_t byte, uint32_t scale, uint8_t* k_pool,
+                                           uint8_t* v_pool, uint8_t* ik_pool, int lane) {
+    if (pos < 0 || page < 0 || page >= num_pages) return;
+    const int vec = item - 9 * (item / 9);
+    uint8_t* dst = vec < 4   ? k_pool + (page * kKvHeads + vec) * kHeadPageBytes
+                   : vec < 8 ? v_pool + (page * kKvHeads + vec - 4) * kHeadPageBytes
+                             : ik_pool + page * kHeadPageBytes;
+    store_quantized(byte, scale, dst, pos & 127, vec >= 4 && vec < 8, lane);
+}
+
+// FUSED (decode step with q_len <= kFusedMaxNew): the launch also inserts the step's new tokens.
+// The 9 q_len head vectors of sequence b are spread over the sequence's workgroups and their
+// wavefronts (wavefront w of workgroup x takes items x + gx (w + 8 m)). A wavefront loads its
+// first item with its start-up loads, requests the item's block-table entry as soon as the
+// context length is known, quantizes while the first pages stream in, and stores after its last
+// page has arrived, so that the stores never stand between page loads in the in-order memory
+// counter. The indexer workgroups patch the new index keys into their page copies
+// (patch_new_tokens): a page may be read before or after another workgroup's store lands.
+template <bool FUSED>
 __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
-    const uint8_t* __restrict__ ik_pool, int64_t num_pages, const int32_t* __restrict__ block_table,
+    const uint8_t* ik_pool, int64_t num_pages, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ ctx_lens, int max_blocks, int q_len,
-    const uint16_t* __restrict__ q_idx, float* __restrict__ scores) {
+    const uint16_t* __restrict__ q_idx, float* __restrict__ scores, uint8_t* k_pool_w,
+    uint8_t* v_pool_w, uint8_t* ik_pool_w, const float* __restrict__ new_k,
+    const float* __restrict__ new_v, const float* __restrict__ new_ik) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves][kBufs][kHalfBytes];
     __shared__ int page_ids[kWaves][kPagesPerPair];
     __shared__ float stash[kPairs][kPagesPerPair][2][16];  // half-page maxima of the row tile
+    __shared__ __attribute__((aligned(16))) uint8_t stage[FUSED ? kWaves : 1][FUSED ? kFusedMaxNew * kStageBytes : 16];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    const int gx = (max_blocks + kPairs * kPagesPerPair - 1) / (kPairs * kPagesPerPair);
+    const int wg = blockIdx.x;
+    const int b = wg / gx;
+    const int n_items = FUSED ? 9 * q_len : 0;
+    int item = (wg - b * gx) + gx * __builtin_amdgcn_readfirstlane(wave);  // first insert item
     const int pair = wave >> 1;
     const int h = wave & 1;
     const int n = lane & 15;  // B/D column: query row within the tile
     const int c = lane >> 4;  // lane group
-    const int b = blockIdx.y;
-    const int blk0 = (blockIdx.x * kPairs + pair) * kPagesPerPair;
+    const int blk0 = ((wg - b * gx) * kPairs + pair) * kPagesPerPair;
     // a pair past the end still takes part in the workgroup barriers below
     const bool active = blk0 < max_blocks;
     const int32_t* table = block_table + (int64_t)b * max_blocks;
@@ -154,7 +255,21 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
     int pid_raw = -1;
     if (lane < kPagesPerPair && blk0 + lane < max_blocks) pid_raw = table[blk0 + lane];
     int T_raw = ctx_lens[b];
-    asm volatile("" : "+v"(pid_raw), "+v"(T_raw));
+    // fused decode step: the sequence's new index keys (fp32) copied to this wavefront's
+    // staging area, two tokens per direct global->LDS load (lanes past the last token re-read
+    // its last 16 bytes into the unused tail), and this wavefront's first insert item; the loads
+    // join the round trip above
+    f32x2 ins_x = {0.f, 0.f};
+    if constexpr (FUSED) {
+        const float* src = new_ik + (int64_t)b * q_len * kDim;
+        for (int i = 0; i < (q_len + 1) / 2; i++)
+            __builtin_amdgcn_global_load_lds(src + min(256 * i + 4 * lane, q_len * kDim - 4),
+                                             (lds_void*)(stage[wave] + 1024 * i), 16, 0, 0);
+        if (item < n_items)
+            ins_x = *reinterpret_cast<const f32x2*>(
+                item_source(item, b, q_len, new_k, new_v, new_ik) + 2 * lane);
+    }
+    asm volatile("" : "+v"(pid_raw), "+v"(T_raw), "+v"(ins_x));
     const int T = clamp_ctx(T_raw, max_blocks);
     const int rows = 4 * q_len;
     const int64_t row_base = (int64_t)b * rows;
@@ -167,6 +282,13 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
         page_ids[wave][lane] = (active && blk0 + lane < n_blocks && pid_raw >= 0 &&
                                 pid_raw < num_pages) ? pid_raw : -1;
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    // position of the first insert item; its block-table entry is requested with the query rows
+    // of every row tile (below) and used after the last
+    const int ins_pos = FUSED && item < n_items
+                            ? __builtin_amdgcn_readfirstlane(T) - q_len + item / 9 : -1;
+    int ins_page = -1;
+    uint32_t ins_byte = 0, ins_scale = 0;
+    int next_patch = 0;  // this wavefront's patch tokens j < next_patch are quantized
 
     for (int rt = 0; rt < rows; rt += 16) {
         const int r = rt + n;
@@ -196,18 +318,38 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
         u32x4 qraw[4];
         {
             const uint16_t* qp = q_idx + (row_base + min(r, rows - 1)) * kDim + 32 * c;
-            asm volatile(
-                "global_load_dwordx4 %0, %4, off\n\t"
-                "global_load_dwordx4 %1, %4, off offset:16\n\t"
-                "global_load_dwordx4 %2, %4, off offset:32\n\t"
-                "global_load_dwordx4 %3, %4, off offset:48"
-                : "=&v"(qraw[0]), "=&v"(qraw[1]), "=&v"(qraw[2]), "=&v"(qraw[3])
-                : "v"(qp)
-                : "memory");
+            if constexpr (FUSED) {
+                // and the insert item's block-table entry (entry 0 when there is none: a valid
+                // address)
+                const int32_t* tp = table + (ins_pos >= 0 ? ins_pos >> 7 : 0);
+                asm volatile(
+                    "global_load_dwordx4 %0, %5, off\n\t"
+                    "global_load_dwordx4 %1, %5, off offset:16\n\t"
+                    "global_load_dwordx4 %2, %5, off offset:32\n\t"
+                    "global_load_dwordx4 %3, %5, off offset:48\n\t"
+                    "global_load_dword %4, %6, off"
+                    : "=&v"(qraw[0]), "=&v"(qraw[1]), "=&v"(qraw[2]), "=&v"(qraw[3]),
+                      "=&v"(ins_page)
+                    : "v"(qp), "v"(tp)
+                    : "memory");
+            } else {
+                asm volatile(
+                    "global_load_dwordx4 %0, %4, off\n\t"
+                    "global_load_dwordx4 %1, %4, off offset:16\n\t"
+                    "global_load_dwordx4 %2, %4, off offset:32\n\t"
+                    "global_load_dwordx4 %3, %4, off offset:48"
+                    : "=&v"(qraw[0]), "=&v"(qraw[1]), "=&v"(qraw[2]), "=&v"(qraw[3])
+                    : "v"(qp)
+                    : "memory");
+            }
         }
 #pragma unroll
         for (int i = 0; i < kBufs - 1; i++) issue(i);
-        wait_halves_then(__popc(issued), qraw);
+        if constexpr (FUSED) {
+            // the first insert item is quantized while the first pages are in flight
+            if (rt == 0 && item < n_items) quantize_pair(ins_x[0], ins_x[1], ins_byte, ins_scale);
+        }
+        wait_halves_then(__popc(issued), qraw, ins_page);
         bf16x8 qb[4];
 #pragma unroll
         for (int m = 0; m < 4; m++)
@@ -226,9 +368,23 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
             const int k = blk - blk0;
             issue(k + kBufs - 1);
             const int tok0 = blk * kBlock;
+            if constexpr (FUSED) {
+                // patch bytes, quantized while this page is in flight
+                for (int budget = tok0 + kBlock > T - q_len ? q_len : 1;
+                     next_patch < q_len && budget > 0; next_patch++) {
+                    if (!is_patch_token(next_patch, blk0, blk_end, T, q_len, h)) continue;
+                    prepare_patch_token(stage[wave], next_patch, lane);
+                    budget--;
+                }
+            }
             float best = -INFINITY;
             if (issued & (1u << k)) {
                 wait_halves(__popc(issued >> (k + 1)));
+                if constexpr (FUSED) {
+                    if (tok0 + kBlock > T - q_len)
+                        patch_new_tokens(lds[wave][k % kBufs], tok0, T, q_len, h, lane,
+                                         stage[wave]);
+                }
                 HalfRegs hr;
                 read_half(hr, lds[wave][k % kBufs], h, lane);
                 const bool full = tok0 + kBlock - 1 <= p_lo;
@@ -247,7 +403,29 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
                 asm volatile("ds_write_b32 %0, %1" ::"v"(a), "v"(best) : "memory");
             }
         }
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        if constexpr (FUSED) {
+            // the insert stores, after the wavefront's last page load has returned; then any
+            // further items (more items than wavefronts: short contexts), one at a time
+            if (rt + 16 >= rows && item < n_items) {
+                store_item(item, __builtin_amdgcn_readfirstlane(ins_page), ins_pos, num_pages,
+                           ins_byte, ins_scale, k_pool_w, v_pool_w, ik_pool_w, lane);
+                for (item += kWaves * gx; item < n_items; item += kWaves * gx) {
+                    const f32x2 x = *reinterpret_cast<const f32x2*>(
+                        item_source(item, b, q_len, new_k, new_v, new_ik) + 2 * lane);
+                    const int pos = T - q_len + item / 9;
+                    const int64_t page = pos >= 0 ? table[pos >> 7] : -1;
+                    quantize_pair(x[0], x[1], ins_byte, ins_scale);
+                    store_item(item, page, pos, num_pages, ins_byte, ins_scale, k_pool_w,
+                               v_pool_w, ik_pool_w, lane);
+                }
+            }
+        }
+        // every page and query load has been waited for; the insert stores may still be in
+        // flight and are left to complete on their own
+        if constexpr (FUSED)
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         __syncthreads();
         // lane (n, c) of wavefront h writes block c + 4h of row rt + n: the max of both halves
         {
@@ -262,14 +440,40 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
 
 }  // namespace
 
+static int indexer_wgs(int batch, int max_blocks) {
+    const int per_wg = kPairs * kPagesPerPair;
+    return (max_blocks + per_wg - 1) / per_wg * batch;
+}
+
 hipError_t launch_indexer(const uint8_t* ik_pool, int64_t num_pages, const int32_t* block_table,
                           const int32_t* ctx_lens, int batch, int max_blocks, int q_len,
                           const uint16_t* q_idx, float* scores, hipStream_t stream) {
-    const int per_wg = kPairs * kPagesPerPair;
-    dim3 grid((max_blocks + per_wg - 1) / per_wg, batch);
-    hipLaunchKernelGGL(indexer_kernel, grid, dim3(kWaves * 64), 0, stream, ik_pool,
-                       num_pages, block_table, ctx_lens, max_blocks, q_len, q_idx, scores);
+    hipLaunchKernelGGL(indexer_kernel<false>, dim3(indexer_wgs(batch, max_blocks)),
+                       dim3(kWaves * 64), 0, stream, ik_pool, num_pages, block_table, ctx_lens,
+                       max_blocks, q_len, q_idx, scores, nullptr, nullptr, nullptr, nullptr,
+                       nullptr, nullptr);
     return hipGetLastError();
+}
+
+hipError_t launch_insert_indexer(uint8_t* k_pool, uint8_t* v_pool, uint8_t* ik_pool,
+                                 int64_t num_pages, const int32_t* block_table,
+                                 const int32_t* ctx_lens, int batch, int max_blocks, int q_len,
+                                 const float* new_k, const float* new_v, const float* new_ik,
+                                 const uint16_t* q_idx, float* scores, hipStream_t stream) {
+    if (q_len <= kFusedMaxNew) {
+        hipLaunchKernelGGL(indexer_kernel<true>, dim3(indexer_wgs(batch, max_blocks)),
+                           dim3(kWaves * 64), 0, stream, ik_pool, num_pages, block_table, ctx_lens,
+                           max_blocks, q_len, q_idx, scores, k_pool, v_pool, ik_pool, new_k, new_v,
+                           new_ik);
+        return hipGetLastError();
+    }
+    // more new tokens than the patch stages: the insert launch first, then the indexer
+    const hipError_t err =
+        launch_insert_at_positions(k_pool, v_pool, ik_pool, num_pages, block_table, ctx_lens,
+                                   batch, max_blocks, q_len, new_k, new_v, new_ik, stream);
+    if (err != hipSuccess) return err;
+    return launch_indexer(ik_pool, num_pages, block_table, ctx_lens, batch, max_blocks, q_len,
+                          q_idx, scores, stream);
 }
 
 }  // namespace msa

@@ -16,6 +16,21 @@ hipError_t launch_indexer(const uint8_t* ik_pool, int64_t num_pages, const int32
                           const int32_t* ctx_lens, int batch, int max_blocks, int q_len,
                           const uint16_t* q_idx, float* scores, hipStream_t stream);
 
+// Insert of a decode step's new tokens at their own positions (slots from the block table).
+hipError_t launch_insert_at_positions(uint8_t* k_pool, uint8_t* v_pool, uint8_t* ik_pool,
+                                      int64_t num_pages, const int32_t* block_table,
+                                      const int32_t* ctx_lens, int batch, int max_blocks,
+                                      int q_len, const float* k, const float* v, const float* ik,
+                                      hipStream_t stream);
+
+// Insert of a decode step's new tokens (positions T - q_len .. T - 1 of each sequence, slots
+// from the block table) and the indexer, in one launch when q_len <= 16 (two otherwise).
+hipError_t launch_insert_indexer(uint8_t* k_pool, uint8_t* v_pool, uint8_t* ik_pool,
+                                 int64_t num_pages, const int32_t* block_table,
+                                 const int32_t* ctx_lens, int batch, int max_blocks, int q_len,
+                                 const float* new_k, const float* new_v, const float* new_ik,
+                                 const uint16_t* q_idx, float* scores, hipStream_t stream);
+
 hipError_t launch_topk(const float* scores, const int32_t* ctx_lens, int batch, int max_blocks,
                        int q_len, int32_t* ids, hipStream_t stream);
 

@@ -20,6 +20,8 @@
  *   msa_kv_insert_nvfp4 -> msa_indexer_score -> msa_block_topk -> msa_sparse_attn_decode
  * or three, with the last two fused:
  *   msa_kv_insert_nvfp4 -> msa_indexer_score -> msa_select_attn_decode
+ * or two, msa_insert_indexer_score -> msa_select_attn_decode, which one call, msa_decode_step,
+ * also makes.
  *
  * Conventions for every entry point
  *   - All tensor arguments are device pointers owned by the caller. The library allocates
@@ -213,6 +215,46 @@ int msa_select_attn_decode(const msa_cache_t *cache, const msa_batch_t *batch,
                            const float *block_scores, int32_t topk, int32_t *block_ids,
                            const uint16_t *q, float softmax_scale, uint16_t *out,
                            void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Insert of the step's new tokens and the indexer in one launch: the effect of
+ *   msa_kv_insert_nvfp4(cache, slots, k, v, ik, batch * q_len)
+ *   msa_indexer_score(cache, batch, q_idx, block_scores)
+ * with the slots of the new tokens' own positions (as msa_decode_step below states), the same
+ * results bit for bit, cache bytes included. Arguments as for msa_decode_step. Errors:
+ * MSA_ERR_INVALID_ARG (a NULL pointer, sizes < 1).
+ */
+int msa_insert_indexer_score(const msa_cache_t *cache, const msa_batch_t *batch, const float *k,
+                             const float *v, const float *ik, const uint16_t *q_idx,
+                             float *block_scores, void *stream);
+
+/*
+ * One whole decode step in two launches (msa_insert_indexer_score, then
+ * msa_select_attn_decode): the effect of
+ *   msa_kv_insert_nvfp4(cache, slots, k, v, ik, batch * q_len)
+ *   msa_indexer_score(cache, batch, q_idx, block_scores)
+ *   msa_select_attn_decode(cache, batch, block_scores, topk, block_ids, q, softmax_scale, out,
+ *                          workspace, ws_bytes)
+ * where the slots are the new tokens' own positions: query token j of sequence b is written at
+ * position T_b - q_len + j, into page block_table(b, (T_b - q_len + j) / 128) at token
+ * (T_b - q_len + j) % 128 ("MiniMax M3 on vLLM", section "Decode execution": the step's keys,
+ * values and index keys are written to the paged caches before the indexer and attention read
+ * them). Tokens at negative positions (T_b < q_len) are skipped. Results, cache bytes included,
+ * are those of the three calls bit for bit. The insert runs in the indexer's launch: the
+ * indexer quantizes the sequence's new index keys itself into its copy of the pages it scores,
+ * so it needs no finished insert ("vLLM day-0 support for MiniMax-M3.1-Flash", section "QKV GEMM
+ * + norm + RoPE + KV insert fusion": the insert is fused into the step's first kernel). With
+ * q_len > 16 the insert runs as a launch of its own before the indexer.
+ *   k, v : device fp32 [batch * q_len][4][128]; ik : device fp32 [batch * q_len][128]
+ *          (request-major, as q); q_idx, q, block_scores, block_ids, out, workspace as for the
+ *          calls above.
+ * Errors: MSA_ERR_INVALID_ARG (a NULL pointer, sizes < 1), MSA_ERR_UNSUPPORTED (topk != 16),
+ * MSA_ERR_WORKSPACE.
+ */
+int msa_decode_step(const msa_cache_t *cache, const msa_batch_t *batch, const float *k,
+                    const float *v, const float *ik, const uint16_t *q_idx, const uint16_t *q,
+                    int32_t topk, float softmax_scale, float *block_scores, int32_t *block_ids,
+                    uint16_t *out, void *workspace, size_t ws_bytes, void *stream);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char *msa_last_error(void);

@@ -70,7 +70,7 @@ def gpu_sequence_caches(cache, w: mi.Workload, b: int):
 # ------------------------------------------------------------------ GPU side
 class GpuRun:
     def __init__(self, w: mi.Workload, device: str = "cuda", chunk: int = 1 << 15,
-                 fused: bool = True):
+                 mode: str = "step", snapshot: bool = False):
         import block_sparse_attention_nvfp4_amd as msa
         self.msa = msa
         self.w = w
@@ -85,6 +85,9 @@ class GpuRun:
             for t0 in range(0, T - q, chunk):
                 t1 = min(T - q, t0 + chunk)
                 self.insert(b, t0, t1)
+        # the pools holding the cached prefix only (snapshot=True), to run the step again from
+        self.prefix = ([t.clone() for t in (self.cache.k, self.cache.v, self.cache.ik)]
+                       if snapshot else None)
         # the step's new tokens, request-major
         toks = [(b, w.ctx_lens[b] - q, w.ctx_lens[b]) for b in range(w.batch)]
         self.new_slots = torch.from_numpy(np.concatenate([w.slots(b, t0, t1) for b, t0, t1 in toks])).to(device)
@@ -93,13 +96,17 @@ class GpuRun:
         self.new_ik = torch.cat([w.ik_rows(b, t0, t1, device) for b, t0, t1 in toks])
         self.q_idx = w.q_idx.to(device)
         self.q = w.q.to(device)
-        self.step = msa.DecodeStep(self.cache, self.batch, device, fused=fused)
+        self.step = msa.DecodeStep(self.cache, self.batch, device, mode=mode)
 
     def insert(self, b: int, t0: int, t1: int):
         w, dev = self.w, self.cache.ik.device
         slots = torch.from_numpy(w.slots(b, t0, t1)).to(dev)
         self.msa.msa_kv_insert_nvfp4(self.cache, slots, w.kv_rows("k", b, t0, t1, dev),
                                      w.kv_rows("v", b, t0, t1, dev), w.ik_rows(b, t0, t1, dev))
+
+    def restore_prefix(self):
+        for dst, src in zip((self.cache.k, self.cache.v, self.cache.ik), self.prefix):
+            dst.copy_(src)
 
     def run(self):
         out = self.step.run(self.new_slots, self.new_k, self.new_v, self.new_ik, self.q_idx, self.q)

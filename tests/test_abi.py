@@ -107,3 +107,26 @@ def test_invalid_arguments_return_codes_without_launch(msa):
     assert sel(by(_cache(k=None)), small, 1, 16, 1, 1, 0.1, 1, 256, need, None) == msa.MSA_ERR_INVALID_ARG
     assert sel(by(_cache()), small, 1, 16, 1, 1, 0.1, 1, None, 0, None) == msa.MSA_ERR_WORKSPACE
     assert sel(by(_cache()), small, 1, 16, 1, 1, 0.1, 1, 257, need, None) == msa.MSA_ERR_WORKSPACE
+    # the whole step: the checks of insert, indexer and selection + attention
+    st = L.msa_decode_step
+    args = [1, 1, 1, 1, 1, 16, 0.1, 1, 1, 1, 256, need, None]  # k v ik q_idx q topk scale scores ids out ws bytes stream
+    def call(cache=None, batch=small, **over):
+        a = list(args)
+        for i, val in over.items():
+            a[int(i[1:])] = val
+        return st(by(cache or _cache()), batch, *a)
+    assert call(a5=8) == msa.MSA_ERR_UNSUPPORTED
+    for i in (0, 1, 2, 3, 4, 7, 8, 9):
+        assert call(**{f"a{i}": None}) == msa.MSA_ERR_INVALID_ARG, i
+    assert call(cache=_cache(ik=None)) == msa.MSA_ERR_INVALID_ARG
+    assert call(cache=_cache(v=None)) == msa.MSA_ERR_INVALID_ARG
+    assert call(batch=by(_batch(q=0))) == msa.MSA_ERR_INVALID_ARG
+    assert call(a10=None, a11=0) == msa.MSA_ERR_WORKSPACE
+    assert call(a10=257) == msa.MSA_ERR_WORKSPACE
+    ii = L.msa_insert_indexer_score
+    for i in range(5):
+        a = [1] * 5
+        a[i] = None
+        assert ii(by(_cache()), small, *a, None) == msa.MSA_ERR_INVALID_ARG, i
+    assert ii(by(_cache(k=None)), small, 1, 1, 1, 1, 1, None) == msa.MSA_ERR_INVALID_ARG
+    assert ii(by(_cache()), by(_batch(mb=0)), 1, 1, 1, 1, 1, None) == msa.MSA_ERR_INVALID_ARG

@@ -50,8 +50,11 @@ def run(request):
     cfg, kw = CASES[request.param]
     _log(f"[case {request.param}] config {cfg} {kw}")
     w = mi.make_workload(cfg, **kw)
-    g = GpuRun(w)
+    g = GpuRun(w, snapshot=True)
     out = g.run()
+    # the first step's results (msa_decode_step from the prefix-only cache)
+    g.first = dict(scores=g.step.block_scores.clone(), ids=g.step.block_ids.clone(),
+                   out=out.clone(), pools=[t.clone() for t in (g.cache.k, g.cache.v, g.cache.ik)])
     return request.param, w, g, out
 
 
@@ -128,15 +131,41 @@ def test_step_is_deterministic(run):
     assert torch.equal(first, again)
 
 
-def test_fused_selection_matches_separate_launches(run):
-    """msa_select_attn_decode (the fixture's step) equals msa_block_topk + msa_sparse_attn_decode
-    bit for bit, ids and outputs."""
+def _assert_same_as_first(g, step, what):
+    first = g.first
+    assert torch.equal(step.block_scores, first["scores"]), (what, "scores")
+    assert torch.equal(step.block_ids, first["ids"]), (what, "ids")
+    assert torch.equal(step.out, first["out"]), (what, "out")
+    for name, got, want in zip("k v ik".split(), (g.cache.k, g.cache.v, g.cache.ik), first["pools"]):
+        assert torch.equal(got, want), (what, name, "pool bytes")
+
+
+def test_step_modes_agree(run):
+    """msa_decode_step (the fixture's step: insert and indexer in one launch, then selection and
+    attention in one) equals the three-call and the four-call sequences bit for bit: scores, ids,
+    outputs and every cache byte, each run from the same prefix-only cache."""
     import block_sparse_attention_nvfp4_amd as msa
     name, w, g, _ = run
-    fused_ids = g.step.block_ids.clone()
-    fused_out = g.step.out.clone()
-    sep = msa.DecodeStep(g.cache, g.batch, "cuda", fused=False)
-    sep.run(g.new_slots, g.new_k, g.new_v, g.new_ik, g.q_idx, g.q)
+    for mode in ("select", "separate"):
+        g.restore_prefix()
+        st = msa.DecodeStep(g.cache, g.batch, "cuda", mode=mode)
+        st.run(g.new_slots, g.new_k, g.new_v, g.new_ik, g.q_idx, g.q)
+        torch.cuda.synchronize()
+        _assert_same_as_first(g, st, (name, mode))
+
+
+def test_step_over_stale_slots(run):
+    """The new tokens' slots first hold other tokens' bytes (a step with other values), so the
+    indexer workgroups of msa_decode_step read stale bytes wherever the insert of the same launch
+    has not landed yet: the results must still equal the first step's bit for bit."""
+    import block_sparse_attention_nvfp4_amd as msa
+    name, w, g, _ = run
+    g.restore_prefix()
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    stale = [(torch.randn(t.shape, generator=gen) * 3.0).to(t.device) for t in (g.new_k, g.new_v, g.new_ik)]
+    msa.DecodeStep(g.cache, g.batch, "cuda", mode="separate").run(g.new_slots, *stale, g.q_idx, g.q)
     torch.cuda.synchronize()
-    assert torch.equal(sep.block_ids, fused_ids), name
-    assert torch.equal(sep.out, fused_out), name
+    assert not torch.equal(g.cache.ik, g.first["pools"][2]), name  # the slots do hold other bytes
+    g.step.run(g.new_slots, g.new_k, g.new_v, g.new_ik, g.q_idx, g.q)
+    torch.cuda.synchronize()
+    _assert_same_as_first(g, g.step, (name, "stale"))
