@@ -34,8 +34,8 @@ constexpr int kFusedMaxNew = 8;    // new tokens per sequence the fused step's p
 constexpr int kPairs = 4;            // wavefront pairs per workgroup; a pair shares its blocks
 constexpr int kWaves = 2 * kPairs;   // wavefront h of a pair scores the tokens of half h of each page
 constexpr int kBufs = 2;             // LDS buffers per wavefront (half pages in flight: kBufs - 1)
-constexpr int kPagesPerPair = 8;
-static_assert(kPagesPerPair <= 8, "the score write-out covers at most eight blocks per pair");
+constexpr int kPagesPerWg = 32;     // blocks of one sequence per workgroup
+static_assert(kPagesPerWg * 16 == kWaves * 64, "the score write-out: one thread per block and row");
 constexpr int kHalfBytes = 5 * 1024; // four code slabs of a half page + the page's scale chunk
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -67,16 +67,17 @@ __device__ __forceinline__ void wait_halves(int after) {
 }
 static_assert(kBufs <= 3, "wait_halves covers at most two half pages in flight");
 
-// The same wait for loads issued before `after` half pages, and the registers those loads
-// write: the asm operands keep every use of `v` after the wait.
-__device__ __forceinline__ void wait_halves_then(int after, u32x4 (&v)[4], int& w) {
-#define MSA_WAIT(n) asm volatile("s_waitcnt vmcnt(" #n ")" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(w) :: "memory")
-    switch (after) {
-        case 0: MSA_WAIT(0); break;
-        case 1: MSA_WAIT(5); break;
-        default: MSA_WAIT(10); break;
-    }
-#undef MSA_WAIT
+// This lane's query operand (four 16-byte pieces, piece m at q + 1024 m + 16 lane) read from
+// LDS, where direct global->LDS loads put it: no register is written by a load the compiler
+// does not see, so no copy of one can be taken before its wait.
+__device__ __forceinline__ void read_query(u32x4 (&v)[4], const uint8_t* q, int lane) {
+    const uint32_t a = (uint32_t)(uintptr_t)(q + lane * 16);
+    asm volatile("ds_read_b128 %0, %4\n\t"
+                 "ds_read_b128 %1, %4 offset:1024\n\t"
+                 "ds_read_b128 %2, %4 offset:2048\n\t"
+                 "ds_read_b128 %3, %4 offset:3072\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]) : "v"(a) : "memory");
 }
 
 // This lane's four 16-byte code chunks and the two scale words of its slabs, read from LDS
@@ -140,18 +141,24 @@ __device__ __forceinline__ float half_max(const HalfRegs& hr, const u32x4 (&qop)
 // old bytes when it streams in. The wavefront scoring half h of such a page writes the NVFP4
 // bytes of those of the new index keys that fall in its half into its LDS copy of the page,
 // exactly where the insert writes them in memory (the token's code chunks of the half and its
-// scale bytes, which only this half reads). Every wavefront copies the sequence's new index keys
-// (fp32) into its own staging area `pq` at start-up, token j at pq + 512 j (no workgroup barrier:
-// only the wavefront itself reads them); prepare_patch_token quantizes one of its tokens (one
-// per page while the pages stream in, every remaining one at the first page that holds new
-// tokens) and overwrites the token's first 72 bytes with the result: the code byte of lane l's
-// elements 2l, 2l+1 at pq + 512 j + l, scale g at pq + 512 j + 64 + g.
+// scale bytes, which only this half reads). Such a page is always one of the two highest
+// visible blocks of the row tile, the fixed first pages of wavefront pairs 0 and 1 (pages are
+// scored from the highest block down), so only those wavefronts patch. One that does copies the
+// sequence's new index keys (fp32) into its own staging area `pq` (token j at pq + 512 j; no
+// workgroup barrier: only the wavefront itself reads them) with the query rows of the tile, and
+// prepare_patch_token quantizes each token it needs once, overwriting the token's first 72 bytes
+// with the result: the code byte of lane l's elements 2l, 2l+1 at pq + 512 j + l, scale g at
+// pq + 512 j + 64 + g.
 constexpr int kStageBytes = kDim * 4;
 
-__device__ __forceinline__ bool is_patch_token(int j, int blk0, int blk_end, int T, int q_len,
-                                               int h) {
-    const int pos = T - q_len + j;
-    return pos >= 0 && (pos >> 7) >= blk0 && (pos >> 7) < blk_end && ((pos & 31) >> 4) == h;
+// Tokens j (bit j) of the step whose position lies in block blk and in half h of it.
+__device__ __forceinline__ uint32_t patch_tokens(int blk, int T, int q_len, int h) {
+    uint32_t mask = 0;
+    for (int j = 0; j < q_len; j++) {
+        const int pos = T - q_len + j;
+        if (pos >= 0 && (pos >> 7) == blk && ((pos & 31) >> 4) == h) mask |= 1u << j;
+    }
+    return mask;
 }
 
 __device__ __forceinline__ void prepare_patch_token(uint8_t* pq, int j, int lane) {
@@ -216,14 +223,32 @@ __device__ __forceinline__ void store_item(int item, int64_t page, int pos, int6
     store_quantized(byte, scale, dst, pos & 127, vec >= 4 && vec < 8, lane);
 }
 
+// Claim the next unscored page of this half for the wavefront: one lane adds to the counter.
+__device__ __forceinline__ int claim_page(const int* counter, int lane) {
+    int old = 0;
+    if (lane == 0)
+        asm volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)"
+                     : "=v"(old) : "v"((uint32_t)(uintptr_t)counter), "v"(1) : "memory");
+    return __builtin_amdgcn_readfirstlane(old);
+}
+
+// One workgroup scores blocks [kPagesPerWg x, kPagesPerWg (x + 1)) of sequence b for every query
+// row, one row tile (16 rows: four query tokens x four groups) at a time. Wavefront w = 2 m + h
+// scores half h of a page (tokens with (t % 32) / 16 == h); the two halves of a page meet in the
+// LDS stash. Pages are handed out dynamically, from the highest visible block down: wavefront
+// pair m starts with page m, then each wavefront claims the next page of its half from an LDS
+// counter, so that the wavefronts that run ahead (the older wavefront of each SIMD gets the
+// issue slots first) take more pages and the workgroup finishes together. The half page of the
+// next claimed page streams into LDS while the current one is scored.
+//
 // FUSED (decode step with q_len <= kFusedMaxNew): the launch also inserts the step's new tokens.
 // The 9 q_len head vectors of sequence b are spread over the sequence's workgroups and their
 // wavefronts (wavefront w of workgroup x takes items x + gx (w + 8 m)). A wavefront loads its
-// first item with its start-up loads, requests the item's block-table entry as soon as the
-// context length is known, quantizes while the first pages stream in, and stores after its last
-// page has arrived, so that the stores never stand between page loads in the in-order memory
-// counter. The indexer workgroups patch the new index keys into their page copies
-// (patch_new_tokens): a page may be read before or after another workgroup's store lands.
+// first item with its start-up loads, requests the item's block-table entry with its query
+// rows, quantizes while the first pages stream in, and stores after its last page has arrived,
+// so that the stores never stand between page loads in the in-order memory counter. The
+// indexer wavefronts patch the new index keys into their page copies (patch_new_tokens): a
+// page may be read before or after another workgroup's store lands.
 template <bool FUSED>
 __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
     const uint8_t* ik_pool, int64_t num_pages, const int32_t* __restrict__ block_table,
@@ -232,63 +257,66 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
     uint8_t* v_pool_w, uint8_t* ik_pool_w, const float* __restrict__ new_k,
     const float* __restrict__ new_v, const float* __restrict__ new_ik) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves][kBufs][kHalfBytes];
-    __shared__ int page_ids[kWaves][kPagesPerPair];
-    __shared__ float stash[kPairs][kPagesPerPair][2][16];  // half-page maxima of the row tile
-    __shared__ __attribute__((aligned(16))) uint8_t stage[FUSED ? kWaves : 1][FUSED ? kFusedMaxNew * kStageBytes : 16];
+    // half-page maxima of the row tile: [half][row][block - wg_blk0], rows padded apart in banks
+    __shared__ float stash[2][16][kPagesPerWg + 1];
+    __shared__ int next_page[2];  // page counters of the two halves
+    __shared__ __attribute__((aligned(16))) uint8_t qbuf[kWaves][4 * 1024];  // query operands
+    __shared__ __attribute__((aligned(16))) uint8_t stage[FUSED ? 4 : 1][FUSED ? kFusedMaxNew * kStageBytes : 16];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int gx = (max_blocks + kPairs * kPagesPerPair - 1) / (kPairs * kPagesPerPair);
+    const int gx = (max_blocks + kPagesPerWg - 1) / kPagesPerWg;
     const int wg = blockIdx.x;
     const int b = wg / gx;
+    const int wg_blk0 = (wg - b * gx) * kPagesPerWg;
+    const int wg_end = min(wg_blk0 + kPagesPerWg, max_blocks);
     const int n_items = FUSED ? 9 * q_len : 0;
     int item = (wg - b * gx) + gx * __builtin_amdgcn_readfirstlane(wave);  // first insert item
-    const int pair = wave >> 1;
+    const int pair = __builtin_amdgcn_readfirstlane(wave >> 1);
     const int h = wave & 1;
     const int n = lane & 15;  // B/D column: query row within the tile
     const int c = lane >> 4;  // lane group
-    const int blk0 = ((wg - b * gx) * kPairs + pair) * kPagesPerPair;
-    // a pair past the end still takes part in the workgroup barriers below
-    const bool active = blk0 < max_blocks;
     const int32_t* table = block_table + (int64_t)b * max_blocks;
-    // the pair's block-table entries and the context length are requested together (the
-    // entries do not depend on it): one memory round trip before the first page load
-    int pid_raw = -1;
-    if (lane < kPagesPerPair && blk0 + lane < max_blocks) pid_raw = table[blk0 + lane];
+    // the page counters are set before any wavefront claims a page (and before the start-up
+    // loads, so that the barrier does not wait for them)
+    if (threadIdx.x < 2) {
+        const uint32_t a = (uint32_t)(uintptr_t)&next_page[threadIdx.x];
+        asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(a), "v"(kPairs) : "memory");
+    }
+    __builtin_amdgcn_s_barrier();
+    // the workgroup's block-table entries (lane l: block wg_blk0 + l) and the context length are
+    // requested together (the entries do not depend on it): one memory round trip before the
+    // first page load; and, fused, this wavefront's first insert item
+    int pid_all = -1;
+    if (wg_blk0 + lane < wg_end && lane < kPagesPerWg) pid_all = table[wg_blk0 + lane];
     int T_raw = ctx_lens[b];
-    // fused decode step: the sequence's new index keys (fp32) copied to this wavefront's
-    // staging area, two tokens per direct global->LDS load (lanes past the last token re-read
-    // its last 16 bytes into the unused tail), and this wavefront's first insert item; the loads
-    // join the round trip above
     f32x2 ins_x = {0.f, 0.f};
     if constexpr (FUSED) {
-        const float* src = new_ik + (int64_t)b * q_len * kDim;
-        for (int i = 0; i < (q_len + 1) / 2; i++)
-            __builtin_amdgcn_global_load_lds(src + min(256 * i + 4 * lane, q_len * kDim - 4),
-                                             (lds_void*)(stage[wave] + 1024 * i), 16, 0, 0);
         if (item < n_items)
             ins_x = *reinterpret_cast<const f32x2*>(
                 item_source(item, b, q_len, new_k, new_v, new_ik) + 2 * lane);
     }
-    asm volatile("" : "+v"(pid_raw), "+v"(T_raw), "+v"(ins_x));
-    const int T = clamp_ctx(T_raw, max_blocks);
+    asm volatile("" : "+v"(pid_all), "+v"(T_raw), "+v"(ins_x));
+    // the same value in every lane
+    const int T = __builtin_amdgcn_readfirstlane(clamp_ctx(T_raw, max_blocks));
     const int rows = 4 * q_len;
     const int64_t row_base = (int64_t)b * rows;
-    const int blk_end = active ? min(blk0 + kPagesPerPair, max_blocks) : blk0;
     // blocks past the last query position hold no visible key and are never loaded
     const int n_blocks = T > 0 ? min(max_blocks, (T - 1) / kBlock + 1) : 0;
-    // page ids of the pair's blocks, read once into LDS: a block-table load issued between page
-    // loads would make the in-order memory counter wait for every page in flight
-    if (lane < kPagesPerPair)
-        page_ids[wave][lane] = (active && blk0 + lane < n_blocks && pid_raw >= 0 &&
-                                pid_raw < num_pages) ? pid_raw : -1;
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    // position of the first insert item; its block-table entry is requested with the query rows
-    // of every row tile (below) and used after the last
-    const int ins_pos = FUSED && item < n_items
-                            ? __builtin_amdgcn_readfirstlane(T) - q_len + item / 9 : -1;
-    int ins_page = -1;
+    pid_all = (wg_blk0 + lane < n_blocks && pid_all >= 0 && pid_all < num_pages) ? pid_all : -1;
+    // position of the first insert item and its block-table entry: a load the compiler sees
+    // (vector, through an index it cannot prove uniform), so that it waits for it at its use,
+    // the store after the last page, long after it returned
+    const int ins_pos = FUSED && item < n_items ? T - q_len + item / 9 : -1;
+    int ins_page_v = -1;
+    if (ins_pos >= 0) {
+        int idx = ins_pos >> 7;
+        asm volatile("" : "+v"(idx));
+        ins_page_v = table[idx];
+    }
     uint32_t ins_byte = 0, ins_scale = 0;
-    int next_patch = 0;  // this wavefront's patch tokens j < next_patch are quantized
+    uint32_t prepped = 0;  // fused: tokens whose patch bytes are in this wavefront's staging area
+    bool staged = false;   // fused: the new index keys were copied to the staging area
 
     for (int rt = 0; rt < rows; rt += 16) {
         const int r = rt + n;
@@ -296,60 +324,54 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
         const int j_hi = min((rt >> 2) + 3, q_len - 1);
         const int p_lo = T - q_len + (rt >> 2);                  // lowest position in the tile
         const int p_hi = T - q_len + j_hi;                       // highest position in the tile
-        const int vis_end = min(blk_end, p_hi >= 0 ? p_hi / kBlock + 1 : 0);
+        const int vis_end = min(wg_end, p_hi >= 0 ? p_hi / kBlock + 1 : 0);
+        // page u (u = 0 .. n_pages - 1) of the tile is block vis_end - 1 - u
+        const int n_pages = max(vis_end - wg_blk0, 0);
 
-        // software pipeline: half pages of blocks blk+1 .. blk+kBufs-1 stream into LDS while
-        // block blk is scored. issued: bit i set when block blk0+i had its half page loaded.
-        uint32_t issued = 0;
-        auto issue = [&](int i) {
-            const int blk = blk0 + i;
-            const int pid = (i < kPagesPerPair && blk < vis_end)
-                                ? __builtin_amdgcn_readfirstlane(page_ids[wave][i]) : -1;
-            if (pid >= 0) {
-                half_to_lds(ik_pool + (int64_t)pid * kHeadPageBytes, h, lds[wave][i % kBufs], lane);
-                issued |= 1u << i;
-            }
+        // load half h of page u into LDS buffer `buf`; false when the page is absent
+        auto issue = [&](int u, int buf) {
+            const int pid = __builtin_amdgcn_readlane(pid_all, vis_end - 1 - u - wg_blk0);
+            if (pid < 0) return false;
+            half_to_lds(ik_pool + (int64_t)pid * kHeadPageBytes, h, lds[wave][buf], lane);
+            return true;
         };
-        // B operand: row r, dims 32c + 8m .. 32c + 8m + 7 for MFMA m = 0..3. The query rows are
-        // requested first and the first pages right after; the loads are written out so that
-        // the wait for the query (placed here, not by the compiler, which would wait for every
-        // page as well) leaves the pages in flight. Every lane loads a valid row (rows past the
-        // tile read row rows - 1) and zeroes it after the wait.
-        u32x4 qraw[4];
+        // fused: the tokens this wavefront patches into its first page (pairs 0 and 1 only)
+        uint32_t patch_mask = 0;
+        if constexpr (FUSED) {
+            if (pair < 2 && pair < n_pages)
+                patch_mask = patch_tokens(vis_end - 1 - pair, T, q_len, h);
+            if ((patch_mask & ~prepped) && !staged) {
+                // the sequence's new index keys into the staging area, two tokens per direct
+                // global->LDS load (lanes past the last token re-read its last 16 bytes into the
+                // unused tail); waited for with the query rows
+                const float* src = new_ik + (int64_t)b * q_len * kDim;
+                for (int i = 0; i < (q_len + 1) / 2; i++)
+                    __builtin_amdgcn_global_load_lds(
+                        src + min(256 * i + 4 * lane, q_len * kDim - 4),
+                        (lds_void*)(stage[pair * 2 + h] + 1024 * i), 16, 0, 0);
+                staged = true;
+            }
+        }
+        // B operand: row r, dims 32c + 8m .. 32c + 8m + 7 for MFMA m = 0..3, copied into this
+        // wavefront's query buffer with direct global->LDS loads, requested before the first
+        // page: the wait for it leaves the page in flight. Every lane loads a valid row (rows
+        // past the tile read row rows - 1) and zeroes it after the wait.
         {
             const uint16_t* qp = q_idx + (row_base + min(r, rows - 1)) * kDim + 32 * c;
-            if constexpr (FUSED) {
-                // and the insert item's block-table entry (entry 0 when there is none: a valid
-                // address)
-                const int32_t* tp = table + (ins_pos >= 0 ? ins_pos >> 7 : 0);
-                asm volatile(
-                    "global_load_dwordx4 %0, %5, off\n\t"
-                    "global_load_dwordx4 %1, %5, off offset:16\n\t"
-                    "global_load_dwordx4 %2, %5, off offset:32\n\t"
-                    "global_load_dwordx4 %3, %5, off offset:48\n\t"
-                    "global_load_dword %4, %6, off"
-                    : "=&v"(qraw[0]), "=&v"(qraw[1]), "=&v"(qraw[2]), "=&v"(qraw[3]),
-                      "=&v"(ins_page)
-                    : "v"(qp), "v"(tp)
-                    : "memory");
-            } else {
-                asm volatile(
-                    "global_load_dwordx4 %0, %4, off\n\t"
-                    "global_load_dwordx4 %1, %4, off offset:16\n\t"
-                    "global_load_dwordx4 %2, %4, off offset:32\n\t"
-                    "global_load_dwordx4 %3, %4, off offset:48"
-                    : "=&v"(qraw[0]), "=&v"(qraw[1]), "=&v"(qraw[2]), "=&v"(qraw[3])
-                    : "v"(qp)
-                    : "memory");
-            }
-        }
 #pragma unroll
-        for (int i = 0; i < kBufs - 1; i++) issue(i);
+            for (int m = 0; m < 4; m++)
+                __builtin_amdgcn_global_load_lds(qp + 8 * m, (lds_void*)(qbuf[wave] + 1024 * m),
+                                                 16, 0, 0);
+        }
+        int cur = pair < n_pages ? pair : n_pages;  // this wavefront's page (n_pages: none)
+        bool cur_loaded = cur < n_pages && issue(cur, 0);
         if constexpr (FUSED) {
-            // the first insert item is quantized while the first pages are in flight
+            // the first insert item is quantized while the first page is in flight
             if (rt == 0 && item < n_items) quantize_pair(ins_x[0], ins_x[1], ins_byte, ins_scale);
         }
-        wait_halves_then(__popc(issued), qraw, ins_page);
+        wait_halves(cur_loaded ? 1 : 0);
+        u32x4 qraw[4];
+        read_query(qraw, qbuf[wave], lane);
         bf16x8 qb[4];
 #pragma unroll
         for (int m = 0; m < 4; m++)
@@ -362,31 +384,31 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
         for (int m = 0; m < 4; m++)
             qop[m] = f16 ? __builtin_bit_cast(u32x4, qh[m]) : __builtin_bit_cast(u32x4, qb[m]);
         if (!f16) out_scale = 1.0f;
-
-#pragma unroll 1
-        for (int blk = blk0; blk < blk_end; blk++) {
-            const int k = blk - blk0;
-            issue(k + kBufs - 1);
-            const int tok0 = blk * kBlock;
-            if constexpr (FUSED) {
-                // patch bytes, quantized while this page is in flight
-                for (int budget = tok0 + kBlock > T - q_len ? q_len : 1;
-                     next_patch < q_len && budget > 0; next_patch++) {
-                    if (!is_patch_token(next_patch, blk0, blk_end, T, q_len, h)) continue;
-                    prepare_patch_token(stage[wave], next_patch, lane);
-                    budget--;
-                }
+        if constexpr (FUSED) {
+            // patch bytes of the tokens of the first page (staged with the query rows)
+            for (uint32_t todo = patch_mask & ~prepped; todo; todo &= todo - 1) {
+                prepare_patch_token(stage[pair * 2 + h], __builtin_ctz(todo), lane);
             }
+            prepped |= patch_mask;
+        }
+
+        int buf = 0;
+#pragma unroll 1
+        while (cur < n_pages) {
+            const int nxt = claim_page(&next_page[h], lane);
+            const bool nxt_loaded = nxt < n_pages && issue(nxt, buf ^ 1);
+            const int blk = vis_end - 1 - cur;
+            const int tok0 = blk * kBlock;
             float best = -INFINITY;
-            if (issued & (1u << k)) {
-                wait_halves(__popc(issued >> (k + 1)));
+            if (cur_loaded) {
+                wait_halves(nxt_loaded ? 1 : 0);
                 if constexpr (FUSED) {
-                    if (tok0 + kBlock > T - q_len)
-                        patch_new_tokens(lds[wave][k % kBufs], tok0, T, q_len, h, lane,
-                                         stage[wave]);
+                    if (cur == pair && patch_mask)
+                        patch_new_tokens(lds[wave][buf], tok0, T, q_len, h, lane,
+                                         stage[pair * 2 + h]);
                 }
                 HalfRegs hr;
-                read_half(hr, lds[wave][k % kBufs], h, lane);
+                read_half(hr, lds[wave][buf], h, lane);
                 const bool full = tok0 + kBlock - 1 <= p_lo;
                 if (f16)
                     best = (full ? half_max<true, true>(hr, qop, h, tok0, c, p_row)
@@ -399,15 +421,18 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
             // kept in LDS until the tile ends: a global store here would join the page loads in
             // the in-order memory counter and make the next wait cover part of a later page
             if (c == 0) {
-                const uint32_t a = (uint32_t)(uintptr_t)&stash[pair][k][h][n];
+                const uint32_t a = (uint32_t)(uintptr_t)&stash[h][n][blk - wg_blk0];
                 asm volatile("ds_write_b32 %0, %1" ::"v"(a), "v"(best) : "memory");
             }
+            cur = nxt;
+            cur_loaded = nxt_loaded;
+            buf ^= 1;
         }
         if constexpr (FUSED) {
             // the insert stores, after the wavefront's last page load has returned; then any
             // further items (more items than wavefronts: short contexts), one at a time
             if (rt + 16 >= rows && item < n_items) {
-                store_item(item, __builtin_amdgcn_readfirstlane(ins_page), ins_pos, num_pages,
+                store_item(item, __builtin_amdgcn_readfirstlane(ins_page_v), ins_pos, num_pages,
                            ins_byte, ins_scale, k_pool_w, v_pool_w, ik_pool_w, lane);
                 for (item += kWaves * gx; item < n_items; item += kWaves * gx) {
                     const f32x2 x = *reinterpret_cast<const f32x2*>(
@@ -427,22 +452,24 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
         else
             asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         __syncthreads();
-        // lane (n, c) of wavefront h writes block c + 4h of row rt + n: the max of both halves
+        // thread (row rn, block slot kb) writes the max of both halves; blocks above the tile's
+        // visible range are -inf; the counters are reset for the next tile
         {
-            const int k = c + 4 * h;
-            if (k < kPagesPerPair && r < rows && blk0 + k < blk_end)
-                scores[(row_base + r) * max_blocks + blk0 + k] =
-                    fmaxf(stash[pair][k][0][n], stash[pair][k][1][n]);
+            const int rn = threadIdx.x >> 5, kb = threadIdx.x & 31;
+            if (wg_blk0 + kb < wg_end && rt + rn < rows)
+                scores[(row_base + rt + rn) * max_blocks + wg_blk0 + kb] =
+                    wg_blk0 + kb < vis_end ? fmaxf(stash[0][rn][kb], stash[1][rn][kb])
+                                           : -INFINITY;
+            if (threadIdx.x < 2) next_page[threadIdx.x] = kPairs;
         }
-        __syncthreads();  // the next row tile rewrites the stash
+        __syncthreads();  // the next row tile rewrites the stash and claims pages anew
     }
 }
 
 }  // namespace
 
 static int indexer_wgs(int batch, int max_blocks) {
-    const int per_wg = kPairs * kPagesPerPair;
-    return (max_blocks + per_wg - 1) / per_wg * batch;
+    return (max_blocks + kPagesPerWg - 1) / kPagesPerWg * batch;
 }
 
 hipError_t launch_indexer(const uint8_t* ik_pool, int64_t num_pages, const int32_t* block_table,
