@@ -76,22 +76,61 @@ __device__ __forceinline__ void block_to_lds(const uint8_t* kp, const uint8_t* v
 __device__ __forceinline__ void store16_coherent(float* p, const f32x4& v) {
     asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
 }
-__device__ __forceinline__ f32x4 load16_coherent(const float* p) {
-    f32x4 v;
-    asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(v) : "v"(p) : "memory");
-    return v;
+// The three agent-coherent 16-byte loads of each of kMaxSplits partials, all in flight
+// together and waited for within the one asm statement.
+__device__ __forceinline__ void load_partials_coherent(const float* const (&p)[4][3],
+                                                       f32x4 (&v)[4][3]) {
+    asm volatile(
+        "global_load_dwordx4 %0, %12, off sc1\n\t"
+        "global_load_dwordx4 %1, %13, off sc1\n\t"
+        "global_load_dwordx4 %2, %14, off sc1\n\t"
+        "global_load_dwordx4 %3, %15, off sc1\n\t"
+        "global_load_dwordx4 %4, %16, off sc1\n\t"
+        "global_load_dwordx4 %5, %17, off sc1\n\t"
+        "global_load_dwordx4 %6, %18, off sc1\n\t"
+        "global_load_dwordx4 %7, %19, off sc1\n\t"
+        "global_load_dwordx4 %8, %20, off sc1\n\t"
+        "global_load_dwordx4 %9, %21, off sc1\n\t"
+        "global_load_dwordx4 %10, %22, off sc1\n\t"
+        "global_load_dwordx4 %11, %23, off sc1\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[1][0]), "=&v"(v[1][1]),
+          "=&v"(v[1][2]), "=&v"(v[2][0]), "=&v"(v[2][1]), "=&v"(v[2][2]), "=&v"(v[3][0]),
+          "=&v"(v[3][1]), "=&v"(v[3][2])
+        : "v"(p[0][0]), "v"(p[0][1]), "v"(p[0][2]), "v"(p[1][0]), "v"(p[1][1]), "v"(p[1][2]),
+          "v"(p[2][0]), "v"(p[2][1]), "v"(p[2][2]), "v"(p[3][0]), "v"(p[3][1]), "v"(p[3][2])
+        : "memory");
 }
 
-// LDS reads as explicit instructions: the compiler would otherwise wait for every page load in
-// flight before any LDS read. The waits below make the results available.
-__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
-    u32x4 v;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
-    return v;
+// LDS reads as explicit instructions (the compiler would otherwise wait for every page load in
+// flight before any LDS read), each group issued and waited for within one asm statement: no
+// register written by a read the compiler does not see is live outside it, so the compiler can
+// never copy one before its data has arrived.
+__device__ __forceinline__ void lds_read16x9(u32x4 (&v)[8], u32x4& w, uint32_t a, uint32_t aw) {
+    asm volatile("ds_read_b128 %0, %9\n\t"
+                 "ds_read_b128 %1, %9 offset:1024\n\t"
+                 "ds_read_b128 %2, %9 offset:2048\n\t"
+                 "ds_read_b128 %3, %9 offset:3072\n\t"
+                 "ds_read_b128 %4, %9 offset:4096\n\t"
+                 "ds_read_b128 %5, %9 offset:5120\n\t"
+                 "ds_read_b128 %6, %9 offset:6144\n\t"
+                 "ds_read_b128 %7, %9 offset:7168\n\t"
+                 "ds_read_b128 %8, %10\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+                   "=&v"(v[6]), "=&v"(v[7]), "=&v"(w)
+                 : "v"(a), "v"(aw)
+                 : "memory");
 }
-template <typename T>
-__device__ __forceinline__ void lds_wait(T& v) {
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v));
+__device__ __forceinline__ void lds_read16x3(u32x4& v0, u32x4& v1, u32x4& v2, uint32_t a0,
+                                             uint32_t a1) {
+    asm volatile("ds_read_b128 %0, %3\n\t"
+                 "ds_read_b128 %1, %4\n\t"
+                 "ds_read_b128 %2, %4 offset:16\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v0), "=&v"(v1), "=&v"(v2)
+                 : "v"(a0), "v"(a1)
+                 : "memory");
 }
 
 // One block of one wavefront: logits, online-softmax update, output accumulation.
@@ -102,13 +141,8 @@ __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c
     const uint32_t kbase = (uint32_t)(uintptr_t)buf;
     const uint32_t vbase = kbase + kHeadPageBytes;
     // ---- logits S^T (log2 domain)
-    u32x4 kc[8];
-#pragma unroll
-    for (int s = 0; s < 8; s++) kc[s] = lds_read16(kbase + s * 1024 + lane * 16);
-    u32x4 ksc = lds_read16(kbase + kCodeBytes + lane * 16);
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(kc[0]), "+v"(kc[1]), "+v"(kc[2]), "+v"(kc[3]), "+v"(kc[4]), "+v"(kc[5]),
-                   "+v"(kc[6]), "+v"(kc[7]), "+v"(ksc));
+    u32x4 kc[8], ksc;
+    lds_read16x9(kc, ksc, kbase + lane * 16, kbase + kCodeBytes + lane * 16);
     f32x4 sv[8];
 #pragma unroll
     for (int s = 0; s < 8; s++) {
@@ -161,12 +195,9 @@ __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c
 #pragma unroll
     for (int dt = 0; dt < 8; dt++) {
         const int d = 16 * dt + (lane & 15);
-        u32x4 vc = lds_read16(vbase + d * 64 + 16 * c);                    // tokens 32c..32c+31
-        u32x4 vs0 = lds_read16(vbase + kCodeBytes + dt * 128 + 32 * c);       // scales, tokens 32c..+15
-        u32x4 vs1 = lds_read16(vbase + kCodeBytes + dt * 128 + 32 * c + 16);  // tokens 32c+16..+31
-        lds_wait(vc);
-        lds_wait(vs0);
-        lds_wait(vs1);
+        // codes of tokens 32c..32c+31; scales of tokens 32c..+15 and 32c+16..+31
+        u32x4 vc, vs0, vs1;
+        lds_read16x3(vc, vs0, vs1, vbase + d * 64 + 16 * c, vbase + kCodeBytes + dt * 128 + 32 * c);
 #pragma unroll
         for (int s = 0; s < 8; s++) {
             const uint32_t sw = s < 4 ? vs0[s] : vs1[s - 4];  // tokens 32c + 4s .. +3
@@ -375,24 +406,32 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
                                              __HIP_MEMORY_SCOPE_AGENT) == n_split - 1;
         __syncthreads();
         if (!sh_last) return;
-        // every other split's values requested before any is used: one memory round trip
+        // every split's values requested before any is used (one memory round trip): splits
+        // past n_split read this split's own partial, then every value not from another split
+        // is replaced
+        static_assert(kMaxSplits == 4, "load_partials_coherent loads four partials");
+        const float* pp4[kMaxSplits][3];
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplits; sp++) {
+            const int src = sp < n_split ? sp : split;
+            const float* qp = partials + ((part_base + (int64_t)src * kGroupHeads) + h) * kPartStride;
+            pp4[sp][0] = qp;
+            pp4[sp][1] = qp + 4 + d0;
+            pp4[sp][2] = qp + 8 + d0;
+        }
+        f32x4 part[kMaxSplits][3];
+        load_partials_coherent(pp4, part);
         f32x4 ml[kMaxSplits], a0[kMaxSplits], a1[kMaxSplits];
 #pragma unroll
         for (int sp = 0; sp < kMaxSplits; sp++) {
-            if (sp < n_split && sp != split) {
-                const float* qp = partials + ((part_base + (int64_t)sp * kGroupHeads) + h) * kPartStride;
-                ml[sp] = load16_coherent(qp);
-                a0[sp] = load16_coherent(qp + 4 + d0);
-                a1[sp] = load16_coherent(qp + 8 + d0);
-            } else {
-                ml[sp] = f32x4{sp == split ? M : -INFINITY, sp == split ? L : 0.f, 0.f, 0.f};
-                a0[sp] = sp == split ? f32x4{acc[0], acc[1], acc[2], acc[3]} : f32x4{0.f, 0.f, 0.f, 0.f};
-                a1[sp] = sp == split ? f32x4{acc[4], acc[5], acc[6], acc[7]} : f32x4{0.f, 0.f, 0.f, 0.f};
-            }
+            const bool other = sp < n_split && sp != split;
+            ml[sp] = other ? part[sp][0]
+                           : f32x4{sp == split ? M : -INFINITY, sp == split ? L : 0.f, 0.f, 0.f};
+            a0[sp] = other ? part[sp][1]
+                           : (sp == split ? f32x4{acc[0], acc[1], acc[2], acc[3]} : f32x4{0.f, 0.f, 0.f, 0.f});
+            a1[sp] = other ? part[sp][2]
+                           : (sp == split ? f32x4{acc[4], acc[5], acc[6], acc[7]} : f32x4{0.f, 0.f, 0.f, 0.f});
         }
-        asm volatile("s_waitcnt vmcnt(0)"
-                     : "+v"(ml[0]), "+v"(ml[1]), "+v"(ml[2]), "+v"(ml[3]), "+v"(a0[0]), "+v"(a0[1]),
-                       "+v"(a0[2]), "+v"(a0[3]), "+v"(a1[0]), "+v"(a1[1]), "+v"(a1[2]), "+v"(a1[3]));
         if (threadIdx.x == 0)
             __hip_atomic_store(&counters[rg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         M = -INFINITY;

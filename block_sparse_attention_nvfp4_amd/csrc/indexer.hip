@@ -90,17 +90,18 @@ struct HalfRegs {
 __device__ __forceinline__ void read_half(HalfRegs& hr, const uint8_t* buf, int h, int lane) {
     const uint32_t a = (uint32_t)(uintptr_t)(buf + lane * 16);
     const uint32_t as = (uint32_t)(uintptr_t)(buf + 4096 + lane * 16 + h * 8);
-#define MSA_DS_READ(dst, off) asm volatile("ds_read_b128 %0, %1 offset:" #off : "=v"(dst) : "v"(a))
-    MSA_DS_READ(hr.code[0], 0);
-    MSA_DS_READ(hr.code[1], 1024);
-    MSA_DS_READ(hr.code[2], 2048);
-    MSA_DS_READ(hr.code[3], 3072);
-#undef MSA_DS_READ
-    asm volatile("ds_read_b32 %0, %1" : "=v"(hr.scale[0]) : "v"(as));
-    asm volatile("ds_read_b32 %0, %1 offset:4" : "=v"(hr.scale[1]) : "v"(as));
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(hr.code[0]), "+v"(hr.code[1]), "+v"(hr.code[2]), "+v"(hr.code[3]),
-                   "+v"(hr.scale[0]), "+v"(hr.scale[1]));
+    // issued and waited for within one asm statement (no pending register outside it)
+    asm volatile("ds_read_b128 %0, %6\n\t"
+                 "ds_read_b128 %1, %6 offset:1024\n\t"
+                 "ds_read_b128 %2, %6 offset:2048\n\t"
+                 "ds_read_b128 %3, %6 offset:3072\n\t"
+                 "ds_read_b32 %4, %7\n\t"
+                 "ds_read_b32 %5, %7 offset:4\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(hr.code[0]), "=&v"(hr.code[1]), "=&v"(hr.code[2]), "=&v"(hr.code[3]),
+                   "=&v"(hr.scale[0]), "=&v"(hr.scale[1])
+                 : "v"(a), "v"(as)
+                 : "memory");
 }
 
 // Max over this lane's 16 tokens of half h of a page (token 32c + 4s + i for slabs s = 4h..4h+3,
