@@ -1,7 +1,8 @@
 // NVFP4 quantize-and-insert of K, V and index keys into their paged caches.
 //
-// "vLLM day-0 support for MiniMax-M3.1-Flash", section "QKV GEMM + norm + RoPE + KV insert
-// fusion": K, V and the index key are quantized to NVFP4 when they are written to their caches.
+// "vLLM day-0 support for MiniMax-M3.1-Flash", section "TL;DR", its item on fusing the QKV
+// GEMM, norm, RoPE and KV insert: K, V and the index key are quantized to NVFP4 when they are
+// written to their caches.
 // "MiniMax-M3.1-Flash serving notes", section "The capacity numbers": 4-bit E2M1 values and one
 // E4M3 scale per 16 values.
 //

@@ -24,7 +24,7 @@ hipError_t launch_insert_at_positions(uint8_t* k_pool, uint8_t* v_pool, uint8_t*
                                       hipStream_t stream);
 
 // Insert of a decode step's new tokens (positions T - q_len .. T - 1 of each sequence, slots
-// from the block table) and the indexer, in one launch when q_len <= 16 (two otherwise).
+// from the block table) and the indexer, in one launch when q_len <= 8 (two otherwise).
 hipError_t launch_insert_indexer(uint8_t* k_pool, uint8_t* v_pool, uint8_t* ik_pool,
                                  int64_t num_pages, const int32_t* block_table,
                                  const int32_t* ctx_lens, int batch, int max_blocks, int q_len,

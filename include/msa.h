@@ -127,8 +127,8 @@ size_t msa_page_bytes(int which);
 
 /*
  * NVFP4-quantize n tokens and write them into their cache slots. ("vLLM day-0 support for
- * MiniMax-M3.1-Flash", section "QKV GEMM + norm + RoPE + KV insert fusion": K, V and the
- * index key are quantized to NVFP4 as they are written to their caches.)
+ * MiniMax-M3.1-Flash", section "TL;DR", its item on fusing the QKV GEMM, norm, RoPE and KV insert:
+ * K, V and the index key are quantized to NVFP4 as they are written to their caches.)
  *   slots : device int64 [n]; slot = page * 128 + token offset in the page. A negative slot or
  *           one whose page is outside [0, num_pages) skips that token. Slots must be distinct
  *           within one call (two tokens in one slot race).
@@ -242,9 +242,11 @@ int msa_insert_indexer_score(const msa_cache_t *cache, const msa_batch_t *batch,
  * them). Tokens at negative positions (T_b < q_len) are skipped. Results, cache bytes included,
  * are those of the three calls bit for bit. The insert runs in the indexer's launch: the
  * indexer quantizes the sequence's new index keys itself into its copy of the pages it scores,
- * so it needs no finished insert ("vLLM day-0 support for MiniMax-M3.1-Flash", section "QKV GEMM
- * + norm + RoPE + KV insert fusion": the insert is fused into the step's first kernel). With
- * q_len > 16 the insert runs as a launch of its own before the indexer.
+ * so it needs no finished insert ("vLLM day-0 support for MiniMax-M3.1-Flash", section "TL;DR",
+ * its item on fusing the QKV GEMM, norm, RoPE and KV insert: the insert is fused into the step's
+ * first kernel; "MiniMax M3 on vLLM", its roadmap section: fusing the many small indexer, top-k
+ * and quantization kernels). With q_len > 8 the insert runs as a launch of its own before the
+ * indexer.
  *   k, v : device fp32 [batch * q_len][4][128]; ik : device fp32 [batch * q_len][128]
  *          (request-major, as q); q_idx, q, block_scores, block_ids, out, workspace as for the
  *          calls above.
