@@ -56,10 +56,17 @@ def parse():
 
 
 def source_digest(*names):
+    """Digest of the kernel sources with comments and blank lines removed: a change of the code
+    changes it, a change of a comment does not."""
+    import re
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "block_sparse_attention_nvfp4_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "block_sparse_attention_nvfp4_amd", "csrc", n)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+        h.update(code.encode())
     return h.hexdigest()[:16]
 
 

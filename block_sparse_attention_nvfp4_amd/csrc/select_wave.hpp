@@ -20,7 +20,7 @@
 
 namespace msa {
 
-constexpr int kSelectScratch = 128;  // LDS entries per wavefront: 64 candidates + one spare per lane
+constexpr int kSelectScratch = 64;  // LDS entries per wavefront: up to 64 candidates
 
 // Order-preserving map of a non-NaN float to uint32 (larger float -> larger key); -0 == +0.
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -29,7 +29,20 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ int popc64(uint64_t x) { return __popcll(x); }
+// Population count of a lane mask as two 32-bit counts: the result stays a 32-bit scalar, so
+// comparisons of it are scalar instructions (a 64-bit count is compared on the vector unit).
+__device__ __forceinline__ int popc64(uint64_t x) {
+    return (int)(__builtin_popcount((uint32_t)x) + __builtin_popcount((uint32_t)(x >> 32)));
+}
+
+// Lane mask of x >= c, written to a scalar register pair by an explicit compare: several such
+// compares issue back to back, and the scalar unit then waits once for all of their results
+// (through the condition register the compiler would chain them, one wait each).
+__device__ __forceinline__ uint64_t ge_mask(uint32_t x, uint32_t c) {
+    uint64_t m;
+    asm("v_cmp_le_u32_e64 %0, %1, %2" : "=s"(m) : "s"(c), "v"(x));
+    return m;
+}
 
 // Number of lanes before this one whose bit is set.
 __device__ __forceinline__ int lanes_before(uint64_t mask) {
@@ -77,28 +90,28 @@ __device__ __forceinline__ void select_row(const float (&v)[KPL], int n, int lan
 #pragma unroll
     for (int bit = 30; bit >= 0; bit -= 2) {
         const uint32_t c3 = bound | (3u << bit), c2 = bound | (2u << bit), c1 = bound | (1u << bit);
-        const int n3 = popc64(__ballot(lmax >= c3));
-        const int n2 = popc64(__ballot(lmax >= c2));
-        const int n1 = popc64(__ballot(lmax >= c1));
+        const uint64_t m3 = ge_mask(lmax, c3), m2 = ge_mask(lmax, c2), m1 = ge_mask(lmax, c1);
+        const int n3 = popc64(m3), n2 = popc64(m2), n1 = popc64(m1);
         bound = n3 >= kTopk - 1 ? c3 : (n2 >= kTopk - 1 ? c2 : (n1 >= kTopk - 1 ? c1 : bound));
     }
-    // candidates: the keys at or above the bound
-    int count = 0;
+    // candidates: the keys at or above the bound (all slots' masks first, then their counts)
+    uint64_t cmask[KPL];
 #pragma unroll
-    for (int k = 0; k < KPL; k++) count += popc64(__ballot(key[k] >= bound));
+    for (int k = 0; k < KPL; k++) cmask[k] = ge_mask(key[k], bound);
+    int base[KPL + 1];
+    base[0] = 0;
+#pragma unroll
+    for (int k = 0; k < KPL; k++) base[k + 1] = base[k] + popc64(cmask[k]);
+    const int count = base[KPL];
     if (count <= 64) {
         // compact the candidates in ascending block order (k-major, lane-minor) as composites
         // (key, inverted block index): a larger composite ranks first, and equal keys rank by
-        // the lower block. Lanes without a candidate in slot k write a spare entry instead of
-        // branching.
-        int base = 0;
+        // the lower block; only candidate lanes store
 #pragma unroll
         for (int k = 0; k < KPL; k++) {
-            const bool c = key[k] >= bound;
-            const uint64_t mask = __ballot(c);
-            const int pos = c ? base + lanes_before(mask) : 64 + lane;
-            cand[pos] = ((uint64_t)key[k] << 32) | (uint32_t)~(uint32_t)(lane + 64 * k);
-            base += popc64(mask);
+            if (key[k] >= bound)
+                cand[base[k] + lanes_before(cmask[k])] =
+                    ((uint64_t)key[k] << 32) | (uint32_t)~(uint32_t)(lane + 64 * k);
         }
         __builtin_amdgcn_wave_barrier();
         // candidate t of lane t counts the candidates ranked before it, reading them eight at a
