@@ -122,14 +122,28 @@ __device__ __forceinline__ void lds_read16x9(u32x4 (&v)[8], u32x4& w, uint32_t a
                  : "v"(a), "v"(aw)
                  : "memory");
 }
-__device__ __forceinline__ void lds_read16x3(u32x4& v0, u32x4& v1, u32x4& v2, uint32_t a0,
-                                             uint32_t a1) {
-    asm volatile("ds_read_b128 %0, %3\n\t"
-                 "ds_read_b128 %1, %4\n\t"
-                 "ds_read_b128 %2, %4 offset:16\n\t"
+__device__ __forceinline__ void lds_read16x5(u32x4& v, u32x4 (&w)[4], uint32_t a, uint32_t aw) {
+    asm volatile("ds_read_b128 %0, %5\n\t"
+                 "ds_read_b128 %1, %6\n\t"
+                 "ds_read_b128 %2, %6 offset:16\n\t"
+                 "ds_read_b128 %3, %6 offset:32\n\t"
+                 "ds_read_b128 %4, %6 offset:48\n\t"
                  "s_waitcnt lgkmcnt(0)"
-                 : "=&v"(v0), "=&v"(v1), "=&v"(v2)
-                 : "v"(a0), "v"(a1)
+                 : "=&v"(v), "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3])
+                 : "v"(a), "v"(aw)
+                 : "memory");
+}
+__device__ __forceinline__ u32x4 lds_read16(uint32_t a) {
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(a) : "memory");
+    return v;
+}
+// Two 16-byte LDS writes, complete when the statement ends (reads that follow see them).
+__device__ __forceinline__ void lds_write32(uint32_t a, const u32x4& v0, const u32x4& v1) {
+    asm volatile("ds_write_b128 %0, %1\n\t"
+                 "ds_write_b128 %0, %2 offset:16\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 :: "v"(a), "v"(v0), "v"(v1)
                  : "memory");
 }
 
@@ -191,18 +205,36 @@ __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c
         }
     l_run += sum_over_c(ls);
 
+    // ---- the block's 1,024 V scales as fp16, [group][token], written over the K codes (read
+    // into registers above and not needed again): lane l converts the 16 scale bytes of group
+    // l / 8, tokens 16 (l % 8) .. +15. Each lane then reads its scales ready for the packed
+    // multiply instead of converting 256 of them.
+    {
+        const u32x4 raw = lds_read16(vbase + kCodeBytes + lane * 16);
+        u32x4 h0, h1;
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            h0[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[i], 1.0f, false));
+            h0[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[i], 1.0f, true));
+            h1[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[i + 2], 1.0f, false));
+            h1[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[i + 2], 1.0f, true));
+        }
+        lds_write32(kbase + lane * 32, h0, h1);
+    }
+
     // ---- O^T += V^T P^T, one 16-dim tile (= one scale group) at a time
 #pragma unroll
     for (int dt = 0; dt < 8; dt++) {
         const int d = 16 * dt + (lane & 15);
-        // codes of tokens 32c..32c+31; scales of tokens 32c..+15 and 32c+16..+31
-        u32x4 vc, vs0, vs1;
-        lds_read16x3(vc, vs0, vs1, vbase + d * 64 + 16 * c, vbase + kCodeBytes + dt * 128 + 32 * c);
+        // codes of tokens 32c..32c+31 and their fp16 scales of group dt
+        u32x4 vc, sc[4];
+        lds_read16x5(vc, sc, vbase + d * 64 + 16 * c, kbase + dt * 256 + 64 * c);
 #pragma unroll
         for (int s = 0; s < 8; s++) {
-            const uint32_t sw = s < 4 ? vs0[s] : vs1[s - 4];  // tokens 32c + 4s .. +3
-            const f16x4 a = (s & 1) ? dequant4_f16_percode<2>(vc[s >> 1], sw)
-                                    : dequant4_f16_percode<0>(vc[s >> 1], sw);
+            // tokens 32c + 4s .. +3: scale pairs (4s, 4s+1) and (4s+2, 4s+3)
+            const uint32_t s01 = sc[s >> 1][(s & 1) * 2], s23 = sc[s >> 1][(s & 1) * 2 + 1];
+            const f16x4 a = (s & 1) ? dequant4_f16_scaled<2>(vc[s >> 1], s01, s23)
+                                    : dequant4_f16_scaled<0>(vc[s >> 1], s01, s23);
             o[dt] = mfma_f16_k16(a, pt[s], o[dt]);
         }
     }

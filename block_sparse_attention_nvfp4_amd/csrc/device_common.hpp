@@ -78,24 +78,20 @@ __device__ __forceinline__ bf16x8 dequant8_bf16(uint32_t w, float s) {
     return r;
 }
 
-// Four E2M1 codes (bytes SEL, SEL+1 of `w`) times four per-code E4M3 scales (the four bytes
-// of `sw`) -> four fp16 values, exact: E2M1 and E4M3 values are exact in fp16 and so is their
-// product (at most 6 significant bits, magnitude within [2^-10, 2688]). The conversions carry a
-// power-of-two scale operand only, so 1.0 is passed and the E4M3 scale is applied by one packed
-// fp16 multiply per pair.
+// Four E2M1 codes (bytes SEL, SEL+1 of `w`) times four per-code scales, given in fp16 as the
+// pairs (s0, s1) and (s2, s3) -> four fp16 values, exact: E2M1 and E4M3 values are exact in fp16
+// and so is their product (at most 6 significant bits, magnitude within [2^-10, 2688]). The
+// conversion carries a power-of-two scale operand only, so 1.0 is passed and the E4M3 scale is
+// applied by one packed fp16 multiply per pair.
 template <int SEL>
-__device__ __forceinline__ f16x4 dequant4_f16_percode(uint32_t w, uint32_t sw) {
-    const f16x2 v01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
-    const f16x2 v23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL + 1);
-    const f16x2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
-    const f16x2 s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, true);
-    const f16x2 a = v01 * s01;
-    const f16x2 b = v23 * s23;
+__device__ __forceinline__ f16x4 dequant4_f16_scaled(uint32_t w, uint32_t s01, uint32_t s23) {
+    const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL) * __builtin_bit_cast(f16x2, s01);
+    const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL + 1) * __builtin_bit_cast(f16x2, s23);
     return f16x4{a[0], a[1], b[0], b[1]};
 }
 
 // Eight E2M1 codes (one 32-bit word) times the scale pair {s, s} -> eight fp16 values, exact
-// (see dequant4_f16_percode): the conversion gives the unscaled E2M1 values, one packed fp16
+// (see dequant4_f16_scaled): the conversion gives the unscaled E2M1 values, one packed fp16
 // multiply per pair applies the E4M3 scale.
 __device__ __forceinline__ f16x8 dequant8_f16(uint32_t w, f16x2 ss) {
     const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
