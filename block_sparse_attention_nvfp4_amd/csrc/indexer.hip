@@ -199,6 +199,14 @@ __device__ __forceinline__ void patch_new_tokens(const uint8_t* buf, int tok0, i
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
+// A 64-bit value that is the same in every lane, as a scalar. (readfirstlane returns a signed
+// int: each half goes through uint32_t so that the low half is not sign-extended.)
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (uint64_t)lo | ((uint64_t)hi << 32);
+}
+
 // Source of insert item i = 9 j + vec of sequence b: new token j, head vector vec (K heads
 // 0-3, V heads 4-7, the index key 8).
 __device__ __forceinline__ const float* item_source(int item, int b, int q_len,
@@ -255,12 +263,13 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
     const uint8_t* ik_pool, int64_t num_pages, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ ctx_lens, int max_blocks, int q_len,
     const uint16_t* __restrict__ q_idx, float* __restrict__ scores, uint8_t* k_pool_w,
-    uint8_t* v_pool_w, uint8_t* ik_pool_w, const float* __restrict__ new_k,
+    uint8_t* v_pool_w, const float* __restrict__ new_k,
     const float* __restrict__ new_v, const float* __restrict__ new_ik) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves][kBufs][kHalfBytes];
     // half-page maxima of the row tile: [half][row][block - wg_blk0], rows padded apart in banks
     __shared__ float stash[2][16][kPagesPerWg + 1];
     __shared__ int next_page[2];  // page counters of the two halves
+    __shared__ __attribute__((aligned(8))) uint64_t fused_ptrs[FUSED ? 5 : 1];
     __shared__ __attribute__((aligned(16))) uint8_t qbuf[kWaves][4 * 1024];  // query operands
     __shared__ __attribute__((aligned(16))) uint8_t stage[FUSED ? 4 : 1][FUSED ? kFusedMaxNew * kStageBytes : 16];
     const int lane = threadIdx.x & 63;
@@ -282,6 +291,20 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
     if (threadIdx.x < 2) {
         const uint32_t a = (uint32_t)(uintptr_t)&next_page[threadIdx.x];
         asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(a), "v"(kPairs) : "memory");
+    }
+    if constexpr (FUSED) {
+        // the insert's pointers, needed again only by the stores after the last page, are kept
+        // in LDS rather than in scalar registers through the whole scan
+        if (threadIdx.x == 0) {
+            const uint32_t a = (uint32_t)(uintptr_t)&fused_ptrs[0];
+            const uint64_t p0 = (uint64_t)(uintptr_t)new_k, p1 = (uint64_t)(uintptr_t)new_v;
+            const uint64_t p2 = (uint64_t)(uintptr_t)new_ik, p3 = (uint64_t)(uintptr_t)k_pool_w;
+            const uint64_t p4 = (uint64_t)(uintptr_t)v_pool_w;
+            asm volatile("ds_write_b64 %0, %1\n\tds_write_b64 %0, %2 offset:8\n\t"
+                         "ds_write_b64 %0, %3 offset:16\n\tds_write_b64 %0, %4 offset:24\n\t"
+                         "ds_write_b64 %0, %5 offset:32\n\ts_waitcnt lgkmcnt(0)"
+                         ::"v"(a), "v"(p0), "v"(p1), "v"(p2), "v"(p3), "v"(p4) : "memory");
+        }
     }
     __builtin_amdgcn_s_barrier();
     // the workgroup's block-table entries (lane l: block wg_blk0 + l) and the context length are
@@ -305,39 +328,34 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
     const int n_blocks = T > 0 ? min(max_blocks, (T - 1) / kBlock + 1) : 0;
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     pid_all = (wg_blk0 + lane < n_blocks && pid_all >= 0 && pid_all < num_pages) ? pid_all : -1;
-    // position of the first insert item and its block-table entry: a load the compiler sees
-    // (vector, through an index it cannot prove uniform), so that it waits for it at its use,
-    // the store after the last page, long after it returned
-    const int ins_pos = FUSED && item < n_items ? T - q_len + item / 9 : -1;
+    // the first insert item's position and block-table entry (set after the first page of the
+    // first row tile is requested)
+    int ins_pos = -1;
     int ins_page_v = -1;
-    if (ins_pos >= 0) {
-        int idx = ins_pos >> 7;
-        asm volatile("" : "+v"(idx));
-        ins_page_v = table[idx];
-    }
     uint32_t ins_byte = 0, ins_scale = 0;
     uint32_t prepped = 0;  // fused: tokens whose patch bytes are in this wavefront's staging area
     bool staged = false;   // fused: the new index keys were copied to the staging area
 
-    for (int rt = 0; rt < rows; rt += 16) {
-        const int r = rt + n;
-        const int p_row = T - q_len + (r >> 2);                  // position of row r's token
-        const int j_hi = min((rt >> 2) + 3, q_len - 1);
-        const int p_lo = T - q_len + (rt >> 2);                  // lowest position in the tile
-        const int p_hi = T - q_len + j_hi;                       // highest position in the tile
-        const int vis_end = min(wg_end, p_hi >= 0 ? p_hi / kBlock + 1 : 0);
-        // page u (u = 0 .. n_pages - 1) of the tile is block vis_end - 1 - u
+    // row tile rt (query rows rt .. rt + 15): one past its highest visible block; page u of the
+    // tile is block vis_end - 1 - u
+    auto tile_vis_end = [&](int rt) {
+        const int p_hi = T - q_len + min((rt >> 2) + 3, q_len - 1);  // highest position in it
+        return min(wg_end, p_hi >= 0 ? p_hi / kBlock + 1 : 0);
+    };
+    // load half h of page u of a tile into LDS buffer `buf`; false when the page is absent
+    auto issue = [&](int u, int buf, int vis_end) {
+        const int pid = __builtin_amdgcn_readlane(pid_all, vis_end - 1 - u - wg_blk0);
+        if (pid < 0) return false;
+        half_to_lds(ik_pool + (int64_t)pid * kHeadPageBytes, h, lds[wave][buf], lane);
+        return true;
+    };
+    // request a row tile's loads: the patch staging (fused, pairs 0 and 1), the query rows and
+    // this wavefront's first page
+    auto request_tile = [&](int rt, uint32_t& patch_mask, int& cur, bool& cur_loaded) {
+        const int vis_end = tile_vis_end(rt);
         const int n_pages = max(vis_end - wg_blk0, 0);
-
-        // load half h of page u into LDS buffer `buf`; false when the page is absent
-        auto issue = [&](int u, int buf) {
-            const int pid = __builtin_amdgcn_readlane(pid_all, vis_end - 1 - u - wg_blk0);
-            if (pid < 0) return false;
-            half_to_lds(ik_pool + (int64_t)pid * kHeadPageBytes, h, lds[wave][buf], lane);
-            return true;
-        };
         // fused: the tokens this wavefront patches into its first page (pairs 0 and 1 only)
-        uint32_t patch_mask = 0;
+        patch_mask = 0;
         if constexpr (FUSED) {
             if (pair < 2 && pair < n_pages)
                 patch_mask = patch_tokens(vis_end - 1 - pair, T, q_len, h);
@@ -358,17 +376,44 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
         // page: the wait for it leaves the page in flight. Every lane loads a valid row (rows
         // past the tile read row rows - 1) and zeroes it after the wait.
         {
-            const uint16_t* qp = q_idx + (row_base + min(r, rows - 1)) * kDim + 32 * c;
+            const uint16_t* qp = q_idx + (row_base + min(rt + n, rows - 1)) * kDim + 32 * c;
 #pragma unroll
             for (int m = 0; m < 4; m++)
                 __builtin_amdgcn_global_load_lds(qp + 8 * m, (lds_void*)(qbuf[wave] + 1024 * m),
                                                  16, 0, 0);
         }
-        int cur = pair < n_pages ? pair : n_pages;  // this wavefront's page (n_pages: none)
-        bool cur_loaded = cur < n_pages && issue(cur, 0);
+        cur = pair < n_pages ? pair : n_pages;  // this wavefront's page (n_pages: none)
+        cur_loaded = cur < n_pages && issue(cur, 0, vis_end);
+    };
+    uint32_t patch_mask;
+    int cur;
+    bool cur_loaded;
+    // the first tile's loads go out right after start-up, ahead of any other set-up
+    request_tile(0, patch_mask, cur, cur_loaded);
+
+    for (int rt = 0; rt < rows; rt += 16) {
+        const int r = rt + n;
+        const int p_row = T - q_len + (r >> 2);                  // position of row r's token
+        const int p_lo = T - q_len + (rt >> 2);                  // lowest position in the tile
+        const int vis_end = tile_vis_end(rt);
+        const int n_pages = max(vis_end - wg_blk0, 0);
+        if (rt > 0) request_tile(rt, patch_mask, cur, cur_loaded);
         if constexpr (FUSED) {
-            // the first insert item is quantized while the first page is in flight
-            if (rt == 0 && item < n_items) quantize_pair(ins_x[0], ins_x[1], ins_byte, ins_scale);
+            if (rt == 0 && item < n_items) {
+                // after the first loads are issued (the item's work never delays them): the
+                // item's block-table entry, a load the compiler sees (vector, through an index it
+                // cannot prove uniform) and waits for at its use, the store after the last page;
+                // and its quantization, while the first page is in flight
+                int t_late = T;
+                asm volatile("" : "+v"(t_late));
+                ins_pos = __builtin_amdgcn_readfirstlane(t_late) - q_len + item / 9;
+                if (ins_pos >= 0) {
+                    int idx = ins_pos >> 7;
+                    asm volatile("" : "+v"(idx));
+                    ins_page_v = table[idx];
+                }
+                quantize_pair(ins_x[0], ins_x[1], ins_byte, ins_scale);
+            }
         }
         wait_halves(cur_loaded ? 1 : 0);
         u32x4 qraw[4];
@@ -397,7 +442,7 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
 #pragma unroll 1
         while (cur < n_pages) {
             const int nxt = claim_page(&next_page[h], lane);
-            const bool nxt_loaded = nxt < n_pages && issue(nxt, buf ^ 1);
+            const bool nxt_loaded = nxt < n_pages && issue(nxt, buf ^ 1, vis_end);
             const int blk = vis_end - 1 - cur;
             const int tok0 = blk * kBlock;
             float best = -INFINITY;
@@ -433,16 +478,30 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
             // the insert stores, after the wavefront's last page load has returned; then any
             // further items (more items than wavefronts: short contexts), one at a time
             if (rt + 16 >= rows && item < n_items) {
+                uint64_t fp[5];
+                {
+                    const uint32_t a = (uint32_t)(uintptr_t)&fused_ptrs[0];
+                    asm volatile("ds_read_b64 %0, %5\n\tds_read_b64 %1, %5 offset:8\n\t"
+                                 "ds_read_b64 %2, %5 offset:16\n\tds_read_b64 %3, %5 offset:24\n\t"
+                                 "ds_read_b64 %4, %5 offset:32\n\ts_waitcnt lgkmcnt(0)"
+                                 : "=&v"(fp[0]), "=&v"(fp[1]), "=&v"(fp[2]), "=&v"(fp[3]), "=&v"(fp[4])
+                                 : "v"(a) : "memory");
+                }
+                const float* nk = (const float*)uniform64(fp[0]);
+                const float* nv = (const float*)uniform64(fp[1]);
+                const float* nik = (const float*)uniform64(fp[2]);
+                uint8_t* kp = (uint8_t*)uniform64(fp[3]);
+                uint8_t* vpw = (uint8_t*)uniform64(fp[4]);
                 store_item(item, __builtin_amdgcn_readfirstlane(ins_page_v), ins_pos, num_pages,
-                           ins_byte, ins_scale, k_pool_w, v_pool_w, ik_pool_w, lane);
+                           ins_byte, ins_scale, kp, vpw, const_cast<uint8_t*>(ik_pool), lane);
                 for (item += kWaves * gx; item < n_items; item += kWaves * gx) {
                     const f32x2 x = *reinterpret_cast<const f32x2*>(
-                        item_source(item, b, q_len, new_k, new_v, new_ik) + 2 * lane);
+                        item_source(item, b, q_len, nk, nv, nik) + 2 * lane);
                     const int pos = T - q_len + item / 9;
                     const int64_t page = pos >= 0 ? table[pos >> 7] : -1;
                     quantize_pair(x[0], x[1], ins_byte, ins_scale);
-                    store_item(item, page, pos, num_pages, ins_byte, ins_scale, k_pool_w,
-                               v_pool_w, ik_pool_w, lane);
+                    store_item(item, page, pos, num_pages, ins_byte, ins_scale, kp, vpw,
+                               const_cast<uint8_t*>(ik_pool), lane);
                 }
             }
         }
@@ -479,7 +538,7 @@ hipError_t launch_indexer(const uint8_t* ik_pool, int64_t num_pages, const int32
     hipLaunchKernelGGL(indexer_kernel<false>, dim3(indexer_wgs(batch, max_blocks)),
                        dim3(kWaves * 64), 0, stream, ik_pool, num_pages, block_table, ctx_lens,
                        max_blocks, q_len, q_idx, scores, nullptr, nullptr, nullptr, nullptr,
-                       nullptr, nullptr);
+                       nullptr);
     return hipGetLastError();
 }
 
@@ -491,8 +550,7 @@ hipError_t launch_insert_indexer(uint8_t* k_pool, uint8_t* v_pool, uint8_t* ik_p
     if (q_len <= kFusedMaxNew) {
         hipLaunchKernelGGL(indexer_kernel<true>, dim3(indexer_wgs(batch, max_blocks)),
                            dim3(kWaves * 64), 0, stream, ik_pool, num_pages, block_table, ctx_lens,
-                           max_blocks, q_len, q_idx, scores, k_pool, v_pool, ik_pool, new_k, new_v,
-                           new_ik);
+                           max_blocks, q_len, q_idx, scores, k_pool, v_pool, new_k, new_v, new_ik);
         return hipGetLastError();
     }
     // more new tokens than the patch stages: the insert launch first, then the indexer
