@@ -276,18 +276,22 @@ def main():
             torch.cuda.synchronize()
             alt_ms[key] = e4s.elapsed_time(e4e) / (max(1, args.steps // L) * L)
 
-        # per-kernel durations: graphs of L back-to-back launches, HIP events around each replay
+        # per-kernel durations: graphs of L back-to-back launches, HIP events around series of
+        # kernel_reps replays; the median of five series
         kernel_us = {}
         for name, g in kgraphs.items():
             g.replay()
             torch.cuda.synchronize()
-            es, ee = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            es.record(stream)
-            for _ in range(args.kernel_reps):
-                g.replay()
-            ee.record(stream)
-            torch.cuda.synchronize()
-            kernel_us[name] = es.elapsed_time(ee) * 1e3 / (args.kernel_reps * L)
+            series = []
+            for _ in range(5):
+                es, ee = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                es.record(stream)
+                for _ in range(args.kernel_reps):
+                    g.replay()
+                ee.record(stream)
+                torch.cuda.synchronize()
+                series.append(es.elapsed_time(ee) * 1e3 / (args.kernel_reps * L))
+            kernel_us[name] = sorted(series)[2]
 
     ms_per_step = wall * 1e3 / args.steps
     tokens_per_step = B * q
