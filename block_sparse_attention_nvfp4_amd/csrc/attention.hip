@@ -260,11 +260,13 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
     __shared__ int sh_pages[kWaves][BPW];
     __shared__ int sh_last;
     __shared__ int sh_sel[SELECT ? kTopk : 1];
-    __shared__ uint64_t sel_cand[SELECT ? kSelectScratch : 1];
+    static_assert(kSelectScratch * 8 <= kBlockBytes, "selection scratch must fit in a page buffer");
     __shared__ int sh_tbl[SELECT ? kSelectFusedMaxBlocks : 1];  // the sequence's block table
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // wavefront-uniform (a scalar value): the per-wavefront roles below are scalar branches, so
+    // no wavefront waits for memory that only another role's code path requested
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15;
     const int c = lane >> 4;
     // XCD-aware work mapping: pair = (b, g) -> XCD pair % 8
@@ -279,6 +281,14 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
     const int g = pair & 3;
     const int bq = b * q_len + j;
     const int rg = bq * kKvHeads + g;  // row group
+    // the B operand of S^T is requested first (head 16g + n, dims 32c + 8m .. +7): it arrives
+    // during the selection, and no later wait for it also waits for the page loads
+    bf16x8 qb[4];
+    {
+        const uint16_t* qp = q + ((int64_t)bq * kQHeads + kGroupHeads * g + n) * kDim + 32 * c;
+#pragma unroll
+        for (int m = 0; m < 4; m++) qb[m] = *reinterpret_cast<const bf16x8*>(qp + 8 * m);
+    }
     // this wavefront's blocks (id and page, or -1 when the id is not selected, has no visible
     // token or maps to a page out of range), read once: a table load issued between page loads
     // would make the in-order memory counter wait for every page in flight. The ids and the
@@ -295,7 +305,9 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
             for (int k = 0; k < 16; k++) asm volatile("" : "+v"(sv[k]));
             asm volatile("" : "+v"(t_sel));
             const int p_sel = clamp_ctx(t_sel, max_blocks) - q_len + j;
-            select_row<16>(sv, eligible_blocks(p_sel, max_blocks), lane, sel_cand, sh_sel);
+            // scratch: this wavefront's page buffer, not in use before the selection is done
+            select_row<16>(sv, eligible_blocks(p_sel, max_blocks), lane,
+                           reinterpret_cast<uint64_t*>(&lds[0][0][0]), sh_sel);
             if (split == 0 && lane < kTopk) block_ids[(int64_t)rg * kTopk + lane] = sh_sel[lane];
         } else {
             // meanwhile the other wavefronts copy the sequence's block-table row into LDS (all
@@ -305,12 +317,13 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
             constexpr int kPer = (kSelectFusedMaxBlocks + kThr - 1) / kThr;
             const int t0 = threadIdx.x - 64;
             const int32_t* trow = block_table + (int64_t)b * max_blocks;
+            // (indexes past the row are clamped to its last entry, which they then rewrite with
+            // its own value: every store is unconditional and writes the right value)
             int tv[kPer];
 #pragma unroll
             for (int r = 0; r < kPer; r++) tv[r] = trow[min(t0 + r * kThr, max_blocks - 1)];
 #pragma unroll
-            for (int r = 0; r < kPer; r++)
-                if (t0 + r * kThr < max_blocks) sh_tbl[t0 + r * kThr] = tv[r];
+            for (int r = 0; r < kPer; r++) sh_tbl[min(t0 + r * kThr, max_blocks - 1)] = tv[r];
         }
         __syncthreads();
         id = lane < BPW ? sh_sel[(split * kWaves + wave) * BPW + lane] : -1;
@@ -347,13 +360,7 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
         const int pg = __builtin_amdgcn_readfirstlane(sh_pages[wave][0]);
         block_to_lds(kg + pg * kPageStride, vg + pg * kPageStride, lds[wave][0], lane);
     }
-    // B operand of S^T (prepared while the first block streams in): head 16g + n, dims 32c + 8m .. +7
-    bf16x8 qb[4];
-    {
-        const uint16_t* qp = q + ((int64_t)bq * kQHeads + kGroupHeads * g + n) * kDim + 32 * c;
-#pragma unroll
-        for (int m = 0; m < 4; m++) qb[m] = *reinterpret_cast<const bf16x8*>(qp + 8 * m);
-    }
+    // the B operand is prepared while the first block streams in
     f16x8 qh[4];
     float q_unscale;
     const bool f16 = __all(query_to_f16(qb, qh, q_unscale));

@@ -7,26 +7,30 @@
 // twice. Ties go to the lower block index.
 //
 // The row's scores become order-preserving integer keys in registers (block i in lane i % 64,
-// slot i / 64). The 15th-largest of the 64 per-lane maxima, found by a bitwise search with
-// ballot counts (two bits per step), is a lower bound of the 15th-largest key (at least 15 keys
-// reach it), so the selection lies among the keys at or above it. Those few candidates are
-// compacted into LDS in ascending block order as (key, inverted block index) composites and each
-// is ranked exactly against the others by reading them back as LDS broadcasts; the 15 best,
-// already in ascending block order, are written with the forced block last. When more than 64
-// candidates reach the bound (heavy ties), the wavefront extracts the 15 best one by one instead.
+// slot i / 64). The 15th-largest of the 64 per-lane maxima is a lower bound of the 15th-largest
+// key (at least 15 keys reach it), so the selection lies among the keys at or above it. It is
+// found without a serial search: every lane counts the maxima above its own (all 64 read back
+// from LDS as broadcasts), and the bound is the smallest maximum that fewer than 15 others
+// exceed. The few candidates are compacted into LDS in ascending block order as (key, inverted
+// block index) composites, without branches, and each is ranked exactly against the others by
+// reading them back as LDS broadcasts; the 15 best, already in ascending block order, are written
+// with the forced block last. When more than 64 candidates reach the bound (heavy ties), the
+// wavefront extracts the 15 best one by one instead.
 #pragma once
 
 #include "device_common.hpp"
 
 namespace msa {
 
-constexpr int kSelectScratch = 64;  // LDS entries per wavefront: up to 64 candidates
+// LDS entries (8 bytes) per wavefront: candidates [0, 64), writes of non-candidates [64, 128),
+// the 64 lane maxima as 4-byte words [128, 160).
+constexpr int kSelectScratch = 160;
 
-// Order-preserving map of a non-NaN float to uint32 (larger float -> larger key); -0 == +0.
+// Order-preserving map of a non-NaN float to uint32 (larger float -> larger key); -0 == +0
+// (adding +0 turns -0 into +0).
 __device__ __forceinline__ uint32_t order_key(float f) {
-    if (f == 0.0f) f = 0.0f;
-    const uint32_t u = __float_as_uint(f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const uint32_t u = __float_as_uint(f + 0.0f);
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 // Population count of a lane mask as two 32-bit counts: the result stays a 32-bit scalar, so
@@ -49,6 +53,43 @@ __device__ __forceinline__ int lanes_before(uint64_t mask) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
 }
 
+// if_set in the lanes whose bit of mask is set, if_clear elsewhere: the lane mask (a scalar
+// register pair) selects directly. The two wait states cover a mask just written by a compare.
+__device__ __forceinline__ uint32_t select_by_mask(uint64_t mask, uint32_t if_set, uint32_t if_clear) {
+    uint32_t r;
+    asm("s_nop 1\n\tv_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(if_clear), "v"(if_set), "s"(mask));
+    return r;
+}
+
+// acc plus the number of the four values above x: four compares into scalar register pairs, then
+// four carry additions (each compare's result is read three instructions after it is written).
+__device__ __forceinline__ int add_count_above(const u32x4& w, uint32_t x, int acc) {
+    uint64_t c0, c1, c2, c3, dummy;
+    asm("v_cmp_gt_u32_e64 %1, %6, %10\n\t"
+        "v_cmp_gt_u32_e64 %2, %7, %10\n\t"
+        "v_cmp_gt_u32_e64 %3, %8, %10\n\t"
+        "v_cmp_gt_u32_e64 %4, %9, %10\n\t"
+        "v_addc_co_u32_e64 %0, %5, %0, 0, %1\n\t"
+        "v_addc_co_u32_e64 %0, %5, %0, 0, %2\n\t"
+        "v_addc_co_u32_e64 %0, %5, %0, 0, %3\n\t"
+        "v_addc_co_u32_e64 %0, %5, %0, 0, %4"
+        : "+v"(acc), "=&s"(c0), "=&s"(c1), "=&s"(c2), "=&s"(c3), "=&s"(dummy)
+        : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(x));
+    return acc;
+}
+
+// Minimum over the wavefront's 64 lanes, in every lane of the last row (lane 63 is read):
+// within each row of 16 by quad swaps and mirrors, then across rows by the row broadcasts.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // half-row mirror
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row mirror
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));  // row 0 -> 1, 2 -> 3
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));  // row 1 -> 2, 3
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // Eligible blocks of a query token at position p (blocks 0..n-1; the last one, n - 1, holds the
 // token and is forced); 0 when the token has no position.
 __device__ __forceinline__ int eligible_blocks(int p, int max_blocks) {
@@ -60,8 +101,10 @@ __device__ __forceinline__ int eligible_blocks(int p, int max_blocks) {
 template <int KPL>
 __device__ __forceinline__ void load_row_scores(const float* s, int max_blocks, int lane,
                                                 float (&v)[KPL]) {
+    const uint8_t* row = reinterpret_cast<const uint8_t*>(s);  // 32-bit byte offsets from it
 #pragma unroll
-    for (int k = 0; k < KPL; k++) v[k] = s[min(lane + 64 * k, max_blocks - 1)];
+    for (int k = 0; k < KPL; k++)
+        v[k] = *reinterpret_cast<const float*>(row + 4u * (uint32_t)min(lane + 64 * k, max_blocks - 1));
 }
 
 // Select the row's blocks from its scores v (as load_row_scores holds them) and its n eligible
@@ -83,17 +126,22 @@ __device__ __forceinline__ void select_row(const float (&v)[KPL], int n, int lan
         key[k] = i < m ? order_key(v[k]) : 0u;
         lmax = max(lmax, key[k]);
     }
-    // bound: the 15th-largest per-lane maximum (bitwise search, most significant bits first, two
-    // bits per step: the three candidate values of a step are tested by independent ballots, and
-    // the count of maxima at or above a value falls as the value grows)
-    uint32_t bound = 0;
+    // bound: the 15th-largest per-lane maximum, the smallest maximum that fewer than 15 others
+    // exceed (each lane counts the maxima above its own, read back as LDS broadcasts). The
+    // candidate area is cleared in the same pass: entries past the candidate count read as 0,
+    // below every candidate.
+    uint32_t* lane_max = reinterpret_cast<uint32_t*>(cand + 128);
+    lane_max[lane] = lmax;
+    cand[lane] = 0;
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");  // the reads below follow these stores
+    u32x4 w[16];
 #pragma unroll
-    for (int bit = 30; bit >= 0; bit -= 2) {
-        const uint32_t c3 = bound | (3u << bit), c2 = bound | (2u << bit), c1 = bound | (1u << bit);
-        const uint64_t m3 = ge_mask(lmax, c3), m2 = ge_mask(lmax, c2), m1 = ge_mask(lmax, c1);
-        const int n3 = popc64(m3), n2 = popc64(m2), n1 = popc64(m1);
-        bound = n3 >= kTopk - 1 ? c3 : (n2 >= kTopk - 1 ? c2 : (n1 >= kTopk - 1 ? c1 : bound));
-    }
+    for (int r = 0; r < 16; r++) w[r] = reinterpret_cast<const u32x4*>(lane_max)[r];
+    int above = 0;
+#pragma unroll
+    for (int r = 0; r < 16; r++) above = add_count_above(w[r], lmax, above);
+    const uint32_t bound = wave_min_u32(above < kTopk - 1 ? lmax : 0xFFFFFFFFu);
     // candidates: the keys at or above the bound (all slots' masks first, then their counts)
     uint64_t cmask[KPL];
 #pragma unroll
@@ -102,28 +150,32 @@ __device__ __forceinline__ void select_row(const float (&v)[KPL], int n, int lan
     base[0] = 0;
 #pragma unroll
     for (int k = 0; k < KPL; k++) base[k + 1] = base[k] + popc64(cmask[k]);
-    const int count = base[KPL];
+    const int count = __builtin_amdgcn_readfirstlane(base[KPL]);  // uniform: a scalar loop bound
     if (count <= 64) {
         // compact the candidates in ascending block order (k-major, lane-minor) as composites
         // (key, inverted block index): a larger composite ranks first, and equal keys rank by
-        // the lower block; only candidate lanes store
+        // the lower block. Every lane stores; a non-candidate's store goes to its own entry of
+        // the discard area.
+        const uint32_t inv_lane = ~(uint32_t)lane;
 #pragma unroll
         for (int k = 0; k < KPL; k++) {
-            if (key[k] >= bound)
-                cand[base[k] + lanes_before(cmask[k])] =
-                    ((uint64_t)key[k] << 32) | (uint32_t)~(uint32_t)(lane + 64 * k);
+            const uint32_t pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(cmask[k] >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)cmask[k], base[k]));
+            cand[select_by_mask(cmask[k], pos, 64 + lane)] =
+                ((uint64_t)key[k] << 32) | (inv_lane - 64u * k);
         }
         __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
         // candidate t of lane t counts the candidates ranked before it, reading them eight at a
-        // time as LDS broadcasts
-        const uint64_t mine = lane < count ? cand[lane] : 0u;
+        // time as LDS broadcasts (the cleared entries past the count never rank before it)
+        const uint64_t mine = cand[lane];
         int rank = 0;
         for (int t0 = 0; t0 < count; t0 += 8) {
             uint64_t o[8];
 #pragma unroll
             for (int i = 0; i < 8; i++) o[i] = cand[t0 + i];
 #pragma unroll
-            for (int i = 0; i < 8; i++) rank += (t0 + i < count) && o[i] > mine;
+            for (int i = 0; i < 8; i++) rank += (int)(o[i] > mine);
         }
         const bool sel = lane < count && rank < kTopk - 1;
         const uint64_t smask = __ballot(sel);
