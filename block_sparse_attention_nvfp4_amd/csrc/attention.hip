@@ -20,10 +20,10 @@
 //   O^T += V^T P^T on fp16 matrix cores: P^T in the same lanes is already the B operand and V^T
 //   (A operand, dims x tokens) is the exact fp16 dequantization of the column-layout V page.
 // The wavefronts merge through LDS. With one split the workgroup writes the bf16 output;
-// otherwise it writes an fp32 partial (max, sum, output) with agent-coherent stores and counts
-// itself finished on the row group's counter; the split that finishes last reads the others'
-// partials, merges them by log-sum-exp and writes the output, so no second launch (and no
-// second kernel boundary) is needed. Workgroup ids map all work of one (sequence, group) pair
+// otherwise each wavefront writes the fp32 partial (max, sum, output) of four heads with
+// agent-coherent stores and counts itself finished on their counter; the wavefront that
+// finishes last reads the other splits' partials, merges them by log-sum-exp and writes the
+// output, so no second launch (and no second kernel boundary) is needed. Workgroup ids map all work of one (sequence, group) pair
 // to one XCD, so the blocks that the query tokens of a pair share are read from HBM once and
 // then hit that XCD's L2.
 #include "device_common.hpp"
@@ -258,7 +258,6 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
     __shared__ float sh_l[kWaves][kGroupHeads];
     __shared__ int sh_ids[kWaves][BPW];
     __shared__ int sh_pages[kWaves][BPW];
-    __shared__ int sh_last;
     __shared__ int sh_sel[SELECT ? kTopk : 1];
     static_assert(kSelectScratch * 8 <= kBlockBytes, "selection scratch must fit in a page buffer");
     __shared__ int sh_tbl[SELECT ? kSelectFusedMaxBlocks : 1];  // the sequence's block table
@@ -430,21 +429,21 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
         }
     }
     if (n_split > 1) {
-        // hand this split's (max, sum, output) over; the split that finishes last merges all of
-        // them and writes the output (the counter of the row group counts finished splits and is
-        // left at zero again for the next launch)
+        // hand this split's (max, sum, output) over; the wavefront that finishes last among the
+        // splits' wavefronts of the same four heads merges them and writes the output (its
+        // counter counts finished wavefronts and is left at zero again for the next launch)
         const int64_t part_base = (int64_t)rg * n_split * kGroupHeads;
         float* pp = partials + ((part_base + (int64_t)split * kGroupHeads) + h) * kPartStride;
         if (d0 == 0) store16_coherent(pp, f32x4{M, L, 0.f, 0.f});
         store16_coherent(pp + 4 + d0, f32x4{acc[0], acc[1], acc[2], acc[3]});
         store16_coherent(pp + 8 + d0, f32x4{acc[4], acc[5], acc[6], acc[7]});
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // stores complete, agent-wide
-        __syncthreads();
-        if (threadIdx.x == 0)
-            sh_last = __hip_atomic_fetch_add(&counters[rg], 1, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT) == n_split - 1;
-        __syncthreads();
-        if (!sh_last) return;
+        // each wavefront counts itself finished on the counter of its four heads: the last of
+        // them merges those heads, with no barrier between the wavefronts of a workgroup
+        int32_t* counter = counters + (int64_t)rg * kWaves + wave;
+        int prior = 0;
+        if (lane == 0) prior = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (__builtin_amdgcn_readlane(prior, 0) != n_split - 1) return;
         // every split's values requested before any is used (one memory round trip): splits
         // past n_split read this split's own partial, then every value not from another split
         // is replaced
@@ -471,8 +470,7 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
             a1[sp] = other ? part[sp][2]
                            : (sp == split ? f32x4{acc[4], acc[5], acc[6], acc[7]} : f32x4{0.f, 0.f, 0.f, 0.f});
         }
-        if (threadIdx.x == 0)
-            __hip_atomic_store(&counters[rg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         M = -INFINITY;
 #pragma unroll
         for (int sp = 0; sp < kMaxSplits; sp++) M = fmaxf(M, ml[sp][0]);
@@ -510,10 +508,10 @@ int attn_num_splits(int batch, int q_len) {
     return 4;
 }
 
-// Workspace with split partials: one int32 counter per row group (zero between launches),
-// padded to 256 bytes, then the partials.
+// Workspace with split partials: one int32 counter per (row group, wavefront of four heads),
+// zero between launches, padded to 256 bytes, then the partials.
 static size_t attn_counter_bytes(int batch, int q_len) {
-    return ((size_t)batch * q_len * kKvHeads * sizeof(int32_t) + 255) / 256 * 256;
+    return ((size_t)batch * q_len * kKvHeads * kWaves * sizeof(int32_t) + 255) / 256 * 256;
 }
 
 size_t attn_workspace_bytes(int batch, int q_len) {
