@@ -147,8 +147,10 @@ __device__ __forceinline__ void lds_write32(uint32_t a, const u32x4& v0, const u
                  : "memory");
 }
 
-// One block of one wavefront: logits, online-softmax update, output accumulation.
-template <bool F16>
+// One block of one wavefront: logits, online-softmax update, output accumulation. The K page
+// is in LDS on entry; the V page may still be arriving (NEXT: the next block's 18 loads were
+// issued after it) and is waited for only before its first read.
+template <bool F16, bool NEXT>
 __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c, int tok0, int p,
                                              const u32x4 (&qop)[4], float logit_scale,
                                              float& m_run, float& l_run, f32x4 (&o)[8]) {
@@ -205,6 +207,9 @@ __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c
         }
     l_run += sum_over_c(ls);
 
+    // ---- the V page's 9 loads (issued after the K page's 9) complete here
+    if constexpr (NEXT) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     // ---- the block's 1,024 V scales as fp16, [group][token], written over the K codes (read
     // into registers above and not needed again): lane l converts the 16 scale bytes of group
     // l / 8, tokens 16 (l % 8) .. +15. Each lane then reads its scales ready for the packed
@@ -344,7 +349,10 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
         sh_ids[wave][lane] = page >= 0 ? id : -1;
         sh_pages[wave][lane] = page;
     }
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    // every load so far is complete (the query's included), and the compiler knows it: it
+    // waits for nothing of them after the page loads are issued
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
 
     float m_run = -INFINITY, l_run = 0.f;
     f32x4 o[8];
@@ -381,14 +389,18 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
             }
         }
         if (cur_id >= 0) {
-            if (nxt_id >= 0) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            if (f16)
-                attend_block<true>(lds[wave][kb % kBufs], lane, c, cur_id * kBlock, p, qop,
-                                   logit_scale, m_run, l_run, o);
-            else
-                attend_block<false>(lds[wave][kb % kBufs], lane, c, cur_id * kBlock, p, qop,
-                                    logit_scale, m_run, l_run, o);
+            // the current block's K page (its first 9 loads) has arrived
+            uint8_t* buf = lds[wave][kb % kBufs];
+            const int tok0 = cur_id * kBlock;
+            if (nxt_id >= 0) {
+                asm volatile("s_waitcnt vmcnt(27)" ::: "memory");
+                if (f16) attend_block<true, true>(buf, lane, c, tok0, p, qop, logit_scale, m_run, l_run, o);
+                else attend_block<false, true>(buf, lane, c, tok0, p, qop, logit_scale, m_run, l_run, o);
+            } else {
+                asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+                if (f16) attend_block<true, false>(buf, lane, c, tok0, p, qop, logit_scale, m_run, l_run, o);
+                else attend_block<false, false>(buf, lane, c, tok0, p, qop, logit_scale, m_run, l_run, o);
+            }
         }
         cur_id = nxt_id;
     }
