@@ -38,7 +38,10 @@ constexpr int kPartStride = 132;  // floats per (row group, split, head): m, l, 
 constexpr int kMaxSplits = 4;     // attn_num_splits returns 1, 2 or 4
 constexpr int kBlockBytes = 2 * kHeadPageBytes;  // K page then V page of one (block, group)
 constexpr int kMergeStride = kDim + 4;           // LDS row of the wavefront merge
-constexpr int kNonTemporal = 2;                  // cache-policy bits of the page loads
+// Cache policy of the page loads: the default (0). The query tokens of one (sequence, group)
+// pair read mostly the same blocks on the same XCD, and the later reads hit its L2; the
+// non-temporal hint measured 0.25 us slower.
+constexpr int kPagePolicy = 0;
 // Lazy rescaling: a row keeps its running maximum until a block's maximum exceeds it by more
 // than this (log2 units); probabilities then stay below 2^kTau, well inside fp16, and the
 // accumulators are rescaled only when the maximum jumps.
@@ -61,12 +64,12 @@ __device__ __forceinline__ void block_to_lds(const uint8_t* kp, const uint8_t* v
 #pragma unroll
     for (int s = 0; s < 9; s++)
         __builtin_amdgcn_global_load_lds(kp + s * 1024 + lane * 16, (lds_void*)(buf + s * 1024), 16,
-                                         0, kNonTemporal);
+                                         0, kPagePolicy);
 #pragma unroll
     for (int s = 0; s < 9; s++)
         __builtin_amdgcn_global_load_lds(vp + s * 1024 + lane * 16,
                                          (lds_void*)(buf + kHeadPageBytes + s * 1024), 16, 0,
-                                         kNonTemporal);
+                                         kPagePolicy);
 }
 
 // Agent-coherent 16-byte store and load (cache policy sc1): written through to, and read from,

@@ -127,17 +127,21 @@ __device__ __forceinline__ bool query_to_f16(const bf16x8 (&qb)[4], f16x8 (&qh)[
     if (mx > 0.f) (void)frexpf(mx, &e);  // mx in [2^(e-1), 2^e)
     const int k = 15 - e;
     inv_scale = ldexpf(1.0f, -k);
-    bool exact = inv_scale > 0.f;  // k beyond the fp32 range: keep the bf16 path
+    // a value converted exactly when its fp16 value widens back to the same bits: the OR of
+    // the differences is zero for a row that converts exactly (bitwise vector operations only,
+    // no per-value lane-mask updates)
+    uint32_t diff = 0;
 #pragma unroll
     for (int m = 0; m < 4; m++)
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             const float f = ldexpf((float)qb[m][i], k);  // exact: no intermediate 2^k
             const _Float16 h = (_Float16)f;
-            exact = exact && ((float)h == f);
+            diff |= __float_as_uint((float)h) ^ __float_as_uint(f);
             qh[m][i] = h;
         }
-    return exact;
+    asm volatile("" : "+v"(diff));  // keeps the test one comparison (not one per value)
+    return inv_scale > 0.f && diff == 0u;  // k beyond the fp32 range: keep the bf16 path
 }
 
 // Exact fp16 -> bf16 of eight dequantized values (E2M1 x E4M3 products fit both formats).
