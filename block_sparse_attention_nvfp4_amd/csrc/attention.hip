@@ -178,7 +178,7 @@ __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c
             else
                 acc = mfma_bf16_k32(f16x8_to_bf16x8(a), __builtin_bit_cast(bf16x8, qop[m]), acc);
         }
-        sv[s] = acc * logit_scale;
+        sv[s] = acc;  // unscaled: the scale (> 0) is applied inside the exponent below
     }
     const bool full = tok0 + kBlock - 1 <= p;
     float mb = -INFINITY;
@@ -189,7 +189,7 @@ __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c
             if (!full && tok0 + 32 * c + 4 * s + i > p) sv[s][i] = -INFINITY;
             mb = fmaxf(mb, sv[s][i]);
         }
-    mb = max_over_c(mb);  // finite: token tok0 <= p is valid
+    mb = max_over_c(mb) * logit_scale;  // finite (token tok0 <= p is valid); scaling keeps order
     const float m_new = (mb > m_run + kTau) ? mb : m_run;  // m_run = -inf -> m_new = mb
     if (__any(m_new != m_run)) {
         const float alpha = fast_exp2(m_run - m_new);  // 0 when m_run = -inf (o, l are 0)
@@ -204,7 +204,7 @@ __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c
     for (int s = 0; s < 8; s++)
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            const float e = fast_exp2(sv[s][i] - m_new);
+            const float e = fast_exp2(fmaf(sv[s][i], logit_scale, -m_new));
             ls += e;
             pt[s][i] = (_Float16)e;
         }
@@ -256,9 +256,10 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
     const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool, int64_t num_pages,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens, int batch,
     int max_blocks, int q_len, const uint16_t* __restrict__ q, int32_t* __restrict__ block_ids,
-    const float* __restrict__ scores, float scale_log2, int n_split, uint16_t* __restrict__ out,
+    const float* __restrict__ scores, float scale_log2, uint16_t* __restrict__ out,
     int32_t* __restrict__ counters, float* __restrict__ partials) {
     constexpr int kBufs = BPW > 1 ? 2 : 1;
+    constexpr int n_split = kMaxSplits / BPW;  // workgroups per row group (BPW blocks per wavefront)
     static_assert(kWaves * kBufs * kBlockBytes >= kWaves * kGroupHeads * kMergeStride * 4,
                   "merge area must fit in the page buffers");
     __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves][kBufs][kBlockBytes];
@@ -378,7 +379,13 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
 #pragma unroll
     for (int m = 0; m < 4; m++)
         qop[m] = f16 ? __builtin_bit_cast(u32x4, qh[m]) : __builtin_bit_cast(u32x4, qb[m]);
-    const float logit_scale = scale_log2 * (f16 ? q_unscale : 1.0f);
+    // a negative softmax scale is applied as the negated query (an exact sign flip of every
+    // fp16 / bf16 value) times its magnitude, so the scale inside the blocks is never negative
+    if (scale_log2 < 0.f) {
+#pragma unroll
+        for (int m = 0; m < 4; m++) qop[m] ^= 0x80008000u;
+    }
+    const float logit_scale = fabsf(scale_log2) * (f16 ? q_unscale : 1.0f);
 
 #pragma unroll
     for (int kb = 0; kb < BPW; kb++) {
@@ -559,7 +566,7 @@ hipError_t launch_attention_t(const uint8_t* k_pool, const uint8_t* v_pool, int6
 #define MSA_LAUNCH_ATTN(BPW_)                                                                    \
     hipLaunchKernelGGL((attention_kernel<BPW_, SELECT>), grid, block, 0, stream, k_pool, v_pool, \
                        num_pages, block_table, ctx_lens, batch, max_blocks, q_len, q, ids,       \
-                       scores, scale_log2, ns, out, counters, partials)
+                       scores, scale_log2, out, counters, partials)
     switch (ns) {
         case 1: MSA_LAUNCH_ATTN(4); break;
         case 2: MSA_LAUNCH_ATTN(2); break;

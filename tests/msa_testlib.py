@@ -116,7 +116,7 @@ class GpuRun:
 
 # ------------------------------------------------------------------ oracle side
 def oracle_sequence(w: mi.Workload, b: int, attention_tokens: Optional[Sequence[int]] = None,
-                    ids_override: Optional[np.ndarray] = None):
+                    ids_override: Optional[np.ndarray] = None, scale: Optional[float] = None):
     """Oracle reference for sequence b: scores [q][4][max_blocks], ids [q][4][16], margins
     [q][4], and attention [len(tokens)][64][128] for the requested query tokens j."""
     import oracle
@@ -141,8 +141,9 @@ def oracle_sequence(w: mi.Workload, b: int, attention_tokens: Optional[Sequence[
         kc[t0:t1], ks[t0:t1] = oracle.quantize(w.kv_rows("k", b, t0, t1).numpy())
         vc[t0:t1], vs[t0:t1] = oracle.quantize(w.kv_rows("v", b, t0, t1).numpy())
     qb = mi.bf16_bits(w.q[b * q:(b + 1) * q])
-    att = np.stack([oracle.sparse_attention_token(qb[j], kc, ks, vc, vs, T, use_ids[j], T - q + j,
-                                                  oracle.default_scale()) for j in tokens])
+    sc = oracle.default_scale() if scale is None else scale
+    att = np.stack([oracle.sparse_attention_token(qb[j], kc, ks, vc, vs, T, use_ids[j], T - q + j, sc)
+                    for j in tokens])
     res["attention"] = att
     res["kv_blocks"] = blocks
     return res

@@ -92,6 +92,24 @@ def test_indexer_topk_attention(run):
     _log(f"[case {name}] rows below margin (validated, not bit-compared): {exempt_total}")
 
 
+def test_attention_other_scales(run):
+    """Attention with softmax scales other than 1/sqrt(128), a negative one included, over the
+    step's own selection (first sequence, up to four query tokens), against the oracle."""
+    import block_sparse_attention_nvfp4_amd as msa
+    name, w, g, _ = run
+    q = w.q_len
+    ids = g.step.block_ids
+    toks = list(range(min(q, 4)))
+    for scale in (0.37, -0.05):
+        out = torch.empty_like(g.step.out)
+        msa.msa_sparse_attn_decode(g.cache, g.batch, g.q, ids, scale, out, g.step.workspace)
+        torch.cuda.synchronize()
+        att = bf16_to_f64(out)
+        ref = oracle_sequence(w, 0, attention_tokens=toks, ids_override=ids.cpu().numpy()[:q],
+                              scale=scale)
+        check_attention(att[:q][toks], ref["attention"])
+
+
 def test_topk_bit_exact_on_shared_scores(run):
     """The selection kernel alone, fed the oracle's scores rounded to fp32, with planted ties."""
     import block_sparse_attention_nvfp4_amd as msa
