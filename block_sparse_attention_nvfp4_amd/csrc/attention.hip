@@ -265,8 +265,6 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
     __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves][kBufs][kBlockBytes];
     __shared__ float sh_m[kWaves][kGroupHeads];
     __shared__ float sh_l[kWaves][kGroupHeads];
-    __shared__ int sh_ids[kWaves][BPW];
-    __shared__ int sh_pages[kWaves][BPW];
     __shared__ int sh_sel[SELECT ? kTopk : 1];
     static_assert(kSelectScratch * 8 <= kBlockBytes, "selection scratch must fit in a page buffer");
     __shared__ int sh_tbl[SELECT ? kSelectFusedMaxBlocks : 1];  // the sequence's block table
@@ -297,18 +295,21 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
 #pragma unroll
         for (int m = 0; m < 4; m++) qb[m] = *reinterpret_cast<const bf16x8*>(qp + 8 * m);
     }
+    // the context length, requested with the query: every wavefront needs it once its blocks
+    // are known
+    const int T_raw = ctx_lens[b];
     // this wavefront's blocks (id and page, or -1 when the id is not selected, has no visible
-    // token or maps to a page out of range), read once: a table load issued between page loads
-    // would make the in-order memory counter wait for every page in flight. The ids and the
-    // context length are requested together, then the table entries of the ids in range.
-    int id, T_raw;
+    // token or maps to a page out of range), lane k holding its k-th block, read once: a table
+    // load issued between page loads would make the in-order memory counter wait for every
+    // page in flight.
+    int id;
     if constexpr (SELECT) {
         if (wave == 0) {
             // the row's scores and the context length in one memory round trip, then the
             // selection, exactly as msa_block_topk makes it
             float sv[16];
             load_row_scores<16>(scores + (int64_t)rg * max_blocks, max_blocks, lane, sv);
-            int t_sel = ctx_lens[b];
+            int t_sel = T_raw;
 #pragma unroll
             for (int k = 0; k < 16; k++) asm volatile("" : "+v"(sv[k]));
             asm volatile("" : "+v"(t_sel));
@@ -335,24 +336,19 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
         }
         __syncthreads();
         id = lane < BPW ? sh_sel[(split * kWaves + wave) * BPW + lane] : -1;
-        T_raw = ctx_lens[b];
     } else {
         const int32_t* my_ids = block_ids + (int64_t)rg * kTopk + (split * kWaves + wave) * BPW;
         id = lane < BPW ? my_ids[lane] : -1;
-        T_raw = ctx_lens[b];
-        asm volatile("" : "+v"(id), "+v"(T_raw));
+        asm volatile("" : "+v"(id));
     }
     const int T = clamp_ctx(T_raw, max_blocks);
     const int p = T - q_len + j;
-    if (lane < BPW) {
-        int page = -1;
-        if (id >= 0 && id < max_blocks && id * kBlock <= p) {
-            const int pg = SELECT ? sh_tbl[id] : block_table[(int64_t)b * max_blocks + id];
-            page = (pg >= 0 && pg < num_pages) ? pg : -1;
-        }
-        sh_ids[wave][lane] = page >= 0 ? id : -1;
-        sh_pages[wave][lane] = page;
+    int page = -1;
+    if (lane < BPW && id >= 0 && id < max_blocks && id * kBlock <= p) {
+        const int pg = SELECT ? sh_tbl[id] : block_table[(int64_t)b * max_blocks + id];
+        page = (pg >= 0 && pg < num_pages) ? pg : -1;
     }
+    const int blk_id = page >= 0 ? id : -1;
     // every load so far is complete (the query's included), and the compiler knows it: it
     // waits for nothing of them after the page loads are issued
     asm volatile("" ::: "memory");
@@ -366,9 +362,9 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
     const uint8_t* kg = k_pool + (int64_t)g * kHeadPageBytes;
     const uint8_t* vg = v_pool + (int64_t)g * kHeadPageBytes;
     constexpr int64_t kPageStride = (int64_t)kKvHeads * kHeadPageBytes;
-    int cur_id = __builtin_amdgcn_readfirstlane(sh_ids[wave][0]);
+    int cur_id = __builtin_amdgcn_readlane(blk_id, 0);
     if (cur_id >= 0) {
-        const int pg = __builtin_amdgcn_readfirstlane(sh_pages[wave][0]);
+        const int pg = __builtin_amdgcn_readlane(page, 0);
         block_to_lds(kg + pg * kPageStride, vg + pg * kPageStride, lds[wave][0], lane);
     }
     // the B operand is prepared while the first block streams in
@@ -391,9 +387,9 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
     for (int kb = 0; kb < BPW; kb++) {
         int nxt_id = -1;
         if (kb + 1 < BPW) {
-            nxt_id = __builtin_amdgcn_readfirstlane(sh_ids[wave][kb + 1]);
+            nxt_id = __builtin_amdgcn_readlane(blk_id, kb + 1);
             if (nxt_id >= 0) {
-                const int pg = __builtin_amdgcn_readfirstlane(sh_pages[wave][kb + 1]);
+                const int pg = __builtin_amdgcn_readlane(page, kb + 1);
                 block_to_lds(kg + pg * kPageStride, vg + pg * kPageStride,
                              lds[wave][(kb + 1) % kBufs], lane);
             }
