@@ -180,15 +180,27 @@ __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c
         }
         sv[s] = acc;  // unscaled: the scale (> 0) is applied inside the exponent below
     }
-    const bool full = tok0 + kBlock - 1 <= p;
+    // tokens past the query position: only in the block that holds it, a scalar branch that
+    // every other block skips (kept a branch: folded into the selects, the wavefront-uniform
+    // condition cost a vector-to-scalar round trip per value)
+    if (tok0 + kBlock - 1 > p) {
+        asm volatile("");
+        const int last = p - tok0 - 32 * c;  // values 4s + i <= last are visible
+#pragma unroll
+        for (int s = 0; s < 8; s++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                // all ones past the position: vector bit operations, no lane-mask updates
+                uint32_t past = (uint32_t)((last - (4 * s + i)) >> 31);
+                asm("" : "+v"(past));
+                sv[s][i] = __uint_as_float((__float_as_uint(sv[s][i]) & ~past) | (0xFF800000u & past));
+            }
+    }
     float mb = -INFINITY;
 #pragma unroll
     for (int s = 0; s < 8; s++)
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            if (!full && tok0 + 32 * c + 4 * s + i > p) sv[s][i] = -INFINITY;
-            mb = fmaxf(mb, sv[s][i]);
-        }
+        for (int i = 0; i < 4; i++) mb = fmaxf(mb, sv[s][i]);
     mb = max_over_c(mb) * logit_scale;  // finite (token tok0 <= p is valid); scaling keeps order
     const float m_new = (mb > m_run + kTau) ? mb : m_run;  // m_run = -inf -> m_new = mb
     if (__any(m_new != m_run)) {
