@@ -230,7 +230,11 @@ __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c
     // l / 8, tokens 16 (l % 8) .. +15. Each lane then reads its scales ready for the packed
     // multiply instead of converting 256 of them.
     {
-        const u32x4 raw = lds_read16(vbase + kCodeBytes + lane * 16);
+        // (with no later page in flight, ordinary LDS reads: the compiler overlaps them with
+        // the work before their use; otherwise statements that wait for their own reads only)
+        u32x4 raw;
+        if constexpr (NEXT) raw = lds_read16(vbase + kCodeBytes + lane * 16);
+        else raw = *reinterpret_cast<const u32x4*>(buf + kHeadPageBytes + kCodeBytes + lane * 16);
         u32x4 h0, h1;
 #pragma unroll
         for (int i = 0; i < 2; i++) {
@@ -248,7 +252,14 @@ __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c
         const int d = 16 * dt + (lane & 15);
         // codes of tokens 32c..32c+31 and their fp16 scales of group dt
         u32x4 vc, sc[4];
-        lds_read16x5(vc, sc, vbase + d * 64 + 16 * c, kbase + dt * 256 + 64 * c);
+        if constexpr (NEXT) {
+            lds_read16x5(vc, sc, vbase + d * 64 + 16 * c, kbase + dt * 256 + 64 * c);
+        } else {
+            vc = *reinterpret_cast<const u32x4*>(buf + kHeadPageBytes + d * 64 + 16 * c);
+#pragma unroll
+            for (int w = 0; w < 4; w++)
+                sc[w] = *reinterpret_cast<const u32x4*>(buf + dt * 256 + 64 * c + 16 * w);
+        }
 #pragma unroll
         for (int s = 0; s < 8; s++) {
             // tokens 32c + 4s .. +3: scale pairs (4s, 4s+1) and (4s+2, 4s+3)
