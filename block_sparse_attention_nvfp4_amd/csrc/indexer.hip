@@ -58,12 +58,17 @@ __device__ __forceinline__ void half_to_lds(const uint8_t* pg, int h, uint8_t* b
 
 // Wait until the loads of all but the `after` most recently issued half pages (five loads
 // each) have completed.
+// The compiler's own wait instruction (vmcnt only; expcnt 7 and lgkmcnt 15 wait for nothing):
+// its wait insertion then knows which earlier loads have completed and adds no wait of its own
+// for them later.
 __device__ __forceinline__ void wait_halves(int after) {
+    asm volatile("" ::: "memory");
     switch (after) {
-        case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-        case 1: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
-        default: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+        case 0: __builtin_amdgcn_s_waitcnt(0xF70); break;   // vmcnt(0)
+        case 1: __builtin_amdgcn_s_waitcnt(0xF75); break;   // vmcnt(5)
+        default: __builtin_amdgcn_s_waitcnt(0xF7A); break;  // vmcnt(10)
     }
+    asm volatile("" ::: "memory");
 }
 static_assert(kBufs <= 3, "wait_halves covers at most two half pages in flight");
 
@@ -207,6 +212,15 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
     return (uint64_t)lo | ((uint64_t)hi << 32);
 }
 
+// A device-memory pointer rebuilt from its bits, marked global: left generic, its accesses
+// would be flat instructions, which also count in the LDS counter and make the compiler wait
+// for every load in flight before each of them.
+template <typename T>
+__device__ __forceinline__ T* global_ptr(uint64_t v) {
+    typedef __attribute__((address_space(1))) T global_t;
+    return (T*)(global_t*)v;
+}
+
 // Source of insert item i = 9 j + vec of sequence b: new token j, head vector vec (K heads
 // 0-3, V heads 4-7, the index key 8).
 __device__ __forceinline__ const float* item_source(int item, int b, int q_len,
@@ -253,9 +267,11 @@ __device__ __forceinline__ int claim_page(const int* counter, int lane) {
 // FUSED (decode step with q_len <= kFusedMaxNew): the launch also inserts the step's new tokens.
 // The 9 q_len head vectors of sequence b are spread over the sequence's workgroups and their
 // wavefronts (wavefront w of workgroup x takes items x + gx (w + 8 m)). A wavefront loads its
-// first item with its start-up loads, requests the item's block-table entry with its query
-// rows, quantizes while the first pages stream in, and stores after its last page has arrived,
-// so that the stores never stand between page loads in the in-order memory counter. The
+// first item with its start-up loads, requests the item's block-table entry after its first
+// page, quantizes while the first pages stream in, and stores after its last page has arrived,
+// so that the stores never stand between page loads in the in-order memory counter (stores
+// issued after the first page measured 1.1 us slower). The barrier that follows waits for the
+// LDS writes only, not for these stores. The
 // indexer wavefronts patch the new index keys into their page copies (patch_new_tokens): a
 // page may be read before or after another workgroup's store lands.
 template <bool FUSED>
@@ -385,6 +401,25 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
         cur = pair < n_pages ? pair : n_pages;  // this wavefront's page (n_pages: none)
         cur_loaded = cur < n_pages && issue(cur, 0, vis_end);
     };
+    // fused: the insert's source and destination pointers, kept in LDS (not live in scalar
+    // registers through the scan)
+    auto insert_ptrs = [&](uint64_t (&fp)[5]) {
+        const uint32_t a = (uint32_t)(uintptr_t)&fused_ptrs[0];
+        asm volatile("ds_read_b64 %0, %5\n\tds_read_b64 %1, %5 offset:8\n\t"
+                     "ds_read_b64 %2, %5 offset:16\n\tds_read_b64 %3, %5 offset:24\n\t"
+                     "ds_read_b64 %4, %5 offset:32\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(fp[0]), "=&v"(fp[1]), "=&v"(fp[2]), "=&v"(fp[3]), "=&v"(fp[4])
+                     : "v"(a) : "memory");
+    };
+    // fused: the stores of the wavefront's first insert item
+    auto store_first_item = [&]() {
+        uint64_t fp[5];
+        insert_ptrs(fp);
+        store_item(item, __builtin_amdgcn_readfirstlane(ins_page_v), ins_pos, num_pages,
+                   ins_byte, ins_scale, global_ptr<uint8_t>(uniform64(fp[3])),
+                   global_ptr<uint8_t>(uniform64(fp[4])),
+                   const_cast<uint8_t*>(ik_pool), lane);
+    };
     uint32_t patch_mask;
     int cur;
     bool cur_loaded;
@@ -478,22 +513,14 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
             // the insert stores, after the wavefront's last page load has returned; then any
             // further items (more items than wavefronts: short contexts), one at a time
             if (rt + 16 >= rows && item < n_items) {
+                store_first_item();
                 uint64_t fp[5];
-                {
-                    const uint32_t a = (uint32_t)(uintptr_t)&fused_ptrs[0];
-                    asm volatile("ds_read_b64 %0, %5\n\tds_read_b64 %1, %5 offset:8\n\t"
-                                 "ds_read_b64 %2, %5 offset:16\n\tds_read_b64 %3, %5 offset:24\n\t"
-                                 "ds_read_b64 %4, %5 offset:32\n\ts_waitcnt lgkmcnt(0)"
-                                 : "=&v"(fp[0]), "=&v"(fp[1]), "=&v"(fp[2]), "=&v"(fp[3]), "=&v"(fp[4])
-                                 : "v"(a) : "memory");
-                }
-                const float* nk = (const float*)uniform64(fp[0]);
-                const float* nv = (const float*)uniform64(fp[1]);
-                const float* nik = (const float*)uniform64(fp[2]);
-                uint8_t* kp = (uint8_t*)uniform64(fp[3]);
-                uint8_t* vpw = (uint8_t*)uniform64(fp[4]);
-                store_item(item, __builtin_amdgcn_readfirstlane(ins_page_v), ins_pos, num_pages,
-                           ins_byte, ins_scale, kp, vpw, const_cast<uint8_t*>(ik_pool), lane);
+                insert_ptrs(fp);
+                const float* nk = global_ptr<const float>(uniform64(fp[0]));
+                const float* nv = global_ptr<const float>(uniform64(fp[1]));
+                const float* nik = global_ptr<const float>(uniform64(fp[2]));
+                uint8_t* kp = global_ptr<uint8_t>(uniform64(fp[3]));
+                uint8_t* vpw = global_ptr<uint8_t>(uniform64(fp[4]));
                 for (item += kWaves * gx; item < n_items; item += kWaves * gx) {
                     const f32x2 x = *reinterpret_cast<const f32x2*>(
                         item_source(item, b, q_len, nk, nv, nik) + 2 * lane);
@@ -511,7 +538,10 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         else
             asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-        __syncthreads();
+        // a plain barrier: the stash is in LDS, waited for above (a barrier with a fence would
+        // also wait for the insert stores)
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
         // thread (row rn, block slot kb) writes the max of both halves; blocks above the tile's
         // visible range are -inf; the counters are reset for the next tile
         {
