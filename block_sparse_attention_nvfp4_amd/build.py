@@ -24,6 +24,9 @@ COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # the first kernel arguments arrive in scalar registers with the wavefront (no memory load
+    # at kernel start where the firmware supports it; the code falls back to loading them)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 
