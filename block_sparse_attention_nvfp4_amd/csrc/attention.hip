@@ -406,7 +406,7 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
     }
     const float logit_scale = fabsf(scale_log2) * (f16 ? q_unscale : 1.0f);
 
-#pragma unroll
+    // (left to the compiler: with several blocks per wavefront the unrolled body is too large)
     for (int kb = 0; kb < BPW; kb++) {
         int nxt_id = -1;
         if (kb + 1 < BPW) {
