@@ -57,10 +57,9 @@ __device__ __forceinline__ void half_to_lds(const uint8_t* pg, int h, uint8_t* b
 }
 
 // Wait until the loads of all but the `after` most recently issued half pages (five loads
-// each) have completed.
-// The compiler's own wait instruction (vmcnt only; expcnt 7 and lgkmcnt 15 wait for nothing):
-// its wait insertion then knows which earlier loads have completed and adds no wait of its own
-// for them later.
+// each) have completed. It is the compiler's own wait instruction (vmcnt only; expcnt 7 and
+// lgkmcnt 15 wait for nothing), so the compiler knows which earlier loads have completed and
+// adds no wait of its own for them later.
 __device__ __forceinline__ void wait_halves(int after) {
     asm volatile("" ::: "memory");
     switch (after) {
@@ -411,15 +410,6 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
                      : "=&v"(fp[0]), "=&v"(fp[1]), "=&v"(fp[2]), "=&v"(fp[3]), "=&v"(fp[4])
                      : "v"(a) : "memory");
     };
-    // fused: the stores of the wavefront's first insert item
-    auto store_first_item = [&]() {
-        uint64_t fp[5];
-        insert_ptrs(fp);
-        store_item(item, __builtin_amdgcn_readfirstlane(ins_page_v), ins_pos, num_pages,
-                   ins_byte, ins_scale, global_ptr<uint8_t>(uniform64(fp[3])),
-                   global_ptr<uint8_t>(uniform64(fp[4])),
-                   const_cast<uint8_t*>(ik_pool), lane);
-    };
     uint32_t patch_mask;
     int cur;
     bool cur_loaded;
@@ -513,7 +503,6 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
             // the insert stores, after the wavefront's last page load has returned; then any
             // further items (more items than wavefronts: short contexts), one at a time
             if (rt + 16 >= rows && item < n_items) {
-                store_first_item();
                 uint64_t fp[5];
                 insert_ptrs(fp);
                 const float* nk = global_ptr<const float>(uniform64(fp[0]));
@@ -521,6 +510,8 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
                 const float* nik = global_ptr<const float>(uniform64(fp[2]));
                 uint8_t* kp = global_ptr<uint8_t>(uniform64(fp[3]));
                 uint8_t* vpw = global_ptr<uint8_t>(uniform64(fp[4]));
+                store_item(item, __builtin_amdgcn_readfirstlane(ins_page_v), ins_pos, num_pages,
+                           ins_byte, ins_scale, kp, vpw, const_cast<uint8_t*>(ik_pool), lane);
                 for (item += kWaves * gx; item < n_items; item += kWaves * gx) {
                     const f32x2 x = *reinterpret_cast<const f32x2*>(
                         item_source(item, b, q_len, nk, nv, nik) + 2 * lane);
