@@ -333,6 +333,17 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
         if (item < n_items)
             ins_x = *reinterpret_cast<const f32x2*>(
                 item_source(item, b, q_len, new_k, new_v, new_ik) + 2 * lane);
+        // pairs 0 and 1 (the wavefronts whose first pages may hold new tokens): the sequence's
+        // new index keys into their staging area, two tokens per direct global->LDS load
+        // (lanes past the last token re-read its last 16 bytes into the unused tail), with the
+        // start-up loads, so that the first page request waits for nothing of the patch
+        if (pair < 2) {
+            const float* src = new_ik + (int64_t)b * q_len * kDim;
+            for (int i = 0; i < (q_len + 1) / 2; i++)
+                __builtin_amdgcn_global_load_lds(src + min(256 * i + 4 * lane, q_len * kDim - 4),
+                                                 (lds_void*)(stage[pair * 2 + h] + 1024 * i), 16,
+                                                 0, 0);
+        }
     }
     asm volatile("" : "+v"(pid_all), "+v"(T_raw), "+v"(ins_x));
     // the same value in every lane
@@ -349,7 +360,6 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
     int ins_page_v = -1;
     uint32_t ins_byte = 0, ins_scale = 0;
     uint32_t prepped = 0;  // fused: tokens whose patch bytes are in this wavefront's staging area
-    bool staged = false;   // fused: the new index keys were copied to the staging area
 
     // row tile rt (query rows rt .. rt + 15): one past its highest visible block; page u of the
     // tile is block vis_end - 1 - u
@@ -374,17 +384,6 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
         if constexpr (FUSED) {
             if (pair < 2 && pair < n_pages)
                 patch_mask = patch_tokens(vis_end - 1 - pair, T, q_len, h);
-            if ((patch_mask & ~prepped) && !staged) {
-                // the sequence's new index keys into the staging area, two tokens per direct
-                // global->LDS load (lanes past the last token re-read its last 16 bytes into the
-                // unused tail); waited for with the query rows
-                const float* src = new_ik + (int64_t)b * q_len * kDim;
-                for (int i = 0; i < (q_len + 1) / 2; i++)
-                    __builtin_amdgcn_global_load_lds(
-                        src + min(256 * i + 4 * lane, q_len * kDim - 4),
-                        (lds_void*)(stage[pair * 2 + h] + 1024 * i), 16, 0, 0);
-                staged = true;
-            }
         }
         // B operand: row r, dims 32c + 8m .. 32c + 8m + 7 for MFMA m = 0..3, copied into this
         // wavefront's query buffer with direct global->LDS loads, requested before the first
@@ -456,7 +455,7 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
             qop[m] = f16 ? __builtin_bit_cast(u32x4, qh[m]) : __builtin_bit_cast(u32x4, qb[m]);
         if (!f16) out_scale = 1.0f;
         if constexpr (FUSED) {
-            // patch bytes of the tokens of the first page (staged with the query rows)
+            // patch bytes of the tokens of the first page (staged at start-up)
             for (uint32_t todo = patch_mask & ~prepped; todo; todo &= todo - 1) {
                 prepare_patch_token(stage[pair * 2 + h], __builtin_ctz(todo), lane);
             }
