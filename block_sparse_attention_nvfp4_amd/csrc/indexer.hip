@@ -284,7 +284,7 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
     // half-page maxima of the row tile: [half][row][block - wg_blk0], rows padded apart in banks
     __shared__ float stash[2][16][kPagesPerWg + 1];
     __shared__ int next_page[2];  // page counters of the two halves
-    __shared__ __attribute__((aligned(8))) uint64_t fused_ptrs[FUSED ? 5 : 1];
+    __shared__ __attribute__((aligned(8))) uint64_t fused_ptrs[FUSED ? kWaves : 1][5];
     __shared__ __attribute__((aligned(16))) uint8_t qbuf[kWaves][4 * 1024];  // query operands
     __shared__ __attribute__((aligned(16))) uint8_t stage[FUSED ? 4 : 1][FUSED ? kFusedMaxNew * kStageBytes : 16];
     const int lane = threadIdx.x & 63;
@@ -306,20 +306,6 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
     if (threadIdx.x < 2) {
         const uint32_t a = (uint32_t)(uintptr_t)&next_page[threadIdx.x];
         asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(a), "v"(kPairs) : "memory");
-    }
-    if constexpr (FUSED) {
-        // the insert's pointers, needed again only by the stores after the last page, are kept
-        // in LDS rather than in scalar registers through the whole scan
-        if (threadIdx.x == 0) {
-            const uint32_t a = (uint32_t)(uintptr_t)&fused_ptrs[0];
-            const uint64_t p0 = (uint64_t)(uintptr_t)new_k, p1 = (uint64_t)(uintptr_t)new_v;
-            const uint64_t p2 = (uint64_t)(uintptr_t)new_ik, p3 = (uint64_t)(uintptr_t)k_pool_w;
-            const uint64_t p4 = (uint64_t)(uintptr_t)v_pool_w;
-            asm volatile("ds_write_b64 %0, %1\n\tds_write_b64 %0, %2 offset:8\n\t"
-                         "ds_write_b64 %0, %3 offset:16\n\tds_write_b64 %0, %4 offset:24\n\t"
-                         "ds_write_b64 %0, %5 offset:32\n\ts_waitcnt lgkmcnt(0)"
-                         ::"v"(a), "v"(p0), "v"(p1), "v"(p2), "v"(p3), "v"(p4) : "memory");
-        }
     }
     __builtin_amdgcn_s_barrier();
     // the workgroup's block-table entries (lane l: block wg_blk0 + l) and the context length are
@@ -402,7 +388,7 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
     // fused: the insert's source and destination pointers, kept in LDS (not live in scalar
     // registers through the scan)
     auto insert_ptrs = [&](uint64_t (&fp)[5]) {
-        const uint32_t a = (uint32_t)(uintptr_t)&fused_ptrs[0];
+        const uint32_t a = (uint32_t)(uintptr_t)&fused_ptrs[wave][0];
         asm volatile("ds_read_b64 %0, %5\n\tds_read_b64 %1, %5 offset:8\n\t"
                      "ds_read_b64 %2, %5 offset:16\n\tds_read_b64 %3, %5 offset:24\n\t"
                      "ds_read_b64 %4, %5 offset:32\n\ts_waitcnt lgkmcnt(0)"
@@ -437,6 +423,19 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
                     ins_page_v = table[idx];
                 }
                 quantize_pair(ins_x[0], ins_x[1], ins_byte, ins_scale);
+                // the insert's pointers, needed again only by the stores after the last page,
+                // kept in this wavefront's LDS slot rather than in scalar registers through the
+                // scan (written here, off the start-up path, and read back by this wavefront)
+                if (lane == 0) {
+                    const uint32_t a = (uint32_t)(uintptr_t)&fused_ptrs[wave][0];
+                    const uint64_t p0 = (uint64_t)(uintptr_t)new_k, p1 = (uint64_t)(uintptr_t)new_v;
+                    const uint64_t p2 = (uint64_t)(uintptr_t)new_ik, p3 = (uint64_t)(uintptr_t)k_pool_w;
+                    const uint64_t p4 = (uint64_t)(uintptr_t)v_pool_w;
+                    asm volatile("ds_write_b64 %0, %1\n\tds_write_b64 %0, %2 offset:8\n\t"
+                                 "ds_write_b64 %0, %3 offset:16\n\tds_write_b64 %0, %4 offset:24\n\t"
+                                 "ds_write_b64 %0, %5 offset:32\n\ts_waitcnt lgkmcnt(0)"
+                                 ::"v"(a), "v"(p0), "v"(p1), "v"(p2), "v"(p3), "v"(p4) : "memory");
+                }
             }
         }
         wait_halves(cur_loaded ? 1 : 0);
