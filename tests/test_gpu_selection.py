@@ -1,0 +1,66 @@
+"""Block selection on constructed score rows, bit for bit against the oracle (needs an MI355X).
+
+Rows that stress the selection's bound, compaction and tie paths: all scores equal (every
+candidate reaches the bound, the counted-extraction path), more than 64 blocks tied at the top,
+exactly 15 distinct leaders over a flat rest, a tie of 70 blocks at the 15th place, signed
+zeros, -inf scores, and plain random rows; at several row lengths (eligible block counts from
+the trivial 16 to full rows) and for rows held as 16 and as 64 keys per lane.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _patterns(n_blocks, rng):
+    out = []
+    out.append(np.zeros(n_blocks, np.float32))
+    out.append(np.where(rng.random(n_blocks) < 0.5, -0.0, 0.0).astype(np.float32))
+    x = rng.standard_normal(n_blocks).astype(np.float32)
+    x[rng.choice(n_blocks, min(100, n_blocks), replace=False)] = 9.0
+    out.append(x)
+    x = np.full(n_blocks, -1.0, np.float32)
+    lead = rng.choice(n_blocks, min(15, n_blocks), replace=False)
+    x[lead] = np.arange(len(lead), dtype=np.float32) + 2.0
+    out.append(x)
+    x = rng.standard_normal(n_blocks).astype(np.float32) - 10.0
+    top = rng.choice(n_blocks, min(84, n_blocks), replace=False)
+    x[top[:14]] = np.arange(14, dtype=np.float32) + 5.0
+    x[top[14:]] = 3.0
+    out.append(x)
+    x = rng.standard_normal(n_blocks).astype(np.float32)
+    x[rng.random(n_blocks) < 0.3] = -np.inf
+    out.append(x)
+    out.append(rng.standard_normal(n_blocks).astype(np.float32))
+    out.append(np.round(rng.standard_normal(n_blocks) * 4.0).astype(np.float32))
+    return out
+
+
+@pytest.mark.parametrize("max_blocks", [1024, 2048])
+def test_selection_constructed_rows(max_blocks):
+    import block_sparse_attention_nvfp4_amd as msa
+    rng = np.random.default_rng(5 + max_blocks)
+    pats = _patterns(max_blocks, rng)
+    # eligible block counts: the query token of sequence b sits in block n_b - 1
+    n_list = [16, 17, 18, 63, 64, 65, 129, max_blocks - 1, max_blocks]
+    rows, ns = [], []
+    for n in n_list:
+        for g in range(4):
+            rows.append(pats[(len(ns) + g) % len(pats)])
+        ns.append(n)
+    batch = len(n_list)
+    scores = np.stack(rows).reshape(batch, 4, max_blocks).astype(np.float32)
+    ctx = torch.tensor([128 * (n - 1) + 1 for n in ns], dtype=torch.int32, device="cuda")
+    table = torch.zeros((batch, max_blocks), dtype=torch.int32, device="cuda")
+    b = msa.Batch(table, ctx, 1)
+    ids = torch.empty((batch, 4, 16), dtype=torch.int32, device="cuda")
+    msa.msa_block_topk(torch.from_numpy(scores).cuda(), b, 16, ids)
+    torch.cuda.synchronize()
+    got = ids.cpu().numpy()
+    for i, n in enumerate(ns):
+        for g in range(4):
+            want, _ = oracle.block_topk(scores[i, g].astype(np.float64), n)
+            assert np.array_equal(got[i, g], want), (max_blocks, n, g, got[i, g], want)
