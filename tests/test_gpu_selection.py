@@ -4,7 +4,8 @@ Rows that stress the selection's bound, compaction and tie paths: all scores equ
 candidate reaches the bound, the counted-extraction path), more than 64 blocks tied at the top,
 exactly 15 distinct leaders over a flat rest, a tie of 70 blocks at the 15th place, signed
 zeros, -inf scores, and plain random rows; at several row lengths (eligible block counts from
-the trivial 16 to full rows) and for rows held as 16 and as 64 keys per lane.
+the trivial 16 to full rows) and for rows held as 16 and as 64 keys per lane; both through the
+selection kernel and through the selection inside the attention launch (its ids output).
 """
 import numpy as np
 import pytest
@@ -57,10 +58,24 @@ def test_selection_constructed_rows(max_blocks):
     table = torch.zeros((batch, max_blocks), dtype=torch.int32, device="cuda")
     b = msa.Batch(table, ctx, 1)
     ids = torch.empty((batch, 4, 16), dtype=torch.int32, device="cuda")
-    msa.msa_block_topk(torch.from_numpy(scores).cuda(), b, 16, ids)
+    s_dev = torch.from_numpy(scores).cuda()
+    msa.msa_block_topk(s_dev, b, 16, ids)
+    results = {"topk": ids}
+    if max_blocks <= 1024:
+        # the attention launch that selects for itself (an all-zero one-page cache: only its ids
+        # output is checked here)
+        cache = msa.Cache.allocate(1)
+        q = torch.zeros((batch, 64, 128), dtype=torch.bfloat16, device="cuda")
+        out = torch.empty_like(q)
+        ws_bytes = msa.msa_sparse_attn_workspace_bytes(b)
+        ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda") if ws_bytes else None
+        ids2 = torch.full((batch, 4, 16), -7, dtype=torch.int32, device="cuda")
+        msa.msa_select_attn_decode(cache, b, s_dev, 16, ids2, q, 0.088, out, ws)
+        results["select_attention"] = ids2
     torch.cuda.synchronize()
-    got = ids.cpu().numpy()
-    for i, n in enumerate(ns):
-        for g in range(4):
-            want, _ = oracle.block_topk(scores[i, g].astype(np.float64), n)
-            assert np.array_equal(got[i, g], want), (max_blocks, n, g, got[i, g], want)
+    for path, t in results.items():
+        got = t.cpu().numpy()
+        for i, n in enumerate(ns):
+            for g in range(4):
+                want, _ = oracle.block_topk(scores[i, g].astype(np.float64), n)
+                assert np.array_equal(got[i, g], want), (path, max_blocks, n, g, got[i, g], want)
