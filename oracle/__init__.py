@@ -142,6 +142,33 @@ def select_sequence(scores: np.ndarray, T: int, q: int, topk: int = TOPK):
     return ids, margins
 
 
+def dcp_local_topk(scores_row: np.ndarray, n_eligible: int, shard_blocks, topk: int = TOPK):
+    """One shard's local candidates of a row ("vLLM day-0 support for MiniMax-M3.1-Flash",
+    section "Indexer NVFP4 DCP": each device ranks only its own share of the pages and keeps
+    its local top 16 per index head).
+
+    shard_blocks: the block ids the shard holds. Its eligible blocks (id < n_eligible) are
+    ranked by (score descending, id ascending), the forced block n_eligible - 1 first when the
+    shard holds it; the best `topk` are returned as (ids ascending, forced flags).
+    """
+    forced = n_eligible - 1
+    mine = [int(i) for i in shard_blocks if 0 <= int(i) < n_eligible]
+    order = sorted(mine, key=lambda i: (i != forced, -float(scores_row[i]), i))
+    kept = sorted(order[:topk])
+    return kept, [i == forced for i in kept]
+
+
+def dcp_merge(scores_row: np.ndarray, n_eligible: int, local_lists, topk: int = TOPK):
+    """The owner's merge of the shards' local candidates ("vLLM day-0 support for
+    MiniMax-M3.1-Flash", section "Indexer NVFP4 DCP": the local top-16 lists are merged into
+    the final top 16): the best `topk` of their union by the same order (forced block first,
+    then score descending, id ascending); ids ascending, padded with -1."""
+    forced = n_eligible - 1
+    union = [i for ids in local_lists for i in ids]
+    kept = sorted(sorted(union, key=lambda i: (i != forced, -float(scores_row[i]), i))[:topk])
+    return np.array(kept + [-1] * (topk - len(kept)), np.int32)
+
+
 # ------------------------------------------------------------------ attention
 
 def sparse_attention_token(q_bits, k_codes, k_scales, v_codes, v_scales, T, ids, p, scale):

@@ -72,23 +72,44 @@ def test_margin_definition():
     assert margin == pytest.approx((6.0 - 5.0) / 6.0)
 
 
+def _shard_splits(rng, n, shards):
+    """Contiguous slices with random cuts, and the round-robin split (block i on shard i % N)."""
+    cuts = np.sort(rng.choice(np.arange(1, n), size=shards - 1, replace=False))
+    bounds = [0, *cuts.tolist(), n]
+    contiguous = [range(lo, hi) for lo, hi in zip(bounds[:-1], bounds[1:])]
+    round_robin = [range(s, n, shards) for s in range(shards)]
+    return contiguous, round_robin
+
+
 @pytest.mark.parametrize("shards", [2, 3, 4, 8])
 def test_dcp_shard_merge_is_exact(shards):
+    # the merged local lists equal the single-device selection, which the full-sort pins above
+    # fix independently; ties on purpose, and rows of up to 16 eligible blocks (all kept)
     rng = np.random.default_rng(shards)
-    for trial in range(50):
-        n = int(rng.integers(17, 300))
-        scores = np.round(rng.standard_normal(n), 1)  # ties on purpose
+    for trial in range(60):
+        n = int(rng.integers(max(shards, 2), 300)) if trial % 4 else int(rng.integers(max(shards, 2), 17))
+        scores = np.round(rng.standard_normal(n + 5), 1)
         want, _ = oracle.block_topk(scores, n)
-        # each shard takes a contiguous slice of pages and keeps its local best 16 candidates,
-        # with the forced block ranked first on the shard that holds it
-        cuts = np.sort(rng.choice(np.arange(1, n), size=shards - 1, replace=False))
-        bounds = [0, *cuts.tolist(), n]
-        cands = []
-        for lo, hi in zip(bounds[:-1], bounds[1:]):
-            local = sorted(range(lo, hi), key=lambda i: (-(math.inf if i == n - 1 else scores[i]), i))[:16]
-            cands += local
-        merged = sorted(cands, key=lambda i: (-(math.inf if i == n - 1 else scores[i]), i))[:16]
-        assert sorted(merged) == list(want)
+        ref = ref_select(scores, n)
+        assert list(want) == ref + [-1] * (16 - len(ref))
+        for split in _shard_splits(rng, n, shards):
+            lists = [oracle.dcp_local_topk(scores, n, blocks)[0] for blocks in split]
+            assert list(oracle.dcp_merge(scores, n, lists)) == list(want)
+
+
+def test_dcp_local_lists_by_hand():
+    # n = 20 eligible blocks, forced block 19; shard A holds 0..9, shard B 10..24 (its blocks
+    # 20..24 are past the token and never eligible)
+    scores = np.zeros(25)
+    scores[[3, 7, 12, 19]] = [5.0, 5.0, 9.0, -100.0]
+    scores[20:] = 50.0
+    ids_a, forced_a = oracle.dcp_local_topk(scores, 20, range(0, 10), topk=3)
+    assert ids_a == [0, 3, 7] and forced_a == [False] * 3  # 5, 5, then the lowest of the zeros
+    ids_b, forced_b = oracle.dcp_local_topk(scores, 20, range(10, 25), topk=3)
+    assert ids_b == [10, 12, 19] and forced_b == [False, False, True]  # forced first despite -100
+    # merge: forced 19, then 12 (9.0), then the tie of 3 and 7 at 5.0 goes to the lower id
+    assert list(oracle.dcp_merge(scores, 20, [ids_a, ids_b], topk=3)) == [3, 12, 19]
+    assert list(oracle.dcp_merge(scores, 20, [[], [19]], topk=3)) == [19, -1, -1]
 
 
 def _dequant_keys(codes, scales):
