@@ -7,6 +7,9 @@ HIP stream into the C calls, with the same names:
     msa_kv_insert_nvfp4(cache, slots, k, v, ik)
     msa_indexer_score(cache, batch, q_idx, block_scores)
     msa_block_topk(block_scores, batch, topk, block_ids)
+    msa_block_topk_local(shard_scores, block_begin, block_stride, batch, topk, cand_ids,
+                         cand_keys)           # one shard's local lists (context parallelism)
+    msa_block_topk_merge(cand_ids, cand_keys, batch, topk, block_ids)   # merge of all shards
     msa_sparse_attn_workspace_bytes(batch)
     msa_sparse_attn_decode(cache, batch, q, block_ids, softmax_scale, out, workspace)
     msa_select_attn_decode(cache, batch, block_scores, topk, block_ids, q, softmax_scale, out,
@@ -44,6 +47,7 @@ MSA_ERR_WORKSPACE = -3
 MSA_ERR_HIP = -4
 
 EXPORTED = ("msa_page_bytes", "msa_kv_insert_nvfp4", "msa_indexer_score", "msa_block_topk",
+            "msa_block_topk_local", "msa_block_topk_merge",
             "msa_sparse_attn_workspace_bytes", "msa_sparse_attn_decode", "msa_select_attn_decode",
             "msa_insert_indexer_score", "msa_decode_step", "msa_last_error", "msa_version")
 
@@ -78,6 +82,11 @@ def _load() -> ctypes.CDLL:
     L.msa_indexer_score.argtypes = [ctypes.POINTER(_Cache), ctypes.POINTER(_Batch), vp, vp, vp]
     L.msa_block_topk.restype = ctypes.c_int
     L.msa_block_topk.argtypes = [vp, ctypes.POINTER(_Batch), i32, vp, vp]
+    L.msa_block_topk_local.restype = ctypes.c_int
+    L.msa_block_topk_local.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(_Batch), i32, vp, vp,
+                                       vp]
+    L.msa_block_topk_merge.restype = ctypes.c_int
+    L.msa_block_topk_merge.argtypes = [vp, vp, i32, ctypes.POINTER(_Batch), i32, vp, vp]
     L.msa_sparse_attn_workspace_bytes.restype = sz
     L.msa_sparse_attn_workspace_bytes.argtypes = [ctypes.POINTER(_Batch)]
     L.msa_sparse_attn_decode.restype = ctypes.c_int
@@ -202,6 +211,43 @@ def msa_block_topk(block_scores: torch.Tensor, batch: Batch, topk: int, block_id
     _check(lib.msa_block_topk(_ptr(block_scores, torch.float32, "block_scores"),
                               ctypes.byref(batch._c), int(topk),
                               _ptr(block_ids, torch.int32, "block_ids"), _stream(stream)))
+
+
+def msa_block_topk_local(shard_scores: torch.Tensor, block_begin: int, block_stride: int,
+                         batch: Batch, topk: int, cand_ids: torch.Tensor, cand_keys: torch.Tensor,
+                         stream=None) -> None:
+    """shard_scores: [batch*q_len][4][n_cols] fp32 whose columns are contiguous; its row stride
+    may be larger (a column slice of msa_indexer_score's output passes as it is)."""
+    if shard_scores.dim() != 3 or tuple(shard_scores.shape[:2]) != (batch.rows, KV_HEADS):
+        raise ValueError("shard_scores: expected [batch*q_len][4][n_cols]")
+    n_cols = int(shard_scores.shape[2])
+    ld = int(shard_scores.stride(1))
+    if shard_scores.dtype != torch.float32 or not shard_scores.is_cuda:
+        raise TypeError("shard_scores: expected a float32 device tensor")
+    if shard_scores.stride(2) != 1 or shard_scores.stride(0) != KV_HEADS * ld or ld < n_cols:
+        raise ValueError("shard_scores: columns must be contiguous, rows evenly spaced")
+    for name, t in (("cand_ids", cand_ids), ("cand_keys", cand_keys)):
+        if tuple(t.shape) != (batch.rows, KV_HEADS, int(topk)):
+            raise ValueError(f"{name}: expected [batch*q_len][4][topk]")
+    _check(lib.msa_block_topk_local(shard_scores.data_ptr(), ld, int(block_begin),
+                                    int(block_stride), n_cols, ctypes.byref(batch._c), int(topk),
+                                    _ptr(cand_ids, torch.int32, "cand_ids"),
+                                    _ptr(cand_keys, torch.int32, "cand_keys"), _stream(stream)))
+
+
+def msa_block_topk_merge(cand_ids: torch.Tensor, cand_keys: torch.Tensor, batch: Batch, topk: int,
+                         block_ids: torch.Tensor, stream=None) -> None:
+    """cand_ids, cand_keys: [n_shards][batch*q_len][4][topk] (rank keys as int32 bit patterns)."""
+    n_shards = int(cand_ids.shape[0]) if cand_ids.dim() == 4 else -1
+    for name, t in (("cand_ids", cand_ids), ("cand_keys", cand_keys)):
+        if tuple(t.shape) != (n_shards, batch.rows, KV_HEADS, int(topk)):
+            raise ValueError(f"{name}: expected [n_shards][batch*q_len][4][topk]")
+    if tuple(block_ids.shape) != (batch.rows, KV_HEADS, int(topk)):
+        raise ValueError("block_ids: expected [batch*q_len][4][topk]")
+    _check(lib.msa_block_topk_merge(_ptr(cand_ids, torch.int32, "cand_ids"),
+                                    _ptr(cand_keys, torch.int32, "cand_keys"), n_shards,
+                                    ctypes.byref(batch._c), int(topk),
+                                    _ptr(block_ids, torch.int32, "block_ids"), _stream(stream)))
 
 
 def msa_sparse_attn_workspace_bytes(batch: Batch) -> int:

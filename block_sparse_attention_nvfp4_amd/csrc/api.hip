@@ -118,6 +118,50 @@ int msa_block_topk(const float* block_scores, const msa_batch_t* batch, int32_t 
                       fn);
 }
 
+int msa_block_topk_local(const float* shard_scores, int32_t ld, int32_t block_begin,
+                         int32_t block_stride, int32_t n_cols, const msa_batch_t* batch,
+                         int32_t topk, int32_t* cand_ids, uint32_t* cand_keys, void* stream) {
+    static const char* fn = "msa_block_topk_local";
+    int rc = check_batch(batch, fn);
+    if (rc) return rc;
+    if (!shard_scores || !cand_ids || !cand_keys)
+        return fail(MSA_ERR_INVALID_ARG, "%s: shard_scores, cand_ids or cand_keys is NULL", fn);
+    if (n_cols < 1 || n_cols > msa::kLocalMaxBlocks || ld < n_cols)
+        return fail(MSA_ERR_INVALID_ARG, "%s: n_cols=%d must be in [1, %d] and ld=%d >= n_cols", fn,
+                    n_cols, msa::kLocalMaxBlocks, ld);
+    if (block_begin < 0 || block_stride < 1 ||
+        block_begin + (int64_t)(n_cols - 1) * block_stride >= batch->max_blocks)
+        return fail(MSA_ERR_INVALID_ARG,
+                    "%s: blocks %d + c * %d (c < %d) must lie in [0, max_blocks=%d)", fn,
+                    block_begin, block_stride, n_cols, batch->max_blocks);
+    if (topk != MSA_TOPK) return fail(MSA_ERR_UNSUPPORTED, "%s: topk=%d (only 16 is built)", fn, topk);
+    return hip_status(msa::launch_topk_local(shard_scores, ld, block_begin, block_stride, n_cols,
+                                             batch->ctx_lens, batch->batch, batch->max_blocks,
+                                             batch->q_len, cand_ids, cand_keys,
+                                             (hipStream_t)stream),
+                      fn);
+}
+
+int msa_block_topk_merge(const int32_t* cand_ids, const uint32_t* cand_keys, int32_t n_shards,
+                         const msa_batch_t* batch, int32_t topk, int32_t* block_ids,
+                         void* stream) {
+    static const char* fn = "msa_block_topk_merge";
+    if (!batch) return fail(MSA_ERR_INVALID_ARG, "%s: batch is NULL", fn);
+    if (batch->batch < 1 || batch->q_len < 1 || batch->batch > 65535 ||
+        (int64_t)batch->batch * batch->q_len * MSA_KV_HEADS > INT32_MAX / 1024)
+        return fail(MSA_ERR_INVALID_ARG, "%s: batch=%d q_len=%d out of range", fn, batch->batch,
+                    batch->q_len);
+    if (!cand_ids || !cand_keys || !block_ids)
+        return fail(MSA_ERR_INVALID_ARG, "%s: cand_ids, cand_keys or block_ids is NULL", fn);
+    if (n_shards < 1 || n_shards > msa::kMergeMaxShards)
+        return fail(MSA_ERR_INVALID_ARG, "%s: n_shards=%d must be in [1, %d]", fn, n_shards,
+                    msa::kMergeMaxShards);
+    if (topk != MSA_TOPK) return fail(MSA_ERR_UNSUPPORTED, "%s: topk=%d (only 16 is built)", fn, topk);
+    return hip_status(msa::launch_topk_merge(cand_ids, cand_keys, n_shards, batch->batch,
+                                             batch->q_len, block_ids, (hipStream_t)stream),
+                      fn);
+}
+
 size_t msa_sparse_attn_workspace_bytes(const msa_batch_t* batch) {
     if (!batch || batch->batch < 1 || batch->q_len < 1) return 0;
     return msa::attn_workspace_bytes(batch->batch, batch->q_len);

@@ -34,6 +34,16 @@ hipError_t launch_insert_indexer(uint8_t* k_pool, uint8_t* v_pool, uint8_t* ik_p
 hipError_t launch_topk(const float* scores, const int32_t* ctx_lens, int batch, int max_blocks,
                        int q_len, int32_t* ids, hipStream_t stream);
 
+// Context-parallel selection: one shard's local lists (shards of up to kLocalMaxBlocks
+// blocks) and the merge of up to kMergeMaxShards shards' lists.
+constexpr int kLocalMaxBlocks = 64 * 64;
+constexpr int kMergeMaxShards = 16;
+hipError_t launch_topk_local(const float* scores, int ld, int begin, int stride, int n_cols,
+                             const int32_t* ctx_lens, int batch, int max_blocks, int q_len,
+                             int32_t* cand_ids, uint32_t* cand_keys, hipStream_t stream);
+hipError_t launch_topk_merge(const int32_t* cand_ids, const uint32_t* cand_keys, int n_shards,
+                             int batch, int q_len, int32_t* ids, hipStream_t stream);
+
 // Split of the 16 selected blocks of a (sequence, token, group) row over workgroups.
 int attn_num_splits(int batch, int q_len);
 size_t attn_workspace_bytes(int batch, int q_len);

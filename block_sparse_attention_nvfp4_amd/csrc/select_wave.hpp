@@ -107,29 +107,23 @@ __device__ __forceinline__ void load_row_scores(const float* s, int max_blocks, 
         v[k] = *reinterpret_cast<const float*>(row + 4u * (uint32_t)min(lane + 64 * k, max_blocks - 1));
 }
 
-// Select the row's blocks from its scores v (as load_row_scores holds them) and its n eligible
-// blocks: out[0..15] gets the selected block ids in ascending order, padded with -1. `cand` is
-// this wavefront's kSelectScratch entries of LDS; `out` may point to global memory or LDS.
-template <int KPL>
-__device__ __forceinline__ void select_row(const float (&v)[KPL], int n, int lane, uint64_t* cand,
-                                           int32_t* out) {
-    if (n <= kTopk) {
-        if (lane < kTopk) out[lane] = lane < n ? lane : -1;
-        return;
-    }
-    const int m = n - 1;  // candidates 0..m-1 compete for 15 places
-    uint32_t key[KPL];  // 0 marks "no candidate": every real key is above it
+// Select the PICK best of a row's keys (position i in lane i % 64, slot i / 64; key 0 marks
+// "no candidate"; a larger key ranks first, equal keys by the lower position) and write
+// id_of(position) for each in ascending position order to out[0..PICK-1], and their keys to
+// key_out when it is given. With fewer than PICK candidates the remaining entries are -1 (keys
+// 0). `cand` is this wavefront's kSelectScratch entries of LDS; `out` and `key_out` may point
+// to global memory or LDS.
+template <int KPL, int PICK, class IdOf>
+__device__ __forceinline__ void select_top(const uint32_t (&key)[KPL], int lane, uint64_t* cand,
+                                           int32_t* out, uint32_t* key_out, IdOf id_of) {
+    static_assert(PICK >= 1 && PICK <= 64, "at most 64 picks");
     uint32_t lmax = 0;
 #pragma unroll
-    for (int k = 0; k < KPL; k++) {
-        const int i = lane + 64 * k;
-        key[k] = i < m ? order_key(v[k]) : 0u;
-        lmax = max(lmax, key[k]);
-    }
-    // bound: the 15th-largest per-lane maximum, the smallest maximum that fewer than 15 others
-    // exceed (each lane counts the maxima above its own, read back as LDS broadcasts). The
-    // candidate area is cleared in the same pass: entries past the candidate count read as 0,
-    // below every candidate.
+    for (int k = 0; k < KPL; k++) lmax = max(lmax, key[k]);
+    // bound: the PICK-th largest per-lane maximum, the smallest maximum that fewer than PICK
+    // others exceed (each lane counts the maxima above its own, read back as LDS broadcasts),
+    // and at least 1 (never a non-candidate). The candidate area is cleared in the same pass:
+    // entries past the candidate count read as 0, below every candidate.
     uint32_t* lane_max = reinterpret_cast<uint32_t*>(cand + 128);
     lane_max[lane] = lmax;
     cand[lane] = 0;
@@ -141,7 +135,7 @@ __device__ __forceinline__ void select_row(const float (&v)[KPL], int n, int lan
     int above = 0;
 #pragma unroll
     for (int r = 0; r < 16; r++) above = add_count_above(w[r], lmax, above);
-    const uint32_t bound = wave_min_u32(above < kTopk - 1 ? lmax : 0xFFFFFFFFu);
+    const uint32_t bound = max(wave_min_u32(above < PICK ? lmax : 0xFFFFFFFFu), 1u);
     // candidates: the keys at or above the bound (all slots' masks first, then their counts)
     uint64_t cmask[KPL];
 #pragma unroll
@@ -151,6 +145,7 @@ __device__ __forceinline__ void select_row(const float (&v)[KPL], int n, int lan
 #pragma unroll
     for (int k = 0; k < KPL; k++) base[k + 1] = base[k] + popc64(cmask[k]);
     const int count = __builtin_amdgcn_readfirstlane(base[KPL]);  // uniform: a scalar loop bound
+    int n_sel;
     if (count <= 64) {
         // compact the candidates in ascending block order (k-major, lane-minor) as composites
         // (key, inverted block index): a larger composite ranks first, and equal keys rank by
@@ -177,13 +172,18 @@ __device__ __forceinline__ void select_row(const float (&v)[KPL], int n, int lan
 #pragma unroll
             for (int i = 0; i < 8; i++) rank += (int)(o[i] > mine);
         }
-        const bool sel = lane < count && rank < kTopk - 1;
+        const bool sel = lane < count && rank < PICK;
         const uint64_t smask = __ballot(sel);
-        if (sel) out[lanes_before(smask)] = (int)~(uint32_t)mine;
+        if (sel) {
+            const int at = lanes_before(smask);
+            out[at] = id_of((int)~(uint32_t)mine);
+            if (key_out) key_out[at] = (uint32_t)(mine >> 32);
+        }
+        n_sel = popc64(smask);
     } else {
-        // heavy ties: take the best remaining (key, lowest index) 15 times
+        // heavy ties: take the best remaining (key, lowest index) PICK times
         uint32_t taken[(KPL + 31) / 32] = {};
-        for (int r = 0; r < kTopk - 1; r++) {
+        for (int r = 0; r < PICK; r++) {
             uint32_t bk = 0;
             int bi = 0x7fffffff;
 #pragma unroll
@@ -204,20 +204,48 @@ __device__ __forceinline__ void select_row(const float (&v)[KPL], int n, int lan
                     bi = oi;
                 }
             }
-            if ((bi & 63) == lane) {
+            if (bk != 0u && (bi & 63) == lane) {  // (more than 64 candidates: never empty)
                 const int k = bi >> 6;
                 taken[k >> 5] |= 1u << (k & 31);
             }
         }
-        int base = 0;
+        int at = 0;
 #pragma unroll
         for (int k = 0; k < KPL; k++) {
             const bool sel = (taken[k >> 5] >> (k & 31)) & 1u;
             const uint64_t mask = __ballot(sel);
-            if (sel) out[base + lanes_before(mask)] = lane + 64 * k;
-            base += popc64(mask);
+            if (sel) {
+                out[at + lanes_before(mask)] = id_of(lane + 64 * k);
+                if (key_out) key_out[at + lanes_before(mask)] = key[k];
+            }
+            at += popc64(mask);
         }
+        n_sel = at;
     }
+    if (lane >= n_sel && lane < PICK) {
+        out[lane] = -1;
+        if (key_out) key_out[lane] = 0u;
+    }
+}
+
+// Select the row's blocks from its scores v (as load_row_scores holds them) and its n eligible
+// blocks: out[0..15] gets the selected block ids in ascending order, padded with -1. `cand` is
+// this wavefront's kSelectScratch entries of LDS; `out` may point to global memory or LDS.
+template <int KPL>
+__device__ __forceinline__ void select_row(const float (&v)[KPL], int n, int lane, uint64_t* cand,
+                                           int32_t* out) {
+    if (n <= kTopk) {
+        if (lane < kTopk) out[lane] = lane < n ? lane : -1;
+        return;
+    }
+    const int m = n - 1;  // candidates 0..m-1 compete for 15 places
+    uint32_t key[KPL];    // 0 marks "no candidate": every real key is above it
+#pragma unroll
+    for (int k = 0; k < KPL; k++) {
+        const int i = lane + 64 * k;
+        key[k] = i < m ? order_key(v[k]) : 0u;
+    }
+    select_top<KPL, kTopk - 1>(key, lane, cand, out, nullptr, [](int i) { return i; });
     if (lane == 0) out[kTopk - 1] = m;  // the forced block of the query token, the largest id
 }
 

@@ -248,7 +248,128 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void topk_wave_kernel(
     select_row<KPL>(v, eligible_blocks(p, max_blocks), lane, cand[wave], ids + (int64_t)row * kTopk);
 }
 
+// ---------------------------------------------------------------- context-parallel selection
+// "vLLM day-0 support for MiniMax-M3.1-Flash", section "Indexer NVFP4 DCP": each device scores
+// every index head on its own share of the pages, keeps its local top 16 per head, and the
+// device that owns the head merges the lists into the final top 16, which is exact: every
+// member of the global selection is among the best 16 of its own shard. Ranks travel as 32-bit
+// keys (the order key of the score, the forced block as the largest key), so the merge needs
+// neither scores nor context lengths.
+constexpr uint32_t kForcedKey = 0xFFFFFFFFu;  // above every order key of a non-NaN score
+
+// One shard's local lists: column c of a row holds block begin + c * stride.
+template <int KPL>  // keys per lane: shards of up to 64 * KPL blocks
+__global__ __launch_bounds__(kRowsPerWg * 64) void topk_local_kernel(
+    const float* __restrict__ scores, int ld, int begin, int stride, int n_cols,
+    const int32_t* __restrict__ ctx_lens, int max_blocks, int q_len, int rows,
+    int32_t* __restrict__ cand_ids, uint32_t* __restrict__ cand_keys) {
+    __shared__ uint64_t cand[kRowsPerWg][kSelectScratch];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int row = blockIdx.x * kRowsPerWg + wave;  // ((b * q_len + j) * 4 + g)
+    if (row >= rows) return;
+    const int bq = row >> 2;
+    const int b = bq / q_len;
+    const int j = bq - b * q_len;
+    float v[KPL];
+    load_row_scores<KPL>(scores + (int64_t)row * ld, n_cols, lane, v);
+    int T_raw = ctx_lens[b];
+#pragma unroll
+    for (int k = 0; k < KPL; k++) asm volatile("" : "+v"(v[k]));
+    asm volatile("" : "+v"(T_raw));
+    const int n = eligible_blocks(clamp_ctx(T_raw, max_blocks) - q_len + j, max_blocks);
+    uint32_t key[KPL];
+#pragma unroll
+    for (int k = 0; k < KPL; k++) {
+        const int c = lane + 64 * k;
+        // (wraps harmlessly past the shard, where the key is 0 anyway)
+        const int id = (int)((uint32_t)begin + (uint32_t)c * (uint32_t)stride);
+        key[k] = (c < n_cols && id < n) ? (id == n - 1 ? kForcedKey : order_key(v[k])) : 0u;
+    }
+    // columns ascend with the block ids, so the lowest position is the lowest block
+    select_top<KPL, kTopk>(key, lane, cand[wave], cand_ids + (int64_t)row * kTopk,
+                           cand_keys + (int64_t)row * kTopk,
+                           [=](int c) { return begin + c * stride; });
+}
+
+// The owner's merge of n_shards lists per row (shard s at [s][rows][16]): every candidate is
+// ranked against all others by (key, then lower block) and the best 16 are written in
+// ascending block order.
+__global__ __launch_bounds__(kRowsPerWg * 64) void topk_merge_kernel(
+    const int32_t* __restrict__ cand_ids, const uint32_t* __restrict__ cand_keys, int n_shards,
+    int rows, int32_t* __restrict__ ids) {
+    constexpr int kSlots = kMergeMaxShards * kTopk / 64;
+    __shared__ uint64_t comp[kRowsPerWg][kMergeMaxShards * kTopk];
+    __shared__ int32_t kept[kRowsPerWg][kTopk];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int row = blockIdx.x * kRowsPerWg + wave;
+    if (row >= rows) return;
+    const int n_cand = n_shards * kTopk;
+    // candidate c = shard c / 16, entry c % 16, as the composite (key, inverted block id): a
+    // larger composite ranks first; padding (key 0) is 0 and ranks below every candidate
+    uint64_t mine[kSlots];
+#pragma unroll
+    for (int k = 0; k < kSlots; k++) {
+        const int c = lane + 64 * k;
+        mine[k] = 0;
+        if (c < n_cand) {
+            const int64_t at = ((int64_t)(c / kTopk) * rows + row) * kTopk + c % kTopk;
+            const uint32_t key = cand_keys[at];
+            if (key != 0u) mine[k] = ((uint64_t)key << 32) | ~(uint32_t)cand_ids[at];
+            comp[wave][c] = mine[k];
+        }
+    }
+    if (lane < kTopk) kept[wave][lane] = -1;
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");  // the reads below follow these stores
+    int rank[kSlots] = {};
+    for (int t = 0; t < n_cand; t++) {
+        const uint64_t o = comp[wave][t];  // an LDS broadcast
+#pragma unroll
+        for (int k = 0; k < kSlots; k++) rank[k] += (int)(o > mine[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < kSlots; k++)
+        if (mine[k] != 0 && rank[k] < kTopk) kept[wave][rank[k]] = (int)~(uint32_t)mine[k];
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+    if (lane < kTopk) {
+        // ascending block order, -1 padding last (as unsigned it is the largest)
+        const int v = kept[wave][lane];
+        int pos = 0;
+#pragma unroll
+        for (int i = 0; i < kTopk; i++) {
+            const int u = kept[wave][i];
+            pos += (int)((uint32_t)u < (uint32_t)v || (u == v && i < lane));
+        }
+        ids[(int64_t)row * kTopk + pos] = v;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_topk_local(const float* scores, int ld, int begin, int stride, int n_cols,
+                             const int32_t* ctx_lens, int batch, int max_blocks, int q_len,
+                             int32_t* cand_ids, uint32_t* cand_keys, hipStream_t stream) {
+    const int rows = batch * q_len * kKvHeads;
+    const dim3 grid((rows + kRowsPerWg - 1) / kRowsPerWg), block(kRowsPerWg * 64);
+    if (n_cols <= 64 * 16)
+        hipLaunchKernelGGL(topk_local_kernel<16>, grid, block, 0, stream, scores, ld, begin, stride,
+                           n_cols, ctx_lens, max_blocks, q_len, rows, cand_ids, cand_keys);
+    else
+        hipLaunchKernelGGL(topk_local_kernel<64>, grid, block, 0, stream, scores, ld, begin, stride,
+                           n_cols, ctx_lens, max_blocks, q_len, rows, cand_ids, cand_keys);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_merge(const int32_t* cand_ids, const uint32_t* cand_keys, int n_shards,
+                             int batch, int q_len, int32_t* ids, hipStream_t stream) {
+    const int rows = batch * q_len * kKvHeads;
+    hipLaunchKernelGGL(topk_merge_kernel, dim3((rows + kRowsPerWg - 1) / kRowsPerWg),
+                       dim3(kRowsPerWg * 64), 0, stream, cand_ids, cand_keys, n_shards, rows, ids);
+    return hipGetLastError();
+}
 
 hipError_t launch_topk(const float* scores, const int32_t* ctx_lens, int batch, int max_blocks,
                        int q_len, int32_t* ids, hipStream_t stream) {

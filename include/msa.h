@@ -173,6 +173,41 @@ int msa_indexer_score(const msa_cache_t *cache, const msa_batch_t *batch, const 
 int msa_block_topk(const float *block_scores, const msa_batch_t *batch, int32_t topk,
                    int32_t *block_ids, void *stream);
 
+/*
+ * Block selection split over shards of the blocks, as in indexer decode context parallelism
+ * ("vLLM day-0 support for MiniMax-M3.1-Flash", section "Indexer NVFP4 DCP": each device
+ * scores every index head on its own share of the pages and keeps a local top 16 per head;
+ * the device owning the head merges the lists into the final top 16, and the selection stays
+ * exact). Here every shard runs on one device: msa_block_topk_local once per shard, then
+ * msa_block_topk_merge over all shards' lists gives exactly what msa_block_topk writes.
+ *
+ * A candidate list entry is (block id, rank key). The rank key is a 32-bit order-preserving
+ * code of the score (bits u of the fp32 score with -0 read as +0: u ^ 0x80000000 for a
+ * non-negative score, ~u for a negative one), or 0xFFFFFFFF for the forced block of the row
+ * (the block of the query token; it outranks every score), or 0 for padding (id -1). A larger
+ * key ranks first; equal keys rank by the lower block id.
+ *
+ * msa_block_topk_local: the shard holds blocks block_begin + c * block_stride, c = 0..n_cols-1.
+ *   shard_scores : device fp32 [batch * q_len][4][ld]; column c < n_cols holds the score of the
+ *                  shard's block c as msa_indexer_score computes it (other columns unread).
+ *   cand_ids     : device int32 [batch * q_len][4][topk]: the best topk of the shard's eligible
+ *                  blocks (blocks 0..f as for msa_block_topk, f forced), ascending, -1 padded.
+ *   cand_keys    : device uint32, same shape: their rank keys (0 for padding).
+ * msa_block_topk_merge: n_shards lists, shard s's at cand_ids + s * (batch * q_len * 4 * topk)
+ *   (cand_keys likewise) as msa_block_topk_local writes them, shards disjoint.
+ *   block_ids    : device int32 [batch * q_len][4][topk]: the best topk of the union by rank
+ *                  key, ascending, -1 padded. Only batch->batch and batch->q_len are read.
+ * Scores must not be NaN. Errors: MSA_ERR_INVALID_ARG (NULL pointers, sizes < 1, n_cols >
+ * 4096, ld < n_cols, block_begin < 0, block_stride < 1, a shard block >= max_blocks,
+ * n_shards > 16), MSA_ERR_UNSUPPORTED (topk != 16).
+ */
+int msa_block_topk_local(const float *shard_scores, int32_t ld, int32_t block_begin,
+                         int32_t block_stride, int32_t n_cols, const msa_batch_t *batch,
+                         int32_t topk, int32_t *cand_ids, uint32_t *cand_keys, void *stream);
+int msa_block_topk_merge(const int32_t *cand_ids, const uint32_t *cand_keys, int32_t n_shards,
+                         const msa_batch_t *batch, int32_t topk, int32_t *block_ids,
+                         void *stream);
+
 /* Workspace bytes msa_sparse_attn_decode needs for this batch shape (may be 0). */
 size_t msa_sparse_attn_workspace_bytes(const msa_batch_t *batch);
 

@@ -88,6 +88,26 @@ def test_invalid_arguments_return_codes_without_launch(msa):
     assert "topk" in msa.msa_last_error()
     assert L.msa_block_topk(None, by(_batch()), 16, 1, None) == msa.MSA_ERR_INVALID_ARG
     assert L.msa_block_topk(1, by(_batch(mb=0)), 16, 1, None) == msa.MSA_ERR_INVALID_ARG
+    # shard-local lists and their merge (args: scores ld begin stride n_cols batch topk ids keys)
+    loc = L.msa_block_topk_local
+    mb8 = by(_batch(mb=8))
+    assert loc(1, 4, 0, 1, 4, mb8, 8, 1, 1, None) == msa.MSA_ERR_UNSUPPORTED
+    for bad in ([None, 4, 0, 1, 4], [1, 3, 0, 1, 4], [1, 4, 0, 1, 0], [1, 4, -1, 1, 4],
+                [1, 4, 0, 0, 4], [1, 4, 5, 1, 4], [1, 4, 1, 3, 4], [1, 5000, 0, 1, 4097]):
+        assert loc(*bad, mb8, 16, 1, 1, None) == msa.MSA_ERR_INVALID_ARG, bad
+    assert loc(1, 4, 0, 1, 4, mb8, 16, None, 1, None) == msa.MSA_ERR_INVALID_ARG
+    assert loc(1, 4, 0, 1, 4, mb8, 16, 1, None, None) == msa.MSA_ERR_INVALID_ARG
+    assert loc(1, 4, 0, 1, 4, by(_batch(cl=None, mb=8)), 16, 1, 1, None) == msa.MSA_ERR_INVALID_ARG
+    mrg = L.msa_block_topk_merge
+    assert mrg(1, 1, 2, mb8, 8, 1, None) == msa.MSA_ERR_UNSUPPORTED
+    for n_shards in (0, 17):
+        assert mrg(1, 1, n_shards, mb8, 16, 1, None) == msa.MSA_ERR_INVALID_ARG
+    for i in range(3):
+        a = [1, 1, 1]
+        a[i] = None
+        assert mrg(a[0], a[1], 2, mb8, 16, a[2], None) == msa.MSA_ERR_INVALID_ARG, i
+    assert mrg(1, 1, 2, by(_batch(q=0)), 16, 1, None) == msa.MSA_ERR_INVALID_ARG
+    assert mrg(1, 1, 2, None, 16, 1, None) == msa.MSA_ERR_INVALID_ARG
     # attention
     small = by(_batch(b=1, q=1))
     need = L.msa_sparse_attn_workspace_bytes(small)
