@@ -554,6 +554,9 @@ static int indexer_wgs(int batch, int max_blocks) {
 hipError_t launch_indexer(const uint8_t* ik_pool, int64_t num_pages, const int32_t* block_table,
                           const int32_t* ctx_lens, int batch, int max_blocks, int q_len,
                           const uint16_t* q_idx, float* scores, hipStream_t stream) {
+    if (q_len >= kIndexerGemmMinQ)
+        return launch_indexer_gemm(ik_pool, num_pages, block_table, ctx_lens, batch, max_blocks,
+                                   q_len, q_idx, scores, stream);
     hipLaunchKernelGGL(indexer_kernel<false>, dim3(indexer_wgs(batch, max_blocks)),
                        dim3(kWaves * 64), 0, stream, ik_pool, num_pages, block_table, ctx_lens,
                        max_blocks, q_len, q_idx, scores, nullptr, nullptr, nullptr, nullptr,

@@ -1,0 +1,175 @@
+// MSA indexer for many query rows per sequence (prefill chunks, long speculative drafts): the
+// block scores as a score GEMM, each index-key page dequantized once and multiplied with every
+// query row that can see it.
+//
+// "vLLM day-0 support for MiniMax-M3.1-Flash", section "MSA primer": one index query per GQA
+// group scores every key of the shared index-key head, max-pooled per 128-token block. "MiniMax
+// M3 on vLLM", sections "MSA mechanism" and "Prefill execution": the causal boundary inside a
+// block is masked and every query token has its own position (a chunk of q tokens scores
+// 4 q rows against the whole visible context, a GEMM).
+//
+// Work split: a workgroup of eight wavefronts takes eight consecutive blocks of one sequence
+// and a range of up to 512 of its query rows. Each wavefront loads its block's page once into
+// registers and dequantizes it exactly to bf16 (E2M1 x E4M3 products have at most 6 significant
+// bits), as the A operand of 16x16x32 bf16 matrix-core steps: 128 tokens x 128 dims in 128
+// registers. The query rows stream through LDS in stages of 64 rows, loaded by direct
+// global->LDS copies already in operand order and shared by the eight wavefronts (double
+// buffered: the next stage loads while this one is multiplied). Per 16-row tile a wavefront
+// runs 32 matrix-core steps (8 token slabs x 4 dimension steps, fp32 accumulate), takes each
+// row's max over its visible tokens and keeps it in LDS; the workgroup writes its rows' eight
+// block scores at the end as contiguous 32-byte runs.
+// Query rows are bf16 and used as they are: every product is exact in fp32 and the sums are
+// fp32, as in the decode indexer's bf16 path.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace msa {
+namespace {
+
+constexpr int kGWaves = 8;                   // one block per wavefront
+constexpr int kStageRows = 64;               // query rows per LDS stage
+constexpr int kTileBytes = 16 * kDim * 2;    // one 16-row tile of bf16 query rows: 4 KB
+constexpr int kMaxRowsPerWg = 512;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// This lane's B operand of a 16-row tile (dims x rows): piece m holds row n = lane % 16,
+// elements 32 c + 8 m .. +7 (c = lane / 16), stored at tile + 1024 m + 16 lane. Read with
+// explicit instructions, issued and waited for in one statement: the compiler cannot tell
+// which LDS buffer the direct copies in flight write, and would otherwise wait for all of them.
+__device__ __forceinline__ void read_tile(u32x4 (&v)[4], const uint8_t* tile, int lane) {
+    const uint32_t a = (uint32_t)(uintptr_t)(tile + lane * 16);
+    asm volatile("ds_read_b128 %0, %4\n\t"
+                 "ds_read_b128 %1, %4 offset:1024\n\t"
+                 "ds_read_b128 %2, %4 offset:2048\n\t"
+                 "ds_read_b128 %3, %4 offset:3072\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]) : "v"(a) : "memory");
+}
+
+__global__ __launch_bounds__(kGWaves * 64) void indexer_gemm_kernel(
+    const uint8_t* __restrict__ ik_pool, int64_t num_pages, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ ctx_lens, int max_blocks, int q_len, int rows_per_wg,
+    const uint16_t* __restrict__ q_idx, float* __restrict__ scores) {
+    __shared__ __attribute__((aligned(16))) uint8_t stage[2][kStageRows / 16][kTileBytes];
+    __shared__ float best_of[kMaxRowsPerWg][kGWaves];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15, c = lane >> 4;
+    const int b = blockIdx.z;
+    const int rows = 4 * q_len;  // this sequence's rows (j, g) = 4 j + g
+    const int r_begin = blockIdx.y * rows_per_wg;
+    const int r_end = min(rows, r_begin + rows_per_wg);
+    const int blk = blockIdx.x * kGWaves + wave;
+    const int T = clamp_ctx(ctx_lens[b], max_blocks);
+    const uint8_t* qseq = reinterpret_cast<const uint8_t*>(q_idx + (int64_t)b * rows * kDim);
+
+    // stage loads: 16 copies of 1 KB (tile tt, piece m), two per wavefront; lane (n, c) of
+    // copy (tt, m) brings bytes 64 c + 16 m .. +15 of row 16 tt + n (past the range: its last
+    // row, never written out)
+    auto load_stage = [&](int r0, int buf) {
+#pragma unroll
+        for (int k = 0; k < 2; k++) {
+            const int i = 2 * wave + k, tt = i >> 2, m = i & 3;
+            const int r = min(r0 + 16 * tt + n, r_end - 1);
+            __builtin_amdgcn_global_load_lds(qseq + (int64_t)r * (kDim * 2) + 64 * c + 16 * m,
+                                             (lds_void*)(&stage[buf][tt][1024 * m]), 16, 0, 0);
+        }
+    };
+    load_stage(r_begin, 0);
+
+    // this wavefront's page: lane (m, c) holds, for token slab s, the 32 codes of token
+    // 32 (m / 4) + 4 s + m % 4, elements 32 c .. 32 c + 31, and the 16 scale bytes of its
+    // token row (bytes 2 s, 2 s + 1: element groups 2 c, 2 c + 1 of slab s)
+    const bool in_table = blk < max_blocks;
+    int page = in_table ? block_table[(int64_t)b * max_blocks + blk] : -1;
+    const int tok0 = blk * kBlock;
+    const bool has_keys = in_table && tok0 < T && page >= 0 && page < num_pages;
+    bf16x8 ka[8][4];
+    if (has_keys) {
+        const uint8_t* pg = ik_pool + (int64_t)page * kHeadPageBytes;
+        u32x4 code[8];
+#pragma unroll
+        for (int s = 0; s < 8; s++) code[s] = load16(pg + 1024 * s + 16 * lane);
+        const u32x4 sc = load16(pg + kCodeBytes + 16 * lane);
+#pragma unroll
+        for (int s = 0; s < 8; s++) {
+            const f32x2 gs = (s & 1) ? e4m3_pair_f32<true>(sc[s >> 1]) : e4m3_pair_f32<false>(sc[s >> 1]);
+#pragma unroll
+            for (int m = 0; m < 4; m++) ka[s][m] = dequant8_bf16(code[s][m], m < 2 ? gs[0] : gs[1]);
+            // one slab at a time: the fp32 products of later slabs are not all made up front
+            asm volatile("" : "+v"(ka[s][0]), "+v"(ka[s][1]), "+v"(ka[s][2]), "+v"(ka[s][3]));
+        }
+    }
+
+    int buf = 0;
+    for (int r0 = r_begin; r0 < r_end; r0 += kStageRows, buf ^= 1) {
+        // this stage's rows are in LDS for every wavefront, and every wavefront is done with
+        // the other buffer: the next stage may overwrite it
+        __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+        __syncthreads();
+        if (r0 + kStageRows < r_end) load_stage(r0 + kStageRows, buf ^ 1);
+#pragma unroll 1
+        for (int tt = 0; tt < kStageRows / 16; tt++) {
+            const int rt = r0 + 16 * tt;  // rows rt .. rt + 15: tokens rt / 4 .. rt / 4 + 3
+            if (rt >= r_end) break;
+            const int p_lo = T - q_len + (rt >> 2);
+            const int p_hi = T - q_len + min((rt >> 2) + 3, q_len - 1);
+            float best = -INFINITY;
+            if (has_keys && p_hi >= tok0) {
+                u32x4 qv[4];
+                read_tile(qv, &stage[buf][tt][0], lane);
+                f32x4 acc[8];
+#pragma unroll
+                for (int s = 0; s < 8; s++) {
+                    acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int m = 0; m < 4; m++)
+                        acc[s] = mfma_bf16_k32(ka[s][m], __builtin_bit_cast(bf16x8, qv[m]), acc[s]);
+                }
+                // D of slab s in lane (n, c): tokens 32 c + 4 s + i, i = 0..3, of query row n
+                if (p_lo >= tok0 + kBlock - 1) {
+#pragma unroll
+                    for (int s = 0; s < 8; s++)
+#pragma unroll
+                        for (int i = 0; i < 4; i++) best = fmaxf(best, acc[s][i]);
+                } else {
+                    asm volatile("");  // a scalar branch: the mask only where the block is cut
+                    const int lim = T - q_len + min((rt + n) >> 2, q_len - 1) - tok0 - 32 * c;
+#pragma unroll
+                    for (int s = 0; s < 8; s++)
+#pragma unroll
+                        for (int i = 0; i < 4; i++)
+                            best = fmaxf(best, 4 * s + i <= lim ? acc[s][i] : -INFINITY);
+                }
+                best = max_over_c(best);
+            }
+            if (c == 0 && rt + n < r_end) best_of[rt + n - r_begin][wave] = best;
+        }
+    }
+    __syncthreads();
+    // row rl's eight block scores are 32 contiguous bytes
+    const int nr = r_end - r_begin;
+    float* out = scores + ((int64_t)b * rows + r_begin) * max_blocks + blockIdx.x * kGWaves;
+    for (int i = threadIdx.x; i < nr * kGWaves; i += kGWaves * 64) {
+        const int rl = i >> 3, kb = i & 7;
+        if (blockIdx.x * kGWaves + kb < max_blocks) out[(int64_t)rl * max_blocks + kb] = best_of[rl][kb];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_indexer_gemm(const uint8_t* ik_pool, int64_t num_pages,
+                               const int32_t* block_table, const int32_t* ctx_lens, int batch,
+                               int max_blocks, int q_len, const uint16_t* q_idx, float* scores,
+                               hipStream_t stream) {
+    const int rows = 4 * q_len;
+    const int rows_per_wg = min(kMaxRowsPerWg, (rows + 15) / 16 * 16);
+    const dim3 grid((max_blocks + kGWaves - 1) / kGWaves, (rows + rows_per_wg - 1) / rows_per_wg,
+                    batch);
+    hipLaunchKernelGGL(indexer_gemm_kernel, grid, dim3(kGWaves * 64), 0, stream, ik_pool,
+                       num_pages, block_table, ctx_lens, max_blocks, q_len, rows_per_wg, q_idx,
+                       scores);
+    return hipGetLastError();
+}
+
+}  // namespace msa

@@ -16,6 +16,17 @@ hipError_t launch_indexer(const uint8_t* ik_pool, int64_t num_pages, const int32
                           const int32_t* ctx_lens, int batch, int max_blocks, int q_len,
                           const uint16_t* q_idx, float* scores, hipStream_t stream);
 
+// The indexer as a score GEMM (each page dequantized once for all query rows), used by
+// launch_indexer from kIndexerGemmMinQ query tokens per sequence on: the decode indexer streams
+// the pages once per 16 query rows, and from 3 row tiles (q = 9..12) on the GEMM is faster
+// (8 x 131,072 context: 37 against 28 us at q = 12, 99 against 54 us at q = 32; the scores are
+// the same bits).
+constexpr int kIndexerGemmMinQ = 9;
+hipError_t launch_indexer_gemm(const uint8_t* ik_pool, int64_t num_pages,
+                               const int32_t* block_table, const int32_t* ctx_lens, int batch,
+                               int max_blocks, int q_len, const uint16_t* q_idx, float* scores,
+                               hipStream_t stream);
+
 // Insert of a decode step's new tokens at their own positions (slots from the block table).
 hipError_t launch_insert_at_positions(uint8_t* k_pool, uint8_t* v_pool, uint8_t* ik_pool,
                                       int64_t num_pages, const int32_t* block_table,

@@ -37,6 +37,11 @@ CASES = {
     "spec_q8": (3, dict(batch=2, ctx_lens=[4000, 7000], q_len=8)),
     "spec_q16": (3, dict(batch=1, ctx=6000, q_len=16)),
     "spec_q17": (3, dict(batch=1, ctx=6000, q_len=17)),
+    # the score-GEMM indexer: a context that is only its query tokens (first token at p = 0),
+    # partial last blocks, blocks past the shorter sequences, and 800 rows per sequence (two
+    # row ranges, the second partial)
+    "prefill_ragged": (5, dict(batch=3, ctx_lens=[40, 700, 3003], q_len=40)),
+    "prefill_q200": (5, dict(ctx_lens=[2048 + 200, 1500], q_len=200)),
 }
 
 
