@@ -152,13 +152,19 @@ __device__ __forceinline__ void lds_write32(uint32_t a, const u32x4& v0, const u
 
 // One block of one wavefront: logits, online-softmax update, output accumulation. The K page
 // is in LDS on entry; the V page may still be arriving (NEXT: the next block's 18 loads were
-// issued after it) and is waited for only before its first read.
-template <bool F16, bool NEXT>
+// issued after it) and is waited for only before its first read. RESIDENT: both pages have
+// arrived and other loads may be in flight (no wait, and only explicit LDS reads). The V
+// scales are converted into the 2 KB table at `stab` (the K codes' area unless the page buffer
+// is shared with other wavefronts).
+template <bool F16, bool NEXT, bool RESIDENT = false>
 __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c, int tok0, int p,
                                              const u32x4 (&qop)[4], float logit_scale,
-                                             float& m_run, float& l_run, f32x4 (&o)[8]) {
+                                             float& m_run, float& l_run, f32x4 (&o)[8],
+                                             const uint8_t* stab = nullptr) {
+    constexpr bool kAsmReads = NEXT || RESIDENT;
     const uint32_t kbase = (uint32_t)(uintptr_t)buf;
     const uint32_t vbase = kbase + kHeadPageBytes;
+    const uint32_t sbase = stab ? (uint32_t)(uintptr_t)stab : kbase;
     // ---- logits S^T (log2 domain)
     u32x4 kc[8], ksc;
     lds_read16x9(kc, ksc, kbase + lane * 16, kbase + kCodeBytes + lane * 16);
@@ -223,8 +229,12 @@ __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c
     l_run += sum_over_c(ls);
 
     // ---- the V page's 9 loads (issued after the K page's 9) complete here
-    if constexpr (NEXT) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if constexpr (RESIDENT) {
+    } else if constexpr (NEXT) {
+        asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     // ---- the block's 1,024 V scales as fp16, [group][token], written over the K codes (read
     // into registers above and not needed again): lane l converts the 16 scale bytes of group
     // l / 8, tokens 16 (l % 8) .. +15. Each lane then reads its scales ready for the packed
@@ -233,7 +243,7 @@ __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c
         // (with no later page in flight, ordinary LDS reads: the compiler overlaps them with
         // the work before their use; otherwise statements that wait for their own reads only)
         u32x4 raw;
-        if constexpr (NEXT) raw = lds_read16(vbase + kCodeBytes + lane * 16);
+        if constexpr (kAsmReads) raw = lds_read16(vbase + kCodeBytes + lane * 16);
         else raw = *reinterpret_cast<const u32x4*>(buf + kHeadPageBytes + kCodeBytes + lane * 16);
         u32x4 h0, h1;
 #pragma unroll
@@ -243,7 +253,7 @@ __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c
             h1[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[i + 2], 1.0f, false));
             h1[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[i + 2], 1.0f, true));
         }
-        lds_write32(kbase + lane * 32, h0, h1);
+        lds_write32(sbase + lane * 32, h0, h1);
     }
 
     // ---- O^T += V^T P^T, one 16-dim tile (= one scale group) at a time
@@ -252,8 +262,8 @@ __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c
         const int d = 16 * dt + (lane & 15);
         // codes of tokens 32c..32c+31 and their fp16 scales of group dt
         u32x4 vc, sc[4];
-        if constexpr (NEXT) {
-            lds_read16x5(vc, sc, vbase + d * 64 + 16 * c, kbase + dt * 256 + 64 * c);
+        if constexpr (kAsmReads) {
+            lds_read16x5(vc, sc, vbase + d * 64 + 16 * c, sbase + dt * 256 + 64 * c);
         } else {
             vc = *reinterpret_cast<const u32x4*>(buf + kHeadPageBytes + d * 64 + 16 * c);
 #pragma unroll
@@ -539,6 +549,165 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
     *reinterpret_cast<u32x4*>(op) = u32x4{packed[0], packed[1], packed[2], packed[3]};
 }
 
+// ---------------------------------------------------------------- token tiles
+// Batches with many query tokens per sequence (prefill chunks): the tokens of one (sequence,
+// group) pair select mostly the same blocks, and reading each block once per token makes the
+// page traffic, not the arithmetic, the bound. A workgroup of eight wavefronts takes eight
+// consecutive query tokens of one pair, one token per wavefront. The union of their selected
+// blocks streams once, in ascending block order, through two LDS buffers that the workgroup
+// shares (the next block's loads spread over the wavefronts and in flight while the current
+// block is used), and each wavefront attends, with attend_block, exactly the blocks its own token
+// selected, keeping its token's whole softmax state: no partials and no merge.
+constexpr int kTileWaves = 8;
+constexpr int kUnionMaxBlocks = 8192;  // rows of up to this many blocks (the union's bitmap)
+constexpr int kTileMinQ = 8;           // from this many query tokens per sequence (and no split)
+
+__global__ __launch_bounds__(kTileWaves * 64) void attention_tile_kernel(
+    const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool, int64_t num_pages,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens, int batch,
+    int max_blocks, int q_len, const uint16_t* __restrict__ q,
+    const int32_t* __restrict__ block_ids, float scale_log2, uint16_t* __restrict__ out) {
+    __shared__ __attribute__((aligned(16))) uint8_t pages[2][kBlockBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t vscale[kTileWaves][2048];
+    __shared__ uint64_t bitmap[kUnionMaxBlocks / 64];
+    __shared__ int ulist[kTileWaves * kTopk];
+    __shared__ int upage[kTileWaves * kTopk];
+    __shared__ int ucount;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15;
+    const int c = lane >> 4;
+    // XCD-aware work mapping as in attention_kernel: pair = (b, g) -> XCD pair % 8
+    const int tiles = (q_len + kTileWaves - 1) / kTileWaves;
+    const int local = blockIdx.x >> 3;
+    const int pair = (local / tiles) * 8 + (blockIdx.x & 7);
+    if (pair >= batch * kKvHeads) return;  // the whole workgroup
+    const int tile = local - (local / tiles) * tiles;
+    const int b = pair >> 2;
+    const int g = pair & 3;
+    const int j_raw = tile * kTileWaves + wave;
+    const bool has_tok = j_raw < q_len;  // wavefront-uniform
+    const int j = min(j_raw, q_len - 1);
+    const int bq = b * q_len + j;
+    bf16x8 qb[4];
+    {
+        const uint16_t* qp = q + ((int64_t)bq * kQHeads + kGroupHeads * g + n) * kDim + 32 * c;
+#pragma unroll
+        for (int m = 0; m < 4; m++) qb[m] = *reinterpret_cast<const bf16x8*>(qp + 8 * m);
+    }
+    const int T = clamp_ctx(ctx_lens[b], max_blocks);
+    const int p = T - q_len + j;
+    int id = -1;
+    if (has_tok && lane < kTopk) id = block_ids[((int64_t)bq * kKvHeads + g) * kTopk + lane];
+    // the token's usable blocks (as attention_kernel: in the table and holding a visible key)
+    const int myid = (id >= 0 && id < max_blocks && id * kBlock <= p) ? id : -1;
+
+    // the union: a bitmap over the row's blocks, then its set bits in ascending order
+    const int nwords = (max_blocks + 63) >> 6;
+    for (int i = threadIdx.x; i < nwords; i += kTileWaves * 64) bitmap[i] = 0;
+    __syncthreads();
+    if (myid >= 0) atomicOr(reinterpret_cast<unsigned long long*>(&bitmap[myid >> 6]), 1ull << (myid & 63));
+    __syncthreads();
+    if (wave == 0) {
+        int base = 0;
+        for (int w0 = 0; w0 < nwords; w0 += 64) {
+            const int wi = w0 + lane;
+            uint64_t bits = wi < nwords ? bitmap[wi] : 0ull;
+            const int cnt = popc64(bits);
+            int incl = cnt;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int y = __shfl_up(incl, d, 64);
+                if (lane >= d) incl += y;
+            }
+            int at = base + incl - cnt;
+            while (bits) {
+                ulist[at++] = wi * 64 + __builtin_ctzll(bits);
+                bits &= bits - 1;
+            }
+            base += __shfl(incl, 63, 64);
+        }
+        if (lane == 0) ucount = base;  // at most 8 x 16 blocks
+    }
+    __syncthreads();
+    const int nu = ucount;
+    if ((int)threadIdx.x < nu) {
+        const int pg = block_table[(int64_t)b * max_blocks + ulist[threadIdx.x]];
+        upage[threadIdx.x] = (pg >= 0 && pg < num_pages) ? pg : -1;
+    }
+    __syncthreads();
+    // the union in registers (entry u in lane u % 64 of register u / 64), read before any page
+    // load is in flight
+    const int uid0 = lane < nu ? ulist[lane] : -1, uid1 = 64 + lane < nu ? ulist[64 + lane] : -1;
+    const int upg0 = lane < nu ? upage[lane] : -1, upg1 = 64 + lane < nu ? upage[64 + lane] : -1;
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+
+    const uint8_t* kg = k_pool + (int64_t)g * kHeadPageBytes;
+    const uint8_t* vg = v_pool + (int64_t)g * kHeadPageBytes;
+    constexpr int64_t kPageStride = (int64_t)kKvHeads * kHeadPageBytes;
+    // block u's 18 page pieces (1 KB each: 9 of K, then 9 of V) spread over the wavefronts
+    auto issue = [&](int u) {
+        const int pg = __builtin_amdgcn_readlane(u < 64 ? upg0 : upg1, u & 63);
+        if (pg < 0) return;
+        uint8_t* dst = pages[u & 1];
+        for (int i = wave; i < 18; i += kTileWaves) {
+            const uint8_t* src = i < 9 ? kg + pg * kPageStride + i * 1024
+                                       : vg + pg * kPageStride + (i - 9) * 1024;
+            __builtin_amdgcn_global_load_lds(src + lane * 16, (lds_void*)(dst + i * 1024), 16, 0,
+                                             kPagePolicy);
+        }
+    };
+    if (nu > 0) issue(0);
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 o[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f16x8 qh[4];
+    float q_unscale;
+    const bool f16 = __all(query_to_f16(qb, qh, q_unscale));
+    u32x4 qop[4];
+#pragma unroll
+    for (int m = 0; m < 4; m++)
+        qop[m] = f16 ? __builtin_bit_cast(u32x4, qh[m]) : __builtin_bit_cast(u32x4, qb[m]);
+    if (scale_log2 < 0.f) {
+#pragma unroll
+        for (int m = 0; m < 4; m++) qop[m] ^= 0x80008000u;
+    }
+    const float logit_scale = fabsf(scale_log2) * (f16 ? q_unscale : 1.0f);
+    const uint8_t* stab = vscale[wave];
+
+    for (int u = 0; u < nu; u++) {
+        // block u has arrived for every wavefront, and every wavefront is done with block u - 1,
+        // whose buffer the next loads overwrite
+        __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wavefront's pieces of block u
+        __syncthreads();
+        if (u + 1 < nu) issue(u + 1);
+        const int bid = __builtin_amdgcn_readlane(u < 64 ? uid0 : uid1, u & 63);
+        const int pg = __builtin_amdgcn_readlane(u < 64 ? upg0 : upg1, u & 63);
+        if (pg >= 0 && __ballot(myid == bid) != 0ull) {
+            if (f16)
+                attend_block<true, false, true>(pages[u & 1], lane, c, bid * kBlock, p, qop,
+                                                logit_scale, m_run, l_run, o, stab);
+            else
+                attend_block<false, false, true>(pages[u & 1], lane, c, bid * kBlock, p, qop,
+                                                 logit_scale, m_run, l_run, o, stab);
+        }
+    }
+    if (!has_tok) return;
+    // lane (n, c) holds o[dt][i] = out(head n, dim 16 dt + 4 c + i); l_run is the head's sum
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    uint16_t* op = out + ((int64_t)bq * kQHeads + kGroupHeads * g + n) * kDim + 4 * c;
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++) {
+        const uint32_t lo = (uint32_t)bf16_bits_rne(o[dt][0] * inv) | ((uint32_t)bf16_bits_rne(o[dt][1] * inv) << 16);
+        const uint32_t hi = (uint32_t)bf16_bits_rne(o[dt][2] * inv) | ((uint32_t)bf16_bits_rne(o[dt][3] * inv) << 16);
+        *reinterpret_cast<uint2*>(op + 16 * dt) = uint2{lo, hi};
+    }
+}
+
 }  // namespace
 
 int attn_num_splits(int batch, int q_len) {
@@ -574,6 +743,19 @@ hipError_t launch_attention_t(const uint8_t* k_pool, const uint8_t* v_pool, int6
     const int pairs = batch * kKvHeads;
     const int pair_slots = 8 * ((pairs + 7) / 8);
     const float scale_log2 = softmax_scale * 1.4426950408889634f;
+    if (ns == 1 && q_len >= kTileMinQ && max_blocks <= kUnionMaxBlocks) {
+        // many tokens per sequence: token tiles over the union of their blocks (the selection,
+        // if asked for, as its own launch first)
+        if constexpr (SELECT) {
+            const hipError_t err = launch_topk(scores, ctx_lens, batch, max_blocks, q_len, ids, stream);
+            if (err != hipSuccess) return err;
+        }
+        const int tiles = (q_len + kTileWaves - 1) / kTileWaves;
+        hipLaunchKernelGGL(attention_tile_kernel, dim3(pair_slots * tiles), dim3(kTileWaves * 64),
+                           0, stream, k_pool, v_pool, num_pages, block_table, ctx_lens, batch,
+                           max_blocks, q_len, q, ids, scale_log2, out);
+        return hipGetLastError();
+    }
     const dim3 grid(pair_slots * q_len * ns), block(kWaves * 64);
     int32_t* counters = nullptr;
     float* partials = nullptr;
