@@ -150,21 +150,65 @@ __device__ __forceinline__ void lds_write32(uint32_t a, const u32x4& v0, const u
                  : "memory");
 }
 
+// A block's logits sv (lane (n, c): head n, tokens tok0 + 32c + 4s + i, unscaled) -> tokens past
+// the query position masked, the online-softmax state (m_run, l_run, o) updated, and the
+// block's probabilities in fp16 (pt, the B operand of O^T += V^T P^T).
+__device__ __forceinline__ void softmax_block(f32x4 (&sv)[8], int c, int tok0, int p,
+                                              float logit_scale, float& m_run, float& l_run,
+                                              f32x4 (&o)[8], f16x4 (&pt)[8]) {
+    // tokens past the query position: only in the block that holds it, a scalar branch that
+    // every other block skips (kept a branch: folded into the selects, the wavefront-uniform
+    // condition cost a vector-to-scalar round trip per value)
+    if (tok0 + kBlock - 1 > p) {
+        asm volatile("");
+        const int last = p - tok0 - 32 * c;  // values 4s + i <= last are visible
+#pragma unroll
+        for (int s = 0; s < 8; s++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                // all ones past the position: vector bit operations, no lane-mask updates
+                uint32_t past = (uint32_t)((last - (4 * s + i)) >> 31);
+                asm("" : "+v"(past));
+                sv[s][i] = __uint_as_float((__float_as_uint(sv[s][i]) & ~past) | (0xFF800000u & past));
+            }
+    }
+    float mb = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < 8; s++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) mb = fmaxf(mb, sv[s][i]);
+    mb = max_over_c(mb) * logit_scale;  // finite (token tok0 <= p is valid); scaling keeps order
+    const float m_new = (mb > m_run + kTau) ? mb : m_run;  // m_run = -inf -> m_new = mb
+    if (__any(m_new != m_run)) {
+        const float alpha = fast_exp2(m_run - m_new);  // 0 when m_run = -inf (o, l are 0)
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; dt++) o[dt] *= alpha;
+        m_run = m_new;
+    }
+    float ls = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; s++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float e = fast_exp2(fmaf(sv[s][i], logit_scale, -m_new));
+            ls += e;
+            pt[s][i] = (_Float16)e;
+        }
+    l_run += sum_over_c(ls);
+}
+
 // One block of one wavefront: logits, online-softmax update, output accumulation. The K page
 // is in LDS on entry; the V page may still be arriving (NEXT: the next block's 18 loads were
-// issued after it) and is waited for only before its first read. RESIDENT: both pages have
-// arrived and other loads may be in flight (no wait, and only explicit LDS reads). The V
-// scales are converted into the 2 KB table at `stab` (the K codes' area unless the page buffer
-// is shared with other wavefronts).
-template <bool F16, bool NEXT, bool RESIDENT = false>
+// issued after it) and is waited for only before its first read. (The softmax step is written
+// out here rather than calling softmax_block: the shared helper changed this kernel's register
+// allocation, 48 more accumulator-register reads per block.)
+template <bool F16, bool NEXT>
 __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c, int tok0, int p,
                                              const u32x4 (&qop)[4], float logit_scale,
-                                             float& m_run, float& l_run, f32x4 (&o)[8],
-                                             const uint8_t* stab = nullptr) {
-    constexpr bool kAsmReads = NEXT || RESIDENT;
+                                             float& m_run, float& l_run, f32x4 (&o)[8]) {
     const uint32_t kbase = (uint32_t)(uintptr_t)buf;
     const uint32_t vbase = kbase + kHeadPageBytes;
-    const uint32_t sbase = stab ? (uint32_t)(uintptr_t)stab : kbase;
     // ---- logits S^T (log2 domain)
     u32x4 kc[8], ksc;
     lds_read16x9(kc, ksc, kbase + lane * 16, kbase + kCodeBytes + lane * 16);
@@ -229,12 +273,8 @@ __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c
     l_run += sum_over_c(ls);
 
     // ---- the V page's 9 loads (issued after the K page's 9) complete here
-    if constexpr (RESIDENT) {
-    } else if constexpr (NEXT) {
-        asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-    } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
+    if constexpr (NEXT) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     // ---- the block's 1,024 V scales as fp16, [group][token], written over the K codes (read
     // into registers above and not needed again): lane l converts the 16 scale bytes of group
     // l / 8, tokens 16 (l % 8) .. +15. Each lane then reads its scales ready for the packed
@@ -243,7 +283,7 @@ __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c
         // (with no later page in flight, ordinary LDS reads: the compiler overlaps them with
         // the work before their use; otherwise statements that wait for their own reads only)
         u32x4 raw;
-        if constexpr (kAsmReads) raw = lds_read16(vbase + kCodeBytes + lane * 16);
+        if constexpr (NEXT) raw = lds_read16(vbase + kCodeBytes + lane * 16);
         else raw = *reinterpret_cast<const u32x4*>(buf + kHeadPageBytes + kCodeBytes + lane * 16);
         u32x4 h0, h1;
 #pragma unroll
@@ -253,7 +293,7 @@ __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c
             h1[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[i + 2], 1.0f, false));
             h1[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[i + 2], 1.0f, true));
         }
-        lds_write32(sbase + lane * 32, h0, h1);
+        lds_write32(kbase + lane * 32, h0, h1);
     }
 
     // ---- O^T += V^T P^T, one 16-dim tile (= one scale group) at a time
@@ -262,8 +302,8 @@ __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c
         const int d = 16 * dt + (lane & 15);
         // codes of tokens 32c..32c+31 and their fp16 scales of group dt
         u32x4 vc, sc[4];
-        if constexpr (kAsmReads) {
-            lds_read16x5(vc, sc, vbase + d * 64 + 16 * c, sbase + dt * 256 + 64 * c);
+        if constexpr (NEXT) {
+            lds_read16x5(vc, sc, vbase + d * 64 + 16 * c, kbase + dt * 256 + 64 * c);
         } else {
             vc = *reinterpret_cast<const u32x4*>(buf + kHeadPageBytes + d * 64 + 16 * c);
 #pragma unroll
@@ -556,8 +596,117 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
 // consecutive query tokens of one pair, one token per wavefront. The union of their selected
 // blocks streams once, in ascending block order, through two LDS buffers that the workgroup
 // shares (the next block's loads spread over the wavefronts and in flight while the current
-// block is used), and each wavefront attends, with attend_block, exactly the blocks its own token
-// selected, keeping its token's whole softmax state: no partials and no merge.
+// block is used). The workgroup dequantizes each block once into fp16 operand tables (one K
+// slab and one V dim tile per wavefront), and each wavefront attends exactly the blocks its own
+// token selected, from the tables, keeping its token's whole softmax state: no partials and no
+// merge.
+// Four 16-byte LDS reads at a, a + 1 KB, a + 2 KB, a + 3 KB, issued and waited for together.
+__device__ __forceinline__ void lds_read16x4(u32x4 (&v)[4], uint32_t a) {
+    asm volatile("ds_read_b128 %0, %4\n\t"
+                 "ds_read_b128 %1, %4 offset:1024\n\t"
+                 "ds_read_b128 %2, %4 offset:2048\n\t"
+                 "ds_read_b128 %3, %4 offset:3072\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]) : "v"(a) : "memory");
+}
+// Four 16-byte LDS writes at a, a + 1 KB, a + 2 KB, a + 3 KB (waited for by the caller).
+__device__ __forceinline__ void lds_write16x4(uint32_t a, const u32x4 (&v)[4]) {
+    asm volatile("ds_write_b128 %0, %1\n\t"
+                 "ds_write_b128 %0, %2 offset:1024\n\t"
+                 "ds_write_b128 %0, %3 offset:2048\n\t"
+                 "ds_write_b128 %0, %4 offset:3072"
+                 :: "v"(a), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3])
+                 : "memory");
+}
+
+// The fp16 operand tables of one block, made once per workgroup from its NVFP4 K and V pages
+// (in LDS at `page`): wavefront w dequantizes K slab w and V dims 16w .. 16w + 15, exactly.
+//   kf + 4096 s + 1024 m + 16 l : lane l's A operand of S^T step (slab s, k-step m), f16x8
+//   vf + 4096 dt + 1024 h + 16 l: lane l's A operands of O^T steps (dim tile dt, token slabs
+//                                 2h and 2h + 1), two f16x4
+__device__ __forceinline__ void dequant_tables(const uint8_t* page, uint8_t* kf, uint8_t* vf,
+                                               int wave, int lane) {
+    const int n = lane & 15, c = lane >> 4;
+    const uint32_t pbase = (uint32_t)(uintptr_t)page;
+    u32x4 kc[4], vr[4];
+    // K codes of slab `wave` and the token row's scale bytes; V codes of dim 16 wave + n (tokens
+    // 32c .. 32c + 31) and the raw scales of group `wave` for those tokens
+    asm volatile("ds_read_b128 %0, %4\n\t"
+                 "ds_read_b128 %1, %5\n\t"
+                 "ds_read_b128 %2, %6\n\t"
+                 "ds_read_b128 %3, %6 offset:16\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(kc[0]), "=&v"(kc[1]), "=&v"(vr[0]), "=&v"(vr[1])
+                 : "v"(pbase + 1024 * wave + 16 * lane), "v"(pbase + kCodeBytes + 16 * lane),
+                   "v"(pbase + kHeadPageBytes + kCodeBytes + 128 * wave + 32 * c)
+                 : "memory");
+    const u32x4 code = kc[0], ksc = kc[1];
+    const u32x4 vc = lds_read16(pbase + kHeadPageBytes + (16 * wave + n) * 64 + 16 * c);
+    f16x2 s0, s1;
+    if (wave & 1) e4m3_pair_f16<true>(ksc[wave >> 1], s0, s1);
+    else e4m3_pair_f16<false>(ksc[wave >> 1], s0, s1);
+    u32x4 ko[4];
+#pragma unroll
+    for (int m = 0; m < 4; m++) ko[m] = __builtin_bit_cast(u32x4, dequant8_f16(code[m], m < 2 ? s0 : s1));
+    lds_write16x4((uint32_t)(uintptr_t)(kf + 4096 * wave + 16 * lane), ko);
+    // V: tokens 32c + 4s .. +3 of slab s take the scale pairs (4s, 4s + 1), (4s + 2, 4s + 3)
+    const uint32_t raw[8] = {vr[0][0], vr[0][1], vr[0][2], vr[0][3], vr[1][0], vr[1][1], vr[1][2], vr[1][3]};
+    u32x4 vo[4];
+#pragma unroll
+    for (int h = 0; h < 4; h++) {
+        f16x4 a[2];
+#pragma unroll
+        for (int e = 0; e < 2; e++) {
+            const int sl = 2 * h + e;
+            const uint32_t s01 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[sl], 1.0f, false));
+            const uint32_t s23 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[sl], 1.0f, true));
+            a[e] = e ? dequant4_f16_scaled<2>(vc[h], s01, s23) : dequant4_f16_scaled<0>(vc[h], s01, s23);
+        }
+        const uint2 lo = __builtin_bit_cast(uint2, a[0]), hi = __builtin_bit_cast(uint2, a[1]);
+        vo[h] = u32x4{lo.x, lo.y, hi.x, hi.y};
+    }
+    lds_write16x4((uint32_t)(uintptr_t)(vf + 4096 * wave + 16 * lane), vo);
+}
+
+// One block of one wavefront from the fp16 tables: logits, online-softmax update, output
+// accumulation (the arithmetic of attend_block, with the dequantization done beforehand).
+template <bool F16>
+__device__ __forceinline__ void attend_tables(const uint8_t* kf, const uint8_t* vf, int lane,
+                                              int c, int tok0, int p, const u32x4 (&qop)[4],
+                                              float logit_scale, float& m_run, float& l_run,
+                                              f32x4 (&o)[8]) {
+    f32x4 sv[8];
+#pragma unroll
+    for (int s = 0; s < 8; s++) {
+        u32x4 a[4];
+        lds_read16x4(a, (uint32_t)(uintptr_t)(kf + 4096 * s + 16 * lane));
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 4; m++) {
+            if constexpr (F16)
+                acc = mfma_f16_k32(__builtin_bit_cast(f16x8, a[m]), __builtin_bit_cast(f16x8, qop[m]), acc);
+            else
+                acc = mfma_bf16_k32(f16x8_to_bf16x8(__builtin_bit_cast(f16x8, a[m])),
+                                    __builtin_bit_cast(bf16x8, qop[m]), acc);
+        }
+        sv[s] = acc;
+    }
+    f16x4 pt[8];
+    softmax_block(sv, c, tok0, p, logit_scale, m_run, l_run, o, pt);
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++) {
+        u32x4 a[4];
+        lds_read16x4(a, (uint32_t)(uintptr_t)(vf + 4096 * dt + 16 * lane));
+#pragma unroll
+        for (int h = 0; h < 4; h++) {
+            const f16x4 a0 = __builtin_bit_cast(f16x4, uint2{a[h][0], a[h][1]});
+            const f16x4 a1 = __builtin_bit_cast(f16x4, uint2{a[h][2], a[h][3]});
+            o[dt] = mfma_f16_k16(a0, pt[2 * h], o[dt]);
+            o[dt] = mfma_f16_k16(a1, pt[2 * h + 1], o[dt]);
+        }
+    }
+}
+
 constexpr int kTileWaves = 8;
 constexpr int kUnionMaxBlocks = 8192;  // rows of up to this many blocks (the union's bitmap)
 constexpr int kTileMinQ = 8;           // from this many query tokens per sequence (and no split)
@@ -568,7 +717,8 @@ __global__ __launch_bounds__(kTileWaves * 64) void attention_tile_kernel(
     int max_blocks, int q_len, const uint16_t* __restrict__ q,
     const int32_t* __restrict__ block_ids, float scale_log2, uint16_t* __restrict__ out) {
     __shared__ __attribute__((aligned(16))) uint8_t pages[2][kBlockBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t vscale[kTileWaves][2048];
+    __shared__ __attribute__((aligned(16))) uint8_t kf[8 * 4096];  // fp16 operand tables
+    __shared__ __attribute__((aligned(16))) uint8_t vf[8 * 4096];
     __shared__ uint64_t bitmap[kUnionMaxBlocks / 64];
     __shared__ int ulist[kTileWaves * kTopk];
     __shared__ int upage[kTileWaves * kTopk];
@@ -677,23 +827,25 @@ __global__ __launch_bounds__(kTileWaves * 64) void attention_tile_kernel(
         for (int m = 0; m < 4; m++) qop[m] ^= 0x80008000u;
     }
     const float logit_scale = fabsf(scale_log2) * (f16 ? q_unscale : 1.0f);
-    const uint8_t* stab = vscale[wave];
 
     for (int u = 0; u < nu; u++) {
-        // block u has arrived for every wavefront, and every wavefront is done with block u - 1,
-        // whose buffer the next loads overwrite
+        // block u has arrived for every wavefront, and every wavefront is done with block u - 1
+        // (its page buffer, which the next loads overwrite, and the fp16 tables)
         __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wavefront's pieces of block u
         __syncthreads();
         if (u + 1 < nu) issue(u + 1);
         const int bid = __builtin_amdgcn_readlane(u < 64 ? uid0 : uid1, u & 63);
         const int pg = __builtin_amdgcn_readlane(u < 64 ? upg0 : upg1, u & 63);
-        if (pg >= 0 && __ballot(myid == bid) != 0ull) {
-            if (f16)
-                attend_block<true, false, true>(pages[u & 1], lane, c, bid * kBlock, p, qop,
-                                                logit_scale, m_run, l_run, o, stab);
-            else
-                attend_block<false, false, true>(pages[u & 1], lane, c, bid * kBlock, p, qop,
-                                                 logit_scale, m_run, l_run, o, stab);
+        if (pg < 0) continue;  // (uniform: no wavefront reaches the barrier below)
+        dequant_tables(pages[u & 1], kf, vf, wave, lane);
+        // the tables are complete for every wavefront (LDS only: the next block's loads stay
+        // in flight)
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (__ballot(myid == bid) != 0ull) {
+            if (f16) attend_tables<true>(kf, vf, lane, c, bid * kBlock, p, qop, logit_scale, m_run, l_run, o);
+            else attend_tables<false>(kf, vf, lane, c, bid * kBlock, p, qop, logit_scale, m_run, l_run, o);
         }
     }
     if (!has_tok) return;
