@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix-core peak, TFLOP/s
 COPY_BYTES = 512 << 20  # calibration copy for the HBM traffic counters (read and written once)
 METRIC = "MSA decode query-tokens/s per layer at 128K ctx; achieved HBM GB/s vs peak"
 
@@ -44,6 +45,7 @@ def parse():
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--kernel-reps", type=int, default=20, help="graph replays per kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-workload side measurement")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle CPU time")
     ap.add_argument("--only", default="", help="profiling aid: run a calibration copy of "
                     f"{COPY_BYTES >> 20} MiB, then only this kernel in a loop "
@@ -360,9 +362,90 @@ def main():
                              "algorithmic_bytes": attn_bytes},
     }
 
+    if not args.no_prefill:
+        del steps, caches, kgraphs, alt_graphs, graphs, layers_graph
+        torch.cuda.empty_cache()
+        result["prefill"] = prefill_side(args)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def prefill_side(args):
+    """The chunked-prefill workload (2 sequences, 65,536 cached tokens + a 2,048-token chunk):
+    the same calls with q_len = 2,048, which take the score-GEMM indexer and the token-tile
+    attention. Reported beside the decode metric, against the bf16 matrix-core peak."""
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_nvfp4_amd as msa
+    import msa_inputs as mi
+
+    dev = "cuda"
+    w = mi.full_workload(5)
+    B, q = w.batch, w.q_len
+    cache = msa.Cache.allocate(w.num_pages, dev)
+    for b in range(B):
+        T = w.ctx_lens[b]
+        for t0 in range(0, T - q, 1 << 15):
+            t1 = min(T - q, t0 + (1 << 15))
+            slots = torch.from_numpy(w.slots(b, t0, t1)).to(dev)
+            msa.msa_kv_insert_nvfp4(cache, slots, w.kv_rows("k", b, t0, t1, dev),
+                                    w.kv_rows("v", b, t0, t1, dev), w.ik_rows(b, t0, t1, dev))
+    batch = msa.Batch(torch.from_numpy(w.block_table).to(dev),
+                      torch.tensor(w.ctx_lens, dtype=torch.int32, device=dev), q)
+    toks = [(b, w.ctx_lens[b] - q, w.ctx_lens[b]) for b in range(B)]
+    new_k = torch.cat([w.kv_rows("k", b, t0, t1, dev) for b, t0, t1 in toks])
+    new_v = torch.cat([w.kv_rows("v", b, t0, t1, dev) for b, t0, t1 in toks])
+    new_ik = torch.cat([w.ik_rows(b, t0, t1, dev) for b, t0, t1 in toks])
+    q_idx, qq = w.q_idx.to(dev), w.q.to(dev)
+    st = msa.DecodeStep(cache, batch, dev, mode="separate")
+    scale = msa.default_softmax_scale()
+    calls = {
+        "insert_indexer": lambda: msa.msa_insert_indexer_score(cache, batch, new_k, new_v, new_ik,
+                                                               q_idx, st.block_scores),
+        "indexer": lambda: msa.msa_indexer_score(cache, batch, q_idx, st.block_scores),
+        "topk": lambda: msa.msa_block_topk(st.block_scores, batch, 16, st.block_ids),
+        "attention": lambda: msa.msa_sparse_attn_decode(cache, batch, qq, st.block_ids, scale,
+                                                        st.out, st.workspace),
+    }
+    for name in ("insert_indexer", "topk", "attention"):
+        calls[name]()
+    torch.cuda.synchronize()
+    us = {}
+    for name, fn in calls.items():
+        series = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(5):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            series.append(e0.elapsed_time(e1) * 1e3 / 5)
+        us[name] = round(sorted(series)[1], 2)
+    # algorithmic flops: the indexer multiplies every (row, visible key) pair once (2 x 128 per
+    # pair, 4 rows per query token); the attention does QK and PV for 16 heads over every
+    # visible key of the selected blocks (2 x 2 x 128 x 16 per (token, group, key))
+    ctx = np.array(w.ctx_lens, dtype=np.int64)
+    pos = (ctx[:, None] - q + np.arange(q)[None, :])  # [B][q]
+    idx_flops = float(2 * 128 * 4 * (pos + 1).sum())
+    ids = st.block_ids.cpu().numpy().reshape(B, q, 4, 16).astype(np.int64)
+    vis = np.clip(pos[:, :, None, None] + 1 - 128 * ids, 0, 128) * (ids >= 0)
+    att_flops = float(2 * 2 * 128 * 16 * vis.sum())
+    peak = PEAK_BF16_TFLOPS
+    return {
+        "workload": "prefill: batch 2 x (65,536 cached + 2,048 chunk tokens), q_len 2,048, "
+                    "64 q heads / 4 kv heads / head_dim 128, NVFP4 caches, top-16",
+        "us": us,
+        "step_us": round(us["insert_indexer"] + us["topk"] + us["attention"], 2),
+        "indexer": {"bound": "mfma", "tflops": round(idx_flops / us["indexer"] / 1e6, 1),
+                    "peak": peak, "frac": round(idx_flops / us["indexer"] / 1e6 / peak, 4),
+                    "flops": idx_flops},
+        "attention": {"bound": "mfma", "tflops": round(att_flops / us["attention"] / 1e6, 1),
+                      "peak": peak, "frac": round(att_flops / us["attention"] / 1e6 / peak, 4),
+                      "flops": att_flops},
+    }
 
 
 def cpu_baseline(w, target_seconds):

@@ -78,6 +78,88 @@ __global__ __launch_bounds__(576) void insert_kernel(uint8_t* __restrict__ k_poo
     quantize_store_vector(x, dst, t, column_layout, lane);
 }
 
+// Inserts of several new tokens per sequence at positions T - q_len .. T - 1 (prefill chunks,
+// long drafts): one workgroup per run of 8 aligned positions of one sequence, the tokens that
+// share every 32-bit word of the V pages' column layout (element e's word holds the nibbles of
+// tokens 8k .. 8k + 7). The wavefronts take the head vectors as in insert_kernel, each for every
+// new token of its run; a V word is written with a plain store when all 8 of its tokens are new,
+// and with one atomic and/or pair otherwise (the two ends of the new range), instead of an
+// atomic pair per nibble and token.
+constexpr int kRun = 8;
+
+__global__ __launch_bounds__(576) void insert_run_kernel(
+    uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool, uint8_t* __restrict__ ik_pool,
+    int64_t num_pages, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ ctx_lens, int max_blocks, int q_len, int runs_per_seq,
+    const float* __restrict__ k, const float* __restrict__ v, const float* __restrict__ ik) {
+    const int b = blockIdx.x / runs_per_seq;
+    const int r = blockIdx.x - b * runs_per_seq;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const float* base;
+    int stride;  // floats from one token's vector of this head to the next token's
+    if (wave < 4) {
+        if (!k) return;
+        base = k + wave * kDim;
+        stride = kKvHeads * kDim;
+    } else if (wave < 8) {
+        if (!v) return;
+        base = v + (wave - 4) * kDim;
+        stride = kKvHeads * kDim;
+    } else {
+        if (!ik) return;
+        base = ik;
+        stride = kDim;
+    }
+    const int T = clamp_ctx(ctx_lens[b], max_blocks);
+    const int p_first = T - q_len;                 // position of new token 0 (may be < 0)
+    const int pos0 = ((p_first >> 3) + r) * kRun;  // this run's first position (floor of p / 8)
+    const int lo = max(pos0, max(p_first, 0));
+    const int hi = min(pos0 + kRun, T);
+    if (lo >= hi) return;  // (then pos0 >= 0: a multiple of 8 above -8)
+    const int64_t page = block_table[(int64_t)b * max_blocks + (pos0 >> 7)];
+    if (page < 0 || page >= num_pages) return;
+    const int nt = hi - lo;
+    // every token's values requested before any is quantized
+    f32x2 x[kRun];
+#pragma unroll
+    for (int i = 0; i < kRun; i++) {
+        const int j = min(lo + i, hi - 1) - p_first;  // new-token index (past nt: a repeat)
+        x[i] = *reinterpret_cast<const f32x2*>(base + ((int64_t)b * q_len + j) * stride + 2 * lane);
+    }
+    uint8_t* dst;
+    if (wave < 4) dst = k_pool + (page * kKvHeads + wave) * kHeadPageBytes;
+    else if (wave < 8) dst = v_pool + (page * kKvHeads + (wave - 4)) * kHeadPageBytes;
+    else dst = ik_pool + page * kHeadPageBytes;
+    if (wave < 4 || wave == 8) {
+        for (int i = 0; i < nt; i++) quantize_store_vector(x[i], dst, (lo + i) & 127, false, lane);
+        return;
+    }
+    // V: the lane's elements e = 2 lane and e + 1, nibble 4 (p % 8) of their words
+    uint32_t w0 = 0, w1 = 0, mask = 0;
+    for (int i = 0; i < nt; i++) {
+        uint32_t byte, scale;
+        quantize_pair(x[i][0], x[i][1], byte, scale);
+        const int t = (lo + i) & 127;
+        const int sh = 4 * (t & 7);
+        w0 |= (byte & 15u) << sh;
+        w1 |= (byte >> 4) << sh;
+        mask |= 15u << sh;
+        if ((lane & 7) == 0) dst[col_scale_offset(t, lane >> 3)] = (uint8_t)scale;
+    }
+    uint32_t* p0 = reinterpret_cast<uint32_t*>(dst + col_code_byte(2 * lane, pos0 & 127));
+    uint32_t* p1 = reinterpret_cast<uint32_t*>(dst + col_code_byte(2 * lane + 1, pos0 & 127));
+    if (nt == kRun) {
+        *p0 = w0;
+        *p1 = w1;
+    } else {
+        atomicAnd(p0, ~mask);
+        atomicOr(p0, w0);
+        atomicAnd(p1, ~mask);
+        atomicOr(p1, w1);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_insert(uint8_t* k_pool, uint8_t* v_pool, uint8_t* ik_pool, int64_t num_pages,
@@ -93,6 +175,14 @@ hipError_t launch_insert_at_positions(uint8_t* k_pool, uint8_t* v_pool, uint8_t*
                                       const int32_t* ctx_lens, int batch, int max_blocks,
                                       int q_len, const float* k, const float* v, const float* ik,
                                       hipStream_t stream) {
+    if (q_len >= 2) {
+        // a range of q_len positions meets at most q_len / 8 + 2 aligned runs of 8
+        const int runs = q_len / kRun + 2;
+        hipLaunchKernelGGL(insert_run_kernel, dim3(batch * runs), dim3(576), 0, stream, k_pool,
+                           v_pool, ik_pool, num_pages, block_table, ctx_lens, max_blocks, q_len,
+                           runs, k, v, ik);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(insert_kernel<true>, dim3(batch * q_len), dim3(576), 0, stream, k_pool,
                        v_pool, ik_pool, num_pages, nullptr, block_table, ctx_lens, max_blocks,
                        q_len, k, v, ik);
