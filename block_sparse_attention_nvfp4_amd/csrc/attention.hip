@@ -697,12 +697,14 @@ __device__ __forceinline__ void attend_tables(const uint8_t* kf, const uint8_t* 
     for (int dt = 0; dt < 8; dt++) {
         u32x4 a[4];
         lds_read16x4(a, (uint32_t)(uintptr_t)(vf + 4096 * dt + 16 * lane));
+        // one 32-token step per slab pair: lane (n, c) holds dim 16 dt + n of tokens
+        // 32c + 8h .. +7 in A and the same tokens' probabilities of head n in B (any order of
+        // the reduction index works when both operands agree)
 #pragma unroll
         for (int h = 0; h < 4; h++) {
-            const f16x4 a0 = __builtin_bit_cast(f16x4, uint2{a[h][0], a[h][1]});
-            const f16x4 a1 = __builtin_bit_cast(f16x4, uint2{a[h][2], a[h][3]});
-            o[dt] = mfma_f16_k16(a0, pt[2 * h], o[dt]);
-            o[dt] = mfma_f16_k16(a1, pt[2 * h + 1], o[dt]);
+            const f16x8 pp = {pt[2 * h][0], pt[2 * h][1], pt[2 * h][2], pt[2 * h][3],
+                              pt[2 * h + 1][0], pt[2 * h + 1][1], pt[2 * h + 1][2], pt[2 * h + 1][3]};
+            o[dt] = mfma_f16_k32(__builtin_bit_cast(f16x8, a[h]), pp, o[dt]);
         }
     }
 }
