@@ -311,12 +311,15 @@ __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c
                 sc[w] = *reinterpret_cast<const u32x4*>(buf + dt * 256 + 64 * c + 16 * w);
         }
 #pragma unroll
-        for (int s = 0; s < 8; s++) {
-            // tokens 32c + 4s .. +3: scale pairs (4s, 4s+1) and (4s+2, 4s+3)
-            const uint32_t s01 = sc[s >> 1][(s & 1) * 2], s23 = sc[s >> 1][(s & 1) * 2 + 1];
-            const f16x4 a = (s & 1) ? dequant4_f16_scaled<2>(vc[s >> 1], s01, s23)
-                                    : dequant4_f16_scaled<0>(vc[s >> 1], s01, s23);
-            o[dt] = mfma_f16_k16(a, pt[s], o[dt]);
+        for (int h = 0; h < 4; h++) {
+            // tokens 32c + 8h .. +7 (slabs 2h, 2h + 1) in one 32-token step: scale pairs
+            // (8h, 8h+1), (8h+2, 8h+3) and (8h+4, 8h+5), (8h+6, 8h+7)
+            const f16x4 a0 = dequant4_f16_scaled<0>(vc[h], sc[h][0], sc[h][1]);
+            const f16x4 a1 = dequant4_f16_scaled<2>(vc[h], sc[h][2], sc[h][3]);
+            const f16x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+            const f16x8 pp = {pt[2 * h][0], pt[2 * h][1], pt[2 * h][2], pt[2 * h][3],
+                              pt[2 * h + 1][0], pt[2 * h + 1][1], pt[2 * h + 1][2], pt[2 * h + 1][3]};
+            o[dt] = mfma_f16_k32(a, pp, o[dt]);
         }
     }
 }
