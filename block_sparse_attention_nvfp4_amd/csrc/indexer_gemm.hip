@@ -8,16 +8,18 @@
 // block is masked and every query token has its own position (a chunk of q tokens scores
 // 4 q rows against the whole visible context, a GEMM).
 //
-// Work split: a workgroup of eight wavefronts takes eight consecutive blocks of one sequence
-// and a range of up to 512 of its query rows. Each wavefront loads its block's page once into
-// registers and dequantizes it exactly to bf16 (E2M1 x E4M3 products have at most 6 significant
-// bits), as the A operand of 16x16x32 bf16 matrix-core steps: 128 tokens x 128 dims in 128
-// registers. The query rows stream through LDS in stages of 64 rows, loaded by direct
-// global->LDS copies already in operand order and shared by the eight wavefronts (double
-// buffered: the next stage loads while this one is multiplied). Per 16-row tile a wavefront
-// runs 32 matrix-core steps (8 token slabs x 4 dimension steps, fp32 accumulate), takes each
-// row's max over its visible tokens and keeps it in LDS; the workgroup writes its rows' eight
-// block scores at the end as contiguous 32-byte runs.
+// Work split: a workgroup of four wavefronts takes four consecutive blocks of one sequence
+// and a range of up to 512 of its query rows; two workgroups share a CU, so one's page load
+// and dequantization overlap the other's matrix-core work (one workgroup of eight wavefronts
+// per CU measured 12% slower). Each wavefront loads its block's page once into registers and
+// dequantizes it exactly to bf16 (E2M1 x E4M3 products have at most 6 significant bits), as
+// the A operand of 16x16x32 bf16 matrix-core steps: 128 tokens x 128 dims in 128 registers.
+// The query rows stream through LDS in stages of 64 rows, loaded by direct global->LDS copies
+// already in operand order and shared by the workgroup's wavefronts (double buffered: the next
+// stage loads while this one is multiplied). Per 16-row tile a wavefront runs 32 matrix-core
+// steps (8 token slabs x 4 dimension steps, fp32 accumulate), takes each row's max over its
+// visible tokens and keeps it in LDS; the workgroup writes its rows' four block scores at the
+// end as contiguous 16-byte runs.
 // Query rows are bf16 and used as they are: every product is exact in fp32 and the sums are
 // fp32, as in the decode indexer's bf16 path.
 #include "device_common.hpp"
@@ -26,7 +28,7 @@
 namespace msa {
 namespace {
 
-constexpr int kGWaves = 8;                   // one block per wavefront
+constexpr int kGWaves = 4;                   // one block per wavefront
 constexpr int kStageRows = 64;               // query rows per LDS stage
 constexpr int kTileBytes = 16 * kDim * 2;    // one 16-row tile of bf16 query rows: 4 KB
 constexpr int kMaxRowsPerWg = 512;
@@ -46,7 +48,7 @@ __device__ __forceinline__ void read_tile(u32x4 (&v)[4], const uint8_t* tile, in
                  : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]) : "v"(a) : "memory");
 }
 
-__global__ __launch_bounds__(kGWaves * 64) void indexer_gemm_kernel(
+__global__ __launch_bounds__(kGWaves * 64, 2) void indexer_gemm_kernel(
     const uint8_t* __restrict__ ik_pool, int64_t num_pages, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ ctx_lens, int max_blocks, int q_len, int rows_per_wg,
     const uint16_t* __restrict__ q_idx, float* __restrict__ scores) {
@@ -63,13 +65,14 @@ __global__ __launch_bounds__(kGWaves * 64) void indexer_gemm_kernel(
     const int T = clamp_ctx(ctx_lens[b], max_blocks);
     const uint8_t* qseq = reinterpret_cast<const uint8_t*>(q_idx + (int64_t)b * rows * kDim);
 
-    // stage loads: 16 copies of 1 KB (tile tt, piece m), two per wavefront; lane (n, c) of
-    // copy (tt, m) brings bytes 64 c + 16 m .. +15 of row 16 tt + n (past the range: its last
-    // row, never written out)
+    // stage loads: copies of 1 KB (tile tt, piece m), kCopies per wavefront; lane
+    // (n, c) of copy (tt, m) brings bytes 64 c + 16 m .. +15 of row 16 tt + n (past the range:
+    // its last row, never written out)
+    constexpr int kCopies = kStageRows / 4 / kGWaves;  // 4 copies per 16-row tile
     auto load_stage = [&](int r0, int buf) {
 #pragma unroll
-        for (int k = 0; k < 2; k++) {
-            const int i = 2 * wave + k, tt = i >> 2, m = i & 3;
+        for (int k = 0; k < kCopies; k++) {
+            const int i = kCopies * wave + k, tt = i >> 2, m = i & 3;
             const int r = min(r0 + 16 * tt + n, r_end - 1);
             __builtin_amdgcn_global_load_lds(qseq + (int64_t)r * (kDim * 2) + 64 * c + 16 * m,
                                              (lds_void*)(&stage[buf][tt][1024 * m]), 16, 0, 0);
@@ -147,11 +150,11 @@ __global__ __launch_bounds__(kGWaves * 64) void indexer_gemm_kernel(
         }
     }
     __syncthreads();
-    // row rl's eight block scores are 32 contiguous bytes
+    // row rl's block scores are kGWaves contiguous floats
     const int nr = r_end - r_begin;
     float* out = scores + ((int64_t)b * rows + r_begin) * max_blocks + blockIdx.x * kGWaves;
     for (int i = threadIdx.x; i < nr * kGWaves; i += kGWaves * 64) {
-        const int rl = i >> 3, kb = i & 7;
+        const int rl = i / kGWaves, kb = i % kGWaves;
         if (blockIdx.x * kGWaves + kb < max_blocks) out[(int64_t)rl * max_blocks + kb] = best_of[rl][kb];
     }
 }
