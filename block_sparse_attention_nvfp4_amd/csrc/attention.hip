@@ -595,14 +595,14 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
 // ---------------------------------------------------------------- token tiles
 // Batches with many query tokens per sequence (prefill chunks): the tokens of one (sequence,
 // group) pair select mostly the same blocks, and reading each block once per token makes the
-// page traffic, not the arithmetic, the bound. A workgroup of eight wavefronts takes eight
-// consecutive query tokens of one pair, one token per wavefront. The union of their selected
+// page traffic, not the arithmetic, the bound. A workgroup of eight wavefronts takes 16
+// consecutive query tokens of one pair, two per wavefront. The union of their selected
 // blocks streams once, in ascending block order, through two LDS buffers that the workgroup
 // shares (the next block's loads spread over the wavefronts and in flight while the current
 // block is used). The workgroup dequantizes each block once into fp16 operand tables (one K
-// slab and one V dim tile per wavefront), and each wavefront attends exactly the blocks its own
-// token selected, from the tables, keeping its token's whole softmax state: no partials and no
-// merge.
+// slab and one V dim tile per wavefront), and each wavefront attends exactly the blocks its
+// tokens selected, from the tables (each table read serving both tokens), keeping its tokens'
+// whole softmax state: no partials and no merge.
 // Four 16-byte LDS reads at a, a + 1 KB, a + 2 KB, a + 3 KB, issued and waited for together.
 __device__ __forceinline__ void lds_read16x4(u32x4 (&v)[4], uint32_t a) {
     asm volatile("ds_read_b128 %0, %4\n\t"
@@ -671,31 +671,42 @@ __device__ __forceinline__ void dequant_tables(const uint8_t* page, uint8_t* kf,
     lds_write16x4((uint32_t)(uintptr_t)(vf + 4096 * wave + 16 * lane), vo);
 }
 
-// One block of one wavefront from the fp16 tables: logits, online-softmax update, output
-// accumulation (the arithmetic of attend_block, with the dequantization done beforehand).
-template <bool F16>
+// One block of one wavefront from the fp16 tables, for the TPW tokens the wavefront holds
+// (those with sel[t]): logits, online-softmax update, output accumulation (the arithmetic of
+// attend_block, with the dequantization done beforehand). Each 16-byte table read feeds the
+// matrix-core steps of every selecting token.
+template <bool F16, int TPW>
 __device__ __forceinline__ void attend_tables(const uint8_t* kf, const uint8_t* vf, int lane,
-                                              int c, int tok0, int p, const u32x4 (&qop)[4],
-                                              float logit_scale, float& m_run, float& l_run,
-                                              f32x4 (&o)[8]) {
-    f32x4 sv[8];
+                                              int c, int tok0, const int (&p)[TPW],
+                                              const bool (&sel)[TPW], const u32x4 (&qop)[TPW][4],
+                                              const float (&logit_scale)[TPW],
+                                              float (&m_run)[TPW], float (&l_run)[TPW],
+                                              f32x4 (&o)[TPW][8]) {
+    f32x4 sv[TPW][8];
 #pragma unroll
     for (int s = 0; s < 8; s++) {
         u32x4 a[4];
         lds_read16x4(a, (uint32_t)(uintptr_t)(kf + 4096 * s + 16 * lane));
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int m = 0; m < 4; m++) {
-            if constexpr (F16)
-                acc = mfma_f16_k32(__builtin_bit_cast(f16x8, a[m]), __builtin_bit_cast(f16x8, qop[m]), acc);
-            else
-                acc = mfma_bf16_k32(f16x8_to_bf16x8(__builtin_bit_cast(f16x8, a[m])),
-                                    __builtin_bit_cast(bf16x8, qop[m]), acc);
+        for (int t = 0; t < TPW; t++) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (sel[t]) {
+#pragma unroll
+                for (int m = 0; m < 4; m++) {
+                    if constexpr (F16)
+                        acc = mfma_f16_k32(__builtin_bit_cast(f16x8, a[m]), __builtin_bit_cast(f16x8, qop[t][m]), acc);
+                    else
+                        acc = mfma_bf16_k32(f16x8_to_bf16x8(__builtin_bit_cast(f16x8, a[m])),
+                                            __builtin_bit_cast(bf16x8, qop[t][m]), acc);
+                }
+            }
+            sv[t][s] = acc;
         }
-        sv[s] = acc;
     }
-    f16x4 pt[8];
-    softmax_block(sv, c, tok0, p, logit_scale, m_run, l_run, o, pt);
+    f16x4 pt[TPW][8];
+#pragma unroll
+    for (int t = 0; t < TPW; t++)
+        if (sel[t]) softmax_block(sv[t], c, tok0, p[t], logit_scale[t], m_run[t], l_run[t], o[t], pt[t]);
 #pragma unroll
     for (int dt = 0; dt < 8; dt++) {
         u32x4 a[4];
@@ -704,15 +715,22 @@ __device__ __forceinline__ void attend_tables(const uint8_t* kf, const uint8_t* 
         // 32c + 8h .. +7 in A and the same tokens' probabilities of head n in B (any order of
         // the reduction index works when both operands agree)
 #pragma unroll
-        for (int h = 0; h < 4; h++) {
-            const f16x8 pp = {pt[2 * h][0], pt[2 * h][1], pt[2 * h][2], pt[2 * h][3],
-                              pt[2 * h + 1][0], pt[2 * h + 1][1], pt[2 * h + 1][2], pt[2 * h + 1][3]};
-            o[dt] = mfma_f16_k32(__builtin_bit_cast(f16x8, a[h]), pp, o[dt]);
+        for (int t = 0; t < TPW; t++) {
+            if (!sel[t]) continue;
+#pragma unroll
+            for (int h = 0; h < 4; h++) {
+                const f16x8 pp = {pt[t][2 * h][0], pt[t][2 * h][1], pt[t][2 * h][2], pt[t][2 * h][3],
+                                  pt[t][2 * h + 1][0], pt[t][2 * h + 1][1], pt[t][2 * h + 1][2],
+                                  pt[t][2 * h + 1][3]};
+                o[t][dt] = mfma_f16_k32(__builtin_bit_cast(f16x8, a[h]), pp, o[t][dt]);
+            }
         }
     }
 }
 
 constexpr int kTileWaves = 8;
+constexpr int kTileTpw = 2;                         // tokens per wavefront
+constexpr int kTileTokens = kTileWaves * kTileTpw;  // tokens per workgroup
 constexpr int kUnionMaxBlocks = 8192;  // rows of up to this many blocks (the union's bitmap)
 constexpr int kTileMinQ = 8;           // from this many query tokens per sequence (and no split)
 
@@ -725,8 +743,9 @@ __global__ __launch_bounds__(kTileWaves * 64) void attention_tile_kernel(
     __shared__ __attribute__((aligned(16))) uint8_t kf[8 * 4096];  // fp16 operand tables
     __shared__ __attribute__((aligned(16))) uint8_t vf[8 * 4096];
     __shared__ uint64_t bitmap[kUnionMaxBlocks / 64];
-    __shared__ int ulist[kTileWaves * kTopk];
-    __shared__ int upage[kTileWaves * kTopk];
+    __shared__ uint64_t tokmap[kTileWaves][kTileTpw][kUnionMaxBlocks / 64];  // per token
+    __shared__ int ulist[kTileTokens * kTopk];
+    __shared__ int upage[kTileTokens * kTopk];
     __shared__ int ucount;
 
     const int lane = threadIdx.x & 63;
@@ -734,35 +753,49 @@ __global__ __launch_bounds__(kTileWaves * 64) void attention_tile_kernel(
     const int n = lane & 15;
     const int c = lane >> 4;
     // XCD-aware work mapping as in attention_kernel: pair = (b, g) -> XCD pair % 8
-    const int tiles = (q_len + kTileWaves - 1) / kTileWaves;
+    const int tiles = (q_len + kTileTokens - 1) / kTileTokens;
     const int local = blockIdx.x >> 3;
     const int pair = (local / tiles) * 8 + (blockIdx.x & 7);
     if (pair >= batch * kKvHeads) return;  // the whole workgroup
     const int tile = local - (local / tiles) * tiles;
     const int b = pair >> 2;
     const int g = pair & 3;
-    const int j_raw = tile * kTileWaves + wave;
-    const bool has_tok = j_raw < q_len;  // wavefront-uniform
-    const int j = min(j_raw, q_len - 1);
-    const int bq = b * q_len + j;
-    bf16x8 qb[4];
-    {
-        const uint16_t* qp = q + ((int64_t)bq * kQHeads + kGroupHeads * g + n) * kDim + 32 * c;
-#pragma unroll
-        for (int m = 0; m < 4; m++) qb[m] = *reinterpret_cast<const bf16x8*>(qp + 8 * m);
-    }
+    // this wavefront's tokens j[t] = tile * 16 + 2 wave + t
+    bool has_tok[kTileTpw];
+    int bq[kTileTpw], p[kTileTpw];
+    bf16x8 qb[kTileTpw][4];
     const int T = clamp_ctx(ctx_lens[b], max_blocks);
-    const int p = T - q_len + j;
-    int id = -1;
-    if (has_tok && lane < kTopk) id = block_ids[((int64_t)bq * kKvHeads + g) * kTopk + lane];
-    // the token's usable blocks (as attention_kernel: in the table and holding a visible key)
-    const int myid = (id >= 0 && id < max_blocks && id * kBlock <= p) ? id : -1;
+#pragma unroll
+    for (int t = 0; t < kTileTpw; t++) {
+        const int j_raw = tile * kTileTokens + kTileTpw * wave + t;
+        has_tok[t] = j_raw < q_len;  // wavefront-uniform
+        const int j = min(j_raw, q_len - 1);
+        bq[t] = b * q_len + j;
+        p[t] = T - q_len + j;
+        const uint16_t* qp = q + ((int64_t)bq[t] * kQHeads + kGroupHeads * g + n) * kDim + 32 * c;
+#pragma unroll
+        for (int m = 0; m < 4; m++) qb[t][m] = *reinterpret_cast<const bf16x8*>(qp + 8 * m);
+    }
+    // lanes 16 t .. 16 t + 15 hold token t's ids
+    int myid = -1;
+    if (lane < kTileTpw * kTopk) {
+        const int t = lane >> 4;
+        const int id = has_tok[t] ? block_ids[((int64_t)bq[t] * kKvHeads + g) * kTopk + (lane & 15)] : -1;
+        // the token's usable blocks (as attention_kernel: in the table and holding a visible key)
+        myid = (id >= 0 && id < max_blocks && id * kBlock <= p[t]) ? id : -1;
+    }
 
     // the union: a bitmap over the row's blocks, then its set bits in ascending order
+    // (and each token's own bitmap, which the block loop reads instead of keeping the ids)
     const int nwords = (max_blocks + 63) >> 6;
     for (int i = threadIdx.x; i < nwords; i += kTileWaves * 64) bitmap[i] = 0;
+    for (int i = lane; i < kTileTpw * nwords; i += 64) tokmap[wave][i / nwords][i % nwords] = 0;
     __syncthreads();
-    if (myid >= 0) atomicOr(reinterpret_cast<unsigned long long*>(&bitmap[myid >> 6]), 1ull << (myid & 63));
+    if (myid >= 0) {
+        atomicOr(reinterpret_cast<unsigned long long*>(&bitmap[myid >> 6]), 1ull << (myid & 63));
+        atomicOr(reinterpret_cast<unsigned long long*>(&tokmap[wave][lane >> 4][myid >> 6]),
+                 1ull << (myid & 63));
+    }
     __syncthreads();
     if (wave == 0) {
         int base = 0;
@@ -783,7 +816,7 @@ __global__ __launch_bounds__(kTileWaves * 64) void attention_tile_kernel(
             }
             base += __shfl(incl, 63, 64);
         }
-        if (lane == 0) ucount = base;  // at most 8 x 16 blocks
+        if (lane == 0) ucount = base;  // at most 16 x 16 blocks
     }
     __syncthreads();
     const int nu = ucount;
@@ -792,19 +825,29 @@ __global__ __launch_bounds__(kTileWaves * 64) void attention_tile_kernel(
         upage[threadIdx.x] = (pg >= 0 && pg < num_pages) ? pg : -1;
     }
     __syncthreads();
-    // the union in registers (entry u in lane u % 64 of register u / 64), read before any page
-    // load is in flight
-    const int uid0 = lane < nu ? ulist[lane] : -1, uid1 = 64 + lane < nu ? ulist[64 + lane] : -1;
-    const int upg0 = lane < nu ? upage[lane] : -1, upg1 = 64 + lane < nu ? upage[64 + lane] : -1;
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0);
+    // union entry u (block id, page) read back from LDS as a broadcast, by an explicit read
+    // waited for on its own (page loads are in flight from here on)
+    auto entry = [&](int u, int& id_u, int& page_u) {
+        int a, bb;
+        asm volatile("ds_read_b32 %0, %2\n\t"
+                     "ds_read_b32 %1, %3\n\t"
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(a), "=&v"(bb)
+                     : "v"((uint32_t)(uintptr_t)&ulist[u]), "v"((uint32_t)(uintptr_t)&upage[u])
+                     : "memory");
+        id_u = __builtin_amdgcn_readfirstlane(a);
+        page_u = __builtin_amdgcn_readfirstlane(bb);
+    };
 
     const uint8_t* kg = k_pool + (int64_t)g * kHeadPageBytes;
     const uint8_t* vg = v_pool + (int64_t)g * kHeadPageBytes;
     constexpr int64_t kPageStride = (int64_t)kKvHeads * kHeadPageBytes;
     // block u's 18 page pieces (1 KB each: 9 of K, then 9 of V) spread over the wavefronts
     auto issue = [&](int u) {
-        const int pg = __builtin_amdgcn_readlane(u < 64 ? upg0 : upg1, u & 63);
+        int bid_u, pg;
+        entry(u, bid_u, pg);
         if (pg < 0) return;
         uint8_t* dst = pages[u & 1];
         for (int i = wave; i < 18; i += kTileWaves) {
@@ -816,22 +859,28 @@ __global__ __launch_bounds__(kTileWaves * 64) void attention_tile_kernel(
     };
     if (nu > 0) issue(0);
 
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x4 o[8];
+    float m_run[kTileTpw], l_run[kTileTpw], logit_scale[kTileTpw];
+    f32x4 o[kTileTpw][8];
+    u32x4 qop[kTileTpw][4];
+    f16x8 qh[kTileTpw][4];
+    float q_unscale[kTileTpw];
+    bool exact = true;
 #pragma unroll
-    for (int dt = 0; dt < 8; dt++) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    f16x8 qh[4];
-    float q_unscale;
-    const bool f16 = __all(query_to_f16(qb, qh, q_unscale));
-    u32x4 qop[4];
+    for (int t = 0; t < kTileTpw; t++) exact = query_to_f16(qb[t], qh[t], q_unscale[t]) && exact;
+    const bool f16 = __all(exact);  // both tokens in fp16, or both in bf16
 #pragma unroll
-    for (int m = 0; m < 4; m++)
-        qop[m] = f16 ? __builtin_bit_cast(u32x4, qh[m]) : __builtin_bit_cast(u32x4, qb[m]);
-    if (scale_log2 < 0.f) {
+    for (int t = 0; t < kTileTpw; t++) {
+        m_run[t] = -INFINITY;
+        l_run[t] = 0.f;
 #pragma unroll
-        for (int m = 0; m < 4; m++) qop[m] ^= 0x80008000u;
+        for (int dt = 0; dt < 8; dt++) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 4; m++) {
+            qop[t][m] = f16 ? __builtin_bit_cast(u32x4, qh[t][m]) : __builtin_bit_cast(u32x4, qb[t][m]);
+            if (scale_log2 < 0.f) qop[t][m] ^= 0x80008000u;
+        }
+        logit_scale[t] = fabsf(scale_log2) * (f16 ? q_unscale[t] : 1.0f);
     }
-    const float logit_scale = fabsf(scale_log2) * (f16 ? q_unscale : 1.0f);
 
     for (int u = 0; u < nu; u++) {
         // block u has arrived for every wavefront, and every wavefront is done with block u - 1
@@ -839,29 +888,49 @@ __global__ __launch_bounds__(kTileWaves * 64) void attention_tile_kernel(
         __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wavefront's pieces of block u
         __syncthreads();
         if (u + 1 < nu) issue(u + 1);
-        const int bid = __builtin_amdgcn_readlane(u < 64 ? uid0 : uid1, u & 63);
-        const int pg = __builtin_amdgcn_readlane(u < 64 ? upg0 : upg1, u & 63);
+        int bid, pg;
+        entry(u, bid, pg);
         if (pg < 0) continue;  // (uniform: no wavefront reaches the barrier below)
-        dequant_tables(pages[u & 1], kf, vf, wave, lane);
+        // the lane's LDS addresses are recomputed in every iteration, not held across the loop
+        // (registers are the limit here: held, they were spilled to scratch)
+        int lane_i = lane;
+        asm volatile("" : "+v"(lane_i));
+        dequant_tables(pages[u & 1], kf, vf, wave, lane_i);
         // the tables are complete for every wavefront (LDS only: the next block's loads stay
         // in flight)
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (__ballot(myid == bid) != 0ull) {
-            if (f16) attend_tables<true>(kf, vf, lane, c, bid * kBlock, p, qop, logit_scale, m_run, l_run, o);
-            else attend_tables<false>(kf, vf, lane, c, bid * kBlock, p, qop, logit_scale, m_run, l_run, o);
+        // did this wavefront's tokens select block bid (their bitmaps' words, LDS broadcasts)
+        static_assert(kTileTpw == 2, "two token bitmaps read below");
+        uint64_t w0, w1;
+        asm volatile("ds_read_b64 %0, %2\n\t"
+                     "ds_read_b64 %1, %3\n\t"
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(w0), "=&v"(w1)
+                     : "v"((uint32_t)(uintptr_t)&tokmap[wave][0][bid >> 6]),
+                       "v"((uint32_t)(uintptr_t)&tokmap[wave][1][bid >> 6])
+                     : "memory");
+        bool sel[kTileTpw];
+        sel[0] = __builtin_amdgcn_readfirstlane((uint32_t)(w0 >> (bid & 63)) & 1u) != 0u;
+        sel[1] = __builtin_amdgcn_readfirstlane((uint32_t)(w1 >> (bid & 63)) & 1u) != 0u;
+        if (sel[0] || sel[1]) {
+            if (f16) attend_tables<true, kTileTpw>(kf, vf, lane_i, c, bid * kBlock, p, sel, qop, logit_scale, m_run, l_run, o);
+            else attend_tables<false, kTileTpw>(kf, vf, lane_i, c, bid * kBlock, p, sel, qop, logit_scale, m_run, l_run, o);
         }
     }
-    if (!has_tok) return;
-    // lane (n, c) holds o[dt][i] = out(head n, dim 16 dt + 4 c + i); l_run is the head's sum
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    uint16_t* op = out + ((int64_t)bq * kQHeads + kGroupHeads * g + n) * kDim + 4 * c;
 #pragma unroll
-    for (int dt = 0; dt < 8; dt++) {
-        const uint32_t lo = (uint32_t)bf16_bits_rne(o[dt][0] * inv) | ((uint32_t)bf16_bits_rne(o[dt][1] * inv) << 16);
-        const uint32_t hi = (uint32_t)bf16_bits_rne(o[dt][2] * inv) | ((uint32_t)bf16_bits_rne(o[dt][3] * inv) << 16);
-        *reinterpret_cast<uint2*>(op + 16 * dt) = uint2{lo, hi};
+    for (int t = 0; t < kTileTpw; t++) {
+        if (!has_tok[t]) continue;
+        // lane (n, c) holds o[dt][i] = out(head n, dim 16 dt + 4 c + i); l_run is the head's sum
+        const float inv = l_run[t] > 0.f ? 1.f / l_run[t] : 0.f;
+        uint16_t* op = out + ((int64_t)bq[t] * kQHeads + kGroupHeads * g + n) * kDim + 4 * c;
+#pragma unroll
+        for (int dt = 0; dt < 8; dt++) {
+            const uint32_t lo = (uint32_t)bf16_bits_rne(o[t][dt][0] * inv) | ((uint32_t)bf16_bits_rne(o[t][dt][1] * inv) << 16);
+            const uint32_t hi = (uint32_t)bf16_bits_rne(o[t][dt][2] * inv) | ((uint32_t)bf16_bits_rne(o[t][dt][3] * inv) << 16);
+            *reinterpret_cast<uint2*>(op + 16 * dt) = uint2{lo, hi};
+        }
     }
 }
 
@@ -907,7 +976,7 @@ hipError_t launch_attention_t(const uint8_t* k_pool, const uint8_t* v_pool, int6
             const hipError_t err = launch_topk(scores, ctx_lens, batch, max_blocks, q_len, ids, stream);
             if (err != hipSuccess) return err;
         }
-        const int tiles = (q_len + kTileWaves - 1) / kTileWaves;
+        const int tiles = (q_len + kTileTokens - 1) / kTileTokens;
         hipLaunchKernelGGL(attention_tile_kernel, dim3(pair_slots * tiles), dim3(kTileWaves * 64),
                            0, stream, k_pool, v_pool, num_pages, block_table, ctx_lens, batch,
                            max_blocks, q_len, q, ids, scale_log2, out);
