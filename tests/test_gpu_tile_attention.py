@@ -2,10 +2,10 @@
 takes the token-tile kernel (8+ query tokens per sequence, 1,024+ rows), against the oracle
 (needs an MI355X).
 
-The selections here are random rather than from the indexer, so the eight tokens of a tile
-share few blocks and their union reaches past 64 entries (the union's second register). They
-also include blocks past a token's position (skipped for that token, still in the union for
-the others), -1 padding, and rows left with no block at all (output 0). "vLLM day-0 support
+The selections here are random rather than from the indexer, so the 16 tokens of a tile
+(two per wavefront) share few blocks and their union reaches past 128 entries. They also
+include blocks past a token's position (skipped for that token, still in the union for the
+others), -1 padding, and rows left with no block at all (output 0). "vLLM day-0 support
 for MiniMax-M3.1-Flash", section "MSA primer": exact attention over the selected blocks only;
 "MiniMax M3 on vLLM", section "Prefill execution": per-token causal positions.
 """
@@ -55,10 +55,10 @@ def test_tile_attention_random_selections():
     import block_sparse_attention_nvfp4_amd as msa
     rng = np.random.default_rng(11)
     ids = _random_ids(w, rng)
-    # union sizes of the tiles of 8 tokens (this test's point: past 64 entries for some)
-    unions = [len({int(x) for x in ids[b * Q_LEN + t0:b * Q_LEN + t0 + 8, gg].ravel() if x >= 0})
-              for b in range(w.batch) for t0 in range(0, Q_LEN, 8) for gg in range(4)]
-    assert max(unions) > 64
+    # union sizes of the tiles of 16 tokens (this test's point: past 128 entries for some)
+    unions = [len({int(x) for x in ids[b * Q_LEN + t0:b * Q_LEN + t0 + 16, gg].ravel() if x >= 0})
+              for b in range(w.batch) for t0 in range(0, Q_LEN, 16) for gg in range(4)]
+    assert max(unions) > 128
     ids_dev = torch.from_numpy(ids).cuda()
     out = torch.full_like(g.step.out, 7.0)
     msa.msa_sparse_attn_decode(g.cache, g.batch, g.q, ids_dev, msa.default_softmax_scale(), out,
