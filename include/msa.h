@@ -243,7 +243,10 @@ int msa_sparse_attn_decode(const msa_cache_t *cache, const msa_batch_t *batch, c
  * each attention workgroup selects its row's blocks itself from the scores, so the selection
  * needs no launch of its own and its ids no round trip through memory ("MiniMax M3 on vLLM",
  * section "Decode indexer score kernel": the top-k boundary stays close to the scores). Rows of
- * more than 1,025 blocks (max_blocks > 1025) run the two steps as two launches.
+ * more than 1,025 blocks (max_blocks > 1025) run the two steps as two launches, and so do
+ * batches of 8 or more query tokens per sequence with at least 1,024 (token, group) rows
+ * (prefill chunks), whose attention streams the union of 16 tokens' blocks once per
+ * workgroup instead of once per token.
  * Arguments and workspace as for the two calls. Errors: as for the two calls.
  */
 int msa_select_attn_decode(const msa_cache_t *cache, const msa_batch_t *batch,
@@ -256,7 +259,10 @@ int msa_select_attn_decode(const msa_cache_t *cache, const msa_batch_t *batch,
  *   msa_kv_insert_nvfp4(cache, slots, k, v, ik, batch * q_len)
  *   msa_indexer_score(cache, batch, q_idx, block_scores)
  * with the slots of the new tokens' own positions (as msa_decode_step below states), the same
- * results bit for bit, cache bytes included. Arguments as for msa_decode_step. Errors:
+ * results bit for bit, cache bytes included. With more than 8 query tokens per sequence the
+ * two run as two launches (the indexer then as a score GEMM, each page dequantized once for
+ * all the sequence's query rows; msa_indexer_score does the same from 9 tokens on).
+ * Arguments as for msa_decode_step. Errors:
  * MSA_ERR_INVALID_ARG (a NULL pointer, sizes < 1).
  */
 int msa_insert_indexer_score(const msa_cache_t *cache, const msa_batch_t *batch, const float *k,
