@@ -142,6 +142,25 @@ def select_sequence(scores: np.ndarray, T: int, q: int, topk: int = TOPK):
     return ids, margins
 
 
+def block_topk_variant(scores_row: np.ndarray, n_eligible: int, topk: int, init_blocks: int,
+                       local_blocks: int) -> np.ndarray:
+    """Selection with the window knobs of "MiniMax M3 on vLLM", section "MSA mechanism" (the
+    config exposes init blocks and local blocks; the current recipe uses 0 and 1): of the
+    eligible blocks 0..n-1, the first `init_blocks` and the last `local_blocks` are always kept,
+    and the rest of the `topk` places go to the best other blocks by (score descending, index
+    ascending); a forced block is never counted twice. With at most `topk` eligible blocks all
+    are kept. Ids ascending, padded with -1 to `topk`."""
+    n = int(n_eligible)
+    if n <= topk:
+        kept = list(range(max(n, 0)))
+    else:
+        forced = set(range(min(init_blocks, n))) | set(range(max(n - local_blocks, 0), n))
+        rest = [i for i in range(n) if i not in forced]
+        best = sorted(rest, key=lambda i: (-float(scores_row[i]), i))[:topk - len(forced)]
+        kept = sorted(forced | set(best))
+    return np.array(kept + [-1] * (topk - len(kept)), np.int32)
+
+
 def dcp_local_topk(scores_row: np.ndarray, n_eligible: int, shard_blocks, topk: int = TOPK):
     """One shard's local candidates of a row ("vLLM day-0 support for MiniMax-M3.1-Flash",
     section "Indexer NVFP4 DCP": each device ranks only its own share of the pages and keeps

@@ -72,6 +72,57 @@ def test_margin_definition():
     assert margin == pytest.approx((6.0 - 5.0) / 6.0)
 
 
+@pytest.mark.parametrize("seed", range(20))
+def test_variant_default_knobs_are_the_recipe(seed):
+    # init_blocks = 0, local_blocks = 1 is the current recipe: the C oracle's selection, which
+    # the full-sort pins above fix independently
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(1, 200))
+    scores = np.round(rng.standard_normal(n), 1)
+    want, _ = oracle.block_topk(scores, n)
+    assert list(oracle.block_topk_variant(scores, n, 16, 0, 1)) == list(want)
+
+
+def test_variant_by_hand():
+    # n = 12 eligible blocks, scores rising with the id except two planted highs
+    scores = np.arange(12, dtype=np.float64)
+    scores[[2, 5]] = [100.0, 50.0]
+    # topk 6, init 2, local 2: forced {0, 1, 10, 11}, then the best two others: 2 (100), 5 (50)
+    assert list(oracle.block_topk_variant(scores, 12, 6, 2, 2)) == [0, 1, 2, 5, 10, 11]
+    # no forced block at all: the plain top 4 (ties none): 2, 5, 11, 10
+    assert list(oracle.block_topk_variant(scores, 12, 4, 0, 0)) == [2, 5, 10, 11]
+    # init and local overlap when they reach each other: topk 5, init 3, local 2 -> 0, 1, 2,
+    # 10, 11 and nothing else
+    assert list(oracle.block_topk_variant(scores, 12, 5, 3, 2)) == [0, 1, 2, 10, 11]
+    # at most topk eligible blocks: all of them, padded
+    assert list(oracle.block_topk_variant(scores, 3, 4, 1, 1)) == [0, 1, 2, -1]
+    # ties at the boundary go to the lower id
+    flat = np.zeros(10)
+    assert list(oracle.block_topk_variant(flat, 10, 5, 1, 1)) == [0, 1, 2, 3, 9]
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_variant_brute_force_invariants(seed):
+    rng = np.random.default_rng(200 + seed)
+    n = int(rng.integers(1, 120))
+    topk = int(rng.choice([4, 8, 16, 32]))
+    init = int(rng.integers(0, topk // 2 + 1))
+    local = int(rng.integers(0, topk - init + 1))
+    scores = rng.integers(-3, 4, n).astype(np.float64)  # many ties
+    got = [int(x) for x in oracle.block_topk_variant(scores, n, topk, init, local) if x >= 0]
+    assert got == sorted(set(got)) and len(got) == min(n, topk)
+    if n <= topk:
+        return
+    forced = set(range(min(init, n))) | set(range(max(n - local, 0), n))
+    assert forced <= set(got)
+    free_kept = [i for i in got if i not in forced]
+    dropped = [i for i in range(n) if i not in got]
+    # every free kept block ranks before every dropped one by (score desc, id asc)
+    for i in free_kept:
+        for d in dropped:
+            assert (scores[i], -i) > (scores[d], -d)
+
+
 def _shard_splits(rng, n, shards):
     """Contiguous slices with random cuts, and the round-robin split (block i on shard i % N)."""
     cuts = np.sort(rng.choice(np.arange(1, n), size=shards - 1, replace=False))
