@@ -7,6 +7,7 @@ HIP stream into the C calls, with the same names:
     msa_kv_insert_nvfp4(cache, slots, k, v, ik)
     msa_indexer_score(cache, batch, q_idx, block_scores)
     msa_block_topk(block_scores, batch, topk, block_ids)
+    msa_block_topk_window(block_scores, batch, topk, init_blocks, local_blocks, block_ids)
     msa_block_topk_local(shard_scores, block_begin, block_stride, batch, topk, cand_ids,
                          cand_keys)           # one shard's local lists (context parallelism)
     msa_block_topk_merge(cand_ids, cand_keys, batch, topk, block_ids)   # merge of all shards
@@ -47,7 +48,7 @@ MSA_ERR_WORKSPACE = -3
 MSA_ERR_HIP = -4
 
 EXPORTED = ("msa_page_bytes", "msa_kv_insert_nvfp4", "msa_indexer_score", "msa_block_topk",
-            "msa_block_topk_local", "msa_block_topk_merge",
+            "msa_block_topk_window", "msa_block_topk_local", "msa_block_topk_merge",
             "msa_sparse_attn_workspace_bytes", "msa_sparse_attn_decode", "msa_select_attn_decode",
             "msa_insert_indexer_score", "msa_decode_step", "msa_last_error", "msa_version")
 
@@ -82,6 +83,8 @@ def _load() -> ctypes.CDLL:
     L.msa_indexer_score.argtypes = [ctypes.POINTER(_Cache), ctypes.POINTER(_Batch), vp, vp, vp]
     L.msa_block_topk.restype = ctypes.c_int
     L.msa_block_topk.argtypes = [vp, ctypes.POINTER(_Batch), i32, vp, vp]
+    L.msa_block_topk_window.restype = ctypes.c_int
+    L.msa_block_topk_window.argtypes = [vp, ctypes.POINTER(_Batch), i32, i32, i32, vp, vp]
     L.msa_block_topk_local.restype = ctypes.c_int
     L.msa_block_topk_local.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(_Batch), i32, vp, vp,
                                        vp]
@@ -211,6 +214,18 @@ def msa_block_topk(block_scores: torch.Tensor, batch: Batch, topk: int, block_id
     _check(lib.msa_block_topk(_ptr(block_scores, torch.float32, "block_scores"),
                               ctypes.byref(batch._c), int(topk),
                               _ptr(block_ids, torch.int32, "block_ids"), _stream(stream)))
+
+
+def msa_block_topk_window(block_scores: torch.Tensor, batch: Batch, topk: int, init_blocks: int,
+                          local_blocks: int, block_ids: torch.Tensor, stream=None) -> None:
+    if tuple(block_scores.shape) != (batch.rows, KV_HEADS, batch.max_blocks):
+        raise ValueError("block_scores: expected [batch*q_len][4][max_blocks]")
+    if tuple(block_ids.shape) != (batch.rows, KV_HEADS, int(topk)):
+        raise ValueError("block_ids: expected [batch*q_len][4][topk]")
+    _check(lib.msa_block_topk_window(_ptr(block_scores, torch.float32, "block_scores"),
+                                     ctypes.byref(batch._c), int(topk), int(init_blocks),
+                                     int(local_blocks), _ptr(block_ids, torch.int32, "block_ids"),
+                                     _stream(stream)))
 
 
 def msa_block_topk_local(shard_scores: torch.Tensor, block_begin: int, block_stride: int,

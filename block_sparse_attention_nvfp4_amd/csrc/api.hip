@@ -118,6 +118,29 @@ int msa_block_topk(const float* block_scores, const msa_batch_t* batch, int32_t 
                       fn);
 }
 
+int msa_block_topk_window(const float* block_scores, const msa_batch_t* batch, int32_t topk,
+                          int32_t init_blocks, int32_t local_blocks, int32_t* block_ids,
+                          void* stream) {
+    static const char* fn = "msa_block_topk_window";
+    int rc = check_batch(batch, fn);
+    if (rc) return rc;
+    if (!block_scores || !block_ids)
+        return fail(MSA_ERR_INVALID_ARG, "%s: block_scores or block_ids is NULL", fn);
+    if (topk < 1 || topk > 64)
+        return fail(MSA_ERR_UNSUPPORTED, "%s: topk=%d (1..64 are built)", fn, topk);
+    if (init_blocks < 0 || local_blocks < 0 || init_blocks + local_blocks > topk)
+        return fail(MSA_ERR_INVALID_ARG,
+                    "%s: init_blocks=%d and local_blocks=%d must be >= 0 and sum to at most topk=%d",
+                    fn, init_blocks, local_blocks, topk);
+    if (batch->max_blocks > msa::kWindowMaxBlocks)
+        return fail(MSA_ERR_UNSUPPORTED, "%s: max_blocks=%d (up to %d are built)", fn,
+                    batch->max_blocks, msa::kWindowMaxBlocks);
+    return hip_status(msa::launch_topk_window(block_scores, batch->ctx_lens, batch->batch,
+                                              batch->max_blocks, batch->q_len, topk, init_blocks,
+                                              local_blocks, block_ids, (hipStream_t)stream),
+                      fn);
+}
+
 int msa_block_topk_local(const float* shard_scores, int32_t ld, int32_t block_begin,
                          int32_t block_stride, int32_t n_cols, const msa_batch_t* batch,
                          int32_t topk, int32_t* cand_ids, uint32_t* cand_keys, void* stream) {

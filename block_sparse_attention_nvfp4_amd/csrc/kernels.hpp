@@ -45,6 +45,12 @@ hipError_t launch_insert_indexer(uint8_t* k_pool, uint8_t* v_pool, uint8_t* ik_p
 hipError_t launch_topk(const float* scores, const int32_t* ctx_lens, int batch, int max_blocks,
                        int q_len, int32_t* ids, hipStream_t stream);
 
+// Selection with the window knobs (rows of up to kWindowMaxBlocks blocks).
+constexpr int kWindowMaxBlocks = 64 * 64;
+hipError_t launch_topk_window(const float* scores, const int32_t* ctx_lens, int batch,
+                              int max_blocks, int q_len, int topk, int init, int local,
+                              int32_t* ids, hipStream_t stream);
+
 // Context-parallel selection: one shard's local lists (shards of up to kLocalMaxBlocks
 // blocks) and the merge of up to kMergeMaxShards shards' lists.
 constexpr int kLocalMaxBlocks = 64 * 64;

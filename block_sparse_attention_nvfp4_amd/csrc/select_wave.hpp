@@ -107,20 +107,20 @@ __device__ __forceinline__ void load_row_scores(const float* s, int max_blocks, 
         v[k] = *reinterpret_cast<const float*>(row + 4u * (uint32_t)min(lane + 64 * k, max_blocks - 1));
 }
 
-// Select the PICK best of a row's keys (position i in lane i % 64, slot i / 64; key 0 marks
+// Select the `pick` best of a row's keys (position i in lane i % 64, slot i / 64; key 0 marks
 // "no candidate"; a larger key ranks first, equal keys by the lower position) and write
-// id_of(position) for each in ascending position order to out[0..PICK-1], and their keys to
-// key_out when it is given. With fewer than PICK candidates the remaining entries are -1 (keys
-// 0). `cand` is this wavefront's kSelectScratch entries of LDS; `out` and `key_out` may point
-// to global memory or LDS.
-template <int KPL, int PICK, class IdOf>
+// id_of(position) for each in ascending position order to out[0..pick-1], and their keys to
+// key_out when it is given. With fewer than `pick` candidates the remaining entries are -1
+// (keys 0). 0 <= pick <= 64, wavefront-uniform (a constant where the caller has one). `cand` is
+// this wavefront's kSelectScratch entries of LDS; `out` and `key_out` may point to global
+// memory or LDS.
+template <int KPL, class IdOf>
 __device__ __forceinline__ void select_top(const uint32_t (&key)[KPL], int lane, uint64_t* cand,
-                                           int32_t* out, uint32_t* key_out, IdOf id_of) {
-    static_assert(PICK >= 1 && PICK <= 64, "at most 64 picks");
+                                           int32_t* out, uint32_t* key_out, IdOf id_of, int pick) {
     uint32_t lmax = 0;
 #pragma unroll
     for (int k = 0; k < KPL; k++) lmax = max(lmax, key[k]);
-    // bound: the PICK-th largest per-lane maximum, the smallest maximum that fewer than PICK
+    // bound: the pick-th largest per-lane maximum, the smallest maximum that fewer than `pick`
     // others exceed (each lane counts the maxima above its own, read back as LDS broadcasts),
     // and at least 1 (never a non-candidate). The candidate area is cleared in the same pass:
     // entries past the candidate count read as 0, below every candidate.
@@ -135,7 +135,7 @@ __device__ __forceinline__ void select_top(const uint32_t (&key)[KPL], int lane,
     int above = 0;
 #pragma unroll
     for (int r = 0; r < 16; r++) above = add_count_above(w[r], lmax, above);
-    const uint32_t bound = max(wave_min_u32(above < PICK ? lmax : 0xFFFFFFFFu), 1u);
+    const uint32_t bound = max(wave_min_u32(above < pick ? lmax : 0xFFFFFFFFu), 1u);
     // candidates: the keys at or above the bound (all slots' masks first, then their counts)
     uint64_t cmask[KPL];
 #pragma unroll
@@ -172,7 +172,7 @@ __device__ __forceinline__ void select_top(const uint32_t (&key)[KPL], int lane,
 #pragma unroll
             for (int i = 0; i < 8; i++) rank += (int)(o[i] > mine);
         }
-        const bool sel = lane < count && rank < PICK;
+        const bool sel = lane < count && rank < pick;
         const uint64_t smask = __ballot(sel);
         if (sel) {
             const int at = lanes_before(smask);
@@ -181,9 +181,9 @@ __device__ __forceinline__ void select_top(const uint32_t (&key)[KPL], int lane,
         }
         n_sel = popc64(smask);
     } else {
-        // heavy ties: take the best remaining (key, lowest index) PICK times
+        // heavy ties: take the best remaining (key, lowest index) `pick` times
         uint32_t taken[(KPL + 31) / 32] = {};
-        for (int r = 0; r < PICK; r++) {
+        for (int r = 0; r < pick; r++) {
             uint32_t bk = 0;
             int bi = 0x7fffffff;
 #pragma unroll
@@ -222,7 +222,7 @@ __device__ __forceinline__ void select_top(const uint32_t (&key)[KPL], int lane,
         }
         n_sel = at;
     }
-    if (lane >= n_sel && lane < PICK) {
+    if (lane >= n_sel && lane < pick) {
         out[lane] = -1;
         if (key_out) key_out[lane] = 0u;
     }
@@ -245,8 +245,35 @@ __device__ __forceinline__ void select_row(const float (&v)[KPL], int n, int lan
         const int i = lane + 64 * k;
         key[k] = i < m ? order_key(v[k]) : 0u;
     }
-    select_top<KPL, kTopk - 1>(key, lane, cand, out, nullptr, [](int i) { return i; });
+    select_top<KPL>(key, lane, cand, out, nullptr, [](int i) { return i; }, kTopk - 1);
     if (lane == 0) out[kTopk - 1] = m;  // the forced block of the query token, the largest id
+}
+
+// The selection with the window knobs ("MiniMax M3 on vLLM", section "MSA mechanism": init
+// blocks and local blocks): of the row's n eligible blocks the first `init` and the last
+// `local` are kept, and the best others fill the rest of the `topk` places; out[0..topk-1]
+// gets the ids in ascending order, padded with -1. init + local <= topk <= 64.
+template <int KPL>
+__device__ __forceinline__ void select_row_window(const float (&v)[KPL], int n, int lane,
+                                                  uint64_t* cand, int32_t* out, int topk,
+                                                  int init, int local) {
+    if (n <= topk) {
+        if (lane < topk) out[lane] = lane < n ? lane : -1;
+        return;
+    }
+    const int lo = min(init, n);              // blocks 0..lo-1: forced
+    const int hi = max(n - local, lo);        // blocks hi..n-1: forced
+    uint32_t key[KPL];
+#pragma unroll
+    for (int k = 0; k < KPL; k++) {
+        const int i = lane + 64 * k;
+        key[k] = (i >= lo && i < hi) ? order_key(v[k]) : 0u;
+    }
+    // the picks lie between the two forced ranges, so the ascending order is kept
+    select_top<KPL>(key, lane, cand, out + lo, nullptr, [](int i) { return i; },
+                    topk - lo - (n - hi));
+    if (lane < lo) out[lane] = lane;
+    if (lane < n - hi) out[topk - (n - hi) + lane] = hi + lane;
 }
 
 }  // namespace msa

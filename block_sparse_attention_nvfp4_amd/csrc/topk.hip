@@ -248,6 +248,30 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void topk_wave_kernel(
     select_row<KPL>(v, eligible_blocks(p, max_blocks), lane, cand[wave], ids + (int64_t)row * kTopk);
 }
 
+// ---------------------------------------------------------------- window knobs
+template <int KPL>
+__global__ __launch_bounds__(kRowsPerWg * 64) void topk_window_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ ctx_lens, int max_blocks,
+    int q_len, int rows, int topk, int init, int local, int32_t* __restrict__ ids) {
+    __shared__ uint64_t cand[kRowsPerWg][kSelectScratch];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int row = blockIdx.x * kRowsPerWg + wave;
+    if (row >= rows) return;
+    const int bq = row >> 2;
+    const int b = bq / q_len;
+    const int j = bq - b * q_len;
+    float v[KPL];
+    load_row_scores<KPL>(scores + (int64_t)row * max_blocks, max_blocks, lane, v);
+    int T_raw = ctx_lens[b];
+#pragma unroll
+    for (int k = 0; k < KPL; k++) asm volatile("" : "+v"(v[k]));
+    asm volatile("" : "+v"(T_raw));
+    const int p = clamp_ctx(T_raw, max_blocks) - q_len + j;
+    select_row_window<KPL>(v, eligible_blocks(p, max_blocks), lane, cand[wave],
+                           ids + (int64_t)row * topk, topk, init, local);
+}
+
 // ---------------------------------------------------------------- context-parallel selection
 // "vLLM day-0 support for MiniMax-M3.1-Flash", section "Indexer NVFP4 DCP": each device scores
 // every index head on its own share of the pages, keeps its local top 16 per head, and the
@@ -287,9 +311,9 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void topk_local_kernel(
         key[k] = (c < n_cols && id < n) ? (id == n - 1 ? kForcedKey : order_key(v[k])) : 0u;
     }
     // columns ascend with the block ids, so the lowest position is the lowest block
-    select_top<KPL, kTopk>(key, lane, cand[wave], cand_ids + (int64_t)row * kTopk,
-                           cand_keys + (int64_t)row * kTopk,
-                           [=](int c) { return begin + c * stride; });
+    select_top<KPL>(key, lane, cand[wave], cand_ids + (int64_t)row * kTopk,
+                    cand_keys + (int64_t)row * kTopk, [=](int c) { return begin + c * stride; },
+                    kTopk);
 }
 
 // The owner's merge of n_shards lists per row (shard s at [s][rows][16]): every candidate is
@@ -348,6 +372,20 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void topk_merge_kernel(
 }
 
 }  // namespace
+
+hipError_t launch_topk_window(const float* scores, const int32_t* ctx_lens, int batch,
+                              int max_blocks, int q_len, int topk, int init, int local,
+                              int32_t* ids, hipStream_t stream) {
+    const int rows = batch * q_len * kKvHeads;
+    const dim3 grid((rows + kRowsPerWg - 1) / kRowsPerWg), block(kRowsPerWg * 64);
+    if (max_blocks <= 64 * 16)
+        hipLaunchKernelGGL(topk_window_kernel<16>, grid, block, 0, stream, scores, ctx_lens,
+                           max_blocks, q_len, rows, topk, init, local, ids);
+    else
+        hipLaunchKernelGGL(topk_window_kernel<64>, grid, block, 0, stream, scores, ctx_lens,
+                           max_blocks, q_len, rows, topk, init, local, ids);
+    return hipGetLastError();
+}
 
 hipError_t launch_topk_local(const float* scores, int ld, int begin, int stride, int n_cols,
                              const int32_t* ctx_lens, int batch, int max_blocks, int q_len,

@@ -174,6 +174,25 @@ int msa_block_topk(const float *block_scores, const msa_batch_t *batch, int32_t 
                    int32_t *block_ids, void *stream);
 
 /*
+ * Block selection with the window knobs of "MiniMax M3 on vLLM", section "MSA mechanism" (its
+ * config exposes init blocks and local blocks; the current recipe, which msa_block_topk
+ * implements, uses init_blocks = 0, local_blocks = 1 and topk = 16). For each row (b, j, g)
+ * with eligible blocks 0..f (as for msa_block_topk, n = f + 1): if n <= topk all are kept;
+ * otherwise blocks 0..init_blocks-1 and n-local_blocks..n-1 are always kept (a block in both
+ * ranges once), and the best others by (score descending, block index ascending) fill the rest
+ * of the topk places.
+ *   block_ids : device int32 [batch * q_len][4][topk], ascending, padded with -1.
+ * With topk = 16, init_blocks = 0, local_blocks = 1 the result is msa_block_topk's. The
+ * attention calls take 16 ids per row; other counts are for selection studies.
+ * Scores must not be NaN. Errors: MSA_ERR_INVALID_ARG (NULL pointers, sizes < 1, init_blocks
+ * or local_blocks < 0, init_blocks + local_blocks > topk), MSA_ERR_UNSUPPORTED (topk outside
+ * 1..64, max_blocks > 4096).
+ */
+int msa_block_topk_window(const float *block_scores, const msa_batch_t *batch, int32_t topk,
+                          int32_t init_blocks, int32_t local_blocks, int32_t *block_ids,
+                          void *stream);
+
+/*
  * Block selection split over shards of the blocks, as in indexer decode context parallelism
  * ("vLLM day-0 support for MiniMax-M3.1-Flash", section "Indexer NVFP4 DCP": each device
  * scores every index head on its own share of the pages and keeps a local top 16 per head;

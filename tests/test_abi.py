@@ -88,6 +88,15 @@ def test_invalid_arguments_return_codes_without_launch(msa):
     assert "topk" in msa.msa_last_error()
     assert L.msa_block_topk(None, by(_batch()), 16, 1, None) == msa.MSA_ERR_INVALID_ARG
     assert L.msa_block_topk(1, by(_batch(mb=0)), 16, 1, None) == msa.MSA_ERR_INVALID_ARG
+    # selection with the window knobs (args: scores batch topk init local ids stream)
+    win = L.msa_block_topk_window
+    assert win(1, by(_batch(mb=8)), 0, 0, 1, 1, None) == msa.MSA_ERR_UNSUPPORTED
+    assert win(1, by(_batch(mb=8)), 65, 0, 1, 1, None) == msa.MSA_ERR_UNSUPPORTED
+    assert win(1, by(_batch(mb=5000)), 16, 0, 1, 1, None) == msa.MSA_ERR_UNSUPPORTED
+    for init, local in ((-1, 1), (0, -1), (10, 7)):
+        assert win(1, by(_batch(mb=8)), 16, init, local, 1, None) == msa.MSA_ERR_INVALID_ARG
+    assert win(None, by(_batch(mb=8)), 16, 0, 1, 1, None) == msa.MSA_ERR_INVALID_ARG
+    assert win(1, by(_batch(mb=8)), 16, 0, 1, None, None) == msa.MSA_ERR_INVALID_ARG
     # shard-local lists and their merge (args: scores ld begin stride n_cols batch topk ids keys)
     loc = L.msa_block_topk_local
     mb8 = by(_batch(mb=8))

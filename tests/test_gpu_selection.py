@@ -79,3 +79,38 @@ def test_selection_constructed_rows(max_blocks):
             for g in range(4):
                 want, _ = oracle.block_topk(scores[i, g].astype(np.float64), n)
                 assert np.array_equal(got[i, g], want), (path, max_blocks, n, g, got[i, g], want)
+
+
+@pytest.mark.parametrize("max_blocks", [1024, 2048])
+@pytest.mark.parametrize("topk,init,local", [(16, 0, 1), (16, 2, 3), (8, 1, 1), (32, 0, 4),
+                                             (64, 4, 2), (16, 0, 0), (5, 3, 2)])
+def test_window_selection_constructed_rows(max_blocks, topk, init, local):
+    # the window knobs ("MiniMax M3 on vLLM", section "MSA mechanism": init and local blocks),
+    # bit for bit against the oracle; (16, 0, 1) is the recipe and must equal msa_block_topk
+    import block_sparse_attention_nvfp4_amd as msa
+    rng = np.random.default_rng(7 + max_blocks + 100 * topk + 10 * init + local)
+    pats = _patterns(max_blocks, rng)
+    n_list = [1, 5, topk, topk + 1, topk + 2, 63, 64, 65, 129, max_blocks - 1, max_blocks]
+    rows = []
+    for i in range(len(n_list)):
+        for g in range(4):
+            rows.append(pats[(i + g) % len(pats)])
+    batch = len(n_list)
+    scores = np.stack(rows).reshape(batch, 4, max_blocks).astype(np.float32)
+    ctx = torch.tensor([128 * (n - 1) + 1 for n in n_list], dtype=torch.int32, device="cuda")
+    b = msa.Batch(torch.zeros((batch, max_blocks), dtype=torch.int32, device="cuda"), ctx, 1)
+    s_dev = torch.from_numpy(scores).cuda()
+    ids = torch.full((batch, 4, topk), -7, dtype=torch.int32, device="cuda")
+    msa.msa_block_topk_window(s_dev, b, topk, init, local, ids)
+    direct = None
+    if (topk, init, local) == (16, 0, 1):
+        direct = torch.full((batch, 4, 16), -7, dtype=torch.int32, device="cuda")
+        msa.msa_block_topk(s_dev, b, 16, direct)
+    torch.cuda.synchronize()
+    got = ids.cpu().numpy()
+    for i, n in enumerate(n_list):
+        for g in range(4):
+            want = oracle.block_topk_variant(scores[i, g].astype(np.float64), n, topk, init, local)
+            assert list(got[i, g]) == list(want), (n, g, list(got[i, g]), list(want))
+    if direct is not None:
+        assert np.array_equal(direct.cpu().numpy(), got)
