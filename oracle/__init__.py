@@ -56,6 +56,8 @@ def lib():
     L.orc_index_scores.restype = None
     L.orc_index_scores.argtypes = [_u16p, _u8p, _u8p, ctypes.c_int32, ctypes.c_int32,
                                    ctypes.c_int32, _f64p]
+    L.orc_index_scores_lse.restype = None
+    L.orc_index_scores_lse.argtypes = L.orc_index_scores.argtypes
     L.orc_block_topk.restype = ctypes.c_int
     L.orc_block_topk.argtypes = [_f64p, ctypes.c_int32, ctypes.c_int32, _i32p,
                                  ctypes.POINTER(ctypes.c_double)]
@@ -118,6 +120,17 @@ def index_scores(q_idx_bits: np.ndarray, ik_codes: np.ndarray, ik_scales: np.nda
     ik_scales = np.ascontiguousarray(ik_scales[:T], dtype=np.uint8)
     out = np.empty((q, 4, nb_out), np.float64)
     lib().orc_index_scores(q_idx_bits, ik_codes, ik_scales, int(T), int(q), int(nb_out), out)
+    return out
+
+
+def index_scores_lse(q_idx_bits: np.ndarray, ik_codes: np.ndarray, ik_scales: np.ndarray,
+                     T: int, q: int, nb_out: int) -> np.ndarray:
+    """As index_scores, with the block's log-sum-exp of its token scores instead of the max."""
+    q_idx_bits = np.ascontiguousarray(q_idx_bits, dtype=np.uint16).reshape(q, 4, D)
+    ik_codes = np.ascontiguousarray(ik_codes[:T], dtype=np.uint8)
+    ik_scales = np.ascontiguousarray(ik_scales[:T], dtype=np.uint8)
+    out = np.empty((q, 4, nb_out), np.float64)
+    lib().orc_index_scores_lse(q_idx_bits, ik_codes, ik_scales, int(T), int(q), int(nb_out), out)
     return out
 
 

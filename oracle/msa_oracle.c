@@ -191,6 +191,42 @@ void orc_index_scores(const uint16_t *q_idx, const uint8_t *ik_codes, const uint
     free(key);
 }
 
+/* The same scores with the block's log-sum-exp in place of its max ([M3] "Prefill execution":
+ * the block-level reduction may be max or log-sum-exp depending on the model config).
+ * READING: natural logarithm of the sum of exp of the plain token scores of the block's valid
+ * tokens (no temperature), -inf if none; computed as m + log(sum exp(s - m)), m the max. */
+void orc_index_scores_lse(const uint16_t *q_idx, const uint8_t *ik_codes, const uint8_t *ik_scales,
+                          int32_t T, int32_t q, int32_t nb_out, double *out) {
+    double *key = (double *)malloc(sizeof(double) * 128 * (size_t)(T > 0 ? T : 1));
+    orc_nvfp4_dequantize(ik_codes, ik_scales, T, key);
+    double qv[128], sc[128];
+    for (int j = 0; j < q; j++) {
+        int64_t p = (int64_t)T - q + j;
+        for (int g = 0; g < 4; g++) {
+            for (int d = 0; d < 128; d++) qv[d] = orc_bf16_value(q_idx[((size_t)j * 4 + g) * 128 + d]);
+            for (int blk = 0; blk < nb_out; blk++) {
+                int cnt = 0;
+                double m = -INFINITY;
+                for (int64_t t = (int64_t)blk * 128; t < (int64_t)blk * 128 + 128; t++) {
+                    if (t > p || t >= T) break;
+                    double s = 0.0;
+                    for (int d = 0; d < 128; d++) s += qv[d] * key[t * 128 + d];
+                    sc[cnt++] = s;
+                    if (s > m) m = s;
+                }
+                double r = -INFINITY;
+                if (cnt > 0) {
+                    double sum = 0.0;
+                    for (int i = 0; i < cnt; i++) sum += exp(sc[i] - m);
+                    r = m + log(sum);
+                }
+                out[((size_t)j * 4 + g) * nb_out + blk] = r;
+            }
+        }
+    }
+    free(key);
+}
+
 /* ---------------------------------------------------------------- selection ------------- */
 
 /* Block selection for one (sequence, query token, group) row ([M31] "MSA primer": keep the 16

@@ -16,6 +16,8 @@ void orc_nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t n
 double orc_bf16_value(uint16_t bits);
 void orc_index_scores(const uint16_t *q_idx, const uint8_t *ik_codes, const uint8_t *ik_scales,
                       int32_t T, int32_t q, int32_t nb_out, double *out);
+void orc_index_scores_lse(const uint16_t *q_idx, const uint8_t *ik_codes, const uint8_t *ik_scales,
+                          int32_t T, int32_t q, int32_t nb_out, double *out);
 int orc_block_topk(const double *scores, int32_t n, int32_t topk, int32_t *ids_out, double *margin);
 void orc_sparse_attention_token(const uint16_t *q, const uint8_t *k_codes, const uint8_t *k_scales,
                                 const uint8_t *v_codes, const uint8_t *v_scales, int32_t T,

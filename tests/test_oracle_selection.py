@@ -213,6 +213,34 @@ def test_index_scores_planted_closed_form():
     assert np.all(got[0, :, 2] == max(dot, 0.0))
 
 
+def test_index_scores_lse_closed_forms():
+    # "MiniMax M3 on vLLM", section "Prefill execution": the block reduction may be log-sum-exp.
+    # Keys that quantize exactly make every token score exact: block 0 holds 128 equal scores
+    # (LSE = s + log 128), block 1 a single valid token (LSE = its score), block 2 nothing
+    # valid (-inf); and the max is never above the LSE nor the LSE above max + log(count).
+    T = 129
+    w = np.array([1.0, -0.5, 6.0, 0.0] * 32, np.float32)
+    ik = np.tile(w, (T, 1))
+    codes, scales = oracle.quantize(ik)
+    assert np.array_equal(oracle.dequantize(codes, scales), ik.astype(np.float64))
+    qv = np.tile(np.array([0.5, 1.0, 0.25, 3.0], np.float32), 32)
+    qb = _bf16_bits(np.tile(qv, (1, 4, 1)))
+    lse = oracle.index_scores_lse(qb, codes, scales, T, 1, 3)
+    s = float(np.dot(w.astype(np.float64), qv.astype(np.float64)))
+    assert np.allclose(lse[0, :, 0], s + math.log(128), rtol=0, atol=1e-12)
+    assert np.all(lse[0, :, 1] == s)
+    assert np.all(np.isneginf(lse[0, :, 2]))
+    rng = np.random.default_rng(3)
+    ik = rng.standard_normal((700, 128)).astype(np.float32)
+    codes, scales = oracle.quantize(ik)
+    qb = _bf16_bits(rng.standard_normal((2, 4, 128)))
+    mx = oracle.index_scores(qb, codes, scales, 700, 2, 6)
+    lse = oracle.index_scores_lse(qb, codes, scales, 700, 2, 6)
+    fin = np.isfinite(mx)
+    assert np.array_equal(fin, np.isfinite(lse))
+    assert np.all(lse[fin] >= mx[fin]) and np.all(lse[fin] <= mx[fin] + math.log(128) + 1e-12)
+
+
 def test_causal_mask_inside_last_block():
     # q = 4 draft tokens in the last block: token j sees keys up to T - 4 + j only
     T, q = 256, 4
