@@ -6,6 +6,7 @@ HIP stream into the C calls, with the same names:
 
     msa_kv_insert_nvfp4(cache, slots, k, v, ik)
     msa_indexer_score(cache, batch, q_idx, block_scores)
+    msa_indexer_score_ex(cache, batch, q_idx, reduction, block_scores)   # max or log-sum-exp
     msa_block_topk(block_scores, batch, topk, block_ids)
     msa_block_topk_window(block_scores, batch, topk, init_blocks, local_blocks, block_ids)
     msa_block_topk_local(shard_scores, block_begin, block_stride, batch, topk, cand_ids,
@@ -46,8 +47,11 @@ MSA_ERR_INVALID_ARG = -1
 MSA_ERR_UNSUPPORTED = -2
 MSA_ERR_WORKSPACE = -3
 MSA_ERR_HIP = -4
+MSA_REDUCE_MAX = 0
+MSA_REDUCE_LSE = 1
 
-EXPORTED = ("msa_page_bytes", "msa_kv_insert_nvfp4", "msa_indexer_score", "msa_block_topk",
+EXPORTED = ("msa_page_bytes", "msa_kv_insert_nvfp4", "msa_indexer_score", "msa_indexer_score_ex",
+            "msa_block_topk",
             "msa_block_topk_window", "msa_block_topk_local", "msa_block_topk_merge",
             "msa_sparse_attn_workspace_bytes", "msa_sparse_attn_decode", "msa_select_attn_decode",
             "msa_insert_indexer_score", "msa_decode_step", "msa_last_error", "msa_version")
@@ -81,6 +85,9 @@ def _load() -> ctypes.CDLL:
     L.msa_kv_insert_nvfp4.argtypes = [ctypes.POINTER(_Cache), vp, vp, vp, vp, i32, vp]
     L.msa_indexer_score.restype = ctypes.c_int
     L.msa_indexer_score.argtypes = [ctypes.POINTER(_Cache), ctypes.POINTER(_Batch), vp, vp, vp]
+    L.msa_indexer_score_ex.restype = ctypes.c_int
+    L.msa_indexer_score_ex.argtypes = [ctypes.POINTER(_Cache), ctypes.POINTER(_Batch), vp, i32, vp,
+                                       vp]
     L.msa_block_topk.restype = ctypes.c_int
     L.msa_block_topk.argtypes = [vp, ctypes.POINTER(_Batch), i32, vp, vp]
     L.msa_block_topk_window.restype = ctypes.c_int
@@ -203,6 +210,18 @@ def msa_indexer_score(cache: Cache, batch: Batch, q_idx: torch.Tensor, block_sco
     _check(lib.msa_indexer_score(ctypes.byref(cache._c), ctypes.byref(batch._c),
                                  _ptr(q_idx, torch.bfloat16, "q_idx"),
                                  _ptr(block_scores, torch.float32, "block_scores"), _stream(stream)))
+
+
+def msa_indexer_score_ex(cache: Cache, batch: Batch, q_idx: torch.Tensor, reduction: int,
+                         block_scores: torch.Tensor, stream=None) -> None:
+    if tuple(q_idx.shape) != (batch.rows, KV_HEADS, HEAD_DIM):
+        raise ValueError(f"q_idx: expected {(batch.rows, KV_HEADS, HEAD_DIM)}, got {tuple(q_idx.shape)}")
+    if tuple(block_scores.shape) != (batch.rows, KV_HEADS, batch.max_blocks):
+        raise ValueError("block_scores: expected [batch*q_len][4][max_blocks]")
+    _check(lib.msa_indexer_score_ex(ctypes.byref(cache._c), ctypes.byref(batch._c),
+                                    _ptr(q_idx, torch.bfloat16, "q_idx"), int(reduction),
+                                    _ptr(block_scores, torch.float32, "block_scores"),
+                                    _stream(stream)))
 
 
 def msa_block_topk(block_scores: torch.Tensor, batch: Batch, topk: int, block_ids: torch.Tensor,

@@ -104,6 +104,28 @@ int msa_indexer_score(const msa_cache_t* cache, const msa_batch_t* batch, const 
                       fn);
 }
 
+int msa_indexer_score_ex(const msa_cache_t* cache, const msa_batch_t* batch,
+                         const uint16_t* q_idx, int32_t reduction, float* block_scores,
+                         void* stream) {
+    static const char* fn = "msa_indexer_score_ex";
+    int rc = check_cache(cache, fn, false, true);
+    if (rc) return rc;
+    if ((rc = check_batch(batch, fn))) return rc;
+    if (!q_idx || !block_scores) return fail(MSA_ERR_INVALID_ARG, "%s: q_idx or block_scores is NULL", fn);
+    if (reduction == MSA_REDUCE_MAX)
+        return hip_status(msa::launch_indexer(cache->ik, cache->num_pages, batch->block_table,
+                                              batch->ctx_lens, batch->batch, batch->max_blocks,
+                                              batch->q_len, q_idx, block_scores, (hipStream_t)stream),
+                          fn);
+    if (reduction != MSA_REDUCE_LSE)
+        return fail(MSA_ERR_UNSUPPORTED, "%s: reduction=%d (0 = max, 1 = log-sum-exp)", fn, reduction);
+    return hip_status(msa::launch_indexer_gemm(cache->ik, cache->num_pages, batch->block_table,
+                                               batch->ctx_lens, batch->batch, batch->max_blocks,
+                                               batch->q_len, q_idx, block_scores,
+                                               (hipStream_t)stream, true),
+                      fn);
+}
+
 int msa_block_topk(const float* block_scores, const msa_batch_t* batch, int32_t topk,
                    int32_t* block_ids, void* stream) {
     static const char* fn = "msa_block_topk";

@@ -48,6 +48,9 @@ __device__ __forceinline__ void read_tile(u32x4 (&v)[4], const uint8_t* tile, in
                  : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]) : "v"(a) : "memory");
 }
 
+// LSE: the block's log-sum-exp of its token scores instead of their max ("MiniMax M3 on
+// vLLM", section "Prefill execution": the block reduction may be max or log-sum-exp).
+template <bool LSE>
 __global__ __launch_bounds__(kGWaves * 64, 2) void indexer_gemm_kernel(
     const uint8_t* __restrict__ ik_pool, int64_t num_pages, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ ctx_lens, int max_blocks, int q_len, int rows_per_wg,
@@ -130,21 +133,33 @@ __global__ __launch_bounds__(kGWaves * 64, 2) void indexer_gemm_kernel(
                         acc[s] = mfma_bf16_k32(ka[s][m], __builtin_bit_cast(bf16x8, qv[m]), acc[s]);
                 }
                 // D of slab s in lane (n, c): tokens 32 c + 4 s + i, i = 0..3, of query row n
-                if (p_lo >= tok0 + kBlock - 1) {
-#pragma unroll
-                    for (int s = 0; s < 8; s++)
-#pragma unroll
-                        for (int i = 0; i < 4; i++) best = fmaxf(best, acc[s][i]);
-                } else {
+                if (p_lo < tok0 + kBlock - 1) {
                     asm volatile("");  // a scalar branch: the mask only where the block is cut
                     const int lim = T - q_len + min((rt + n) >> 2, q_len - 1) - tok0 - 32 * c;
 #pragma unroll
                     for (int s = 0; s < 8; s++)
 #pragma unroll
                         for (int i = 0; i < 4; i++)
-                            best = fmaxf(best, 4 * s + i <= lim ? acc[s][i] : -INFINITY);
+                            if (4 * s + i > lim) acc[s][i] = -INFINITY;
                 }
+#pragma unroll
+                for (int s = 0; s < 8; s++)
+#pragma unroll
+                    for (int i = 0; i < 4; i++) best = fmaxf(best, acc[s][i]);
                 best = max_over_c(best);
+                if constexpr (LSE) {
+                    // log-sum-exp about the row's max (masked tokens are -inf: weight 0)
+                    float sum = 0.f;
+                    if (best > -INFINITY) {
+#pragma unroll
+                        for (int s = 0; s < 8; s++)
+#pragma unroll
+                            for (int i = 0; i < 4; i++)
+                                sum += exp2f((acc[s][i] - best) * 1.4426950408889634f);
+                    }
+                    sum = sum_over_c(sum);
+                    best = best > -INFINITY ? best + logf(sum) : -INFINITY;
+                }
             }
             if (c == 0 && rt + n < r_end) best_of[rt + n - r_begin][wave] = best;
         }
@@ -164,14 +179,19 @@ __global__ __launch_bounds__(kGWaves * 64, 2) void indexer_gemm_kernel(
 hipError_t launch_indexer_gemm(const uint8_t* ik_pool, int64_t num_pages,
                                const int32_t* block_table, const int32_t* ctx_lens, int batch,
                                int max_blocks, int q_len, const uint16_t* q_idx, float* scores,
-                               hipStream_t stream) {
+                               hipStream_t stream, bool lse) {
     const int rows = 4 * q_len;
     const int rows_per_wg = min(kMaxRowsPerWg, (rows + 15) / 16 * 16);
     const dim3 grid((max_blocks + kGWaves - 1) / kGWaves, (rows + rows_per_wg - 1) / rows_per_wg,
                     batch);
-    hipLaunchKernelGGL(indexer_gemm_kernel, grid, dim3(kGWaves * 64), 0, stream, ik_pool,
-                       num_pages, block_table, ctx_lens, max_blocks, q_len, rows_per_wg, q_idx,
-                       scores);
+    if (lse)
+        hipLaunchKernelGGL(indexer_gemm_kernel<true>, grid, dim3(kGWaves * 64), 0, stream, ik_pool,
+                           num_pages, block_table, ctx_lens, max_blocks, q_len, rows_per_wg, q_idx,
+                           scores);
+    else
+        hipLaunchKernelGGL(indexer_gemm_kernel<false>, grid, dim3(kGWaves * 64), 0, stream, ik_pool,
+                           num_pages, block_table, ctx_lens, max_blocks, q_len, rows_per_wg, q_idx,
+                           scores);
     return hipGetLastError();
 }
 

@@ -22,10 +22,11 @@ hipError_t launch_indexer(const uint8_t* ik_pool, int64_t num_pages, const int32
 // (8 x 131,072 context: 37 against 28 us at q = 12, 99 against 54 us at q = 32; the scores are
 // the same bits).
 constexpr int kIndexerGemmMinQ = 9;
+// lse: the block's log-sum-exp of its token scores instead of their max (any q_len).
 hipError_t launch_indexer_gemm(const uint8_t* ik_pool, int64_t num_pages,
                                const int32_t* block_table, const int32_t* ctx_lens, int batch,
                                int max_blocks, int q_len, const uint16_t* q_idx, float* scores,
-                               hipStream_t stream);
+                               hipStream_t stream, bool lse = false);
 
 // Insert of a decode step's new tokens at their own positions (slots from the block table).
 hipError_t launch_insert_at_positions(uint8_t* k_pool, uint8_t* v_pool, uint8_t* ik_pool,

@@ -160,6 +160,22 @@ int msa_indexer_score(const msa_cache_t *cache, const msa_batch_t *batch, const 
                       float *block_scores, void *stream);
 
 /*
+ * The indexer with a choice of block reduction ("MiniMax M3 on vLLM", section "Prefill
+ * execution": the block-level rule may be max or log-sum-exp, depending on the model config).
+ *   reduction : MSA_REDUCE_MAX (msa_indexer_score's scores) or MSA_REDUCE_LSE:
+ *               score(b, j, g, i) = log(sum over the block's valid tokens t of exp(s_t)), s_t the
+ *               token score as above, computed as m + log(sum exp(s_t - m)) with m the max
+ *               (fp32 exp and log); -inf when the block holds no valid token.
+ * Other arguments, layouts and errors as for msa_indexer_score; MSA_ERR_UNSUPPORTED for another
+ * reduction value. The LSE scores feed msa_block_topk like any scores.
+ */
+#define MSA_REDUCE_MAX 0
+#define MSA_REDUCE_LSE 1
+int msa_indexer_score_ex(const msa_cache_t *cache, const msa_batch_t *batch,
+                         const uint16_t *q_idx, int32_t reduction, float *block_scores,
+                         void *stream);
+
+/*
  * Block selection ("vLLM day-0 support for MiniMax-M3.1-Flash", section "MSA primer"; "MiniMax
  * M3 on vLLM", section "MSA mechanism": local_blocks = 1, init_blocks = 0, the local block is
  * not counted twice). For each row (b, j, g): the eligible blocks are 0..f with

@@ -83,6 +83,12 @@ def test_invalid_arguments_return_codes_without_launch(msa):
     assert L.msa_indexer_score(by(_cache()), by(_batch(bt=None)), 1, 1, None) == msa.MSA_ERR_INVALID_ARG
     assert L.msa_indexer_score(by(_cache()), by(_batch()), None, 1, None) == msa.MSA_ERR_INVALID_ARG
     assert L.msa_indexer_score(by(_cache()), by(_batch(b=70000)), 1, 1, None) == msa.MSA_ERR_INVALID_ARG
+    # indexer with a reduction choice
+    ix = L.msa_indexer_score_ex
+    assert ix(by(_cache()), by(_batch()), 1, 2, 1, None) == msa.MSA_ERR_UNSUPPORTED
+    assert ix(by(_cache()), by(_batch()), None, 1, 1, None) == msa.MSA_ERR_INVALID_ARG
+    assert ix(by(_cache(ik=None)), by(_batch()), 1, 1, 1, None) == msa.MSA_ERR_INVALID_ARG
+    assert ix(by(_cache()), by(_batch(q=0)), 1, 1, 1, None) == msa.MSA_ERR_INVALID_ARG
     # top-k
     assert L.msa_block_topk(1, by(_batch()), 8, 1, None) == msa.MSA_ERR_UNSUPPORTED
     assert "topk" in msa.msa_last_error()

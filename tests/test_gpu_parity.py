@@ -97,6 +97,30 @@ def test_indexer_topk_attention(run):
     _log(f"[case {name}] rows below margin (validated, not bit-compared): {exempt_total}")
 
 
+def test_indexer_lse_scores(run):
+    # the log-sum-exp block reduction ("MiniMax M3 on vLLM", section "Prefill execution"),
+    # against the oracle's: LSE is 1-Lipschitz in the token scores, so the dot-product bound
+    # carries over, plus the fp32 exp / log / final-add rounding (4e-6 + 2^-22 |ref|)
+    import block_sparse_attention_nvfp4_amd as msa
+    name, w, g, _ = run
+    q = w.q_len
+    lse = torch.empty_like(g.step.block_scores)
+    msa.msa_indexer_score_ex(g.cache, g.batch, g.q_idx, msa.MSA_REDUCE_LSE, lse)
+    torch.cuda.synchronize()
+    got = lse.cpu().numpy()
+    for b in range(w.batch):
+        T = w.ctx_lens[b]
+        rows = slice(b * q, (b + 1) * q)
+        ikc, iks = oracle.quantize(w.ik_rows(b, 0, T).numpy())
+        qi = mi.bf16_bits(w.q_idx[rows])
+        ref = oracle.index_scores_lse(qi, ikc, iks, T, q, w.max_blocks)
+        tol = score_tolerance(qi, ikc, iks)[..., None] + 4e-6 + 2.0 ** -22 * np.abs(np.where(np.isfinite(ref), ref, 0))
+        ninf = np.isneginf(ref)
+        assert np.array_equal(np.isneginf(got[rows]), ninf), (name, b)
+        d = np.where(ninf, 0, np.abs(got[rows].astype(np.float64) - np.where(ninf, 0, ref)))
+        assert (d <= tol).all(), (name, b, float(d.max()))
+
+
 def test_attention_other_scales(run):
     """Attention with softmax scales other than 1/sqrt(128), a negative one included, over the
     step's own selection (first sequence, up to four query tokens), against the oracle."""
