@@ -7,6 +7,7 @@ HIP stream into the C calls, with the same names:
     msa_kv_insert_nvfp4(cache, slots, k, v, ik)
     msa_indexer_score(cache, batch, q_idx, block_scores)
     msa_indexer_score_ex(cache, batch, q_idx, reduction, block_scores)   # max or log-sum-exp
+    msa_indexer_score_shared_prefix(cache, batch, q_idx, prefix_blocks, block_scores)
     msa_block_topk(block_scores, batch, topk, block_ids)
     msa_block_topk_window(block_scores, batch, topk, init_blocks, local_blocks, block_ids)
     msa_block_topk_local(shard_scores, block_begin, block_stride, batch, topk, cand_ids,
@@ -51,6 +52,7 @@ MSA_REDUCE_MAX = 0
 MSA_REDUCE_LSE = 1
 
 EXPORTED = ("msa_page_bytes", "msa_kv_insert_nvfp4", "msa_indexer_score", "msa_indexer_score_ex",
+            "msa_indexer_score_shared_prefix",
             "msa_block_topk",
             "msa_block_topk_window", "msa_block_topk_local", "msa_block_topk_merge",
             "msa_sparse_attn_workspace_bytes", "msa_sparse_attn_decode", "msa_select_attn_decode",
@@ -88,6 +90,9 @@ def _load() -> ctypes.CDLL:
     L.msa_indexer_score_ex.restype = ctypes.c_int
     L.msa_indexer_score_ex.argtypes = [ctypes.POINTER(_Cache), ctypes.POINTER(_Batch), vp, i32, vp,
                                        vp]
+    L.msa_indexer_score_shared_prefix.restype = ctypes.c_int
+    L.msa_indexer_score_shared_prefix.argtypes = [ctypes.POINTER(_Cache), ctypes.POINTER(_Batch),
+                                                  vp, i32, vp, vp]
     L.msa_block_topk.restype = ctypes.c_int
     L.msa_block_topk.argtypes = [vp, ctypes.POINTER(_Batch), i32, vp, vp]
     L.msa_block_topk_window.restype = ctypes.c_int
@@ -222,6 +227,20 @@ def msa_indexer_score_ex(cache: Cache, batch: Batch, q_idx: torch.Tensor, reduct
                                     _ptr(q_idx, torch.bfloat16, "q_idx"), int(reduction),
                                     _ptr(block_scores, torch.float32, "block_scores"),
                                     _stream(stream)))
+
+
+def msa_indexer_score_shared_prefix(cache: Cache, batch: Batch, q_idx: torch.Tensor,
+                                    prefix_blocks: int, block_scores: torch.Tensor,
+                                    stream=None) -> None:
+    if tuple(q_idx.shape) != (batch.rows, KV_HEADS, HEAD_DIM):
+        raise ValueError(f"q_idx: expected {(batch.rows, KV_HEADS, HEAD_DIM)}, got {tuple(q_idx.shape)}")
+    if tuple(block_scores.shape) != (batch.rows, KV_HEADS, batch.max_blocks):
+        raise ValueError("block_scores: expected [batch*q_len][4][max_blocks]")
+    _check(lib.msa_indexer_score_shared_prefix(ctypes.byref(cache._c), ctypes.byref(batch._c),
+                                               _ptr(q_idx, torch.bfloat16, "q_idx"),
+                                               int(prefix_blocks),
+                                               _ptr(block_scores, torch.float32, "block_scores"),
+                                               _stream(stream)))
 
 
 def msa_block_topk(block_scores: torch.Tensor, batch: Batch, topk: int, block_ids: torch.Tensor,

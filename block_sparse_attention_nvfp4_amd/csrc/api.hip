@@ -126,6 +126,25 @@ int msa_indexer_score_ex(const msa_cache_t* cache, const msa_batch_t* batch,
                       fn);
 }
 
+int msa_indexer_score_shared_prefix(const msa_cache_t* cache, const msa_batch_t* batch,
+                                    const uint16_t* q_idx, int32_t prefix_blocks,
+                                    float* block_scores, void* stream) {
+    static const char* fn = "msa_indexer_score_shared_prefix";
+    int rc = check_cache(cache, fn, false, true);
+    if (rc) return rc;
+    if ((rc = check_batch(batch, fn))) return rc;
+    if (!q_idx || !block_scores) return fail(MSA_ERR_INVALID_ARG, "%s: q_idx or block_scores is NULL", fn);
+    if (prefix_blocks < 0 || prefix_blocks > batch->max_blocks)
+        return fail(MSA_ERR_INVALID_ARG, "%s: prefix_blocks=%d outside [0, max_blocks=%d]", fn,
+                    prefix_blocks, batch->max_blocks);
+    return hip_status(msa::launch_indexer_shared_prefix(cache->ik, cache->num_pages,
+                                                        batch->block_table, batch->ctx_lens,
+                                                        batch->batch, batch->max_blocks,
+                                                        batch->q_len, q_idx, block_scores,
+                                                        prefix_blocks, (hipStream_t)stream),
+                      fn);
+}
+
 int msa_block_topk(const float* block_scores, const msa_batch_t* batch, int32_t topk,
                    int32_t* block_ids, void* stream) {
     static const char* fn = "msa_block_topk";

@@ -50,22 +50,29 @@ __device__ __forceinline__ void read_tile(u32x4 (&v)[4], const uint8_t* tile, in
 
 // LSE: the block's log-sum-exp of its token scores instead of their max ("MiniMax M3 on
 // vLLM", section "Prefill execution": the block reduction may be max or log-sum-exp).
-template <bool LSE>
+// The blocks scored are blk_begin .. blk_end - 1. SHARED: one row space holds every query row
+// of the batch (blockIdx.z = 0), scored against the pages of sequence 0's table, which all
+// sequences share there and which hold no query token (no mask: every token is visible).
+template <bool LSE, bool SHARED>
 __global__ __launch_bounds__(kGWaves * 64, 2) void indexer_gemm_kernel(
     const uint8_t* __restrict__ ik_pool, int64_t num_pages, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ ctx_lens, int max_blocks, int q_len, int rows_per_wg,
-    const uint16_t* __restrict__ q_idx, float* __restrict__ scores) {
+    const uint16_t* __restrict__ q_idx, float* __restrict__ scores, int blk_begin, int blk_end,
+    int batch) {
     __shared__ __attribute__((aligned(16))) uint8_t stage[2][kStageRows / 16][kTileBytes];
     __shared__ float best_of[kMaxRowsPerWg][kGWaves];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, c = lane >> 4;
     const int b = blockIdx.z;
-    const int rows = 4 * q_len;  // this sequence's rows (j, g) = 4 j + g
+    // this sequence's rows (j, g) = 4 j + g (SHARED: the whole batch's rows)
+    const int rows = SHARED ? 4 * q_len * batch : 4 * q_len;
     const int r_begin = blockIdx.y * rows_per_wg;
     const int r_end = min(rows, r_begin + rows_per_wg);
-    const int blk = blockIdx.x * kGWaves + wave;
-    const int T = clamp_ctx(ctx_lens[b], max_blocks);
+    const int blk0 = blk_begin + blockIdx.x * kGWaves;  // this workgroup's first block
+    const int blk = blk0 + wave;
+    // (SHARED: a context past every block, so that nothing is masked)
+    const int T = SHARED ? max_blocks * kBlock : clamp_ctx(ctx_lens[b], max_blocks);
     const uint8_t* qseq = reinterpret_cast<const uint8_t*>(q_idx + (int64_t)b * rows * kDim);
 
     // stage loads: copies of 1 KB (tile tt, piece m), kCopies per wavefront; lane
@@ -86,7 +93,7 @@ __global__ __launch_bounds__(kGWaves * 64, 2) void indexer_gemm_kernel(
     // this wavefront's page: lane (m, c) holds, for token slab s, the 32 codes of token
     // 32 (m / 4) + 4 s + m % 4, elements 32 c .. 32 c + 31, and the 16 scale bytes of its
     // token row (bytes 2 s, 2 s + 1: element groups 2 c, 2 c + 1 of slab s)
-    const bool in_table = blk < max_blocks;
+    const bool in_table = blk < blk_end;
     int page = in_table ? block_table[(int64_t)b * max_blocks + blk] : -1;
     const int tok0 = blk * kBlock;
     const bool has_keys = in_table && tok0 < T && page >= 0 && page < num_pages;
@@ -118,8 +125,8 @@ __global__ __launch_bounds__(kGWaves * 64, 2) void indexer_gemm_kernel(
         for (int tt = 0; tt < kStageRows / 16; tt++) {
             const int rt = r0 + 16 * tt;  // rows rt .. rt + 15: tokens rt / 4 .. rt / 4 + 3
             if (rt >= r_end) break;
-            const int p_lo = T - q_len + (rt >> 2);
-            const int p_hi = T - q_len + min((rt >> 2) + 3, q_len - 1);
+            const int p_lo = SHARED ? T : T - q_len + (rt >> 2);
+            const int p_hi = SHARED ? T : T - q_len + min((rt >> 2) + 3, q_len - 1);
             float best = -INFINITY;
             if (has_keys && p_hi >= tok0) {
                 u32x4 qv[4];
@@ -167,11 +174,31 @@ __global__ __launch_bounds__(kGWaves * 64, 2) void indexer_gemm_kernel(
     __syncthreads();
     // row rl's block scores are kGWaves contiguous floats
     const int nr = r_end - r_begin;
-    float* out = scores + ((int64_t)b * rows + r_begin) * max_blocks + blockIdx.x * kGWaves;
+    float* out = scores + ((int64_t)b * rows + r_begin) * max_blocks + blk0;
     for (int i = threadIdx.x; i < nr * kGWaves; i += kGWaves * 64) {
         const int rl = i / kGWaves, kb = i % kGWaves;
-        if (blockIdx.x * kGWaves + kb < max_blocks) out[(int64_t)rl * max_blocks + kb] = best_of[rl][kb];
+        if (blk0 + kb < blk_end) out[(int64_t)rl * max_blocks + kb] = best_of[rl][kb];
     }
+}
+
+}  // namespace
+
+namespace {
+
+template <bool LSE, bool SHARED>
+hipError_t launch_gemm_t(const uint8_t* ik_pool, int64_t num_pages, const int32_t* block_table,
+                         const int32_t* ctx_lens, int batch, int max_blocks, int q_len,
+                         const uint16_t* q_idx, float* scores, int blk_begin, int blk_end,
+                         hipStream_t stream) {
+    if (blk_end <= blk_begin) return hipSuccess;
+    const int rows = SHARED ? 4 * q_len * batch : 4 * q_len;
+    const int rows_per_wg = min(kMaxRowsPerWg, (rows + 15) / 16 * 16);
+    const dim3 grid((blk_end - blk_begin + kGWaves - 1) / kGWaves,
+                    (rows + rows_per_wg - 1) / rows_per_wg, SHARED ? 1 : batch);
+    hipLaunchKernelGGL((indexer_gemm_kernel<LSE, SHARED>), grid, dim3(kGWaves * 64), 0, stream,
+                       ik_pool, num_pages, block_table, ctx_lens, max_blocks, q_len, rows_per_wg,
+                       q_idx, scores, blk_begin, blk_end, batch);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -180,19 +207,25 @@ hipError_t launch_indexer_gemm(const uint8_t* ik_pool, int64_t num_pages,
                                const int32_t* block_table, const int32_t* ctx_lens, int batch,
                                int max_blocks, int q_len, const uint16_t* q_idx, float* scores,
                                hipStream_t stream, bool lse) {
-    const int rows = 4 * q_len;
-    const int rows_per_wg = min(kMaxRowsPerWg, (rows + 15) / 16 * 16);
-    const dim3 grid((max_blocks + kGWaves - 1) / kGWaves, (rows + rows_per_wg - 1) / rows_per_wg,
-                    batch);
     if (lse)
-        hipLaunchKernelGGL(indexer_gemm_kernel<true>, grid, dim3(kGWaves * 64), 0, stream, ik_pool,
-                           num_pages, block_table, ctx_lens, max_blocks, q_len, rows_per_wg, q_idx,
-                           scores);
-    else
-        hipLaunchKernelGGL(indexer_gemm_kernel<false>, grid, dim3(kGWaves * 64), 0, stream, ik_pool,
-                           num_pages, block_table, ctx_lens, max_blocks, q_len, rows_per_wg, q_idx,
-                           scores);
-    return hipGetLastError();
+        return launch_gemm_t<true, false>(ik_pool, num_pages, block_table, ctx_lens, batch,
+                                          max_blocks, q_len, q_idx, scores, 0, max_blocks, stream);
+    return launch_gemm_t<false, false>(ik_pool, num_pages, block_table, ctx_lens, batch,
+                                       max_blocks, q_len, q_idx, scores, 0, max_blocks, stream);
+}
+
+hipError_t launch_indexer_shared_prefix(const uint8_t* ik_pool, int64_t num_pages,
+                                        const int32_t* block_table, const int32_t* ctx_lens,
+                                        int batch, int max_blocks, int q_len,
+                                        const uint16_t* q_idx, float* scores, int prefix_blocks,
+                                        hipStream_t stream) {
+    hipError_t err = launch_gemm_t<false, true>(ik_pool, num_pages, block_table, ctx_lens, batch,
+                                                max_blocks, q_len, q_idx, scores, 0, prefix_blocks,
+                                                stream);
+    if (err != hipSuccess) return err;
+    return launch_gemm_t<false, false>(ik_pool, num_pages, block_table, ctx_lens, batch,
+                                       max_blocks, q_len, q_idx, scores, prefix_blocks, max_blocks,
+                                       stream);
 }
 
 }  // namespace msa

@@ -28,6 +28,15 @@ hipError_t launch_indexer_gemm(const uint8_t* ik_pool, int64_t num_pages,
                                int max_blocks, int q_len, const uint16_t* q_idx, float* scores,
                                hipStream_t stream, bool lse = false);
 
+// Indexer for a batch whose sequences share their first prefix_blocks pages (sequence 0's
+// table entries) with no query token in them: those pages scored once for every query row of
+// the batch, the rest per sequence.
+hipError_t launch_indexer_shared_prefix(const uint8_t* ik_pool, int64_t num_pages,
+                                        const int32_t* block_table, const int32_t* ctx_lens,
+                                        int batch, int max_blocks, int q_len,
+                                        const uint16_t* q_idx, float* scores, int prefix_blocks,
+                                        hipStream_t stream);
+
 // Insert of a decode step's new tokens at their own positions (slots from the block table).
 hipError_t launch_insert_at_positions(uint8_t* k_pool, uint8_t* v_pool, uint8_t* ik_pool,
                                       int64_t num_pages, const int32_t* block_table,

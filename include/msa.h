@@ -176,6 +176,25 @@ int msa_indexer_score_ex(const msa_cache_t *cache, const msa_batch_t *batch,
                          void *stream);
 
 /*
+ * The indexer for a batch that shares a prefix (requests over one long common context): every
+ * sequence's blocks 0..prefix_blocks-1 are the same pages, and sequence 0's block-table entries
+ * are the ones read for them. Each shared page is then dequantized once, for all the batch's
+ * query rows together (a score GEMM of batch * q_len * 4 rows), instead of once per sequence
+ * ("vLLM day-0 support for MiniMax-M3.1-Flash", section "NVFP4 MSA kernel": a page of a shared
+ * prefix is dequantized once for up to 64 requests that share it; here the same reuse in the
+ * indexer, which reads every page of every context). Blocks from prefix_blocks on are scored
+ * per sequence. Scores, layout and errors as for msa_indexer_score, with the same values.
+ * Requirement (not checked: the lengths live in device memory): the shared blocks hold no query
+ * token, prefix_blocks * 128 <= T_b - q_len for every b; otherwise their scores for the rows of
+ * such a sequence are unspecified (no memory outside the arguments is touched).
+ * Errors: as msa_indexer_score, and MSA_ERR_INVALID_ARG for prefix_blocks outside
+ * [0, max_blocks].
+ */
+int msa_indexer_score_shared_prefix(const msa_cache_t *cache, const msa_batch_t *batch,
+                                    const uint16_t *q_idx, int32_t prefix_blocks,
+                                    float *block_scores, void *stream);
+
+/*
  * Block selection ("vLLM day-0 support for MiniMax-M3.1-Flash", section "MSA primer"; "MiniMax
  * M3 on vLLM", section "MSA mechanism": local_blocks = 1, init_blocks = 0, the local block is
  * not counted twice). For each row (b, j, g): the eligible blocks are 0..f with

@@ -89,6 +89,11 @@ def test_invalid_arguments_return_codes_without_launch(msa):
     assert ix(by(_cache()), by(_batch()), None, 1, 1, None) == msa.MSA_ERR_INVALID_ARG
     assert ix(by(_cache(ik=None)), by(_batch()), 1, 1, 1, None) == msa.MSA_ERR_INVALID_ARG
     assert ix(by(_cache()), by(_batch(q=0)), 1, 1, 1, None) == msa.MSA_ERR_INVALID_ARG
+    sp = L.msa_indexer_score_shared_prefix
+    assert sp(by(_cache()), by(_batch(mb=4)), 1, -1, 1, None) == msa.MSA_ERR_INVALID_ARG
+    assert sp(by(_cache()), by(_batch(mb=4)), 1, 5, 1, None) == msa.MSA_ERR_INVALID_ARG
+    assert sp(by(_cache()), by(_batch(mb=4)), None, 2, 1, None) == msa.MSA_ERR_INVALID_ARG
+    assert sp(by(_cache(ik=None)), by(_batch(mb=4)), 1, 2, 1, None) == msa.MSA_ERR_INVALID_ARG
     # top-k
     assert L.msa_block_topk(1, by(_batch()), 8, 1, None) == msa.MSA_ERR_UNSUPPORTED
     assert "topk" in msa.msa_last_error()
