@@ -152,10 +152,11 @@ __device__ __forceinline__ void lds_write32(uint32_t a, const u32x4& v0, const u
 
 // A block's logits sv (lane (n, c): head n, tokens tok0 + 32c + 4s + i, unscaled) -> tokens past
 // the query position masked, the online-softmax state (m_run, l_run, o) updated, and the
-// block's probabilities in fp16 (pt, the B operand of O^T += V^T P^T).
+// block's probabilities in fp16, slabs 2h and 2h + 1 in pt[h] (the B operand of one 32-token
+// step of O^T += V^T P^T).
 __device__ __forceinline__ void softmax_block(f32x4 (&sv)[8], int c, int tok0, int p,
                                               float logit_scale, float& m_run, float& l_run,
-                                              f32x4 (&o)[8], f16x4 (&pt)[8]) {
+                                              f32x4 (&o)[8], f16x8 (&pt)[4]) {
     // tokens past the query position: only in the block that holds it, a scalar branch that
     // every other block skips (kept a branch: folded into the selects, the wavefront-uniform
     // condition cost a vector-to-scalar round trip per value)
@@ -193,7 +194,7 @@ __device__ __forceinline__ void softmax_block(f32x4 (&sv)[8], int c, int tok0, i
         for (int i = 0; i < 4; i++) {
             const float e = fast_exp2(fmaf(sv[s][i], logit_scale, -m_new));
             ls += e;
-            pt[s][i] = (_Float16)e;
+            pt[s >> 1][4 * (s & 1) + i] = (_Float16)e;
         }
     l_run += sum_over_c(ls);
 }
@@ -687,26 +688,32 @@ __device__ __forceinline__ void attend_tables(const uint8_t* kf, const uint8_t* 
     for (int s = 0; s < 8; s++) {
         u32x4 a[4];
         lds_read16x4(a, (uint32_t)(uintptr_t)(kf + 4096 * s + 16 * lane));
+        // (every token's steps run: branches around them cost register copies at every merge;
+        // a token that did not select the block gets zero probabilities below)
 #pragma unroll
         for (int t = 0; t < TPW; t++) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            if (sel[t]) {
 #pragma unroll
-                for (int m = 0; m < 4; m++) {
-                    if constexpr (F16)
-                        acc = mfma_f16_k32(__builtin_bit_cast(f16x8, a[m]), __builtin_bit_cast(f16x8, qop[t][m]), acc);
-                    else
-                        acc = mfma_bf16_k32(f16x8_to_bf16x8(__builtin_bit_cast(f16x8, a[m])),
-                                            __builtin_bit_cast(bf16x8, qop[t][m]), acc);
-                }
+            for (int m = 0; m < 4; m++) {
+                if constexpr (F16)
+                    acc = mfma_f16_k32(__builtin_bit_cast(f16x8, a[m]), __builtin_bit_cast(f16x8, qop[t][m]), acc);
+                else
+                    acc = mfma_bf16_k32(f16x8_to_bf16x8(__builtin_bit_cast(f16x8, a[m])),
+                                        __builtin_bit_cast(bf16x8, qop[t][m]), acc);
             }
             sv[t][s] = acc;
         }
     }
-    f16x4 pt[TPW][8];
+    f16x8 pt[TPW][4];
 #pragma unroll
-    for (int t = 0; t < TPW; t++)
-        if (sel[t]) softmax_block(sv[t], c, tok0, p[t], logit_scale[t], m_run[t], l_run[t], o[t], pt[t]);
+    for (int t = 0; t < TPW; t++) {
+        if (sel[t]) {
+            softmax_block(sv[t], c, tok0, p[t], logit_scale[t], m_run[t], l_run[t], o[t], pt[t]);
+        } else {
+#pragma unroll
+            for (int h = 0; h < 4; h++) pt[t][h] = f16x8{};  // adds exactly 0 to the output
+        }
+    }
 #pragma unroll
     for (int dt = 0; dt < 8; dt++) {
         u32x4 a[4];
@@ -715,16 +722,10 @@ __device__ __forceinline__ void attend_tables(const uint8_t* kf, const uint8_t* 
         // 32c + 8h .. +7 in A and the same tokens' probabilities of head n in B (any order of
         // the reduction index works when both operands agree)
 #pragma unroll
-        for (int t = 0; t < TPW; t++) {
-            if (!sel[t]) continue;
+        for (int t = 0; t < TPW; t++)
 #pragma unroll
-            for (int h = 0; h < 4; h++) {
-                const f16x8 pp = {pt[t][2 * h][0], pt[t][2 * h][1], pt[t][2 * h][2], pt[t][2 * h][3],
-                                  pt[t][2 * h + 1][0], pt[t][2 * h + 1][1], pt[t][2 * h + 1][2],
-                                  pt[t][2 * h + 1][3]};
-                o[t][dt] = mfma_f16_k32(__builtin_bit_cast(f16x8, a[h]), pp, o[t][dt]);
-            }
-        }
+            for (int h = 0; h < 4; h++)
+                o[t][dt] = mfma_f16_k32(__builtin_bit_cast(f16x8, a[h]), pt[t][h], o[t][dt]);
     }
 }
 
