@@ -86,6 +86,7 @@ __global__ __launch_bounds__(576) void insert_kernel(uint8_t* __restrict__ k_poo
 // and with one atomic and/or pair otherwise (the two ends of the new range), instead of an
 // atomic pair per nibble and token.
 constexpr int kRun = 8;
+constexpr int kSlotsRunMinTokens = 256;  // inserts from this size on take insert_slots_kernel
 
 __global__ __launch_bounds__(576) void insert_run_kernel(
     uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool, uint8_t* __restrict__ ik_pool,
@@ -160,11 +161,88 @@ __global__ __launch_bounds__(576) void insert_run_kernel(
     }
 }
 
+// Inserts at given slots, eight input tokens per workgroup. When the eight slots are one aligned
+// run of a page (slot[8r + i] = slot[8r] + i, slot[8r] a multiple of 8) they own whole V words
+// (slots are distinct within a call), which are then written with plain stores as in
+// insert_run_kernel; otherwise each token is inserted as insert_kernel does (an atomic pair per
+// V nibble). Prompt prefill hands over consecutive slots, so nearly every group is a run.
+__global__ __launch_bounds__(576) void insert_slots_kernel(
+    uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool, uint8_t* __restrict__ ik_pool,
+    int64_t num_pages, const int64_t* __restrict__ slots, int n, const float* __restrict__ k,
+    const float* __restrict__ v, const float* __restrict__ ik) {
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const float* base;
+    int stride;
+    if (wave < 4) {
+        if (!k) return;
+        base = k + wave * kDim;
+        stride = kKvHeads * kDim;
+    } else if (wave < 8) {
+        if (!v) return;
+        base = v + (wave - 4) * kDim;
+        stride = kKvHeads * kDim;
+    } else {
+        if (!ik) return;
+        base = ik;
+        stride = kDim;
+    }
+    const int t0 = blockIdx.x * kRun;
+    const int nt = min(kRun, n - t0);
+    // every token's slot and values requested before any is used
+    int64_t sl[kRun];
+    f32x2 x[kRun];
+#pragma unroll
+    for (int i = 0; i < kRun; i++) {
+        const int t = t0 + min(i, nt - 1);
+        sl[i] = slots[t];
+        x[i] = *reinterpret_cast<const f32x2*>(base + (int64_t)t * stride + 2 * lane);
+    }
+    const int64_t page0 = sl[0] >> 7;
+    bool run = nt == kRun && sl[0] >= 0 && (sl[0] & 7) == 0 && page0 < num_pages;
+#pragma unroll
+    for (int i = 1; i < kRun; i++) run = run && sl[i] == sl[0] + i;
+    uint8_t* pool = wave < 4 ? k_pool : (wave < 8 ? v_pool : ik_pool);
+    const int64_t head_stride = wave < 8 ? (int64_t)kKvHeads * kHeadPageBytes : kHeadPageBytes;
+    const int head = wave < 8 ? (wave & 3) : 0;
+    if (!run || wave < 4 || wave == 8) {
+        // token by token (V with the per-nibble atomics)
+        for (int i = 0; i < nt; i++) {
+            const int64_t slot = sl[i];
+            if (slot < 0 || (slot >> 7) >= num_pages) continue;
+            uint8_t* dst = pool + (slot >> 7) * head_stride + (int64_t)head * kHeadPageBytes;
+            quantize_store_vector(x[i], dst, (int)(slot & 127), wave >= 4 && wave < 8, lane);
+        }
+        return;
+    }
+    // V of a whole aligned run: the lane's elements e = 2 lane, e + 1, nibble i of their words
+    uint8_t* dst = pool + page0 * head_stride + (int64_t)head * kHeadPageBytes;
+    const int tb = (int)(sl[0] & 127);
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int i = 0; i < kRun; i++) {
+        uint32_t byte, scale;
+        quantize_pair(x[i][0], x[i][1], byte, scale);
+        w0 |= (byte & 15u) << (4 * i);
+        w1 |= (byte >> 4) << (4 * i);
+        if ((lane & 7) == 0) dst[col_scale_offset(tb + i, lane >> 3)] = (uint8_t)scale;
+    }
+    *reinterpret_cast<uint32_t*>(dst + col_code_byte(2 * lane, tb)) = w0;
+    *reinterpret_cast<uint32_t*>(dst + col_code_byte(2 * lane + 1, tb)) = w1;
+}
+
 }  // namespace
 
 hipError_t launch_insert(uint8_t* k_pool, uint8_t* v_pool, uint8_t* ik_pool, int64_t num_pages,
                          const int64_t* slots, const float* k, const float* v, const float* ik,
                          int n, hipStream_t stream) {
+    if (n >= kSlotsRunMinTokens) {
+        hipLaunchKernelGGL(insert_slots_kernel, dim3((n + kRun - 1) / kRun), dim3(576), 0, stream,
+                           k_pool, v_pool, ik_pool, num_pages, slots, n, k, v, ik);
+        return hipGetLastError();
+    }
+    // a decode step's few tokens: one workgroup each, all in parallel (a group of eight that is
+    // no run would take its tokens one after another)
     hipLaunchKernelGGL(insert_kernel<false>, dim3(n), dim3(576), 0, stream, k_pool, v_pool,
                        ik_pool, num_pages, slots, nullptr, nullptr, 0, 1, k, v, ik);
     return hipGetLastError();
