@@ -18,7 +18,7 @@ Each layer's step is captured once in a HIP graph; the timed region replays K st
 Kernel durations for the roofline come from HIP events around graphs of L back-to-back launches
 of one kernel (one per layer), recorded on the stream the kernels run on.
 
-Output: one JSON line (see the keys below). --gpus N > 1 exits: this build runs on one GPU.
+Output: one JSON line (see the keys below). --gpus N > 1 exits: the path runs on one GPU.
 """
 import argparse
 import hashlib
@@ -132,8 +132,8 @@ def main():
         traffic_from(*args.traffic_from)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the MSA decode path "
-              "here is single-GPU, see DESIGN.md for how it would shard.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the MSA decode path "
+              "here is single-GPU; sharding the indexer by pages is not built.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

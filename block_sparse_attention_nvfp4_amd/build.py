@@ -2,7 +2,7 @@
 
     python block_sparse_attention_nvfp4_amd/build.py      # or build() of __graft_entry__
 
-(run as a file: importing the package loads the library this builds)
+(run as a file: importing the package loads the library it builds)
 
 Each .hip file under csrc/ is compiled by hipcc to an object and the objects are linked into
 block_sparse_attention_nvfp4_amd/libmsa.so. Packed-fp32 instructions are disabled for all

@@ -67,7 +67,7 @@ extern "C" {
 /* Status codes */
 #define MSA_OK 0
 #define MSA_ERR_INVALID_ARG (-1) /* null pointer, size out of range */
-#define MSA_ERR_UNSUPPORTED (-2) /* a value this build does not implement (e.g. topk != 16) */
+#define MSA_ERR_UNSUPPORTED (-2) /* a value the library does not implement (e.g. topk != 16) */
 #define MSA_ERR_WORKSPACE (-3)   /* workspace pointer null or smaller than required */
 #define MSA_ERR_HIP (-4)         /* the HIP runtime reported an error at launch */
 

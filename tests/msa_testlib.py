@@ -68,7 +68,7 @@ def gpu_sequence_caches(cache, w: mi.Workload, b: int):
 
 
 # ------------------------------------------------------------------ GPU side
-class GpuRun:
+class DeviceWorkload:
     def __init__(self, w: mi.Workload, device: str = "cuda", chunk: int = 1 << 15,
                  mode: str = "step", snapshot: bool = False):
         import block_sparse_attention_nvfp4_amd as msa

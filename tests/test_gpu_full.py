@@ -21,7 +21,7 @@ import torch
 
 import msa_inputs as mi
 import oracle
-from msa_testlib import (GpuRun, bf16_to_f64, check_attention, check_scores, check_selection,
+from msa_testlib import (DeviceWorkload, bf16_to_f64, check_attention, check_scores, check_selection,
                          gpu_block_caches, oracle_rows, score_tolerance)
 
 pytestmark = pytest.mark.gpu
@@ -40,7 +40,7 @@ def full(request):
     cfg = request.param
     w = mi.full_workload(cfg)
     _log(f"[full {w.name}] batch {w.batch} q_len {w.q_len} ctx {w.ctx_lens} pages {w.num_pages}")
-    g = GpuRun(w)
+    g = DeviceWorkload(w)
     out = g.run()
     _log(f"[full {w.name}] step done")
     yield cfg, w, g, out

@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import msa_inputs as mi
-from msa_testlib import GpuRun
+from msa_testlib import DeviceWorkload
 
 pytestmark = pytest.mark.gpu
 
@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 def test_graph_replays_match_eager(cfg, kw):
     print(f"[graph] config {cfg} {kw}", flush=True)
     w = mi.make_workload(cfg, **kw)
-    g = GpuRun(w)
+    g = DeviceWorkload(w)
     eager_out = g.run().clone()
     eager_ids = g.step.block_ids.clone()
     eager_scores = g.step.block_scores.clone()

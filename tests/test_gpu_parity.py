@@ -14,7 +14,7 @@ import torch
 
 import msa_inputs as mi
 import oracle
-from msa_testlib import (GpuRun, bf16_to_f64, check_attention, check_scores, check_selection,
+from msa_testlib import (DeviceWorkload, bf16_to_f64, check_attention, check_scores, check_selection,
                          gpu_sequence_caches, oracle_sequence, score_tolerance)
 
 pytestmark = pytest.mark.gpu
@@ -55,7 +55,7 @@ def run(request):
     cfg, kw = CASES[request.param]
     _log(f"[case {request.param}] config {cfg} {kw}")
     w = mi.make_workload(cfg, **kw)
-    g = GpuRun(w, snapshot=True)
+    g = DeviceWorkload(w, snapshot=True)
     out = g.run()
     # the first step's results (msa_decode_step from the prefix-only cache)
     g.first = dict(scores=g.step.block_scores.clone(), ids=g.step.block_ids.clone(),

@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import msa_inputs as mi
-from msa_testlib import GpuRun, bf16_to_f64, check_attention, oracle_rows
+from msa_testlib import DeviceWorkload, bf16_to_f64, check_attention, oracle_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -50,7 +50,7 @@ def test_tile_attention_random_selections():
     w = mi.make_workload(3, batch=8, ctx_lens=[3000, 20000, 9000, 30000, 4100, 25000, 8200, 2500],
                          q_len=Q_LEN)
     assert w.batch * w.q_len * 4 >= 1024  # the token-tile launch shape
-    g = GpuRun(w)
+    g = DeviceWorkload(w)
     g.run()
     import block_sparse_attention_nvfp4_amd as msa
     rng = np.random.default_rng(11)
