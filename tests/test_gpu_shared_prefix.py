@@ -58,9 +58,15 @@ def test_shared_prefix_indexer():
     shared = torch.full_like(plain, 7.0)
     msa.msa_indexer_score(cache, batch, q_idx, plain)
     msa.msa_indexer_score_shared_prefix(cache, batch, q_idx, P, shared)
+    none_shared = torch.full_like(plain, 7.0)  # prefix_blocks = 0: every block per sequence
+    msa.msa_indexer_score_shared_prefix(cache, batch, q_idx, 0, none_shared)
+    part = torch.full_like(plain, 7.0)  # a shorter shared range than the pages allow
+    msa.msa_indexer_score_shared_prefix(cache, batch, q_idx, P // 2 + 1, part)
     torch.cuda.synchronize()
     got, want = shared.cpu().numpy(), plain.cpu().numpy()
     assert np.array_equal(got, want)
+    assert np.array_equal(none_shared.cpu().numpy(), want)
+    assert np.array_equal(part.cpu().numpy(), want)
     for b in (0, 3, 5):
         codes, scales = oracle.quantize(ik[b])
         qb = qi_bits[b * Q:(b + 1) * Q]
