@@ -132,3 +132,116 @@ def test_head_to_group_map_is_contiguous():
     out = oracle.sparse_attention_token(qb, kc, ks, vc, vs, T, oracle.dense_ids(T - 1), T - 1, 0.1)
     for h in range(64):
         assert np.allclose(out[h], vals[h // 16], atol=1e-13)
+
+
+# ---------------------------------------------------------------- exact softmax weightings
+# The pins below build the NVFP4 caches byte by byte (E4M3 scale byte 0x38 = 1.0 and E2M1
+# codes of exact grid values, not through the oracle's quantizer) and bf16 queries whose dot
+# products with every key are exact, so the softmax weights follow in closed form from the
+# logit differences: a difference of ln r between two keys gives weights in the ratio r.
+# One-hot values then expose each key's weight directly in one output dimension. They fail
+# for a wrong logit scale (e.g. a doubled scale), a base-2 exponential in place of the natural
+# one, a missing max subtraction (logits above 709), a key past the query position or a
+# missing key in the denominator.
+
+E2M1_CODE = {0.0: 0, 0.5: 1, 1.0: 2, 1.5: 3, 2.0: 4, 3.0: 5, 4.0: 6, 6.0: 7}
+SCALE_ONE = 0x38  # E4M3: exponent field 7, mantissa 0 -> 2^0
+
+
+def hand_cache(T, entries):
+    """NVFP4 codes/scales [T][4][64] / [T][4][8], every group of every head scaled by 1.0.
+
+    entries: {(token, dim): value} set in all four KV heads; value on the E2M1 grid.
+    """
+    codes = np.zeros((T, 4, 64), np.uint8)
+    scales = np.full((T, 4, 8), SCALE_ONE, np.uint8)
+    for (t, d), x in entries.items():
+        nib = E2M1_CODE[abs(x)] | (8 if x < 0 else 0)
+        codes[t, :, d // 2] |= nib << (4 * (d % 2))
+    return codes, scales
+
+
+def query_bits(rows):
+    """bf16 bit patterns [64][128] of a query whose head h has the (dim -> value) map rows(h);
+    every value is a power of two or zero, so it is exact in bf16."""
+    q = np.zeros((64, 128), np.float32)
+    for h in range(64):
+        for d, x in rows(h).items():
+            q[h, d] = x
+    b = (q.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal((b.astype(np.uint32) << 16).view(np.float32), q)
+    return b
+
+
+def test_ln3_logit_gap_gives_three_to_one_weights():
+    # token 0: key 4 e0, value 6 e0; token 1: key 6 e0, value 6 e1. Query +-e0 per head parity:
+    # dot products +-4 and +-6, a gap of 2; scale ln(3)/2 makes the gap ln 3, weights 1/4, 3/4
+    # (swapped for the heads with the negated query).
+    kc, ks = hand_cache(2, {(0, 0): 4.0, (1, 0): 6.0})
+    vc, vs = hand_cache(2, {(0, 0): 6.0, (1, 1): 6.0})
+    qb = query_bits(lambda h: {0: 1.0 if h % 2 == 0 else -1.0})
+    ids = oracle.dense_ids(1)
+    out = oracle.sparse_attention_token(qb, kc, ks, vc, vs, 2, ids, 1, math.log(3.0) / 2)
+    for h in range(64):
+        want = np.zeros(128)
+        want[0], want[1] = (1.5, 4.5) if h % 2 == 0 else (4.5, 1.5)
+        assert np.allclose(out[h], want, rtol=0, atol=1e-12), h
+    # the negated scale swaps the weights of every head; scale 0 gives the plain mean
+    neg = oracle.sparse_attention_token(qb, kc, ks, vc, vs, 2, ids, 1, -math.log(3.0) / 2)
+    zero = oracle.sparse_attention_token(qb, kc, ks, vc, vs, 2, ids, 1, 0.0)
+    for h in range(64):
+        a, b = (4.5, 1.5) if h % 2 == 0 else (1.5, 4.5)
+        assert abs(neg[h, 0] - a) <= 1e-12 and abs(neg[h, 1] - b) <= 1e-12, h
+        assert abs(zero[h, 0] - 3.0) <= 1e-12 and abs(zero[h, 1] - 3.0) <= 1e-12, h
+        assert np.all(neg[h, 2:] == 0) and np.all(zero[h, 2:] == 0)
+
+
+def test_geometric_logits_give_one_two_four_sevenths():
+    # keys 2, 4, 6 along e0 with query e0: logits 2c, 4c, 6c; c = ln(2)/2 makes consecutive
+    # gaps ln 2, so the weights are 1/7, 2/7, 4/7; values 6 e0, 6 e1, 6 e2 show each weight.
+    kc, ks = hand_cache(3, {(0, 0): 2.0, (1, 0): 4.0, (2, 0): 6.0})
+    vc, vs = hand_cache(3, {(0, 0): 6.0, (1, 1): 6.0, (2, 2): 6.0})
+    qb = query_bits(lambda h: {0: 1.0})
+    out = oracle.sparse_attention_token(qb, kc, ks, vc, vs, 3, oracle.dense_ids(2), 2,
+                                        math.log(2.0) / 2)
+    for h in range(64):
+        assert np.allclose(out[h, :3], [6 / 7, 12 / 7, 24 / 7], rtol=0, atol=1e-12), h
+        assert np.all(out[h, 3:] == 0)
+
+
+def test_large_logits_need_the_max_subtraction():
+    # query e0 + 2^-10 e1; keys 6 e0 and 6 e0 + 6 e1: dot products 6 and 6 + 6 * 2^-10. With
+    # scale ln(3) / (6 * 2^-10) ~ 187.5 the logits are ~1125 and ~1126 (exp overflows fp64
+    # without subtracting the maximum) and their gap is ln 3: weights 1/4, 3/4.
+    kc, ks = hand_cache(2, {(0, 0): 6.0, (1, 0): 6.0, (1, 1): 6.0})
+    vc, vs = hand_cache(2, {(0, 0): 6.0, (1, 1): 6.0})
+    qb = query_bits(lambda h: {0: 1.0, 1: 2.0 ** -10})
+    scale = math.log(3.0) / (6 * 2.0 ** -10)
+    out = oracle.sparse_attention_token(qb, kc, ks, vc, vs, 2, oracle.dense_ids(1), 1, scale)
+    assert np.all(np.isfinite(out))
+    for h in range(64):
+        assert np.allclose(out[h, :2], [1.5, 4.5], rtol=0, atol=1e-10), h
+
+
+def test_weights_count_every_visible_key_and_no_later_one():
+    # T = 210, query position p = 200 (a draft token: tokens 201..209 exist but come after it).
+    # Blocks 0 and 1 selected; every key is 0 except token 5 (6 e0), token 200 (6 e0 + 6 e1) and
+    # token 205 (6 e0 + 6 e1 + 6 e2, after the query: must not count). Query e0 + e1, scale
+    # ln(127)/6: token 5 has weight 127/Z, token 200 127^2/Z and the other 199 visible keys
+    # 1/Z each, Z = 199 + 127 + 127^2.
+    T, p = 210, 200
+    kc, ks = hand_cache(T, {(5, 0): 6.0, (200, 0): 6.0, (200, 1): 6.0,
+                            (205, 0): 6.0, (205, 1): 6.0, (205, 2): 6.0})
+    vc, vs = hand_cache(T, {(5, 0): 6.0, (200, 1): 6.0, (205, 2): 6.0})
+    qb = query_bits(lambda h: {0: 1.0, 1: 1.0})
+    ids = np.array([[0, 1] + [-1] * 14] * 4, np.int32)
+    out = oracle.sparse_attention_token(qb, kc, ks, vc, vs, T, ids, p, math.log(127.0) / 6)
+    Z = 199 + 127 + 127 ** 2
+    for h in range(64):
+        assert np.allclose(out[h, :3], [6 * 127 / Z, 6 * 127 ** 2 / Z, 0.0], rtol=0, atol=1e-12), h
+    # only block 1 selected: token 200 and the 72 zero keys 128..199 remain
+    ids1 = np.array([[1] + [-1] * 15] * 4, np.int32)
+    out1 = oracle.sparse_attention_token(qb, kc, ks, vc, vs, T, ids1, p, math.log(127.0) / 6)
+    Z1 = 72 + 127 ** 2
+    for h in range(64):
+        assert np.allclose(out1[h, :3], [0.0, 6 * 127 ** 2 / Z1, 0.0], rtol=0, atol=1e-12), h
