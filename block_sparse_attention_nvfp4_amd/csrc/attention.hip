@@ -58,6 +58,12 @@ __device__ __forceinline__ uint16_t bf16_bits_rne(float x) {
     return __builtin_bit_cast(uint16_t, h);
 }
 
+// A mask of the first n bytes of a 32-bit word (all four for n >= 4, none for n <= 0): applied to
+// four consecutive E4M3 scale bytes, it zeroes the scales of the tokens past the last valid one.
+__device__ __forceinline__ uint32_t keep_bytes(int n) {
+    return n >= 4 ? 0xFFFFFFFFu : (n <= 0 ? 0u : (1u << (8 * n)) - 1u);
+}
+
 // Copy the K and V pages of one (block, group) into an LDS buffer: 18 direct 16-byte loads.
 __device__ __forceinline__ void block_to_lds(const uint8_t* kp, const uint8_t* vp, uint8_t* buf,
                                              int lane) {
@@ -286,6 +292,15 @@ __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c
         u32x4 raw;
         if constexpr (NEXT) raw = lds_read16(vbase + kCodeBytes + lane * 16);
         else raw = *reinterpret_cast<const u32x4*>(buf + kHeadPageBytes + kCodeBytes + lane * 16);
+        // in the block of the query position, the scales of later tokens read as 0: their slots
+        // may hold any bytes (an E4M3 NaN among them), and a zero probability times a NaN value
+        // would still reach the output through P.V
+        if (tok0 + kBlock - 1 > p) {
+            asm volatile("");
+            const int first = tok0 + 16 * (lane & 7);
+#pragma unroll
+            for (int i = 0; i < 4; i++) raw[i] &= keep_bytes(p + 1 - (first + 4 * i));
+        }
         u32x4 h0, h1;
 #pragma unroll
         for (int i = 0; i < 2; i++) {
@@ -629,7 +644,7 @@ __device__ __forceinline__ void lds_write16x4(uint32_t a, const u32x4 (&v)[4]) {
 //   vf + 4096 dt + 1024 h + 16 l: lane l's A operands of O^T steps (dim tile dt, token slabs
 //                                 2h and 2h + 1), two f16x4
 __device__ __forceinline__ void dequant_tables(const uint8_t* page, uint8_t* kf, uint8_t* vf,
-                                               int wave, int lane) {
+                                               int wave, int lane, int valid) {
     const int n = lane & 15, c = lane >> 4;
     const uint32_t pbase = (uint32_t)(uintptr_t)page;
     u32x4 kc[4], vr[4];
@@ -654,7 +669,14 @@ __device__ __forceinline__ void dequant_tables(const uint8_t* page, uint8_t* kf,
     for (int m = 0; m < 4; m++) ko[m] = __builtin_bit_cast(u32x4, dequant8_f16(code[m], m < 2 ? s0 : s1));
     lds_write16x4((uint32_t)(uintptr_t)(kf + 4096 * wave + 16 * lane), ko);
     // V: tokens 32c + 4s .. +3 of slab s take the scale pairs (4s, 4s + 1), (4s + 2, 4s + 3)
-    const uint32_t raw[8] = {vr[0][0], vr[0][1], vr[0][2], vr[0][3], vr[1][0], vr[1][1], vr[1][2], vr[1][3]};
+    uint32_t raw[8] = {vr[0][0], vr[0][1], vr[0][2], vr[0][3], vr[1][0], vr[1][1], vr[1][2], vr[1][3]};
+    // tokens at or past the context length (`valid` tokens of the block are in the cache): their
+    // scales read as 0, so bytes never written (an E4M3 NaN among them) cannot reach the output
+    // through a zero probability
+    if (valid < kBlock) {
+#pragma unroll
+        for (int sl = 0; sl < 8; sl++) raw[sl] &= keep_bytes(valid - (32 * c + 4 * sl));
+    }
     u32x4 vo[4];
 #pragma unroll
     for (int h = 0; h < 4; h++) {
@@ -896,7 +918,7 @@ __global__ __launch_bounds__(kTileWaves * 64) void attention_tile_kernel(
         // (registers are the limit here: held, they were spilled to scratch)
         int lane_i = lane;
         asm volatile("" : "+v"(lane_i));
-        dequant_tables(pages[u & 1], kf, vf, wave, lane_i);
+        dequant_tables(pages[u & 1], kf, vf, wave, lane_i, T - bid * kBlock);
         // the tables are complete for every wavefront (LDS only: the next block's loads stay
         // in flight)
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");

@@ -70,11 +70,15 @@ def gpu_sequence_caches(cache, w: mi.Workload, b: int):
 # ------------------------------------------------------------------ GPU side
 class DeviceWorkload:
     def __init__(self, w: mi.Workload, device: str = "cuda", chunk: int = 1 << 15,
-                 mode: str = "step", snapshot: bool = False):
+                 mode: str = "step", snapshot: bool = False, fill: int = 0):
         import block_sparse_attention_nvfp4_amd as msa
         self.msa = msa
         self.w = w
         self.cache = msa.Cache.allocate(w.num_pages, device)
+        if fill:
+            # every byte no insert writes keeps this value (0xFF: E4M3 NaN scales, -6 codes)
+            for t in (self.cache.k, self.cache.v, self.cache.ik):
+                t.fill_(fill)
         self.table = torch.from_numpy(w.block_table).to(device)
         self.ctx = torch.tensor(w.ctx_lens, dtype=torch.int32, device=device)
         self.batch = msa.Batch(self.table, self.ctx, w.q_len)
@@ -266,3 +270,24 @@ def check_attention(gpu: np.ndarray, ref: np.ndarray):
 
 def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check_step_against_oracle(w: mi.Workload, scores: np.ndarray, ids: np.ndarray,
+                              att: np.ndarray, max_tokens: int = 8) -> int:
+    """A step's block scores, selection and attention outputs (request-major rows) against the
+    oracle, sequence by sequence: scores within the fp32 bound, selections bit-exact where the
+    margin holds (valid otherwise), attention of up to `max_tokens` query tokens per sequence over
+    the GPU's own (validated) selection. Returns the number of rows exempt from the bit compare."""
+    q = w.q_len
+    exempt_total = 0
+    for b in range(w.batch):
+        T = w.ctx_lens[b]
+        rows = slice(b * q, (b + 1) * q)
+        ref = oracle_sequence(w, b)
+        tol = score_tolerance(mi.bf16_bits(w.q_idx[rows]), *ref["ik"])
+        check_scores(scores[rows], ref["scores"], tol)
+        exempt_total += check_selection(ids[rows], ref["ids"], ref["margins"], ref["scores"], tol, T, q)
+        toks = list(range(q)) if q <= max_tokens else sorted(set([0, 1, q // 2, q - 2, q - 1]))
+        ref = oracle_sequence(w, b, attention_tokens=toks, ids_override=ids[rows])
+        check_attention(att[rows][toks], ref["attention"])
+    return exempt_total

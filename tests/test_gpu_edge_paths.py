@@ -1,0 +1,147 @@
+"""Kernel paths that ordinary seeded inputs never reach, against the oracle (needs an MI355X).
+
+1. Query rows with a dynamic range too wide for fp16. The decode indexer and the attention scale
+   each query row by a power of two into fp16 for the matrix cores; a row with values more than
+   about 2^30 apart cannot convert exactly, and its wavefront then runs the bf16 matrix-core path
+   (same exact products, fp32 sums). Every N(0,1) row converts, so only constructed rows reach
+   that path; each test asserts on the host that its rows do not convert exactly by the rule the
+   kernels apply (largest magnitude scaled into [2^14, 2^15)).
+2. Selection rows of more than 4,097 blocks (contexts past 524,416 tokens, up to the 1M-token
+   contexts of "MiniMax M3 on vLLM"): the workgroup radix select, both with the keys held in
+   registers (up to 4,096 candidates) and re-read from memory, on constructed tie, signed-zero
+   and -inf rows, bit for bit against the oracle.
+3. Pools whose bytes past every context length are 0xFF (E4M3 NaN scales): the attention must
+   ignore them (a zero probability times a NaN value would still be NaN), as must the indexer.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import msa_inputs as mi
+import oracle
+from msa_testlib import DeviceWorkload, bf16_to_f64, check_step_against_oracle
+from test_gpu_selection import _patterns
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _fp16_exact(row: np.ndarray) -> bool:
+    """Whether a bf16 row (as fp32 values) converts exactly to fp16 once scaled by the power of
+    two that puts its largest magnitude in [2^14, 2^15)."""
+    mx = float(np.abs(row).max())
+    if mx == 0.0:
+        return True
+    e = int(np.frexp(np.float32(mx))[1])  # mx in [2^(e-1), 2^e)
+    scaled = np.ldexp(row.astype(np.float64), 15 - e).astype(np.float32)
+    return bool(np.array_equal(scaled.astype(np.float16).astype(np.float32), scaled))
+
+
+def _wide_row(rng, n=128) -> torch.Tensor:
+    """One value of 1 and the rest N(0,1) * 1e-12: a relative range of about 2^40, in bf16."""
+    x = rng.standard_normal(n).astype(np.float32) * np.float32(1e-12)
+    x[rng.integers(0, n)] = 1.0
+    return torch.from_numpy(x).to(torch.bfloat16)
+
+
+WIDE_CASES = {
+    # (config, overrides, [(token row, group) of q_idx], [(token row, head range) of q])
+    "q1_batched": (2, dict(batch=3, ctx=5000), [(1, 2)], [(0, range(16, 32)), (2, range(48, 64))]),
+    "q4_spec": (3, dict(batch=2, ctx=6000), [(1, 2), (4, 0)], [(2, range(16, 32)), (7, range(0, 16))]),
+    "q16_gemm": (3, dict(batch=1, ctx=6000, q_len=16), [(3, 1), (15, 3)], [(5, range(32, 48))]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(WIDE_CASES))
+def test_wide_range_queries_take_the_bf16_path(name):
+    cfg, kw, qi_rows, q_rows = WIDE_CASES[name]
+    _log(f"[wide {name}] config {cfg} {kw}")
+    w = mi.make_workload(cfg, **kw)
+    rng = np.random.default_rng(17)
+    for r, g in qi_rows:
+        w.q_idx[r, g] = _wide_row(rng)
+        assert not _fp16_exact(w.q_idx[r, g].float().numpy()), (name, "q_idx", r, g)
+    for r, heads in q_rows:
+        for h in heads:
+            w.q[r, h] = _wide_row(rng)
+        assert not _fp16_exact(w.q[r, heads[0]].float().numpy()), (name, "q", r)
+    # an ordinary row of the same workload still converts (the fp16 path runs beside it)
+    assert _fp16_exact(w.q[0, 0].float().numpy())
+    g = DeviceWorkload(w)
+    out = g.run()
+    exempt = check_step_against_oracle(w, g.step.block_scores.cpu().numpy(),
+                                       g.step.block_ids.cpu().numpy(), bf16_to_f64(out),
+                                       max_tokens=16)
+    _log(f"[wide {name}] ok, {exempt} rows below margin")
+
+
+@pytest.mark.parametrize("max_blocks", [4098, 8192])
+def test_radix_selection_of_long_rows(max_blocks):
+    import block_sparse_attention_nvfp4_amd as msa
+    rng = np.random.default_rng(3 + max_blocks)
+    pats = _patterns(max_blocks, rng)
+    # eligible counts on both sides of 4,097 (the wavefront kernel's limit) and of 4,096
+    # candidates (keys in registers vs re-read from memory)
+    n_list = [16, 17, 1000, 4096, 4097, 4098, 4099, max_blocks - 1, max_blocks]
+    n_list = sorted(set(n for n in n_list if n <= max_blocks))
+    rows = [pats[(i * 4 + g) % len(pats)] for i in range(len(n_list)) for g in range(4)]
+    scores = np.stack(rows).reshape(len(n_list), 4, max_blocks).astype(np.float32)
+    ctx = torch.tensor([128 * (n - 1) + 1 for n in n_list], dtype=torch.int32, device="cuda")
+    table = torch.zeros((len(n_list), max_blocks), dtype=torch.int32, device="cuda")
+    b = msa.Batch(table, ctx, 1)
+    s_dev = torch.from_numpy(scores).cuda()
+    ids = torch.full((len(n_list), 4, 16), -7, dtype=torch.int32, device="cuda")
+    _log(f"[radix {max_blocks}] msa_block_topk")
+    msa.msa_block_topk(s_dev, b, 16, ids)
+    # the fused call, which runs the same selection kernel for rows this long, then the
+    # attention over an all-zero one-page cache (only its ids output is checked here)
+    cache = msa.Cache.allocate(1)
+    q = torch.zeros((len(n_list), 64, 128), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty_like(q)
+    ws_bytes = msa.msa_sparse_attn_workspace_bytes(b)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda") if ws_bytes else None
+    ids2 = torch.full_like(ids, -7)
+    _log(f"[radix {max_blocks}] msa_select_attn_decode")
+    msa.msa_select_attn_decode(cache, b, s_dev, 16, ids2, q, 0.088, out, ws)
+    torch.cuda.synchronize()
+    for path, t in (("topk", ids), ("select_attention", ids2)):
+        got = t.cpu().numpy()
+        for i, n in enumerate(n_list):
+            for g in range(4):
+                want, _ = oracle.block_topk(scores[i, g].astype(np.float64), n)
+                assert np.array_equal(got[i, g], want), (path, max_blocks, n, g, got[i, g], want)
+    assert torch.isfinite(out.float()).all()
+
+
+FILL_CASES = {
+    # partial last blocks everywhere; decode (q = 1, 4) and the token-tile attention (q = 256,
+    # 1,024 rows), fused step and the four separate calls
+    "ragged_q1": (4, dict(ctx_lens=[3000, 129, 7777, 1, 17 * 128 + 5, 2048 + 77])),
+    "spec_q4": (3, dict(batch=2, ctx_lens=[6000, 2 * 128 + 2])),
+    "prefill_q256": (5, dict(batch=1, ctx=2048 + 256 + 50, q_len=256)),
+}
+
+
+@pytest.mark.parametrize("mode", ["step", "separate"])
+@pytest.mark.parametrize("name", sorted(FILL_CASES))
+def test_unwritten_bytes_past_the_context_are_ignored(name, mode):
+    cfg, kw = FILL_CASES[name]
+    _log(f"[fill {name} {mode}] config {cfg} {kw}")
+    w = mi.make_workload(cfg, **kw)
+    g = DeviceWorkload(w, mode=mode, fill=0xFF)
+    # the last page of some sequence does hold 0xFF bytes past its context
+    b = int(np.argmax([(t % 128) != 0 for t in w.ctx_lens]))
+    page = int(w.block_table[b, (w.ctx_lens[b] - 1) // 128])
+    assert int(g.cache.v[page, 0, -1]) == 0xFF and int(g.cache.k[page, 0, -1]) == 0xFF
+    out = g.run()
+    assert torch.isfinite(out.float()).all(), (name, mode, "non-finite outputs")
+    scores = g.step.block_scores.cpu().numpy()
+    assert not np.isnan(scores).any(), (name, mode, "NaN scores")
+    check_step_against_oracle(w, scores, g.step.block_ids.cpu().numpy(), bf16_to_f64(out))
+    _log(f"[fill {name} {mode}] ok")

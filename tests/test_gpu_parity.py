@@ -14,8 +14,8 @@ import torch
 
 import msa_inputs as mi
 import oracle
-from msa_testlib import (DeviceWorkload, bf16_to_f64, check_attention, check_scores, check_selection,
-                         gpu_sequence_caches, oracle_sequence, score_tolerance)
+from msa_testlib import (DeviceWorkload, bf16_to_f64, check_attention, check_step_against_oracle,
+                         gpu_sequence_caches, oracle_sequence)
 
 pytestmark = pytest.mark.gpu
 
@@ -78,22 +78,8 @@ def test_insert_bit_exact(run):
 
 def test_indexer_topk_attention(run):
     name, w, g, out = run
-    q = w.q_len
-    scores = g.step.block_scores.cpu().numpy()
-    ids = g.step.block_ids.cpu().numpy()
-    att = bf16_to_f64(out)
-    exempt_total = 0
-    for b in range(w.batch):
-        T = w.ctx_lens[b]
-        rows = slice(b * q, (b + 1) * q)
-        ref = oracle_sequence(w, b)
-        tol = score_tolerance(mi.bf16_bits(w.q_idx[rows]), *ref["ik"])
-        check_scores(scores[rows], ref["scores"], tol)
-        exempt_total += check_selection(ids[rows], ref["ids"], ref["margins"], ref["scores"], tol, T, q)
-        # attention of up to 8 query tokens of the sequence, given the GPU's (validated) selection
-        toks = list(range(q)) if q <= 8 else sorted(set([0, 1, q // 2, q - 2, q - 1]))
-        ref = oracle_sequence(w, b, attention_tokens=toks, ids_override=ids[rows])
-        check_attention(att[rows][toks], ref["attention"])
+    exempt_total = check_step_against_oracle(w, g.step.block_scores.cpu().numpy(),
+                                             g.step.block_ids.cpu().numpy(), bf16_to_f64(out))
     _log(f"[case {name}] rows below margin (validated, not bit-compared): {exempt_total}")
 
 
