@@ -15,7 +15,7 @@ import torch
 import msa_inputs as mi
 import oracle
 from msa_testlib import (DeviceWorkload, bf16_to_f64, check_attention, check_step_against_oracle,
-                         gpu_sequence_caches, oracle_sequence)
+                         gpu_sequence_caches, oracle_sequence, score_tolerance)
 
 pytestmark = pytest.mark.gpu
 
