@@ -20,6 +20,8 @@ HIP stream into the C calls, with the same names:
     msa_insert_indexer_score(cache, batch, k, v, ik, q_idx, block_scores)  # insert + indexer
     msa_decode_step(cache, batch, k, v, ik, q_idx, q, topk, softmax_scale, block_scores,
                     block_ids, out, workspace)   # the two launches above and below in one call
+    msa_decode_step_noalloc(cache, batch, k, v, ik, q_idx, q, topk, softmax_scale, block_scores,
+                            block_ids, out)     # the same with the library's static workspace
 
 A non-zero status raises MSAError. There is no fallback: importing fails loudly when the
 library has not been built (python block_sparse_attention_nvfp4_amd/build.py).
@@ -56,7 +58,8 @@ EXPORTED = ("msa_page_bytes", "msa_kv_insert_nvfp4", "msa_indexer_score", "msa_i
             "msa_block_topk",
             "msa_block_topk_window", "msa_block_topk_local", "msa_block_topk_merge",
             "msa_sparse_attn_workspace_bytes", "msa_sparse_attn_decode", "msa_select_attn_decode",
-            "msa_insert_indexer_score", "msa_decode_step", "msa_last_error", "msa_version")
+            "msa_insert_indexer_score", "msa_decode_step", "msa_decode_step_noalloc",
+            "msa_last_error", "msa_version")
 
 
 class MSAError(RuntimeError):
@@ -116,6 +119,9 @@ def _load() -> ctypes.CDLL:
     L.msa_decode_step.restype = ctypes.c_int
     L.msa_decode_step.argtypes = [ctypes.POINTER(_Cache), ctypes.POINTER(_Batch), vp, vp, vp, vp,
                                   vp, i32, ctypes.c_float, vp, vp, vp, vp, sz, vp]
+    L.msa_decode_step_noalloc.restype = ctypes.c_int
+    L.msa_decode_step_noalloc.argtypes = [ctypes.POINTER(_Cache), ctypes.POINTER(_Batch), vp, vp,
+                                          vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp]
     L.msa_last_error.restype, L.msa_last_error.argtypes = ctypes.c_char_p, []
     L.msa_version.restype, L.msa_version.argtypes = ctypes.c_char_p, []
     return L
@@ -389,6 +395,26 @@ def msa_decode_step(cache: Cache, batch: Batch, k: torch.Tensor, v: torch.Tensor
                                _ptr(block_ids, torch.int32, "block_ids"),
                                _ptr(out, torch.bfloat16, "out"), ws_ptr, ws_bytes,
                                _stream(stream)))
+
+
+def msa_decode_step_noalloc(cache: Cache, batch: Batch, k: torch.Tensor, v: torch.Tensor,
+                            ik: torch.Tensor, q_idx: torch.Tensor, q: torch.Tensor, topk: int,
+                            softmax_scale: float, block_scores: torch.Tensor,
+                            block_ids: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    """msa_decode_step with the library's static workspace (no workspace argument)."""
+    _check_step_shapes(batch, k=k, v=v, ik=ik, q_idx=q_idx, q=q, out=out,
+                       block_scores=block_scores)
+    if tuple(block_ids.shape) != (batch.rows, KV_HEADS, int(topk)):
+        raise ValueError("block_ids: expected [batch*q_len][4][topk]")
+    _check(lib.msa_decode_step_noalloc(ctypes.byref(cache._c), ctypes.byref(batch._c),
+                                       _ptr(k, torch.float32, "k"), _ptr(v, torch.float32, "v"),
+                                       _ptr(ik, torch.float32, "ik"),
+                                       _ptr(q_idx, torch.bfloat16, "q_idx"),
+                                       _ptr(q, torch.bfloat16, "q"), int(topk),
+                                       float(softmax_scale),
+                                       _ptr(block_scores, torch.float32, "block_scores"),
+                                       _ptr(block_ids, torch.int32, "block_ids"),
+                                       _ptr(out, torch.bfloat16, "out"), _stream(stream)))
 
 
 def default_softmax_scale() -> float:

@@ -3,6 +3,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "../../include/msa.h"
 #include "kernels.hpp"
 
@@ -53,6 +55,35 @@ int check_cache(const msa_cache_t* cache, const char* fn, bool need_kv, bool nee
         return fail(MSA_ERR_INVALID_ARG, "%s: K or V pool is NULL", fn);
     if (need_ik && !cache->ik) return fail(MSA_ERR_INVALID_ARG, "%s: index-key pool is NULL", fn);
     return MSA_OK;
+}
+
+// The attention workspace of msa_decode_step_noalloc: a device array of the library, one copy
+// per GPU, which each device keeps until the process ends. Host code never passes the array's
+// name to a kernel (on the host it only stands for the symbol); it asks the runtime for the
+// array's device address once per device and uses that pointer.
+constexpr size_t kNoallocScratchBytes = (size_t)20 << 20;  // 20 MiB
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device (looked up on the first call there).
+hipError_t noalloc_scratch(void** ptr) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return err;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace
@@ -327,6 +358,46 @@ int msa_decode_step(const msa_cache_t* cache, const msa_batch_t* batch, const fl
                                                    batch->batch, batch->max_blocks, batch->q_len,
                                                    block_scores, block_ids, q, softmax_scale, out,
                                                    workspace, s),
+                      fn);
+}
+
+int msa_decode_step_noalloc(const msa_cache_t* cache, const msa_batch_t* batch, const float* k,
+                            const float* v, const float* ik, const uint16_t* q_idx,
+                            const uint16_t* q, int32_t topk, float softmax_scale,
+                            float* block_scores, int32_t* block_ids, uint16_t* out,
+                            void* stream) {
+    static const char* fn = "msa_decode_step_noalloc";
+    int rc = check_insert_indexer(cache, batch, k, v, ik, q_idx, block_scores, fn);
+    if (rc) return rc;
+    if (!q || !block_ids || !out)
+        return fail(MSA_ERR_INVALID_ARG, "%s: q, block_ids or out is NULL", fn);
+    if (topk != MSA_TOPK) return fail(MSA_ERR_UNSUPPORTED, "%s: topk=%d (only 16 is built)", fn, topk);
+    const size_t need = msa::attn_workspace_bytes(batch->batch, batch->q_len);
+    if (need > kNoallocScratchBytes)
+        return fail(MSA_ERR_WORKSPACE,
+                    "%s: this batch needs %zu bytes of attention workspace; the library's static "
+                    "scratch holds %zu (use msa_decode_step with a workspace)",
+                    fn, need, kNoallocScratchBytes);
+    const hipStream_t s = (hipStream_t)stream;
+    void* ws = nullptr;
+    if (need > 0) {
+        if ((rc = hip_status(noalloc_scratch(&ws), fn))) return rc;
+        // the counters must start at zero whatever an earlier call left there
+        if ((rc = hip_status(msa::launch_attn_workspace_clear(ws, batch->batch, batch->q_len, s),
+                             fn)))
+            return rc;
+    }
+    rc = hip_status(msa::launch_insert_indexer(cache->k, cache->v, cache->ik, cache->num_pages,
+                                               batch->block_table, batch->ctx_lens, batch->batch,
+                                               batch->max_blocks, batch->q_len, k, v, ik, q_idx,
+                                               block_scores, s),
+                    fn);
+    if (rc) return rc;
+    return hip_status(msa::launch_select_attention(cache->k, cache->v, cache->num_pages,
+                                                   batch->block_table, batch->ctx_lens,
+                                                   batch->batch, batch->max_blocks, batch->q_len,
+                                                   block_scores, block_ids, q, softmax_scale, out,
+                                                   ws, s),
                       fn);
 }
 

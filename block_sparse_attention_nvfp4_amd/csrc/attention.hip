@@ -973,6 +973,21 @@ static size_t attn_counter_bytes(int batch, int q_len) {
     return ((size_t)batch * q_len * kKvHeads * kWaves * sizeof(int32_t) + 255) / 256 * 256;
 }
 
+// Zeroes n 32-bit words (a plain kernel rather than a memset, so that a captured graph holds no
+// memset node).
+__global__ __launch_bounds__(256) void clear_words_kernel(uint32_t* __restrict__ p, int n) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
+}
+
+hipError_t launch_attn_workspace_clear(void* workspace, int batch, int q_len, hipStream_t stream) {
+    if (attn_num_splits(batch, q_len) == 1) return hipSuccess;
+    const int words = (int)(attn_counter_bytes(batch, q_len) / sizeof(uint32_t));
+    const int grid = (words + 255) / 256 < 64 ? (words + 255) / 256 : 64;
+    hipLaunchKernelGGL(clear_words_kernel, dim3(grid), dim3(256), 0, stream,
+                       static_cast<uint32_t*>(workspace), words);
+    return hipGetLastError();
+}
+
 size_t attn_workspace_bytes(int batch, int q_len) {
     const int ns = attn_num_splits(batch, q_len);
     if (ns == 1) return 0;

@@ -74,6 +74,8 @@ hipError_t launch_topk_merge(const int32_t* cand_ids, const uint32_t* cand_keys,
 // Split of the 16 selected blocks of a (sequence, token, group) row over workgroups.
 int attn_num_splits(int batch, int q_len);
 size_t attn_workspace_bytes(int batch, int q_len);
+// Zeroes the part of an attention workspace that must be zero on entry (its counters).
+hipError_t launch_attn_workspace_clear(void* workspace, int batch, int q_len, hipStream_t stream);
 
 hipError_t launch_attention(const uint8_t* k_pool, const uint8_t* v_pool, int64_t num_pages,
                             const int32_t* block_table, const int32_t* ctx_lens, int batch,

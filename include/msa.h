@@ -25,7 +25,8 @@
  *
  * Conventions for every entry point
  *   - All tensor arguments are device pointers owned by the caller. The library allocates
- *     nothing and keeps no state besides a thread-local error message.
+ *     nothing and keeps no state besides a thread-local error message and, for
+ *     msa_decode_step_noalloc only, one static device array per GPU (see there).
  *   - `stream` is a hipStream_t (NULL = the null stream). Every call only enqueues work on it
  *     and returns; nothing synchronizes. Launch shapes depend only on the scalar arguments,
  *     so a step can be captured in a HIP graph.
@@ -352,6 +353,25 @@ int msa_decode_step(const msa_cache_t *cache, const msa_batch_t *batch, const fl
                     const float *v, const float *ik, const uint16_t *q_idx, const uint16_t *q,
                     int32_t topk, float softmax_scale, float *block_scores, int32_t *block_ids,
                     uint16_t *out, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * msa_decode_step for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, and harnesses that forbid hipMalloc. The same two launches and results,
+ * bit for bit, as msa_decode_step with a workspace, preceded by one small kernel that zeroes the
+ * workspace's counters. The attention's workspace is instead a static device array of the
+ * library, 20 MiB (20,971,520 bytes), one per GPU, held until the process ends; no allocation of
+ * any kind happens in this call. Every shape the current kernels run needs at most about
+ * 17.3 MB of it (batches with fewer than 1,024 (token, group) rows; larger ones need none); a
+ * batch that would need more is rejected with MSA_ERR_WORKSPACE before anything is launched.
+ * All calls on one GPU share that array: calls that overlap in time on one GPU (different
+ * streams, or threads without ordering) race and give undefined results; calls ordered on one
+ * stream are safe. Arguments as for msa_decode_step, without the workspace.
+ * Errors: as msa_decode_step; MSA_ERR_HIP if the array's device address cannot be obtained.
+ */
+int msa_decode_step_noalloc(const msa_cache_t *cache, const msa_batch_t *batch, const float *k,
+                            const float *v, const float *ik, const uint16_t *q_idx,
+                            const uint16_t *q, int32_t topk, float softmax_scale,
+                            float *block_scores, int32_t *block_ids, uint16_t *out, void *stream);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char *msa_last_error(void);

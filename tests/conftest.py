@@ -14,5 +14,10 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests that create large inputs run last so a failure in a small case shows first.
-    items.sort(key=lambda it: 1 if it.module.__name__.endswith("test_gpu_full") else 0)
+    # GPU tests that create large inputs run late so a failure in a small case shows first; the
+    # static-workspace entry point's test runs last of all (after every other call has used the
+    # GPU), as a stable sort keeps the rest in file order.
+    def rank(it):
+        name = it.module.__name__
+        return 2 if name.endswith("test_zz_no_alloc") else (1 if name.endswith("test_gpu_full") else 0)
+    items.sort(key=rank)
