@@ -979,9 +979,27 @@ __global__ __launch_bounds__(256) void clear_words_kernel(uint32_t* __restrict__
     for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
 }
 
+// Batches that take the union kernel (attention_union.hip): 2 to 4 query tokens per sequence and
+// at least kUnionMinBatch sequences. There the attention is bound by page traffic and
+// dequantization, which the union does once per (sequence, group) instead of once per token
+// (128K context, 4 tokens: 24.7 against 26.3 us at 16 sequences, 31 against 53 us at 32,
+// 46 against 70 us at 64). With fewer sequences the launch is bound by the latency of its
+// steps, and the union's merge of its 64-row partials across splits costs more than it saves
+// (8 sequences: 22.7 against 14.2 us), so the per-token kernel runs.
+constexpr int kUnionMinBatch = 16;
+static bool use_union(int batch, int q_len, int max_blocks, bool select) {
+    return q_len >= 2 && q_len <= 4 && batch >= kUnionMinBatch &&
+           max_blocks <= (select ? kSelectFusedMaxBlocks : kUnionAttnMaxBlocks);
+}
+
 hipError_t launch_attn_workspace_clear(void* workspace, int batch, int q_len, hipStream_t stream) {
-    if (attn_num_splits(batch, q_len) == 1) return hipSuccess;
-    const int words = (int)(attn_counter_bytes(batch, q_len) / sizeof(uint32_t));
+    // the counters of whichever kernel runs sit at the start of the workspace
+    size_t bytes = attn_num_splits(batch, q_len) > 1 ? attn_counter_bytes(batch, q_len) : 0;
+    if (q_len >= 2 && q_len <= 4 && batch >= kUnionMinBatch && union_num_splits(batch) > 1 &&
+        union_counter_bytes(batch) > bytes)
+        bytes = union_counter_bytes(batch);
+    if (bytes == 0) return hipSuccess;
+    const int words = (int)(bytes / sizeof(uint32_t));
     const int grid = (words + 255) / 256 < 64 ? (words + 255) / 256 : 64;
     hipLaunchKernelGGL(clear_words_kernel, dim3(grid), dim3(256), 0, stream,
                        static_cast<uint32_t*>(workspace), words);
@@ -989,10 +1007,17 @@ hipError_t launch_attn_workspace_clear(void* workspace, int batch, int q_len, hi
 }
 
 size_t attn_workspace_bytes(int batch, int q_len) {
+    // enough for either kernel a call of this shape may run (the union kernel for 2 to 4 query
+    // tokens per sequence, the per-token kernel for longer rows)
     const int ns = attn_num_splits(batch, q_len);
-    if (ns == 1) return 0;
-    return attn_counter_bytes(batch, q_len) +
-           (size_t)batch * q_len * kKvHeads * ns * kGroupHeads * kPartStride * sizeof(float);
+    size_t ws = ns == 1 ? 0
+                        : attn_counter_bytes(batch, q_len) +
+                              (size_t)batch * q_len * kKvHeads * ns * kGroupHeads * kPartStride * sizeof(float);
+    if (q_len >= 2 && q_len <= 4 && batch >= kUnionMinBatch) {
+        const size_t u = union_workspace_bytes(batch, q_len);
+        if (u > ws) ws = u;
+    }
+    return ws;
 }
 
 namespace {
@@ -1007,6 +1032,12 @@ hipError_t launch_attention_t(const uint8_t* k_pool, const uint8_t* v_pool, int6
     const int pairs = batch * kKvHeads;
     const int pair_slots = 8 * ((pairs + 7) / 8);
     const float scale_log2 = softmax_scale * 1.4426950408889634f;
+    if (use_union(batch, q_len, max_blocks, SELECT)) {
+        // speculative verify: each (sequence, group) reads the union of its drafts' blocks once
+        return launch_attention_union(k_pool, v_pool, num_pages, block_table, ctx_lens, batch,
+                                      max_blocks, q_len, q, ids, SELECT ? scores : nullptr,
+                                      scale_log2, out, workspace, stream);
+    }
     if (ns == 1 && q_len >= kTileMinQ && max_blocks <= kUnionMaxBlocks) {
         // many tokens per sequence: token tiles over the union of their blocks (the selection,
         // if asked for, as its own launch first)

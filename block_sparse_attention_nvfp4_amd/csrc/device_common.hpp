@@ -109,6 +109,24 @@ __device__ __forceinline__ void e4m3_pair_f16(uint32_t w, f16x2& s0, f16x2& s1) 
     s1 = f16x2{s[1], s[1]};
 }
 
+// ---------------------------------------------------------------- cross-lane
+// Max and sum over the four lanes n, n + 16, n + 32, n + 48 (the four lane groups c of one
+// matrix-core row), in every one of them, by the lane swaps of gfx950: v_permlane32_swap gives
+// each lane the values of lanes l and l ^ 32, v_permlane16_swap those of l and l ^ 16 (no LDS
+// round trip, unlike a shuffle).
+__device__ __forceinline__ float max_over_c(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_c(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Query operands in fp16. A query row (one index query, or one attention head) of 128 bf16
 // values is spread over the four lanes n, n+16, n+32, n+48 (32 values each, as 4 x bf16x8).
 // Multiplying the row by 2^k (k chosen so the row's largest magnitude lands in [2^14, 2^15))
@@ -121,8 +139,7 @@ __device__ __forceinline__ bool query_to_f16(const bf16x8 (&qb)[4], f16x8 (&qh)[
     for (int m = 0; m < 4; m++)
 #pragma unroll
         for (int i = 0; i < 8; i++) mx = fmaxf(mx, fabsf((float)qb[m][i]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = max_over_c(mx);
     int e = 0;
     if (mx > 0.f) (void)frexpf(mx, &e);  // mx in [2^(e-1), 2^e)
     const int k = 15 - e;
@@ -161,16 +178,6 @@ __device__ __forceinline__ f32x4 mfma_f16_k32(const f16x8& a, const f16x8& b, co
 }
 __device__ __forceinline__ f32x4 mfma_f16_k16(const f16x4& a, const f16x4& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-}
-
-// ---------------------------------------------------------------- cross-lane
-__device__ __forceinline__ float max_over_c(float x) {
-    x = fmaxf(x, __shfl_xor(x, 16, 64));
-    return fmaxf(x, __shfl_xor(x, 32, 64));
-}
-__device__ __forceinline__ float sum_over_c(float x) {
-    x += __shfl_xor(x, 16, 64);
-    return x + __shfl_xor(x, 32, 64);
 }
 
 __device__ __forceinline__ int clamp_ctx(int T, int max_blocks) {

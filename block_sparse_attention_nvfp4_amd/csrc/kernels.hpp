@@ -83,6 +83,20 @@ hipError_t launch_attention(const uint8_t* k_pool, const uint8_t* v_pool, int64_
                             float softmax_scale, uint16_t* out, void* workspace,
                             hipStream_t stream);
 
+// Attention for 2 to 4 query tokens per sequence over the union of their selected blocks
+// (attention_union.hip): rows of up to kUnionAttnMaxBlocks blocks; the selection is made in the
+// same launch when `scores` is given (rows of up to kSelectFusedMaxBlocks blocks), else the ids
+// are read. scale_log2 = softmax scale x log2(e).
+constexpr int kUnionAttnMaxBlocks = 8192;
+int union_num_splits(int batch);
+size_t union_counter_bytes(int batch);
+size_t union_workspace_bytes(int batch, int q_len);
+hipError_t launch_attention_union(const uint8_t* k_pool, const uint8_t* v_pool, int64_t num_pages,
+                                  const int32_t* block_table, const int32_t* ctx_lens, int batch,
+                                  int max_blocks, int q_len, const uint16_t* q, int32_t* ids,
+                                  const float* scores, float scale_log2, uint16_t* out,
+                                  void* workspace, hipStream_t stream);
+
 // Selection fused into the attention (one launch): rows of up to this many blocks, whose
 // selection one wavefront holds in 16 keys per lane; longer rows launch the two kernels.
 constexpr int kSelectFusedMaxBlocks = 64 * 16 + 1;

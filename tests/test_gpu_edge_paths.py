@@ -55,6 +55,8 @@ WIDE_CASES = {
     "q1_batched": (2, dict(batch=3, ctx=5000), [(1, 2)], [(0, range(16, 32)), (2, range(48, 64))]),
     "q4_spec": (3, dict(batch=2, ctx=6000), [(1, 2), (4, 0)], [(2, range(16, 32)), (7, range(0, 16))]),
     "q16_gemm": (3, dict(batch=1, ctx=6000, q_len=16), [(3, 1), (15, 3)], [(5, range(32, 48))]),
+    # 16 sequences: the union attention kernel (wide rows in both halves of the row tiles)
+    "q4_union": (3, dict(batch=16, ctx=2000), [(9, 1)], [(1, range(16, 32)), (62, range(48, 64))]),
 }
 
 
@@ -125,6 +127,7 @@ FILL_CASES = {
     "ragged_q1": (4, dict(ctx_lens=[3000, 129, 7777, 1, 17 * 128 + 5, 2048 + 77])),
     "spec_q4": (3, dict(batch=2, ctx_lens=[6000, 2 * 128 + 2])),
     "prefill_q256": (5, dict(batch=1, ctx=2048 + 256 + 50, q_len=256)),
+    "union_q4": (3, dict(batch=16, ctx_lens=[300 + 97 * i for i in range(16)])),
 }
 
 

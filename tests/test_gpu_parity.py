@@ -42,6 +42,13 @@ CASES = {
     # row ranges, the second partial)
     "prefill_ragged": (5, dict(batch=3, ctx_lens=[40, 700, 3003], q_len=40)),
     "prefill_q200": (5, dict(ctx_lens=[2048 + 200, 1500], q_len=200)),
+    # 16 or more sequences with 2 to 4 draft tokens: the union kernel (each (sequence, group)
+    # reads the union of its drafts' blocks once): 4 and 2 splits per pair, ragged lengths with
+    # drafts in two blocks, and one split (64 sequences)
+    "union_q4": (3, dict(batch=16, ctx=2600)),
+    "union_q2": (3, dict(batch=17, ctx_lens=[2500 + 37 * i for i in range(17)], q_len=2)),
+    "union_q3": (3, dict(batch=32, ctx_lens=[258 + 131 * i for i in range(32)], q_len=3)),
+    "union_q4_one_split": (3, dict(batch=64, ctx_lens=[130 + 29 * i for i in range(64)])),
 }
 
 
