@@ -18,6 +18,13 @@ Each layer's step is captured once in a HIP graph; the timed region replays K st
 Kernel durations for the roofline come from HIP events around graphs of L back-to-back launches
 of one kernel (one per layer), recorded on the stream the kernels run on.
 
+Beside the headline line: "side" repeats the step on the batched workload (32 x 32,768 tokens,
+1 query token), the ragged one (6 sequences of 8K to 512K tokens, 1 query token) and 32
+sequences at 128K with 4 query tokens (which takes the union attention kernel), each with its
+two launches against the HBM peak; "hbm_read_ceiling_gbs" is the GPU's measured streaming-read
+rate for a 76 MB and a 2 GiB working set; "prefill" times the chunked-prefill workload's calls
+against the matrix-core peak; "cpu_baseline" times the oracle on the host.
+
 Output: one JSON line (see the keys below). --gpus N > 1 exits: the path runs on one GPU.
 """
 import argparse
@@ -46,14 +53,25 @@ def parse():
     ap.add_argument("--kernel-reps", type=int, default=20, help="graph replays per kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-workload side measurement")
+    ap.add_argument("--no-side", action="store_true",
+                    help="skip the side lines (batched 32K, ragged to 512K, 32 sequences at 128K)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle CPU time")
     ap.add_argument("--only", default="", help="profiling aid: run a calibration copy of "
-                    f"{COPY_BYTES >> 20} MiB, then only this kernel in a loop "
-                    "(insert|indexer|insert_indexer|topk|attention|select_attention), and exit")
+                    f"{COPY_BYTES >> 20} MiB, then only this call in a loop "
+                    "(insert|indexer|insert_indexer|topk|attention|select_attention), and exit; "
+                    "'prefill' runs only the prefill workload's calls")
+    ap.add_argument("--workload", default="spec128k",
+                    choices=("spec128k", "union32x128k", "batched32k", "ragged512k"),
+                    help="decode workload of an --only run")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs of '--only insert_indexer' "
                          "(FETCH_SIZE, WRITE_SIZE) into "
                          "profiles/insert_indexer_spec128k_traffic.json and exit")
+    ap.add_argument("--counters-from", metavar="CSV",
+                    help="summarize a rocprofv3 --pmc counter CSV per kernel (mean per dispatch, "
+                         "duration, matrix-core figures) as a markdown table and exit")
+    ap.add_argument("--trace-from", metavar="CSV",
+                    help="per-kernel duration statistics of a rocprofv3 kernel-trace CSV and exit")
     return ap.parse_args()
 
 
@@ -126,45 +144,217 @@ def traffic_from(fetch_csv, write_csv):
     print(json.dumps(rec, indent=1))
 
 
+def short_name(k):
+    """Kernel name of a rocprofv3 record without return type, namespaces and argument list."""
+    k = k.replace("(anonymous namespace)::", "")
+    k = k[5:] if k.startswith("void ") else k
+    depth = 0
+    for i, ch in enumerate(k):
+        depth += ch == "<"
+        depth -= ch == ">"
+        if ch == "(" and depth == 0:
+            k = k[:i]
+            break
+    return k.replace("msa::", "")
+
+
+def trace_from(path, last=160):
+    """Per-kernel duration statistics of a rocprofv3 kernel-trace CSV over each kernel's last
+    `last` dispatches (for the decode kernels: the event-timed replays of its timing graph).
+    Only the library's kernels and the read probe are listed (torch's input generation is not)."""
+    import csv
+    by = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if "msa::" not in r["Kernel_Name"] and "stream_read_kernel" not in r["Kernel_Name"]:
+                continue
+            us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+            by.setdefault(short_name(r["Kernel_Name"]), []).append(us)
+    w = max(len(k) for k in by)
+    for k, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        t = sorted(v[-last:])
+        print(f"  {k:{w}s} calls {len(v):6d}  last {len(t):3d}: mean {sum(t) / len(t):8.2f} us  "
+              f"median {t[len(t) // 2]:8.2f}  p10 {t[len(t) // 10]:8.2f}  p90 {t[(9 * len(t)) // 10]:8.2f}")
+
+
+def counters_from(path, min_dispatches=2):
+    """Per-kernel means of a rocprofv3 counter CSV (one row per dispatch and counter), with the
+    dispatch duration from its timestamps and two matrix-core figures: the fp16 + bf16 matrix
+    flops the hardware counted (SQ_INSTS_VALU_MFMA_MOPS_* are in units of 512 flops) over the
+    duration, and SQ_VALU_MFMA_BUSY_CYCLES over SQ_BUSY_CU_CYCLES (the share of busy-CU cycles
+    in which a matrix core was busy, summed over the CU's four SIMDs, so 4.0 is the ceiling).
+    Only the library's kernels, the read probe and the runtime's copy kernel are listed."""
+    import csv
+    from collections import defaultdict
+    vals = defaultdict(lambda: defaultdict(list))
+    durs = defaultdict(dict)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            k = r["Kernel_Name"]
+            if not any(n in k for n in ("msa::", "stream_read_kernel", "copyBuffer")):
+                continue
+            vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+                durs[k][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+    names = sorted({c for k in vals for c in vals[k]})
+    print("| kernel | dispatches | mean us | " + " | ".join(names) +
+          " | counted matrix TFLOP/s | MFMA busy / busy CU cycles |")
+    print("|" + "---|" * (len(names) + 5))
+    for k in sorted(vals, key=lambda k: -sum(durs[k].values())):
+        n = max(len(v) for v in vals[k].values())
+        if n < min_dispatches:
+            continue
+        mean = {c: sum(v) / len(v) for c, v in vals[k].items()}
+        us = sorted(durs[k].values())[len(durs[k]) // 2] if durs[k] else float("nan")
+        mops = mean.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0) + mean.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+        tflops = 512.0 * mops / (us * 1e-6) / 1e12 if us == us and us > 0 else float("nan")
+        busy = (mean["SQ_VALU_MFMA_BUSY_CYCLES"] / mean["SQ_BUSY_CU_CYCLES"]
+                if mean.get("SQ_BUSY_CU_CYCLES") else float("nan"))
+        print(f"| `{short_name(k)}` | {n} | {us:.2f} | " + " | ".join(f"{mean.get(c, float('nan')):.4g}" for c in names)
+              + f" | {tflops:.1f} | {busy:.3f} |")
+
+
 def main():
     args = parse()
     if args.traffic_from:
         traffic_from(*args.traffic_from)
+        return
+    if args.counters_from:
+        counters_from(args.counters_from)
+        return
+    if args.trace_from:
+        trace_from(args.trace_from)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the MSA decode path "
               "here is single-GPU; sharding the indexer by pages is not built.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
+    import torch
+
+    import msa_inputs as mi
+
+    torch.cuda.set_device(0)
+    w = mi.full_workload(3)
+    if args.only == "prefill":
+        print(json.dumps(prefill_side(args)), flush=True)
+        return
+    if args.only:
+        ow = {"spec128k": w, "union32x128k": mi.make_workload(3, batch=32),
+              "batched32k": mi.full_workload(2), "ragged512k": mi.full_workload(4)}[args.workload]
+        decode_measure(ow, args.layers, args, only=args.only)
+        return
+    m = decode_measure(w, args.layers, args, full=True)
+    B, q, T = w.batch, w.q_len, w.ctx_lens[0]
+    kernel_us = m["kernels_us"]
+    value = B * q / (m["ms_per_step"] * 1e-3)
+    roof_gbs = m["roof_bytes"] / (kernel_us[ROOF_KERNEL] * 1e-6) / 1e9
+    idx_gbs = m["idx_bytes"] / (kernel_us["indexer"] * 1e-6) / 1e9
+    attn_gbs = m["attn_bytes"] / (kernel_us["select_attention"] * 1e-6) / 1e9
+    traffic = load_traffic(ROOF_KERNEL, source_digest(*ROOF_SOURCES))
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(m["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "spec128k: batch 8 x context 131072 tokens, 4 query tokens each "
+                        "(speculative verify), 64 q heads / 4 kv heads / head_dim 128, "
+                        "NVFP4 K/V/index caches, 128-token pages, top-16",
+            "batch": B, "context": T, "query_tokens": q, "cache_dtype": "nvfp4",
+            "layers_rotated": args.layers, "graph": f"{args.layers} layer steps per graph replay",
+            "device_ms_per_step": round(m["device_ms_per_step"], 5),
+            "step_us_p10_p50_p90": m["step_us_p10_p50_p90"],
+            "step_calls": "msa_insert_indexer_score, msa_select_attn_decode",
+            "ms_per_step_three_calls": round(m["alt_ms"]["three"], 5),
+            "ms_per_step_four_calls": round(m["alt_ms"]["four"], 5),
+        },
+        "kernels_us": {k: round(v, 3) for k, v in kernel_us.items()},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": ROOF_KERNEL,
+            "achieved": round(roof_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(roof_gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes": m["roof_bytes"],
+        },
+        "indexer_alone": {"achieved_gbs": round(idx_gbs, 1), "frac": round(idx_gbs / PEAK_HBM_GBS, 4),
+                          "algorithmic_bytes": m["idx_bytes"]},
+        "attention_gather": {"achieved_gbs": round(attn_gbs, 1), "frac": round(attn_gbs / PEAK_HBM_GBS, 4),
+                             "algorithmic_bytes": m["attn_bytes"]},
+    }
+    torch.cuda.empty_cache()
+    result["hbm_read_ceiling_gbs"] = read_ceiling()
+    if not args.no_side:
+        side = {}
+        for name, sw, layers in (("batched32k", mi.full_workload(2), args.layers),
+                                 ("ragged512k", mi.full_workload(4), args.layers),
+                                 ("union32x128k", mi.make_workload(3, batch=32), 4)):
+            print(f"# side line {name}", file=sys.stderr, flush=True)
+            side[name] = side_line(sw, layers, args)
+            torch.cuda.empty_cache()
+        result["side"] = side
+    if not args.no_prefill:
+        torch.cuda.empty_cache()
+        result["prefill"] = prefill_side(args)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def layer_caches(w, L):
+    """Caches of L layers for workload w: layer 0 built from the generator through the insert
+    kernel (every token but the q query tokens of each sequence), layers 1..L-1 copies of it in
+    their own memory, so the index-key working set is L times one layer's."""
     import torch
 
     import block_sparse_attention_nvfp4_amd as msa
-    import msa_inputs as mi
 
     dev = "cuda"
-    torch.cuda.set_device(0)
-    w = mi.full_workload(3)
-    B, q, T = w.batch, w.q_len, w.ctx_lens[0]
-    L = args.layers
-    t_setup = time.time()
-
-    # ---------------------------------------------------------------- caches (layer 0 built
-    # from the generator through the insert kernel; layers 1..L-1 are copies in their own memory)
+    q = w.q_len
     cache0 = msa.Cache.allocate(w.num_pages, dev)
     chunk = 1 << 15
-    for b in range(B):
+    for b in range(w.batch):
+        T = w.ctx_lens[b]
         for t0 in range(0, T - q, chunk):
             t1 = min(T - q, t0 + chunk)
             slots = torch.from_numpy(w.slots(b, t0, t1)).to(dev)
             msa.msa_kv_insert_nvfp4(cache0, slots, w.kv_rows("k", b, t0, t1, dev),
                                     w.kv_rows("v", b, t0, t1, dev), w.ik_rows(b, t0, t1, dev))
-    caches = [cache0] + [msa.Cache(cache0.k.clone(), cache0.v.clone(), cache0.ik.clone())
-                         for _ in range(L - 1)]
+    return [cache0] + [msa.Cache(cache0.k.clone(), cache0.v.clone(), cache0.ik.clone())
+                       for _ in range(L - 1)]
+
+
+def decode_measure(w, L, args, full=False, only=""):
+    """The decode step of workload w on L rotated layers: one graph runs the step of every
+    layer in turn (as a decode pass runs its layers); K layer-steps are timed between
+    synchronizations (wall clock), then again in ten chunks of HIP events for the spread, and
+    each kernel alone with HIP events around graphs of L back-to-back launches (the median of
+    five series). full: also the step as three and as four calls, and every separate call."""
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_nvfp4_amd as msa
+
+    dev = "cuda"
+    B, q = w.batch, w.q_len
+    t_setup = time.time()
+    caches = layer_caches(w, L)
     table = torch.from_numpy(w.block_table).to(dev)
     ctx = torch.tensor(w.ctx_lens, dtype=torch.int32, device=dev)
     batch = msa.Batch(table, ctx, q)
-    toks = [(b, T - q, T) for b in range(B)]
+    toks = [(b, w.ctx_lens[b] - q, w.ctx_lens[b]) for b in range(B)]
     new_slots = torch.from_numpy(np.concatenate([w.slots(b, t0, t1) for b, t0, t1 in toks])).to(dev)
     new_k = torch.cat([w.kv_rows("k", b, t0, t1, dev) for b, t0, t1 in toks])
     new_v = torch.cat([w.kv_rows("v", b, t0, t1, dev) for b, t0, t1 in toks])
@@ -173,9 +363,9 @@ def main():
     steps = [msa.DecodeStep(c, batch, dev) for c in caches]
     scale = msa.default_softmax_scale()
     torch.cuda.synchronize()
-    setup_s = time.time() - t_setup
-    print(f"# setup {setup_s:.1f}s: {L} layers x {w.num_pages} pages, "
-          f"{torch.cuda.memory_allocated() / 2**30:.2f} GiB allocated", file=sys.stderr, flush=True)
+    print(f"# setup {time.time() - t_setup:.1f}s: {w.name} batch {B}, {L} layers x {w.num_pages} "
+          f"pages, {torch.cuda.memory_allocated() / 2**30:.2f} GiB allocated",
+          file=sys.stderr, flush=True)
 
     calls = {
         "insert": lambda s: msa.msa_kv_insert_nvfp4(s.cache, new_slots, new_k, new_v, new_ik),
@@ -192,6 +382,7 @@ def main():
     STEP = ("insert_indexer", "select_attention")               # the timed step: two launches
     THREE_CALLS = ("insert", "indexer", "select_attention")     # the same step as three calls
     FOUR_CALLS = ("insert", "indexer", "topk", "attention")     # and as four
+    timed_calls = list(calls) if full else list(STEP)
 
     def full_step(s, names=STEP):
         for name in names:
@@ -202,7 +393,7 @@ def main():
         full_step(s)
     torch.cuda.synchronize()
 
-    if args.only:
+    if only:
         # profiling aid: a plain copy of known size (counter calibration), then the chosen
         # kernel alone, L launches per round, no graphs
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -213,26 +404,25 @@ def main():
         del src, dst
         for _ in range(args.kernel_reps):
             for s in steps:
-                calls[args.only](s)
+                calls[only](s)
         torch.cuda.synchronize()
-        print(f"# ran {args.kernel_reps * L} launches of {args.only}", file=sys.stderr)
-        return
+        print(f"# ran {args.kernel_reps * L} launches of {only}", file=sys.stderr)
+        return None
 
     stream = torch.cuda.Stream()
-    # ---------------------------------------------------------------- graphs
     with torch.cuda.stream(stream):
-        # one graph runs the step of every layer in turn (as a decode pass runs its layers)
         layers_graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(layers_graph, stream=stream):
             for s in steps:
                 full_step(s)
         alt_graphs = {}
-        for key, names in (("three", THREE_CALLS), ("four", FOUR_CALLS)):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                for s in steps:
-                    full_step(s, names)
-            alt_graphs[key] = g
+        if full:
+            for key, names in (("three", THREE_CALLS), ("four", FOUR_CALLS)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    for s in steps:
+                        full_step(s, names)
+                alt_graphs[key] = g
         graphs = []  # single-layer steps for a step count that is not a multiple of L
         for s in steps:
             g = torch.cuda.CUDAGraph()
@@ -240,7 +430,7 @@ def main():
                 full_step(s)
             graphs.append(g)
         kgraphs = {}
-        for name in calls:
+        for name in timed_calls:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=stream):
                 for s in steps:
@@ -248,12 +438,14 @@ def main():
             kgraphs[name] = g
     torch.cuda.synchronize()
 
-    # ---------------------------------------------------------------- timed steps
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
             graphs[i % L].replay()
         torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0, ev1 = ev(), ev()
         t0 = time.perf_counter()
         ev0.record(stream)
         for _ in range(args.steps // L):       # exactly `steps` layer steps
@@ -265,12 +457,23 @@ def main():
         wall = time.perf_counter() - t0
         dev_ms = ev0.elapsed_time(ev1)
 
-        # the same steps as three and as four calls
+        # the spread: the same replays in ten chunks, each bracketed by events
+        per_chunk = max(1, args.steps // L // 10)
+        chunk_us = []
+        for _ in range(10):
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            for _ in range(per_chunk):
+                layers_graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            chunk_us.append(e0.elapsed_time(e1) * 1e3 / (per_chunk * L))
+
         alt_ms = {}
         for key, g in alt_graphs.items():
             g.replay()
             torch.cuda.synchronize()
-            e4s, e4e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e4s, e4e = ev(), ev()
             e4s.record(stream)
             for _ in range(max(1, args.steps // L)):
                 g.replay()
@@ -278,15 +481,13 @@ def main():
             torch.cuda.synchronize()
             alt_ms[key] = e4s.elapsed_time(e4e) / (max(1, args.steps // L) * L)
 
-        # per-kernel durations: graphs of L back-to-back launches, HIP events around series of
-        # kernel_reps replays; the median of five series
         kernel_us = {}
         for name, g in kgraphs.items():
             g.replay()
             torch.cuda.synchronize()
             series = []
             for _ in range(5):
-                es, ee = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                es, ee = ev(), ev()
                 es.record(stream)
                 for _ in range(args.kernel_reps):
                     g.replay()
@@ -295,80 +496,85 @@ def main():
                 series.append(es.elapsed_time(ee) * 1e3 / (args.kernel_reps * L))
             kernel_us[name] = sorted(series)[2]
 
-    ms_per_step = wall * 1e3 / args.steps
-    tokens_per_step = B * q
-    value = tokens_per_step / (ms_per_step * 1e-3)
-
-    # algorithmic bytes per launch of the insert + indexer kernel (the dominant one): every
-    # index-key byte of the context (72 B per token), the index queries, the block scores it
-    # writes, and the insert's fp32 inputs (9 vectors of 128 per new token) and NVFP4 outputs
+    # algorithmic bytes per launch: the insert + indexer reads every index-key byte of the
+    # context (72 B per token), the index queries, writes the block scores, and the insert's
+    # fp32 inputs (9 vectors of 128 per new token) and NVFP4 outputs; the selection + attention
+    # launch reads the block scores, gathers the K + V of each selected (sequence, group, block)
+    # once per distinct block over the query tokens (144 B per valid token), reads the queries
+    # and writes the outputs
     sum_T = sum(w.ctx_lens)
     idx_bytes = sum_T * 72 + B * q * 4 * 128 * 2 + B * q * 4 * w.max_blocks * 4
     ins_bytes = B * q * 9 * (128 * 4 + 72)
-    roof_bytes = idx_bytes + ins_bytes
-    roof_gbs = roof_bytes / (kernel_us[ROOF_KERNEL] * 1e-6) / 1e9
-    idx_gbs = idx_bytes / (kernel_us["indexer"] * 1e-6) / 1e9
-    traffic = load_traffic(ROOF_KERNEL, source_digest(*ROOF_SOURCES))
-
-    # gather bytes of the attention: K+V of each selected (sequence, group, block) once per
-    # distinct block over the 4 draft tokens (144 B per valid token), queries and outputs
     ids = steps[0].block_ids.cpu().numpy().reshape(B, q, 4, 16)
     gathered_tokens = 0
     for b in range(B):
+        T = w.ctx_lens[b]
         for g in range(4):
             for blk in set(int(x) for x in ids[b, :, g].ravel() if x >= 0):
-                gathered_tokens += min(128, T - blk * 128)
-    attn_bytes = gathered_tokens * 144 + 2 * B * q * 64 * 128 * 2 + B * q * 4 * 16 * 4
-    attn_gbs = attn_bytes / (kernel_us["select_attention"] * 1e-6) / 1e9
+                gathered_tokens += max(0, min(128, T - blk * 128))
+    attn_bytes = gathered_tokens * 144 + 2 * B * q * 64 * 128 * 2 + B * q * 4 * w.max_blocks * 4
+    ms_per_step = wall * 1e3 / args.steps
+    pct = np.percentile(np.array(chunk_us), [10, 50, 90])
+    out = {"ms_per_step": ms_per_step, "device_ms_per_step": dev_ms / args.steps,
+           "step_us_p10_p50_p90": [round(float(x), 2) for x in pct],
+           "kernels_us": kernel_us, "alt_ms": alt_ms, "idx_bytes": idx_bytes,
+           "roof_bytes": idx_bytes + ins_bytes, "attn_bytes": attn_bytes}
+    del steps, caches, kgraphs, alt_graphs, graphs, layers_graph
+    return out
 
-    result = {
-        "metric": METRIC,
-        "value": round(value, 1),
-        "unit": "query-tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {
-            "workload": "spec128k: batch 8 x context 131072 tokens, 4 query tokens each "
-                        "(speculative verify), 64 q heads / 4 kv heads / head_dim 128, "
-                        "NVFP4 K/V/index caches, 128-token pages, top-16",
-            "batch": B, "context": T, "query_tokens": q, "cache_dtype": "nvfp4",
-            "layers_rotated": L, "graph": f"{L} layer steps per graph replay",
-            "device_ms_per_step": round(dev_ms / args.steps, 5),
-            "step_calls": "msa_insert_indexer_score, msa_select_attn_decode",
-            "ms_per_step_three_calls": round(alt_ms["three"], 5),
-            "ms_per_step_four_calls": round(alt_ms["four"], 5),
-        },
-        "kernels_us": {k: round(v, 3) for k, v in kernel_us.items()},
-        "roofline": {
-            "bound": "hbm",
-            "kernel": ROOF_KERNEL,
-            "achieved": round(roof_gbs, 1),
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": round(roof_gbs / PEAK_HBM_GBS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes": roof_bytes,
-        },
-        "indexer_alone": {"achieved_gbs": round(idx_gbs, 1), "frac": round(idx_gbs / PEAK_HBM_GBS, 4),
-                          "algorithmic_bytes": idx_bytes},
-        "attention_gather": {"achieved_gbs": round(attn_gbs, 1), "frac": round(attn_gbs / PEAK_HBM_GBS, 4),
-                             "algorithmic_bytes": attn_bytes},
+
+def side_line(w, L, args):
+    """A decode step on another workload, reported beside the headline: query-tokens/s per layer
+    and the two launches against the HBM peak."""
+    m = decode_measure(w, L, args)
+    ku = m["kernels_us"]
+    B, q = w.batch, w.q_len
+    return {
+        "workload": f"{w.name}: batch {B}, contexts {min(w.ctx_lens)}..{max(w.ctx_lens)} tokens, "
+                    f"{q} query token(s) each, {L} layers rotated",
+        "query_tokens_per_s": round(B * q / (m["ms_per_step"] * 1e-3), 1),
+        "ms_per_step": round(m["ms_per_step"], 5),
+        "step_us_p10_p50_p90": m["step_us_p10_p50_p90"],
+        "kernels_us": {k: round(v, 3) for k, v in ku.items()},
+        "insert_indexer": {"algorithmic_bytes": m["roof_bytes"],
+                           "frac": round(m["roof_bytes"] / (ku["insert_indexer"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
+        "attention_gather": {"algorithmic_bytes": m["attn_bytes"],
+                             "frac": round(m["attn_bytes"] / (ku["select_attention"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
     }
 
-    if not args.no_prefill:
-        del steps, caches, kgraphs, alt_graphs, graphs, layers_graph
+
+def read_ceiling():
+    """Measured streaming-read rate of this GPU for two working sets, by the library's read probe
+    (include/msa_probe.h: each workgroup streams one contiguous share): 76 MB (one layer's
+    index keys at the headline workload; eight buffers in turn, 608 MB, so they miss the 256 MB
+    Infinity Cache) and 2 GiB. HIP events around repeated launches; the best of five series, in
+    GB/s."""
+    import torch
+
+    import block_sparse_attention_nvfp4_amd as msa
+
+    sink = torch.zeros(msa.msa_probe_sink_words(), dtype=torch.int32, device="cuda")
+    out = {}
+    for label, nbytes, nbuf, reps in (("76MB", 76 << 20, 8, 10), ("2GiB", 2 << 30, 2, 4)):
+        bufs = [torch.ones(nbytes // 4, dtype=torch.float32, device="cuda") for _ in range(nbuf)]
+        for bf in bufs:
+            msa.msa_probe_stream_read(bf, sink)
+        torch.cuda.synchronize()
+        best = 0.0
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                for bf in bufs:
+                    msa.msa_probe_stream_read(bf, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            gbs = nbytes * nbuf * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+            best = max(best, gbs)
+        out[label] = round(best, 1)
+        del bufs
         torch.cuda.empty_cache()
-        result["prefill"] = prefill_side(args)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
+    return out
 
 
 def prefill_side(args):
@@ -497,10 +703,19 @@ def cpu_baseline(w, target_seconds):
         seqs += 1
         if spent >= target_seconds:
             break
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), model)
+    except OSError:
+        pass
     return {
         "value": round(done_tokens / spent, 3),
         "unit": "query-tokens/s",
         "cores": 1,
+        "nproc": os.cpu_count(),
+        "cpus_allowed": len(os.sched_getaffinity(0)),
+        "cpu_model": model,
         "kind": "oracle",
         "sample": f"{seqs} of {w.batch} sequences of the same workload (full 131072-token context, "
                   f"{q} query tokens each); {spent:.1f} s single-threaded; cache quantization of "

@@ -59,7 +59,9 @@ EXPORTED = ("msa_page_bytes", "msa_kv_insert_nvfp4", "msa_indexer_score", "msa_i
             "msa_block_topk_window", "msa_block_topk_local", "msa_block_topk_merge",
             "msa_sparse_attn_workspace_bytes", "msa_sparse_attn_decode", "msa_select_attn_decode",
             "msa_insert_indexer_score", "msa_decode_step", "msa_decode_step_noalloc",
-            "msa_last_error", "msa_version")
+            "msa_last_error", "msa_version",
+            # include/msa_probe.h (measurement aid)
+            "msa_probe_stream_read", "msa_probe_sink_words")
 
 
 class MSAError(RuntimeError):
@@ -122,6 +124,9 @@ def _load() -> ctypes.CDLL:
     L.msa_decode_step_noalloc.restype = ctypes.c_int
     L.msa_decode_step_noalloc.argtypes = [ctypes.POINTER(_Cache), ctypes.POINTER(_Batch), vp, vp,
                                           vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp]
+    L.msa_probe_stream_read.restype = ctypes.c_int
+    L.msa_probe_stream_read.argtypes = [vp, sz, vp, vp]
+    L.msa_probe_sink_words.restype, L.msa_probe_sink_words.argtypes = sz, []
     L.msa_last_error.restype, L.msa_last_error.argtypes = ctypes.c_char_p, []
     L.msa_version.restype, L.msa_version.argtypes = ctypes.c_char_p, []
     return L
@@ -415,6 +420,21 @@ def msa_decode_step_noalloc(cache: Cache, batch: Batch, k: torch.Tensor, v: torc
                                        _ptr(block_scores, torch.float32, "block_scores"),
                                        _ptr(block_ids, torch.int32, "block_ids"),
                                        _ptr(out, torch.bfloat16, "out"), _stream(stream)))
+
+
+def msa_probe_stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Measurement aid (include/msa_probe.h): read every byte of `buf` once from HBM."""
+    if not buf.is_cuda or not buf.is_contiguous() or sink.dtype != torch.int32 or \
+            sink.numel() < msa_probe_sink_words():
+        raise ValueError("buf: contiguous device tensor; sink: int32 of msa_probe_sink_words()")
+    rc = lib.msa_probe_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(),
+                                   _ptr(sink, torch.int32, "sink"), _stream(stream))
+    if rc != MSA_OK:
+        raise MSAError(rc, "msa_probe_stream_read: NULL pointer, misaligned buffer or launch error")
+
+
+def msa_probe_sink_words() -> int:
+    return int(lib.msa_probe_sink_words())
 
 
 def default_softmax_scale() -> float:

@@ -8,14 +8,19 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "msa.h")
+INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(ROOT, "block_sparse_attention_nvfp4_amd", "libmsa.so")
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(msa_[a-z0-9_]+)\s*\(", text)))
+    """Every function the headers under include/ declare (msa.h and msa_probe.h)."""
+    names = set()
+    for h in sorted(os.listdir(INCLUDE)):
+        if h.endswith(".h"):
+            text = open(os.path.join(INCLUDE, h)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(msa_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -170,3 +175,15 @@ def test_invalid_arguments_return_codes_without_launch(msa):
         assert ii(by(_cache()), small, *a, None) == msa.MSA_ERR_INVALID_ARG, i
     assert ii(by(_cache(k=None)), small, 1, 1, 1, 1, 1, None) == msa.MSA_ERR_INVALID_ARG
     assert ii(by(_cache()), by(_batch(mb=0)), 1, 1, 1, 1, 1, None) == msa.MSA_ERR_INVALID_ARG
+
+
+def test_stream_read_probe_rejects_bad_arguments(msa):
+    """The measurement probe of include/msa_probe.h checks its pointers and alignment on the host
+    and launches nothing on an error (no GPU here)."""
+    L = msa.lib
+    assert L.msa_probe_sink_words() >= 256
+    assert L.msa_probe_stream_read(None, 1024, 16, None) == -1
+    assert L.msa_probe_stream_read(16, 1024, None, None) == -1
+    assert L.msa_probe_stream_read(16, 1000, 16, None) == -1   # not a multiple of 16 bytes
+    assert L.msa_probe_stream_read(8, 1024, 16, None) == -1    # misaligned buffer
+    assert L.msa_probe_stream_read(16, 0, 16, None) == 0       # nothing to read
