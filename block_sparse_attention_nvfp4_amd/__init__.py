@@ -54,7 +54,7 @@ MSA_REDUCE_MAX = 0
 MSA_REDUCE_LSE = 1
 
 EXPORTED = ("msa_page_bytes", "msa_kv_insert_nvfp4", "msa_indexer_score", "msa_indexer_score_ex",
-            "msa_indexer_score_shared_prefix",
+            "msa_indexer_score_shared_prefix", "msa_indexer_score_shard",
             "msa_block_topk",
             "msa_block_topk_window", "msa_block_topk_local", "msa_block_topk_merge",
             "msa_sparse_attn_workspace_bytes", "msa_sparse_attn_decode", "msa_select_attn_decode",
@@ -98,6 +98,9 @@ def _load() -> ctypes.CDLL:
     L.msa_indexer_score_shared_prefix.restype = ctypes.c_int
     L.msa_indexer_score_shared_prefix.argtypes = [ctypes.POINTER(_Cache), ctypes.POINTER(_Batch),
                                                   vp, i32, vp, vp]
+    L.msa_indexer_score_shard.restype = ctypes.c_int
+    L.msa_indexer_score_shard.argtypes = [ctypes.POINTER(_Cache), ctypes.POINTER(_Batch), i32, i32,
+                                          i32, vp, vp, vp]
     L.msa_block_topk.restype = ctypes.c_int
     L.msa_block_topk.argtypes = [vp, ctypes.POINTER(_Batch), i32, vp, vp]
     L.msa_block_topk_window.restype = ctypes.c_int
@@ -252,6 +255,22 @@ def msa_indexer_score_shared_prefix(cache: Cache, batch: Batch, q_idx: torch.Ten
                                                int(prefix_blocks),
                                                _ptr(block_scores, torch.float32, "block_scores"),
                                                _stream(stream)))
+
+
+def msa_indexer_score_shard(cache: Cache, shard: Batch, block_begin: int, block_stride: int,
+                            total_blocks: int, q_idx: torch.Tensor, shard_scores: torch.Tensor,
+                            stream=None) -> None:
+    """shard: a Batch whose table column c holds the page of global block
+    block_begin + c * block_stride; shard_scores: [batch*q_len][4][shard.max_blocks]."""
+    if tuple(q_idx.shape) != (shard.rows, KV_HEADS, HEAD_DIM):
+        raise ValueError(f"q_idx: expected {(shard.rows, KV_HEADS, HEAD_DIM)}, got {tuple(q_idx.shape)}")
+    if tuple(shard_scores.shape) != (shard.rows, KV_HEADS, shard.max_blocks):
+        raise ValueError("shard_scores: expected [batch*q_len][4][max_blocks of the shard]")
+    _check(lib.msa_indexer_score_shard(ctypes.byref(cache._c), ctypes.byref(shard._c),
+                                       int(block_begin), int(block_stride), int(total_blocks),
+                                       _ptr(q_idx, torch.bfloat16, "q_idx"),
+                                       _ptr(shard_scores, torch.float32, "shard_scores"),
+                                       _stream(stream)))
 
 
 def msa_block_topk(block_scores: torch.Tensor, batch: Batch, topk: int, block_ids: torch.Tensor,

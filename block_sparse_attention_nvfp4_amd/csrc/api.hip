@@ -176,6 +176,29 @@ int msa_indexer_score_shared_prefix(const msa_cache_t* cache, const msa_batch_t*
                       fn);
 }
 
+int msa_indexer_score_shard(const msa_cache_t* cache, const msa_batch_t* shard,
+                            int32_t block_begin, int32_t block_stride, int32_t total_blocks,
+                            const uint16_t* q_idx, float* shard_scores, void* stream) {
+    static const char* fn = "msa_indexer_score_shard";
+    int rc = check_cache(cache, fn, false, true);
+    if (rc) return rc;
+    if ((rc = check_batch(shard, fn))) return rc;
+    if (!q_idx || !shard_scores) return fail(MSA_ERR_INVALID_ARG, "%s: q_idx or shard_scores is NULL", fn);
+    if (block_begin < 0 || block_stride < 1 || total_blocks < 1 ||
+        (int64_t)total_blocks * MSA_BLOCK > INT32_MAX / 2)
+        return fail(MSA_ERR_INVALID_ARG, "%s: block_begin=%d, block_stride=%d, total_blocks=%d", fn,
+                    block_begin, block_stride, total_blocks);
+    const int64_t last = (int64_t)block_begin + (int64_t)(shard->max_blocks - 1) * block_stride;
+    if (last >= total_blocks)
+        return fail(MSA_ERR_INVALID_ARG, "%s: the shard's last block %lld is past total_blocks=%d",
+                    fn, (long long)last, total_blocks);
+    return hip_status(msa::launch_indexer_shard(cache->ik, cache->num_pages, shard->block_table,
+                                                shard->ctx_lens, shard->batch, shard->max_blocks,
+                                                shard->q_len, q_idx, shard_scores, block_begin,
+                                                block_stride, total_blocks, (hipStream_t)stream),
+                      fn);
+}
+
 int msa_block_topk(const float* block_scores, const msa_batch_t* batch, int32_t topk,
                    int32_t* block_ids, void* stream) {
     static const char* fn = "msa_block_topk";

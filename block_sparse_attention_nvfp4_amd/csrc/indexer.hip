@@ -273,13 +273,23 @@ __device__ __forceinline__ int claim_page(const int* counter, int lane) {
 // LDS writes only, not for these stores. The
 // indexer wavefronts patch the new index keys into their page copies (patch_new_tokens): a
 // page may be read before or after another workgroup's store lands.
+//
+// A shard of the blocks (not FUSED): the table's column c holds the page of global block
+// g_begin + c * g_stride, whose tokens sit at positions 128 (g_begin + c g_stride) onwards, and
+// the context is clamped to total_blocks blocks (the whole table's width); column c of the
+// scores is then the full indexer's column g_begin + c g_stride, bit for bit (every block's score
+// is computed on its own, in the same order of operations).
 template <bool FUSED>
 __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
     const uint8_t* ik_pool, int64_t num_pages, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ ctx_lens, int max_blocks, int q_len,
     const uint16_t* __restrict__ q_idx, float* __restrict__ scores, uint8_t* k_pool_w,
     uint8_t* v_pool_w, const float* __restrict__ new_k,
-    const float* __restrict__ new_v, const float* __restrict__ new_ik) {
+    const float* __restrict__ new_v, const float* __restrict__ new_ik, int g_begin, int g_stride,
+    int total_blocks) {
+    // the fused step scores the whole table
+    const int gb = FUSED ? 0 : g_begin;
+    const int gs = FUSED ? 1 : g_stride;
     __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves][kBufs][kHalfBytes];
     // half-page maxima of the row tile: [half][row][block - wg_blk0], rows padded apart in banks
     __shared__ float stash[2][16][kPagesPerWg + 1];
@@ -333,11 +343,13 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
     }
     asm volatile("" : "+v"(pid_all), "+v"(T_raw), "+v"(ins_x));
     // the same value in every lane
-    const int T = __builtin_amdgcn_readfirstlane(clamp_ctx(T_raw, max_blocks));
+    const int T = __builtin_amdgcn_readfirstlane(clamp_ctx(T_raw, FUSED ? max_blocks : total_blocks));
     const int rows = 4 * q_len;
     const int64_t row_base = (int64_t)b * rows;
-    // blocks past the last query position hold no visible key and are never loaded
-    const int n_blocks = T > 0 ? min(max_blocks, (T - 1) / kBlock + 1) : 0;
+    // blocks past the last query position hold no visible key and are never loaded (columns
+    // below n_blocks hold a global block below the context's block count)
+    const int nb_ctx = T > 0 ? (T - 1) / kBlock + 1 : 0;
+    const int n_blocks = nb_ctx > gb ? min(max_blocks, (nb_ctx - gb + gs - 1) / gs) : 0;
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     pid_all = (wg_blk0 + lane < n_blocks && pid_all >= 0 && pid_all < num_pages) ? pid_all : -1;
     // the first insert item's position and block-table entry (set after the first page of the
@@ -347,11 +359,12 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
     uint32_t ins_byte = 0, ins_scale = 0;
     uint32_t prepped = 0;  // fused: tokens whose patch bytes are in this wavefront's staging area
 
-    // row tile rt (query rows rt .. rt + 15): one past its highest visible block; page u of the
-    // tile is block vis_end - 1 - u
+    // row tile rt (query rows rt .. rt + 15): one past its highest visible column; page u of
+    // the tile is column vis_end - 1 - u
     auto tile_vis_end = [&](int rt) {
         const int p_hi = T - q_len + min((rt >> 2) + 3, q_len - 1);  // highest position in it
-        return min(wg_end, p_hi >= 0 ? p_hi / kBlock + 1 : 0);
+        const int hb = p_hi >= 0 ? p_hi / kBlock : -1;                // its global block
+        return min(wg_end, hb >= gb ? (hb - gb) / gs + 1 : 0);
     };
     // load half h of page u of a tile into LDS buffer `buf`; false when the page is absent
     auto issue = [&](int u, int buf, int vis_end) {
@@ -467,7 +480,7 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
             const int nxt = claim_page(&next_page[h], lane);
             const bool nxt_loaded = nxt < n_pages && issue(nxt, buf ^ 1, vis_end);
             const int blk = vis_end - 1 - cur;
-            const int tok0 = blk * kBlock;
+            const int tok0 = (gb + blk * gs) * kBlock;
             float best = -INFINITY;
             if (cur_loaded) {
                 wait_halves(nxt_loaded ? 1 : 0);
@@ -551,17 +564,27 @@ static int indexer_wgs(int batch, int max_blocks) {
     return (max_blocks + kPagesPerWg - 1) / kPagesPerWg * batch;
 }
 
-hipError_t launch_indexer(const uint8_t* ik_pool, int64_t num_pages, const int32_t* block_table,
-                          const int32_t* ctx_lens, int batch, int max_blocks, int q_len,
-                          const uint16_t* q_idx, float* scores, hipStream_t stream) {
+hipError_t launch_indexer_shard(const uint8_t* ik_pool, int64_t num_pages,
+                                const int32_t* block_table, const int32_t* ctx_lens, int batch,
+                                int max_blocks, int q_len, const uint16_t* q_idx, float* scores,
+                                int block_begin, int block_stride, int total_blocks,
+                                hipStream_t stream) {
     if (q_len >= kIndexerGemmMinQ)
-        return launch_indexer_gemm(ik_pool, num_pages, block_table, ctx_lens, batch, max_blocks,
-                                   q_len, q_idx, scores, stream);
+        return launch_indexer_gemm_shard(ik_pool, num_pages, block_table, ctx_lens, batch,
+                                         max_blocks, q_len, q_idx, scores, block_begin,
+                                         block_stride, total_blocks, stream);
     hipLaunchKernelGGL(indexer_kernel<false>, dim3(indexer_wgs(batch, max_blocks)),
                        dim3(kWaves * 64), 0, stream, ik_pool, num_pages, block_table, ctx_lens,
                        max_blocks, q_len, q_idx, scores, nullptr, nullptr, nullptr, nullptr,
-                       nullptr);
+                       nullptr, block_begin, block_stride, total_blocks);
     return hipGetLastError();
+}
+
+hipError_t launch_indexer(const uint8_t* ik_pool, int64_t num_pages, const int32_t* block_table,
+                          const int32_t* ctx_lens, int batch, int max_blocks, int q_len,
+                          const uint16_t* q_idx, float* scores, hipStream_t stream) {
+    return launch_indexer_shard(ik_pool, num_pages, block_table, ctx_lens, batch, max_blocks,
+                                q_len, q_idx, scores, 0, 1, max_blocks, stream);
 }
 
 hipError_t launch_insert_indexer(uint8_t* k_pool, uint8_t* v_pool, uint8_t* ik_pool,
@@ -572,7 +595,8 @@ hipError_t launch_insert_indexer(uint8_t* k_pool, uint8_t* v_pool, uint8_t* ik_p
     if (q_len <= kFusedMaxNew) {
         hipLaunchKernelGGL(indexer_kernel<true>, dim3(indexer_wgs(batch, max_blocks)),
                            dim3(kWaves * 64), 0, stream, ik_pool, num_pages, block_table, ctx_lens,
-                           max_blocks, q_len, q_idx, scores, k_pool, v_pool, new_k, new_v, new_ik);
+                           max_blocks, q_len, q_idx, scores, k_pool, v_pool, new_k, new_v, new_ik,
+                           0, 1, max_blocks);
         return hipGetLastError();
     }
     // more new tokens than the patch stages: the insert launch first, then the indexer

@@ -50,15 +50,17 @@ __device__ __forceinline__ void read_tile(u32x4 (&v)[4], const uint8_t* tile, in
 
 // LSE: the block's log-sum-exp of its token scores instead of their max ("MiniMax M3 on
 // vLLM", section "Prefill execution": the block reduction may be max or log-sum-exp).
-// The blocks scored are blk_begin .. blk_end - 1. SHARED: one row space holds every query row
-// of the batch (blockIdx.z = 0), scored against the pages of sequence 0's table, which all
-// sequences share there and which hold no query token (no mask: every token is visible).
+// The table columns scored are blk_begin .. blk_end - 1; column c holds the page of global
+// block g_begin + c * g_stride (a shard of the blocks; 0 and 1 for a whole table) and the
+// context is clamped to total_blocks blocks. SHARED: one row space holds every query row of the
+// batch (blockIdx.z = 0), scored against the pages of sequence 0's table, which all sequences
+// share there and which hold no query token (no mask: every token is visible).
 template <bool LSE, bool SHARED>
 __global__ __launch_bounds__(kGWaves * 64, 2) void indexer_gemm_kernel(
     const uint8_t* __restrict__ ik_pool, int64_t num_pages, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ ctx_lens, int max_blocks, int q_len, int rows_per_wg,
     const uint16_t* __restrict__ q_idx, float* __restrict__ scores, int blk_begin, int blk_end,
-    int batch) {
+    int batch, int g_begin, int g_stride, int total_blocks) {
     __shared__ __attribute__((aligned(16))) uint8_t stage[2][kStageRows / 16][kTileBytes];
     __shared__ float best_of[kMaxRowsPerWg][kGWaves];
     const int lane = threadIdx.x & 63;
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(kGWaves * 64, 2) void indexer_gemm_kernel(
     const int blk0 = blk_begin + blockIdx.x * kGWaves;  // this workgroup's first block
     const int blk = blk0 + wave;
     // (SHARED: a context past every block, so that nothing is masked)
-    const int T = SHARED ? max_blocks * kBlock : clamp_ctx(ctx_lens[b], max_blocks);
+    const int T = SHARED ? max_blocks * kBlock : clamp_ctx(ctx_lens[b], total_blocks);
     const uint8_t* qseq = reinterpret_cast<const uint8_t*>(q_idx + (int64_t)b * rows * kDim);
 
     // stage loads: copies of 1 KB (tile tt, piece m), kCopies per wavefront; lane
@@ -95,7 +97,7 @@ __global__ __launch_bounds__(kGWaves * 64, 2) void indexer_gemm_kernel(
     // token row (bytes 2 s, 2 s + 1: element groups 2 c, 2 c + 1 of slab s)
     const bool in_table = blk < blk_end;
     int page = in_table ? block_table[(int64_t)b * max_blocks + blk] : -1;
-    const int tok0 = blk * kBlock;
+    const int tok0 = (g_begin + blk * g_stride) * kBlock;
     const bool has_keys = in_table && tok0 < T && page >= 0 && page < num_pages;
     bf16x8 ka[8][4];
     if (has_keys) {
@@ -189,7 +191,8 @@ template <bool LSE, bool SHARED>
 hipError_t launch_gemm_t(const uint8_t* ik_pool, int64_t num_pages, const int32_t* block_table,
                          const int32_t* ctx_lens, int batch, int max_blocks, int q_len,
                          const uint16_t* q_idx, float* scores, int blk_begin, int blk_end,
-                         hipStream_t stream) {
+                         hipStream_t stream, int g_begin = 0, int g_stride = 1,
+                         int total_blocks = -1) {
     if (blk_end <= blk_begin) return hipSuccess;
     const int rows = SHARED ? 4 * q_len * batch : 4 * q_len;
     const int rows_per_wg = min(kMaxRowsPerWg, (rows + 15) / 16 * 16);
@@ -197,7 +200,8 @@ hipError_t launch_gemm_t(const uint8_t* ik_pool, int64_t num_pages, const int32_
                     (rows + rows_per_wg - 1) / rows_per_wg, SHARED ? 1 : batch);
     hipLaunchKernelGGL((indexer_gemm_kernel<LSE, SHARED>), grid, dim3(kGWaves * 64), 0, stream,
                        ik_pool, num_pages, block_table, ctx_lens, max_blocks, q_len, rows_per_wg,
-                       q_idx, scores, blk_begin, blk_end, batch);
+                       q_idx, scores, blk_begin, blk_end, batch, g_begin, g_stride,
+                       total_blocks < 0 ? max_blocks : total_blocks);
     return hipGetLastError();
 }
 
@@ -212,6 +216,16 @@ hipError_t launch_indexer_gemm(const uint8_t* ik_pool, int64_t num_pages,
                                           max_blocks, q_len, q_idx, scores, 0, max_blocks, stream);
     return launch_gemm_t<false, false>(ik_pool, num_pages, block_table, ctx_lens, batch,
                                        max_blocks, q_len, q_idx, scores, 0, max_blocks, stream);
+}
+
+hipError_t launch_indexer_gemm_shard(const uint8_t* ik_pool, int64_t num_pages,
+                                     const int32_t* block_table, const int32_t* ctx_lens,
+                                     int batch, int max_blocks, int q_len, const uint16_t* q_idx,
+                                     float* scores, int block_begin, int block_stride,
+                                     int total_blocks, hipStream_t stream) {
+    return launch_gemm_t<false, false>(ik_pool, num_pages, block_table, ctx_lens, batch,
+                                       max_blocks, q_len, q_idx, scores, 0, max_blocks, stream,
+                                       block_begin, block_stride, total_blocks);
 }
 
 hipError_t launch_indexer_shared_prefix(const uint8_t* ik_pool, int64_t num_pages,

@@ -28,6 +28,20 @@ hipError_t launch_indexer_gemm(const uint8_t* ik_pool, int64_t num_pages,
                                int max_blocks, int q_len, const uint16_t* q_idx, float* scores,
                                hipStream_t stream, bool lse = false);
 
+// The indexer over a shard of the blocks: the table's column c holds the page of global block
+// block_begin + c * block_stride, the context is clamped to total_blocks blocks; the scores'
+// column c equals the whole-table indexer's column block_begin + c * block_stride.
+hipError_t launch_indexer_shard(const uint8_t* ik_pool, int64_t num_pages,
+                                const int32_t* block_table, const int32_t* ctx_lens, int batch,
+                                int max_blocks, int q_len, const uint16_t* q_idx, float* scores,
+                                int block_begin, int block_stride, int total_blocks,
+                                hipStream_t stream);
+hipError_t launch_indexer_gemm_shard(const uint8_t* ik_pool, int64_t num_pages,
+                                     const int32_t* block_table, const int32_t* ctx_lens,
+                                     int batch, int max_blocks, int q_len, const uint16_t* q_idx,
+                                     float* scores, int block_begin, int block_stride,
+                                     int total_blocks, hipStream_t stream);
+
 // Indexer for a batch whose sequences share their first prefix_blocks pages (sequence 0's
 // table entries) with no query token in them: those pages scored once for every query row of
 // the batch, the rest per sequence.

@@ -229,6 +229,32 @@ int msa_block_topk_window(const float *block_scores, const msa_batch_t *batch, i
                           void *stream);
 
 /*
+ * The indexer over one shard of the blocks, as one device of indexer decode context
+ * parallelism runs it ("vLLM day-0 support for MiniMax-M3.1-Flash", section "Indexer NVFP4
+ * DCP": each device scores every index head on its own share of the context, the scores are
+ * bit for bit those of a single device, and the owner of a head selects from them). The shard
+ * holds global blocks block_begin + c * block_stride, c = 0..shard->max_blocks - 1 (contiguous
+ * shards: stride 1; round-robin shards: begin = shard index, stride = shard count).
+ *   cache          : the pool holding the shard's pages (only its index-key pages are read).
+ *   shard          : block_table [batch][max_blocks]: column c holds the page of global block
+ *                    block_begin + c * block_stride (-1: absent, scored -inf); ctx_lens and
+ *                    q_len are the sequences' own (global positions); batch as usual.
+ *   total_blocks   : the width of the whole block table the shard is cut from; the context is
+ *                    clamped to total_blocks * 128 tokens as msa_indexer_score clamps it.
+ *   q_idx          : device bf16 [batch * q_len][4][128], as for msa_indexer_score.
+ *   shard_scores   : device fp32 [batch * q_len][4][max_blocks]: column c equals, bit for bit,
+ *                    column block_begin + c * block_stride of what msa_indexer_score writes for
+ *                    the whole table (-inf where no key of the block is visible to the row).
+ * Feed shard_scores to msa_block_topk_local with the same begin and stride (ld = max_blocks),
+ * then every shard's list to msa_block_topk_merge: the result is msa_block_topk's.
+ * Errors: as msa_indexer_score, and MSA_ERR_INVALID_ARG for block_begin < 0, block_stride < 1,
+ * total_blocks < 1 or too large, or a shard block >= total_blocks.
+ */
+int msa_indexer_score_shard(const msa_cache_t *cache, const msa_batch_t *shard,
+                            int32_t block_begin, int32_t block_stride, int32_t total_blocks,
+                            const uint16_t *q_idx, float *shard_scores, void *stream);
+
+/*
  * Block selection split over shards of the blocks, as in indexer decode context parallelism
  * ("vLLM day-0 support for MiniMax-M3.1-Flash", section "Indexer NVFP4 DCP": each device
  * scores every index head on its own share of the pages and keeps a local top 16 per head;

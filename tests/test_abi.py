@@ -99,6 +99,15 @@ def test_invalid_arguments_return_codes_without_launch(msa):
     assert sp(by(_cache()), by(_batch(mb=4)), 1, 5, 1, None) == msa.MSA_ERR_INVALID_ARG
     assert sp(by(_cache()), by(_batch(mb=4)), None, 2, 1, None) == msa.MSA_ERR_INVALID_ARG
     assert sp(by(_cache(ik=None)), by(_batch(mb=4)), 1, 2, 1, None) == msa.MSA_ERR_INVALID_ARG
+    # the indexer over a shard (args: cache shard begin stride total q_idx scores stream)
+    sh = L.msa_indexer_score_shard
+    for bad in ((-1, 1, 8), (0, 0, 8), (0, 1, 0), (5, 1, 8), (1, 3, 8), (0, 1, 1 << 30)):
+        assert sh(by(_cache()), by(_batch(mb=4)), *bad, 1, 1, None) == msa.MSA_ERR_INVALID_ARG, bad
+    assert sh(by(_cache()), by(_batch(mb=4)), 0, 1, 8, None, 1, None) == msa.MSA_ERR_INVALID_ARG
+    assert sh(by(_cache()), by(_batch(mb=4)), 0, 1, 8, 1, None, None) == msa.MSA_ERR_INVALID_ARG
+    assert sh(by(_cache(ik=None)), by(_batch(mb=4)), 0, 1, 8, 1, 1, None) == msa.MSA_ERR_INVALID_ARG
+    assert sh(by(_cache()), by(_batch(mb=4, q=0)), 0, 1, 8, 1, 1, None) == msa.MSA_ERR_INVALID_ARG
+    assert "total_blocks" in msa.msa_last_error() or "q_len" in msa.msa_last_error()
     # top-k
     assert L.msa_block_topk(1, by(_batch()), 8, 1, None) == msa.MSA_ERR_UNSUPPORTED
     assert "topk" in msa.msa_last_error()
