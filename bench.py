@@ -59,7 +59,7 @@ def parse():
     ap.add_argument("--only", default="", help="profiling aid: run a calibration copy of "
                     f"{COPY_BYTES >> 20} MiB, then only this call in a loop "
                     "(insert|indexer|insert_indexer|topk|attention|select_attention), and exit; "
-                    "'prefill' runs only the prefill workload's calls")
+                    "'prefill' and 'prefix' run only that side measurement")
     ap.add_argument("--workload", default="spec128k",
                     choices=("spec128k", "union32x128k", "batched32k", "ragged512k"),
                     help="decode workload of an --only run")
@@ -239,6 +239,9 @@ def main():
     if args.only == "prefill":
         print(json.dumps(prefill_side(args)), flush=True)
         return
+    if args.only == "prefix":
+        print(json.dumps(prefix_side(args)), flush=True)
+        return
     if args.only:
         ow = {"spec128k": w, "union32x128k": mi.make_workload(3, batch=32),
               "batched32k": mi.full_workload(2), "ragged512k": mi.full_workload(4)}[args.workload]
@@ -308,6 +311,10 @@ def main():
     if not args.no_prefill:
         torch.cuda.empty_cache()
         result["prefill"] = prefill_side(args)
+    if not args.no_side:
+        torch.cuda.empty_cache()
+        print("# side line prefix64", file=sys.stderr, flush=True)
+        result["side"]["prefix64"] = prefix_side(args)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
@@ -540,6 +547,103 @@ def side_line(w, L, args):
                            "frac": round(m["roof_bytes"] / (ku["insert_indexer"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
         "attention_gather": {"algorithmic_bytes": m["attn_bytes"],
                              "frac": round(m["attn_bytes"] / (ku["select_attention"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
+    }
+
+
+def prefix_side(args, L=4):
+    """The prefix-sharing workload (64 requests sharing a 32,768-token prefix, each with its own
+    1K-8K suffix, 1 query token): the decode step as the per-request path runs it (fused insert
+    + indexer, then selection + attention) and as the shared-prefix path runs it (insert; the
+    indexer scoring each shared page once for all requests; selection; the attention
+    dequantizing each selected shared block once for all requests that selected it), on L
+    rotated layers, with every call timed alone and the blocks each attention dequantizes."""
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_nvfp4_amd as msa
+    import msa_inputs as mi
+
+    dev = "cuda"
+    w = mi.make_workload(6)
+    B, q, P = w.batch, w.q_len, w.prefix_tokens // 128
+    caches = layer_caches(w, L)
+    batch = msa.Batch(torch.from_numpy(w.block_table).to(dev),
+                      torch.tensor(w.ctx_lens, dtype=torch.int32, device=dev), q)
+    toks = [(b, w.ctx_lens[b] - q, w.ctx_lens[b]) for b in range(B)]
+    new_slots = torch.from_numpy(np.concatenate([w.slots(b, t0, t1) for b, t0, t1 in toks])).to(dev)
+    new_k = torch.cat([w.kv_rows("k", b, t0, t1, dev) for b, t0, t1 in toks])
+    new_v = torch.cat([w.kv_rows("v", b, t0, t1, dev) for b, t0, t1 in toks])
+    new_ik = torch.cat([w.ik_rows(b, t0, t1, dev) for b, t0, t1 in toks])
+    q_idx, qq = w.q_idx.to(dev), w.q.to(dev)
+    steps = [msa.DecodeStep(c, batch, dev) for c in caches]
+    ws = torch.empty(msa.msa_sparse_attn_shared_prefix_workspace_bytes(batch), dtype=torch.uint8,
+                     device=dev)
+    scale = msa.default_softmax_scale()
+    calls = {
+        "insert_indexer": lambda s: msa.msa_insert_indexer_score(s.cache, batch, new_k, new_v,
+                                                                 new_ik, q_idx, s.block_scores),
+        "select_attention": lambda s: msa.msa_select_attn_decode(s.cache, batch, s.block_scores, 16,
+                                                                 s.block_ids, qq, scale, s.out,
+                                                                 s.workspace),
+        "insert": lambda s: msa.msa_kv_insert_nvfp4(s.cache, new_slots, new_k, new_v, new_ik),
+        "indexer": lambda s: msa.msa_indexer_score(s.cache, batch, q_idx, s.block_scores),
+        "indexer_shared_prefix": lambda s: msa.msa_indexer_score_shared_prefix(
+            s.cache, batch, q_idx, P, s.block_scores),
+        "topk": lambda s: msa.msa_block_topk(s.block_scores, batch, 16, s.block_ids),
+        "attention": lambda s: msa.msa_sparse_attn_decode(s.cache, batch, qq, s.block_ids, scale,
+                                                          s.out, s.workspace),
+        "attention_shared_prefix": lambda s: msa.msa_sparse_attn_decode_shared_prefix(
+            s.cache, batch, qq, s.block_ids, P, scale, s.out, ws),
+    }
+    paths = {"per_request": ("insert_indexer", "select_attention"),
+             "shared_prefix": ("insert", "indexer_shared_prefix", "topk", "attention_shared_prefix")}
+    for s in steps:
+        for name in paths["per_request"]:
+            calls[name](s)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    graphs = {}
+    with torch.cuda.stream(stream):
+        for key, names in list(paths.items()) + [(n, (n,)) for n in calls]:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for s in steps:
+                    for name in names:
+                        calls[name](s)
+            graphs[key] = g
+    torch.cuda.synchronize()
+    us = {}
+    with torch.cuda.stream(stream):
+        for key, g in graphs.items():
+            g.replay()
+            series = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(args.kernel_reps):
+                    g.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                series.append(e0.elapsed_time(e1) * 1e3 / (args.kernel_reps * L))
+            us[key] = round(sorted(series)[2], 3)
+    # blocks each attention dequantizes (one layer): the per-request kernel every usable
+    # (row, group, slot); the shared-prefix one each selected shared (group, block) once plus
+    # every usable private slot
+    ids = steps[0].block_ids.cpu().numpy().reshape(B, q, 4, 16)
+    pos = np.array(w.ctx_lens)[:, None] - q + np.arange(q)[None, :]
+    usable = (ids >= 0) & (ids * 128 <= pos[:, :, None, None])
+    shared = usable & (ids < P)
+    uniq = sum(len(set(ids[:, :, g][shared[:, :, g]].tolist())) for g in range(4))
+    per_row = int(usable.sum())
+    return {
+        "workload": f"prefix: {B} requests sharing {P * 128} prefix tokens, own suffixes "
+                    f"{min(w.ctx_lens) - P * 128}..{max(w.ctx_lens) - P * 128} tokens, {q} query "
+                    f"token each, 64 q heads / 4 kv heads / head_dim 128, NVFP4 caches, top-16, "
+                    f"{L} layers rotated",
+        "us": us,
+        "query_tokens_per_s": {k: round(B * q / (us[k] * 1e-6), 1) for k in paths},
+        "attention_dequantized_blocks": {"per_request": per_row, "shared_prefix": uniq + per_row - int(shared.sum())},
+        "shared_slots": int(shared.sum()),
     }
 
 

@@ -58,6 +58,7 @@ EXPORTED = ("msa_page_bytes", "msa_kv_insert_nvfp4", "msa_indexer_score", "msa_i
             "msa_block_topk",
             "msa_block_topk_window", "msa_block_topk_local", "msa_block_topk_merge",
             "msa_sparse_attn_workspace_bytes", "msa_sparse_attn_decode", "msa_select_attn_decode",
+            "msa_sparse_attn_shared_prefix_workspace_bytes", "msa_sparse_attn_decode_shared_prefix",
             "msa_insert_indexer_score", "msa_decode_step", "msa_decode_step_noalloc",
             "msa_last_error", "msa_version",
             # include/msa_probe.h (measurement aid)
@@ -115,6 +116,11 @@ def _load() -> ctypes.CDLL:
     L.msa_sparse_attn_decode.restype = ctypes.c_int
     L.msa_sparse_attn_decode.argtypes = [ctypes.POINTER(_Cache), ctypes.POINTER(_Batch), vp, vp,
                                          ctypes.c_float, vp, vp, sz, vp]
+    L.msa_sparse_attn_shared_prefix_workspace_bytes.restype = sz
+    L.msa_sparse_attn_shared_prefix_workspace_bytes.argtypes = [ctypes.POINTER(_Batch)]
+    L.msa_sparse_attn_decode_shared_prefix.restype = ctypes.c_int
+    L.msa_sparse_attn_decode_shared_prefix.argtypes = [ctypes.POINTER(_Cache), ctypes.POINTER(_Batch),
+                                                       vp, vp, i32, ctypes.c_float, vp, vp, sz, vp]
     L.msa_select_attn_decode.restype = ctypes.c_int
     L.msa_select_attn_decode.argtypes = [ctypes.POINTER(_Cache), ctypes.POINTER(_Batch), vp, i32,
                                          vp, vp, ctypes.c_float, vp, vp, sz, vp]
@@ -353,6 +359,25 @@ def msa_sparse_attn_decode(cache: Cache, batch: Batch, q: torch.Tensor, block_id
                                       _ptr(block_ids, torch.int32, "block_ids"),
                                       float(softmax_scale), _ptr(out, torch.bfloat16, "out"),
                                       ws_ptr, ws_bytes, _stream(stream)))
+
+
+def msa_sparse_attn_shared_prefix_workspace_bytes(batch: Batch) -> int:
+    return int(lib.msa_sparse_attn_shared_prefix_workspace_bytes(ctypes.byref(batch._c)))
+
+
+def msa_sparse_attn_decode_shared_prefix(cache: Cache, batch: Batch, q: torch.Tensor,
+                                         block_ids: torch.Tensor, prefix_blocks: int,
+                                         softmax_scale: float, out: torch.Tensor,
+                                         workspace: torch.Tensor, stream=None) -> None:
+    if tuple(q.shape) != (batch.rows, Q_HEADS, HEAD_DIM) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q and out: expected [batch*q_len][64][128]")
+    if tuple(block_ids.shape) != (batch.rows, KV_HEADS, TOPK):
+        raise ValueError("block_ids: expected [batch*q_len][4][16]")
+    _check(lib.msa_sparse_attn_decode_shared_prefix(
+        ctypes.byref(cache._c), ctypes.byref(batch._c), _ptr(q, torch.bfloat16, "q"),
+        _ptr(block_ids, torch.int32, "block_ids"), int(prefix_blocks), float(softmax_scale),
+        _ptr(out, torch.bfloat16, "out"), _ptr(workspace, workspace.dtype, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def msa_select_attn_decode(cache: Cache, batch: Batch, block_scores: torch.Tensor, topk: int,

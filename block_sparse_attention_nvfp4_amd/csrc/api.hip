@@ -314,6 +314,43 @@ int msa_sparse_attn_decode(const msa_cache_t* cache, const msa_batch_t* batch, c
                       fn);
 }
 
+size_t msa_sparse_attn_shared_prefix_workspace_bytes(const msa_batch_t* batch) {
+    if (!batch || batch->batch < 1 || batch->q_len < 1) return 0;
+    return msa::attn_shared_prefix_workspace_bytes(batch->batch, batch->q_len);
+}
+
+int msa_sparse_attn_decode_shared_prefix(const msa_cache_t* cache, const msa_batch_t* batch,
+                                         const uint16_t* q, const int32_t* block_ids,
+                                         int32_t prefix_blocks, float softmax_scale,
+                                         uint16_t* out, void* workspace, size_t ws_bytes,
+                                         void* stream) {
+    static const char* fn = "msa_sparse_attn_decode_shared_prefix";
+    int rc = check_cache(cache, fn, true, false);
+    if (rc) return rc;
+    if ((rc = check_batch(batch, fn))) return rc;
+    if (!q || !block_ids || !out)
+        return fail(MSA_ERR_INVALID_ARG, "%s: q, block_ids or out is NULL", fn);
+    if (prefix_blocks < 0 || prefix_blocks > batch->max_blocks)
+        return fail(MSA_ERR_INVALID_ARG, "%s: prefix_blocks=%d outside [0, max_blocks=%d]", fn,
+                    prefix_blocks, batch->max_blocks);
+    const int64_t rows = (int64_t)batch->batch * batch->q_len;
+    if (rows > msa::attn_shared_prefix_max_rows())
+        return fail(MSA_ERR_UNSUPPORTED, "%s: batch*q_len=%lld above %d", fn, (long long)rows,
+                    msa::attn_shared_prefix_max_rows());
+    const size_t need = msa::attn_shared_prefix_workspace_bytes(batch->batch, batch->q_len);
+    if (!workspace || ws_bytes < need)
+        return fail(MSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                    workspace ? ws_bytes : (size_t)0);
+    if ((uintptr_t)workspace & 255u)
+        return fail(MSA_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+    return hip_status(msa::launch_attention_shared_prefix(
+                          cache->k, cache->v, cache->num_pages, batch->block_table,
+                          batch->ctx_lens, batch->batch, batch->max_blocks, batch->q_len, q,
+                          block_ids, prefix_blocks, softmax_scale, out, workspace,
+                          (hipStream_t)stream),
+                      fn);
+}
+
 int msa_select_attn_decode(const msa_cache_t* cache, const msa_batch_t* batch,
                            const float* block_scores, int32_t topk, int32_t* block_ids,
                            const uint16_t* q, float softmax_scale, uint16_t* out,

@@ -957,6 +957,295 @@ __global__ __launch_bounds__(kTileWaves * 64) void attention_tile_kernel(
     }
 }
 
+// ---------------------------------------------------------------- shared-prefix pages
+// A batch whose requests share the pages of their first prefix_blocks blocks ("vLLM day-0
+// support for MiniMax-M3.1-Flash", section "NVFP4 MSA kernel": a page of a shared prefix is
+// dequantized once for up to 64 requests that share it). Two launches:
+//   shared_block_kernel: one workgroup of eight wavefronts per (shared block, group). It lists
+//   every row (query token of any request) whose selection holds the block (a workgroup with
+//   none ends there), loads the block's K and V pages once and dequantizes them once into the
+//   fp16 operand tables, and then computes the listed rows' attention over that block alone from
+//   the tables, two rows per wavefront at a time (each table read serving both), kept as
+//   partials: per head the row's maximum and sum (log2 domain) and its output normalized by the
+//   sum, in fp16.
+//   shared_combine_kernel: one workgroup of eight wavefronts per row group (row, group). Each
+//   wavefront takes two of the row's 16 selection slots, folds in the partials of its shared
+//   blocks and attends to its private blocks itself (as attention_kernel does), and the eight
+//   wavefronts merge by log-sum-exp.
+// Rows are held in a workgroup list of at most kSharedMaxRows entries per block.
+constexpr int kSharedMaxRows = 1024;
+constexpr int kSharedTpw = 2;  // rows per wavefront at a time
+constexpr int kSPartBytes = 2 * kGroupHeads * 4 + kGroupHeads * kDim * 2;  // m, l; then o in fp16
+constexpr int kCombineWaves = 8;
+
+__global__ __launch_bounds__(kTileWaves * 64) void shared_block_kernel(
+    const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool, int64_t num_pages,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens, int batch,
+    int max_blocks, int q_len, const uint16_t* __restrict__ q,
+    const int32_t* __restrict__ block_ids, float scale_log2, uint8_t* __restrict__ parts) {
+    __shared__ __attribute__((aligned(16))) uint8_t page[kBlockBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t kf[8 * 4096];  // fp16 operand tables
+    __shared__ __attribute__((aligned(16))) uint8_t vf[8 * 4096];
+    __shared__ int items[kSharedMaxRows];  // 16 r + k: slot k of row r selected this block
+    __shared__ int n_items;
+    static_assert(kTileWaves == 8, "dequant_tables: one K slab and one V dim tile per wavefront");
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15;
+    const int c = lane >> 4;
+    // group g on XCDs g and g + 4: the query rows of a group are read from those XCDs' L2
+    const int g = blockIdx.x & 3;
+    const int blk = blockIdx.x >> 2;
+    const int rows = batch * q_len;
+    if (threadIdx.x == 0) n_items = 0;
+    __syncthreads();
+    // the rows that selected the block and see a key of it (the rule of attention_kernel)
+    for (int i = threadIdx.x; i < rows * kTopk; i += kTileWaves * 64) {
+        const int r = i >> 4;
+        if (block_ids[((int64_t)r * kKvHeads + g) * kTopk + (i & 15)] == blk) {
+            const int b = r / q_len;
+            const int p = clamp_ctx(ctx_lens[b], max_blocks) - q_len + (r - b * q_len);
+            if (blk * kBlock <= p) {
+                const int at = atomicAdd(&n_items, 1);
+                if (at < kSharedMaxRows) items[at] = i;
+            }
+        }
+    }
+    __syncthreads();
+    const int count = __builtin_amdgcn_readfirstlane(min(n_items, kSharedMaxRows));
+    // sequence 0's table entry: the page every request holds for the block
+    const int pg = __builtin_amdgcn_readfirstlane(block_table[blk]);
+    if (count == 0 || pg < 0 || pg >= num_pages) return;  // the whole workgroup
+
+    // the block's K and V pages (9 + 9 pieces of 1 KB) spread over the wavefronts
+    const uint8_t* kp = k_pool + ((int64_t)pg * kKvHeads + g) * kHeadPageBytes;
+    const uint8_t* vp = v_pool + ((int64_t)pg * kKvHeads + g) * kHeadPageBytes;
+    for (int i = wave; i < 18; i += kTileWaves) {
+        const uint8_t* src = i < 9 ? kp + i * 1024 : vp + (i - 9) * 1024;
+        __builtin_amdgcn_global_load_lds(src + lane * 16, (lds_void*)(page + i * 1024), 16, 0,
+                                         kPagePolicy);
+    }
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+    __syncthreads();
+    // a shared block lies before every query token: all 128 of its tokens are in the cache
+    dequant_tables(page, kf, vf, wave, lane, kBlock);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    for (int it0 = kSharedTpw * wave; it0 < count; it0 += kSharedTpw * kTileWaves) {
+        int r[kSharedTpw], k[kSharedTpw], p[kSharedTpw];
+        bool sel[kSharedTpw];
+        bf16x8 qb[kSharedTpw][4];
+#pragma unroll
+        for (int t = 0; t < kSharedTpw; t++) {
+            sel[t] = it0 + t < count;  // wavefront-uniform
+            const int code = __builtin_amdgcn_readfirstlane(items[sel[t] ? it0 + t : it0]);
+            r[t] = code >> 4;
+            k[t] = code & 15;
+            const int b = r[t] / q_len;
+            p[t] = clamp_ctx(ctx_lens[b], max_blocks) - q_len + (r[t] - b * q_len);
+            const uint16_t* qp = q + ((int64_t)r[t] * kQHeads + kGroupHeads * g + n) * kDim + 32 * c;
+#pragma unroll
+            for (int m = 0; m < 4; m++) qb[t][m] = *reinterpret_cast<const bf16x8*>(qp + 8 * m);
+        }
+        f16x8 qh[kSharedTpw][4];
+        float q_unscale[kSharedTpw];
+        bool exact = true;
+#pragma unroll
+        for (int t = 0; t < kSharedTpw; t++) exact = query_to_f16(qb[t], qh[t], q_unscale[t]) && exact;
+        const bool f16 = __all(exact);  // both rows in fp16, or both in bf16
+        u32x4 qop[kSharedTpw][4];
+        float logit_scale[kSharedTpw], m_run[kSharedTpw], l_run[kSharedTpw];
+        f32x4 o[kSharedTpw][8];
+#pragma unroll
+        for (int t = 0; t < kSharedTpw; t++) {
+#pragma unroll
+            for (int m = 0; m < 4; m++) {
+                qop[t][m] = f16 ? __builtin_bit_cast(u32x4, qh[t][m]) : __builtin_bit_cast(u32x4, qb[t][m]);
+                if (scale_log2 < 0.f) qop[t][m] ^= 0x80008000u;  // as attention_kernel
+            }
+            logit_scale[t] = fabsf(scale_log2) * (f16 ? q_unscale[t] : 1.0f);
+            m_run[t] = -INFINITY;
+            l_run[t] = 0.f;
+#pragma unroll
+            for (int dt = 0; dt < 8; dt++) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        int lane_i = lane;  // recomputed addresses (as in attention_tile_kernel)
+        asm volatile("" : "+v"(lane_i));
+        if (f16) attend_tables<true, kSharedTpw>(kf, vf, lane_i, c, blk * kBlock, p, sel, qop, logit_scale, m_run, l_run, o);
+        else attend_tables<false, kSharedTpw>(kf, vf, lane_i, c, blk * kBlock, p, sel, qop, logit_scale, m_run, l_run, o);
+        // the partials of (row r, group g, slot k); lane (n, c) holds head n, dims 16 dt + 4c + i
+#pragma unroll
+        for (int t = 0; t < kSharedTpw; t++) {
+            if (!sel[t]) continue;
+            uint8_t* dst = parts + (((int64_t)r[t] * kKvHeads + g) * kTopk + k[t]) * kSPartBytes;
+            if (c == 0) {
+                reinterpret_cast<float*>(dst)[n] = m_run[t];
+                reinterpret_cast<float*>(dst)[kGroupHeads + n] = l_run[t];
+            }
+            const float inv = 1.f / l_run[t];  // >= 1: the block's largest weight is 1
+            _Float16* od = reinterpret_cast<_Float16*>(dst + 2 * kGroupHeads * 4) + n * kDim + 4 * c;
+#pragma unroll
+            for (int dt = 0; dt < 8; dt++)
+                *reinterpret_cast<f16x4*>(od + 16 * dt) =
+                    f16x4{(_Float16)(o[t][dt][0] * inv), (_Float16)(o[t][dt][1] * inv),
+                          (_Float16)(o[t][dt][2] * inv), (_Float16)(o[t][dt][3] * inv)};
+        }
+    }
+}
+
+__global__ __launch_bounds__(kCombineWaves * 64) void shared_combine_kernel(
+    const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool, int64_t num_pages,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens, int batch,
+    int max_blocks, int q_len, const uint16_t* __restrict__ q,
+    const int32_t* __restrict__ block_ids, int prefix_blocks, float scale_log2,
+    const uint8_t* __restrict__ parts, uint16_t* __restrict__ out) {
+    constexpr int kSlots = kTopk / kCombineWaves;  // selection slots per wavefront
+    static_assert(kCombineWaves * kBlockBytes >= kCombineWaves * kGroupHeads * kMergeStride * 4,
+                  "merge area must fit in the page buffers");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kCombineWaves][kBlockBytes];
+    __shared__ float sh_m[kCombineWaves][kGroupHeads];
+    __shared__ float sh_l[kCombineWaves][kGroupHeads];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15;
+    const int c = lane >> 4;
+    const int rg = blockIdx.x;  // row group: row r, group g
+    const int r = rg >> 2;
+    const int g = rg & 3;
+    const int b = r / q_len;
+    bf16x8 qb[4];
+    {
+        const uint16_t* qp = q + ((int64_t)r * kQHeads + kGroupHeads * g + n) * kDim + 32 * c;
+#pragma unroll
+        for (int m = 0; m < 4; m++) qb[m] = *reinterpret_cast<const bf16x8*>(qp + 8 * m);
+    }
+    const int T = clamp_ctx(ctx_lens[b], max_blocks);
+    const int p = T - q_len + (r - b * q_len);
+    // this wavefront's slots, lane k holding slot kSlots wave + k: the block id and its page
+    // (sequence 0's entry for a shared block), or -1 when the slot is unusable
+    int id = -1, page = -1;
+    if (lane < kSlots) {
+        const int v = block_ids[(int64_t)rg * kTopk + kSlots * wave + lane];
+        if (v >= 0 && v < max_blocks && v * kBlock <= p) {
+            const int pgv = block_table[(int64_t)(v < prefix_blocks ? 0 : b) * max_blocks + v];
+            if (pgv >= 0 && pgv < num_pages) {
+                id = v;
+                page = pgv;
+            }
+        }
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+    const uint8_t* kg = k_pool + (int64_t)g * kHeadPageBytes;
+    const uint8_t* vg = v_pool + (int64_t)g * kHeadPageBytes;
+    constexpr int64_t kPageStride = (int64_t)kKvHeads * kHeadPageBytes;
+    // the first private block's pages are requested first, then every shared slot's partial:
+    // all of it is in flight together
+    int first_priv = kSlots;
+    for (int kb = kSlots - 1; kb >= 0; kb--) {
+        if (__builtin_amdgcn_readlane(id, kb) >= prefix_blocks) first_priv = kb;
+    }
+    if (first_priv < kSlots) {
+        const int pg = __builtin_amdgcn_readlane(page, first_priv);
+        block_to_lds(kg + pg * kPageStride, vg + pg * kPageStride, lds[wave], lane);
+    }
+    float pm[kSlots], pl[kSlots];
+    f16x4 pv[kSlots][8];
+#pragma unroll
+    for (int kb = 0; kb < kSlots; kb++) {
+        const int cid = __builtin_amdgcn_readlane(id, kb);
+        pm[kb] = -INFINITY;
+        pl[kb] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < 8; dt++) pv[kb][dt] = f16x4{};
+        if (cid >= 0 && cid < prefix_blocks) {
+            const uint8_t* src = parts + ((int64_t)rg * kTopk + kSlots * wave + kb) * kSPartBytes;
+            pm[kb] = reinterpret_cast<const float*>(src)[n];
+            pl[kb] = reinterpret_cast<const float*>(src)[kGroupHeads + n];
+            const _Float16* op = reinterpret_cast<const _Float16*>(src + 2 * kGroupHeads * 4) + n * kDim + 4 * c;
+#pragma unroll
+            for (int dt = 0; dt < 8; dt++) pv[kb][dt] = *reinterpret_cast<const f16x4*>(op + 16 * dt);
+        }
+    }
+    f16x8 qh[4];
+    float q_unscale;
+    const bool f16 = __all(query_to_f16(qb, qh, q_unscale));
+    u32x4 qop[4];
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+        qop[m] = f16 ? __builtin_bit_cast(u32x4, qh[m]) : __builtin_bit_cast(u32x4, qb[m]);
+        if (scale_log2 < 0.f) qop[m] ^= 0x80008000u;
+    }
+    const float logit_scale = fabsf(scale_log2) * (f16 ? q_unscale : 1.0f);
+
+    // shared blocks: each partial rescaled to the running maximum and added
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 o[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < kSlots; kb++) {
+        if (pm[kb] == -INFINITY) continue;  // not a shared slot (every head agrees)
+        const float m_new = fmaxf(m_run, pm[kb]);
+        const float a = m_run == -INFINITY ? 0.f : fast_exp2(m_run - m_new);
+        const float wp = pl[kb] * fast_exp2(pm[kb] - m_new);
+        l_run = l_run * a + wp;
+#pragma unroll
+        for (int dt = 0; dt < 8; dt++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) o[dt][i] = o[dt][i] * a + wp * (float)pv[kb][dt][i];
+        m_run = m_new;
+    }
+    // private blocks: attended here, as attention_kernel does (the first one's pages requested
+    // above)
+    for (int kb = first_priv; kb < kSlots; kb++) {
+        const int cid = __builtin_amdgcn_readlane(id, kb);
+        if (cid < prefix_blocks) continue;  // shared, or unusable (-1)
+        if (kb != first_priv) {
+            const int pg = __builtin_amdgcn_readlane(page, kb);
+            block_to_lds(kg + pg * kPageStride, vg + pg * kPageStride, lds[wave], lane);
+        }
+        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // the K page has arrived
+        if (f16) attend_block<true, false>(lds[wave], lane, c, cid * kBlock, p, qop, logit_scale, m_run, l_run, o);
+        else attend_block<false, false>(lds[wave], lane, c, cid * kBlock, p, qop, logit_scale, m_run, l_run, o);
+    }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __syncthreads();  // every page buffer is free: the merge area
+
+    // ---- merge the wavefronts: lane (n, c) holds o[dt][i] = out(head n, dim 16dt + 4c + i)
+    float* sh_o = reinterpret_cast<float*>(&lds[0][0]);  // [kCombineWaves][16][kMergeStride]
+#pragma unroll
+    for (int dt = 0; dt < 8; dt++)
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            sh_o[(wave * kGroupHeads + n) * kMergeStride + 16 * dt + 4 * c + i] = o[dt][i];
+    if (c == 0) {
+        sh_m[wave][n] = m_run;
+        sh_l[wave][n] = l_run;
+    }
+    __syncthreads();
+    const int h = threadIdx.x >> 5;         // head 0..15
+    const int d0 = (threadIdx.x & 31) * 4;  // 4 dims
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kCombineWaves; w++) M = fmaxf(M, sh_m[w][h]);
+    float L = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kCombineWaves; w++) {
+        const float wt = sh_m[w][h] == -INFINITY ? 0.f : fast_exp2(sh_m[w][h] - M);
+        L += wt * sh_l[w][h];
+#pragma unroll
+        for (int e = 0; e < 4; e++) acc[e] += wt * sh_o[(w * kGroupHeads + h) * kMergeStride + d0 + e];
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const uint32_t lo = (uint32_t)bf16_bits_rne(acc[0] * inv) | ((uint32_t)bf16_bits_rne(acc[1] * inv) << 16);
+    const uint32_t hi = (uint32_t)bf16_bits_rne(acc[2] * inv) | ((uint32_t)bf16_bits_rne(acc[3] * inv) << 16);
+    uint16_t* op = out + ((int64_t)r * kQHeads + kGroupHeads * g + h) * kDim + d0;
+    *reinterpret_cast<uint2*>(op) = uint2{lo, hi};
+}
+
 }  // namespace
 
 int attn_num_splits(int batch, int q_len) {
@@ -1099,6 +1388,33 @@ hipError_t launch_select_attention(const uint8_t* k_pool, const uint8_t* v_pool,
     return launch_attention_t<true>(k_pool, v_pool, num_pages, block_table, ctx_lens, batch,
                                     max_blocks, q_len, q, ids, scores, softmax_scale, out,
                                     workspace, stream);
+}
+
+int attn_shared_prefix_max_rows() { return kSharedMaxRows; }
+
+size_t attn_shared_prefix_workspace_bytes(int batch, int q_len) {
+    return (size_t)batch * q_len * kKvHeads * kTopk * kSPartBytes;
+}
+
+hipError_t launch_attention_shared_prefix(const uint8_t* k_pool, const uint8_t* v_pool,
+                                          int64_t num_pages, const int32_t* block_table,
+                                          const int32_t* ctx_lens, int batch, int max_blocks,
+                                          int q_len, const uint16_t* q, const int32_t* ids,
+                                          int prefix_blocks, float softmax_scale, uint16_t* out,
+                                          void* workspace, hipStream_t stream) {
+    const float scale_log2 = softmax_scale * 1.4426950408889634f;
+    uint8_t* parts = static_cast<uint8_t*>(workspace);
+    if (prefix_blocks > 0) {
+        hipLaunchKernelGGL(shared_block_kernel, dim3(prefix_blocks * kKvHeads), dim3(kTileWaves * 64),
+                           0, stream, k_pool, v_pool, num_pages, block_table, ctx_lens, batch,
+                           max_blocks, q_len, q, ids, scale_log2, parts);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL(shared_combine_kernel, dim3(batch * q_len * kKvHeads), dim3(kCombineWaves * 64), 0,
+                       stream, k_pool, v_pool, num_pages, block_table, ctx_lens, batch, max_blocks,
+                       q_len, q, ids, prefix_blocks, scale_log2, parts, out);
+    return hipGetLastError();
 }
 
 }  // namespace msa

@@ -120,4 +120,17 @@ hipError_t launch_select_attention(const uint8_t* k_pool, const uint8_t* v_pool,
                                    const uint16_t* q, float softmax_scale, uint16_t* out,
                                    void* workspace, hipStream_t stream);
 
+// Sparse attention for a batch whose requests share their first prefix_blocks pages (sequence
+// 0's table entries): each shared (block, group) dequantized once for every row that selected
+// it, one partial per (row, group, slot) in the workspace, then a combine launch per row group
+// that attends the private blocks and merges. At most attn_shared_prefix_max_rows() rows.
+int attn_shared_prefix_max_rows();
+size_t attn_shared_prefix_workspace_bytes(int batch, int q_len);
+hipError_t launch_attention_shared_prefix(const uint8_t* k_pool, const uint8_t* v_pool,
+                                          int64_t num_pages, const int32_t* block_table,
+                                          const int32_t* ctx_lens, int batch, int max_blocks,
+                                          int q_len, const uint16_t* q, const int32_t* ids,
+                                          int prefix_blocks, float softmax_scale, uint16_t* out,
+                                          void* workspace, hipStream_t stream);
+
 }  // namespace msa

@@ -318,6 +318,36 @@ int msa_sparse_attn_decode(const msa_cache_t *cache, const msa_batch_t *batch, c
                            void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * Sparse attention for a batch whose requests share a prefix: every sequence's blocks
+ * 0..prefix_blocks-1 are the same pages, and sequence 0's block-table entries are the ones read
+ * for them ("vLLM day-0 support for MiniMax-M3.1-Flash", section "NVFP4 MSA kernel": a page of
+ * a shared prefix is dequantized once for up to 64 requests that share it). Each shared
+ * (block, KV group) that any row selected is loaded and dequantized once, for all the rows of
+ * the batch that selected it (one launch, a workgroup per shared block and group), and each
+ * row's own blocks are attended per row in a second launch that merges the two by log-sum-exp.
+ * Arguments, results and errors as msa_sparse_attn_decode (the same values within its
+ * floating-point tolerance; the shared blocks' partial outputs pass through fp16, normalized by
+ * their sums, as the selected V values themselves are), with:
+ *   prefix_blocks : shared blocks, 0..max_blocks (0: every block is attended per row).
+ *   workspace     : device scratch of at least msa_sparse_attn_shared_prefix_workspace_bytes
+ *                   (batch) bytes (4,224 per (row, group, slot)), 256-byte aligned; no fill
+ *                   needed (every partial read is written by the same call first); calls that
+ *                   share it must not overlap in time.
+ * Requirement (not checked: the lengths live in device memory): the shared blocks hold no query
+ * token, prefix_blocks * 128 <= T_b - q_len for every b, and a row's block ids are distinct (as
+ * msa_block_topk writes them). Otherwise the output is unspecified (no memory outside the
+ * arguments is touched).
+ * Errors: as msa_sparse_attn_decode; MSA_ERR_INVALID_ARG for prefix_blocks outside
+ * [0, max_blocks]; MSA_ERR_UNSUPPORTED for batch * q_len above 1,024 rows.
+ */
+size_t msa_sparse_attn_shared_prefix_workspace_bytes(const msa_batch_t *batch);
+int msa_sparse_attn_decode_shared_prefix(const msa_cache_t *cache, const msa_batch_t *batch,
+                                         const uint16_t *q, const int32_t *block_ids,
+                                         int32_t prefix_blocks, float softmax_scale,
+                                         uint16_t *out, void *workspace, size_t ws_bytes,
+                                         void *stream);
+
+/*
  * Selection and attention in one launch: the effect of msa_block_topk(block_scores, batch, topk,
  * block_ids) followed by msa_sparse_attn_decode(cache, batch, q, block_ids, softmax_scale, out,
  * workspace, ws_bytes), with the same results bit for bit (block_ids is written as well), but

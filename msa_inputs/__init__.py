@@ -27,6 +27,12 @@ one shared 128-d index-key head, 128-token blocks, top-16):
   4 ragged    B=6,  T log-uniform in [8K, 512K], never a multiple of 128, q=1; heavy-tailed
                                     index keys (Student-t 3 / sqrt 3), no planting
   5 prefill   B=2,  T=65,536 + 2,048, q=2,048; 15 planted prefix blocks per (sequence, group)
+  6 prefix    B=64 requests sharing a 32,768-token prefix (256 blocks: the same pages and the
+                                    same data in every sequence), each with a suffix of its own
+                                    of log-uniform length in [1K, 8K] tokens (never a multiple of
+                                    128), q=1; index queries (u + z)/sqrt(2) share a direction u
+                                    per group across the whole batch; 32 planted prefix blocks
+                                    per group, the same for every request, alpha ~ U[1.5, 3]
 Planting adds alpha * w[b, g] (w = the group's index-query direction) to every index key of a
 chosen block, in fp32, before quantization.
 """
@@ -129,6 +135,7 @@ class Workload:
     q_idx: torch.Tensor                # bf16 [batch*q][4][128]
     q: torch.Tensor                    # bf16 [batch*q][64][128]
     retries: Dict[int, int]
+    prefix_tokens: int = 0             # tokens 0..prefix_tokens-1: sequence 0's, in every sequence
 
     @property
     def max_blocks(self) -> int:
@@ -141,8 +148,17 @@ class Workload:
         return int(self.retries.get(b, 0))
 
     # --------------------------------------------------------------- bulk fp32 data
+    def _split_prefix(self, b: int, t0: int, t1: int, rows):
+        """Rows [t0, t1) of sequence b when part of them lies in the shared prefix: that part is
+        sequence 0's (the same data in every sequence), the rest the sequence's own."""
+        mid = min(t1, self.prefix_tokens)
+        head = rows(0, t0, mid)
+        return head if mid == t1 else torch.cat([head, rows(b, mid, t1)])
+
     def ik_rows(self, b: int, t0: int, t1: int, device="cpu") -> torch.Tensor:
         """fp32 index keys of sequence b, tokens [t0, t1): noise plus planted directions."""
+        if b != 0 and t0 < self.prefix_tokens:
+            return self._split_prefix(b, t0, t1, lambda bb, a, z: self.ik_rows(bb, a, z, device))
         key = stream_key(self.seed, TAG_IK, b, self.retry(b))
         x = draw(self.ik_kind, key, t0 * D, (t1 - t0) * D, device).view(t1 - t0, D)
         for g in range(KV_HEADS):
@@ -156,6 +172,8 @@ class Workload:
 
     def kv_rows(self, which: str, b: int, t0: int, t1: int, device="cpu") -> torch.Tensor:
         """fp32 K (which='k') or V (which='v') of sequence b, tokens [t0, t1): [n][4][128]."""
+        if b != 0 and t0 < self.prefix_tokens:
+            return self._split_prefix(b, t0, t1, lambda bb, a, z: self.kv_rows(which, bb, a, z, device))
         key = stream_key(self.seed, TAG_K if which == "k" else TAG_V, b)
         return draw("normal", key, t0 * KV_HEADS * D, (t1 - t0) * KV_HEADS * D,
                     device).view(t1 - t0, KV_HEADS, D)
@@ -184,25 +202,37 @@ CONFIGS = {
     3: dict(name="spec128k", batch=8, ctx=131072, q_len=4),
     4: dict(name="ragged", batch=6, ctx=None, q_len=1),
     5: dict(name="prefill", batch=2, ctx=65536 + 2048, q_len=2048),
+    6: dict(name="prefix", batch=64, ctx=None, q_len=1),
 }
+PREFIX_BLOCKS = 256  # config 6: the shared prefix
 
 
 def make_workload(cfg: int, batch: Optional[int] = None, ctx: Optional[int] = None,
                   q_len: Optional[int] = None, ctx_lens: Optional[List[int]] = None,
                   retries: Optional[Dict[int, int]] = None, seed: Optional[int] = None,
-                  n_plant: Optional[int] = None, spare_pages: int = 0) -> Workload:
-    """Build workload `cfg` (1..5) at its stated size, or a reduced variant of the same recipe.
+                  n_plant: Optional[int] = None, spare_pages: int = 0,
+                  prefix_blocks: Optional[int] = None) -> Workload:
+    """Build workload `cfg` (1..6) at its stated size, or a reduced variant of the same recipe.
 
     batch/ctx/q_len/ctx_lens override the sizes; `retries` maps a sequence to the retry counter
     that redraws its index-key noise and plant choices; `seed` defaults to the config number.
+    Config 6: `prefix_blocks` sets the shared prefix (default PREFIX_BLOCKS); explicit
+    `ctx_lens` must leave every sequence's query tokens past it.
     """
     spec = CONFIGS[cfg]
     seed = cfg if seed is None else seed
     B = spec["batch"] if batch is None else batch
     q = spec["q_len"] if q_len is None else q_len
     retries = dict(retries or {})
+    P = (PREFIX_BLOCKS if prefix_blocks is None else prefix_blocks) if cfg == 6 else 0
     if ctx_lens is None:
-        if cfg == 4 and ctx is None:
+        if cfg == 6:
+            rng = _host_rng(seed, TAG_LEN)
+            u = rng.random(B)
+            lens = [P * BLOCK + int(round(math.exp(math.log(1024) + x * (math.log(8192) - math.log(1024)))))
+                    for x in u]
+            ctx_lens = [t - 1 if t % BLOCK == 0 else t for t in lens]
+        elif cfg == 4 and ctx is None:
             rng = _host_rng(seed, TAG_LEN)
             u = rng.random(B)
             lens = [int(round(math.exp(math.log(8192) + x * (math.log(524288) - math.log(8192))))) for x in u]
@@ -211,24 +241,32 @@ def make_workload(cfg: int, batch: Optional[int] = None, ctx: Optional[int] = No
             ctx_lens = [spec["ctx"] if ctx is None else ctx] * B
     ctx_lens = [int(t) for t in ctx_lens]
     assert all(t >= q for t in ctx_lens), "every context must hold its query tokens"
+    assert all(t - q >= P * BLOCK for t in ctx_lens), "the shared prefix holds no query token"
     nbs = [(t + BLOCK - 1) // BLOCK for t in ctx_lens]
     max_blocks = max(nbs)
-    num_pages = sum(nbs) + spare_pages
+    num_pages = sum(nbs) - (B - 1) * P + spare_pages
     if cfg == 1:
         perm = np.arange(num_pages, dtype=np.int64)
     else:
         perm = _host_rng(seed, TAG_PERM).permutation(num_pages)
     table = np.full((B, max_blocks), -1, np.int32)
-    off = 0
+    table[:, :P] = perm[:P]  # config 6: every sequence's prefix blocks are the same pages
+    off = P
     for b, nb in enumerate(nbs):
-        table[b, :nb] = perm[off:off + nb]
-        off += nb
+        table[b, P:nb] = perm[off:off + nb - P]
+        off += nb - P
 
     # queries
     rows = B * q
     qk = stream_key(seed, TAG_Q)
     Q = _bf16(draw("normal", qk, 0, rows * Q_HEADS * D).view(rows, Q_HEADS, D))
-    if cfg in (3, 5):
+    if cfg == 6:
+        # one direction per group for the whole batch
+        u = draw("normal", stream_key(seed, TAG_U), 0, KV_HEADS * D).view(1, 1, KV_HEADS, D)
+        z = draw("normal", stream_key(seed, TAG_Z), 0, rows * KV_HEADS * D).view(B, q, KV_HEADS, D)
+        qi = _bf16(((u + z) * np.float32(1.0 / math.sqrt(2.0))).reshape(rows, KV_HEADS, D))
+        plant_dir = u.expand(B, 1, KV_HEADS, D).reshape(B, KV_HEADS, D).numpy().copy()
+    elif cfg in (3, 5):
         u = draw("normal", stream_key(seed, TAG_U), 0, B * KV_HEADS * D).view(B, 1, KV_HEADS, D)
         z = draw("normal", stream_key(seed, TAG_Z), 0, rows * KV_HEADS * D).view(B, q, KV_HEADS, D)
         qi = _bf16(((u + z) * np.float32(1.0 / math.sqrt(2.0))).reshape(rows, KV_HEADS, D))
@@ -239,7 +277,16 @@ def make_workload(cfg: int, batch: Optional[int] = None, ctx: Optional[int] = No
         plant_dir = qi.view(B, q, KV_HEADS, D)[:, 0].float().numpy().copy()
 
     plants: Dict[Tuple[int, int], List[Tuple[int, float]]] = {}
-    if cfg != 4:
+    if cfg == 6:
+        # planted prefix blocks, the same for every request (they live in the shared data)
+        count = 32 if n_plant is None else n_plant
+        for g in range(KV_HEADS):
+            blocks = _planted_blocks(_host_rng(seed, TAG_PLANT, 0, g, retries.get(0, 0)), P, count)
+            arng = _host_rng(seed, TAG_ALPHA, 0, g, retries.get(0, 0))
+            alphas = [float(np.float32(a)) for a in arng.uniform(1.5, 3.0, len(blocks))]
+            for b in range(B):
+                plants[(b, g)] = list(zip(blocks, alphas))
+    elif cfg != 4:
         count = {1: 16, 2: 16, 3: 16, 5: 15}[cfg] if n_plant is None else n_plant
         for b in range(B):
             r = retries.get(b, 0)
@@ -258,7 +305,7 @@ def make_workload(cfg: int, batch: Optional[int] = None, ctx: Optional[int] = No
                     num_pages=num_pages, block_table=table,
                     ik_kind="t3" if cfg == 4 else "normal", plants=plants,
                     plant_dir=plant_dir.astype(np.float32), q_idx=qi.contiguous(), q=Q.contiguous(),
-                    retries=retries)
+                    retries=retries, prefix_tokens=P * BLOCK)
 
 
 RETRIES_FILE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),

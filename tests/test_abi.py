@@ -153,6 +153,22 @@ def test_invalid_arguments_return_codes_without_launch(msa):
     assert L.msa_sparse_attn_decode(by(_cache()), small, None, 1, 0.1, 1, 256, need, None) == msa.MSA_ERR_INVALID_ARG
     # large batches need no workspace (one workgroup per row group covers the chip)
     assert L.msa_sparse_attn_workspace_bytes(by(_batch(b=256, q=1))) == 0
+    # attention over a shared prefix (args: cache batch q ids prefix scale out ws bytes stream)
+    spa = L.msa_sparse_attn_decode_shared_prefix
+    spn = L.msa_sparse_attn_shared_prefix_workspace_bytes(by(_batch(b=2, q=3, mb=8)))
+    assert spn == 2 * 3 * 4 * 16 * 4224
+    mb8q3 = by(_batch(b=2, q=3, mb=8))
+    for bad_prefix in (-1, 9):
+        assert spa(by(_cache()), mb8q3, 1, 1, bad_prefix, 0.1, 1, 256, spn, None) == msa.MSA_ERR_INVALID_ARG
+    assert spa(by(_cache()), mb8q3, None, 1, 2, 0.1, 1, 256, spn, None) == msa.MSA_ERR_INVALID_ARG
+    assert spa(by(_cache()), mb8q3, 1, None, 2, 0.1, 1, 256, spn, None) == msa.MSA_ERR_INVALID_ARG
+    assert spa(by(_cache()), mb8q3, 1, 1, 2, 0.1, None, 256, spn, None) == msa.MSA_ERR_INVALID_ARG
+    assert spa(by(_cache(v=None)), mb8q3, 1, 1, 2, 0.1, 1, 256, spn, None) == msa.MSA_ERR_INVALID_ARG
+    assert spa(by(_cache()), mb8q3, 1, 1, 2, 0.1, 1, None, 0, None) == msa.MSA_ERR_WORKSPACE
+    assert spa(by(_cache()), mb8q3, 1, 1, 2, 0.1, 1, 256, spn - 1, None) == msa.MSA_ERR_WORKSPACE
+    assert spa(by(_cache()), mb8q3, 1, 1, 2, 0.1, 1, 257, spn, None) == msa.MSA_ERR_WORKSPACE
+    big = by(_batch(b=257, q=4, mb=8))  # 1,028 rows
+    assert spa(by(_cache()), big, 1, 1, 2, 0.1, 1, 256, 1 << 40, None) == msa.MSA_ERR_UNSUPPORTED
     # selection + attention in one launch: the checks of both calls
     sel = L.msa_select_attn_decode
     assert sel(by(_cache()), small, 1, 8, 1, 1, 0.1, 1, 256, need, None) == msa.MSA_ERR_UNSUPPORTED

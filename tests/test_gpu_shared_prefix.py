@@ -72,3 +72,63 @@ def test_shared_prefix_indexer():
         qb = qi_bits[b * Q:(b + 1) * Q]
         ref = oracle.index_scores(qb, codes, scales, T[b], Q, max_blocks)
         check_scores(got[b * Q:(b + 1) * Q], ref, score_tolerance(qb, codes, scales))
+
+
+# ---------------------------------------------------------------- attention over a shared prefix
+def _prefix_case(q_len, batch, prefix_blocks, fill, seed):
+    import block_sparse_attention_nvfp4_amd as msa
+    import msa_inputs as mi
+    from msa_testlib import DeviceWorkload
+    w = mi.make_workload(6, batch=batch, q_len=q_len, prefix_blocks=prefix_blocks, seed=seed)
+    d = DeviceWorkload(w, fill=fill)
+    msa.msa_kv_insert_nvfp4(d.cache, d.new_slots, d.new_k, d.new_v, d.new_ik)
+    rows = batch * q_len
+    scores = torch.empty((rows, 4, w.max_blocks), dtype=torch.float32, device="cuda")
+    msa.msa_indexer_score(d.cache, d.batch, d.q_idx, scores)
+    ids = torch.empty((rows, 4, 16), dtype=torch.int32, device="cuda")
+    msa.msa_block_topk(scores, d.batch, 16, ids)
+    return w, d, scores, ids
+
+
+@pytest.mark.parametrize("q_len,batch,prefix_blocks,fill", [
+    (1, 12, 20, 0), (4, 6, 20, 0xFF), (1, 40, 9, 0xFF)])
+def test_shared_prefix_attention_against_oracle(q_len, batch, prefix_blocks, fill):
+    """Requests sharing a prefix (the seeded prefix workload at reduced size: every request's
+    first blocks are the same pages, its suffix its own); the attention that dequantizes each
+    selected shared block once for all rows that selected it, with the whole prefix shared, part
+    of it, and none, against the oracle over the GPU's own selection (which the same call checks
+    against the oracle's), and against the per-row attention within the same tolerance."""
+    import block_sparse_attention_nvfp4_amd as msa
+    import msa_inputs as mi
+    from msa_testlib import check_attention, check_step_against_oracle, oracle_sequence
+    w, d, scores, ids = _prefix_case(q_len, batch, prefix_blocks, fill, seed=60 + q_len)
+    rows = batch * q_len
+    scale = msa.default_softmax_scale()
+    ws = torch.empty(msa.msa_sparse_attn_shared_prefix_workspace_bytes(d.batch), dtype=torch.uint8,
+                     device="cuda")
+    outs = {}
+    for p in (prefix_blocks, prefix_blocks // 2 + 1, 0):
+        out = torch.full((rows, 64, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+        msa.msa_sparse_attn_decode_shared_prefix(d.cache, d.batch, d.q, ids, p, scale, out, ws)
+        outs[p] = out
+    plain = torch.empty((rows, 64, 128), dtype=torch.bfloat16, device="cuda")
+    need = msa.msa_sparse_attn_workspace_bytes(d.batch)
+    pws = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda")
+    msa.msa_sparse_attn_decode(d.cache, d.batch, d.q, ids, scale, plain, pws if need else None)
+    torch.cuda.synchronize()
+    ids_h = ids.cpu().numpy()
+    # the shared path is exercised: some shared block is selected by several rows of a group
+    sel = ids_h[(ids_h >= 0) & (ids_h < prefix_blocks)]
+    assert sel.size > 0
+    counts = [np.bincount(ids_h[:, g][(ids_h[:, g] >= 0) & (ids_h[:, g] < prefix_blocks)],
+                          minlength=prefix_blocks) for g in range(4)]
+    assert max(c.max() for c in counts) >= 2
+    s_h = scores.cpu().numpy()
+    check_step_against_oracle(w, s_h, ids_h, outs[prefix_blocks].float().cpu().numpy())
+    got = {p: o.float().cpu().numpy().astype(np.float64) for p, o in outs.items()}
+    got["plain"] = plain.float().cpu().numpy().astype(np.float64)
+    for b in range(batch):
+        r = slice(b * q_len, (b + 1) * q_len)
+        ref = oracle_sequence(w, b, attention_tokens=list(range(q_len)), ids_override=ids_h[r])
+        for key, g in got.items():
+            check_attention(g[r], ref["attention"])

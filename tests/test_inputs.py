@@ -69,3 +69,30 @@ def test_retry_redraws_only_that_sequence():
     assert torch.equal(a.ik_rows(0, 0, 256), b.ik_rows(0, 0, 256))
     assert not torch.equal(a.ik_rows(1, 0, 256), b.ik_rows(1, 0, 256))
     assert a.plants[(0, 1)] == b.plants[(0, 1)]
+
+
+def test_prefix_workload_shares_pages_and_data():
+    """The prefix-sharing workload: every request's first blocks are the same pages holding the
+    same data, the suffixes are the requests' own (own pages, own data), the query tokens lie
+    past the prefix, the planted blocks and the index-query direction are the batch's."""
+    w = mi.make_workload(6, batch=5, prefix_blocks=7)
+    P = 7
+    assert w.prefix_tokens == P * 128
+    assert (w.block_table[:, :P] == w.block_table[0, :P]).all()
+    own = [set(w.block_table[b, P:w.n_blocks(b)].tolist()) for b in range(w.batch)]
+    assert all(-1 not in s for s in own)
+    for a in range(w.batch):
+        assert not own[a] & set(w.block_table[0, :P].tolist())
+        for b in range(a + 1, w.batch):
+            assert not own[a] & own[b]
+    used = w.block_table[w.block_table >= 0]
+    assert len(np.unique(used)) == w.num_pages
+    for b in range(1, w.batch):
+        assert torch.equal(w.ik_rows(b, 0, P * 128), w.ik_rows(0, 0, P * 128))
+        assert torch.equal(w.kv_rows("v", b, 100, P * 128 + 50)[: P * 128 - 100],
+                           w.kv_rows("v", 0, 100, P * 128))
+        assert not torch.equal(w.ik_rows(b, P * 128, P * 128 + 64), w.ik_rows(0, P * 128, P * 128 + 64))
+        assert w.plants[(b, 2)] == w.plants[(0, 2)]
+        assert all(blk < P for blk, _ in w.plants[(b, 2)])
+    assert all(T - w.q_len >= P * 128 and T % 128 != 0 for T in w.ctx_lens)
+    assert np.array_equal(w.plant_dir[0], w.plant_dir[3])
