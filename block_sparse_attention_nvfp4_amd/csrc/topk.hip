@@ -7,15 +7,17 @@
 // counted twice; section "Decode indexer score kernel": the top-k boundary stays close to the
 // scores. Ties go to the lower block index.
 //
-// Rows of up to 4,096 candidate blocks: one 64-lane wavefront per row, no atomics. The row's
-// scores become order-preserving integer keys in registers (candidate i in lane i % 64). The
-// 15th-largest of the 64 per-lane maxima, found by a bitwise search with ballot counts (two bits
-// per step), is a lower bound of the 15th-largest key (at least 15 keys reach it), so the
-// selection lies among the keys at or above it. Those few candidates are compacted into LDS in
-// ascending block order as (key, inverted block index) composites and each is ranked exactly
-// against the others by reading them back as LDS broadcasts; the 15 best, already in ascending
-// block order, are written with the forced block last. When more than 64 candidates reach the
-// bound (heavy ties), the wavefront extracts the 15 best one by one instead.
+// Rows of up to 4,096 candidate blocks: one 64-lane wavefront per row, no atomics, the
+// selection of select_wave.hpp. The row's scores become order-preserving integer keys in
+// registers (candidate i in lane i % 64). The 15th-largest of the 64 per-lane maxima is a lower
+// bound of the 15th-largest key (at least 15 keys reach it), so the selection lies among the
+// keys at or above it; it is found by ranks, not by a search: each lane counts the maxima above
+// its own (all 64 read back from LDS as broadcasts), and the bound is the smallest maximum that
+// fewer than 15 others exceed. Those few candidates are compacted into LDS in ascending block
+// order as (key, inverted block index) composites and each is ranked exactly against the others
+// by reading them back as LDS broadcasts; the 15 best, already in ascending block order, are
+// written with the forced block last. When more than 64 candidates reach the bound (heavy
+// ties), the wavefront extracts the 15 best one by one instead.
 // Longer rows: one 256-thread workgroup per row with a 4-pass radix select (8-bit digits, LDS
 // histograms) on the keys, then keys above the found key are kept and keys equal to it are taken
 // in ascending block order.

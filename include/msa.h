@@ -110,7 +110,9 @@ typedef struct {
 /*
  * A decode batch.
  *   block_table : device int32 [batch][max_blocks]; entry (b, i) = page id of logical block i
- *                 of sequence b (entries past the sequence are never read; use -1).
+ *                 of sequence b. The whole row, max_blocks entries, must be allocated: entries
+ *                 past the sequence may be read (and are then ignored); -1 marks an absent
+ *                 page, and so does any id outside [0, num_pages).
  *   ctx_lens    : device int32 [batch]; T_b (tokens in the cache, query tokens included).
  *   q_len       : query tokens per sequence, uniform across the batch (1 for plain decode,
  *                 the draft length for speculative verify, the chunk length for prefill).
@@ -310,7 +312,12 @@ size_t msa_sparse_attn_workspace_bytes(const msa_batch_t *batch);
  *               counters at its start), so one zero fill at allocation serves all later calls.
  *               It holds the split partial results that the workgroups of one call hand to each
  *               other; calls that share a workspace must not overlap in time (same stream, or
- *               ordered).
+ *               ordered). A call that did not run to completion (a launch error reported after
+ *               some of its workgroups ran, a stream torn down mid-call) or two calls that
+ *               overlapped can leave counters non-zero; later calls then merge at the wrong
+ *               moment and their outputs are unspecified (never a fault: every access stays in
+ *               the workspace, and nothing waits on a counter). Zero-fill the workspace again
+ *               before reusing it after such an event.
  * Errors: MSA_ERR_INVALID_ARG (NULL pointers, sizes < 1), MSA_ERR_WORKSPACE.
  */
 int msa_sparse_attn_decode(const msa_cache_t *cache, const msa_batch_t *batch, const uint16_t *q,

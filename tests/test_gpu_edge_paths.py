@@ -148,3 +148,39 @@ def test_unwritten_bytes_past_the_context_are_ignored(name, mode):
     assert not np.isnan(scores).any(), (name, mode, "NaN scores")
     check_step_against_oracle(w, scores, g.step.block_ids.cpu().numpy(), bf16_to_f64(out))
     _log(f"[fill {name} {mode}] ok")
+
+
+@pytest.mark.parametrize("batch,q_len", [(2, 4), (16, 4)], ids=["per_token_splits", "union"])
+def test_workspace_recovers_after_counters_were_left_set(batch, q_len):
+    """A workspace whose split counters were left non-zero (as an interrupted call would leave
+    them) gives unspecified outputs but no fault; zero-filling it again, as the header says,
+    restores the exact results (per-token kernel with four splits, and the union kernel)."""
+    import block_sparse_attention_nvfp4_amd as msa
+    _log(f"workspace recovery batch={batch} q={q_len}")
+    w = mi.make_workload(3, batch=batch, ctx=2600, q_len=q_len, seed=91)
+    d = DeviceWorkload(w)
+    msa.msa_kv_insert_nvfp4(d.cache, d.new_slots, d.new_k, d.new_v, d.new_ik)
+    rows = batch * q_len
+    scores = torch.empty((rows, 4, w.max_blocks), dtype=torch.float32, device="cuda")
+    msa.msa_indexer_score(d.cache, d.batch, d.q_idx, scores)
+    ids = torch.empty((rows, 4, 16), dtype=torch.int32, device="cuda")
+    msa.msa_block_topk(scores, d.batch, 16, ids)
+    need = msa.msa_sparse_attn_workspace_bytes(d.batch)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    scale = msa.default_softmax_scale()
+    ref = torch.empty((rows, 64, 128), dtype=torch.bfloat16, device="cuda")
+    msa.msa_sparse_attn_decode(d.cache, d.batch, d.q, ids, scale, ref, ws)
+    again = torch.empty_like(ref)
+    msa.msa_sparse_attn_decode(d.cache, d.batch, d.q, ids, scale, again, ws)  # left zeroed
+    ws.fill_(1)  # every counter (and partial) byte set: 0x01010101 per counter
+    junk = torch.zeros_like(ref)
+    msa.msa_sparse_attn_decode(d.cache, d.batch, d.q, ids, scale, junk, ws)
+    torch.cuda.synchronize()
+    ws.zero_()
+    fixed = torch.empty_like(ref)
+    msa.msa_sparse_attn_decode(d.cache, d.batch, d.q, ids, scale, fixed, ws)
+    torch.cuda.synchronize()
+    r = ref.view(torch.int16).cpu().numpy()
+    assert np.array_equal(again.view(torch.int16).cpu().numpy(), r)
+    assert np.array_equal(fixed.view(torch.int16).cpu().numpy(), r)
