@@ -184,3 +184,40 @@ def test_workspace_recovers_after_counters_were_left_set(batch, q_len):
     r = ref.view(torch.int16).cpu().numpy()
     assert np.array_equal(again.view(torch.int16).cpu().numpy(), r)
     assert np.array_equal(fixed.view(torch.int16).cpu().numpy(), r)
+
+
+@pytest.mark.parametrize("init_blocks,local_blocks", [(2, 2), (0, 3), (4, 1)])
+def test_window_selection_drives_the_attention(init_blocks, local_blocks):
+    """The selection knobs end to end at 16 blocks per row: msa_block_topk_window's ids (bit for
+    bit those of oracle.block_topk_variant on the same scores) feed msa_sparse_attn_decode, whose
+    outputs match the oracle's attention over those ids."""
+    import block_sparse_attention_nvfp4_amd as msa
+    from msa_testlib import check_attention, oracle_sequence
+    _log(f"window selection init={init_blocks} local={local_blocks}")
+    w = mi.make_workload(3, batch=3, ctx_lens=[5000, 128 * 23 + 7, 2100], q_len=4, seed=17)
+    d = DeviceWorkload(w)
+    msa.msa_kv_insert_nvfp4(d.cache, d.new_slots, d.new_k, d.new_v, d.new_ik)
+    rows = w.batch * w.q_len
+    scores = torch.empty((rows, 4, w.max_blocks), dtype=torch.float32, device="cuda")
+    msa.msa_indexer_score(d.cache, d.batch, d.q_idx, scores)
+    ids = torch.full((rows, 4, 16), -7, dtype=torch.int32, device="cuda")
+    msa.msa_block_topk_window(scores, d.batch, 16, init_blocks, local_blocks, ids)
+    ws_bytes = msa.msa_sparse_attn_workspace_bytes(d.batch)
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty((rows, 64, 128), dtype=torch.bfloat16, device="cuda")
+    msa.msa_sparse_attn_decode(d.cache, d.batch, d.q, ids, msa.default_softmax_scale(), out,
+                               ws if ws_bytes else None)
+    torch.cuda.synchronize()
+    s_h, ids_h = scores.cpu().numpy(), ids.cpu().numpy()
+    got = bf16_to_f64(out)
+    for b in range(w.batch):
+        T = w.ctx_lens[b]
+        for j in range(w.q_len):
+            r = b * w.q_len + j
+            n = (T - w.q_len + j) // 128 + 1
+            for g in range(4):
+                want = oracle.block_topk_variant(s_h[r, g], n, 16, init_blocks, local_blocks)
+                assert list(ids_h[r, g]) == list(want), (r, g)
+        rr = slice(b * w.q_len, (b + 1) * w.q_len)
+        ref = oracle_sequence(w, b, attention_tokens=list(range(w.q_len)), ids_override=ids_h[rr])
+        check_attention(got[rr], ref["attention"])
