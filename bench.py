@@ -47,8 +47,8 @@ METRIC = "MSA decode query-tokens/s per layer at 128K ctx; achieved HBM GB/s vs 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=8000)
+    ap.add_argument("--warmup", type=int, default=80)
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--kernel-reps", type=int, default=20, help="graph replays per kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -193,16 +193,15 @@ __device__ __forceinline__ void softmax_block(f32x4 (&sv)[8], int c, int tok0, i
         for (int dt = 0; dt < 8; dt++) o[dt] *= alpha;
         m_run = m_new;
     }
-    float ls = 0.f;
 #pragma unroll
     for (int s = 0; s < 8; s++)
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const float e = fast_exp2(fmaf(sv[s][i], logit_scale, -m_new));
-            ls += e;
             pt[s >> 1][4 * (s & 1) + i] = (_Float16)e;
         }
-    l_run += sum_over_c(ls);
+    // (the block's sum of these probabilities is added to l_run by the caller, on the matrix
+    // cores, from the same fp16 values the output uses)
 }
 
 // One block of one wavefront: logits, online-softmax update, output accumulation. The K page
@@ -267,17 +266,14 @@ __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c
         for (int dt = 0; dt < 8; dt++) o[dt] *= alpha;
         m_run = m_new;
     }
-    float ls = 0.f;
     f16x4 pt[8];
 #pragma unroll
     for (int s = 0; s < 8; s++)
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const float e = fast_exp2(fmaf(sv[s][i], logit_scale, -m_new));
-            ls += e;
             pt[s][i] = (_Float16)e;
         }
-    l_run += sum_over_c(ls);
 
     // ---- the V page's 9 loads (issued after the K page's 9) complete here
     if constexpr (NEXT) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
@@ -338,6 +334,18 @@ __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c
             o[dt] = mfma_f16_k32(a, pp, o[dt]);
         }
     }
+    // each head's sum of the block's probabilities on the matrix cores (an all-ones A operand),
+    // from the same fp16 values the output uses
+    const f16x8 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f,
+                        (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
+    f32x4 ls = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int h = 0; h < 4; h++) {
+        const f16x8 pp = {pt[2 * h][0], pt[2 * h][1], pt[2 * h][2], pt[2 * h][3],
+                          pt[2 * h + 1][0], pt[2 * h + 1][1], pt[2 * h + 1][2], pt[2 * h + 1][3]};
+        ls = mfma_f16_k32(ones, pp, ls);
+    }
+    l_run += ls[0];
 }
 
 // SELECT: the row's blocks are selected here from its block scores (wavefront 0 of every
@@ -748,6 +756,18 @@ __device__ __forceinline__ void attend_tables(const uint8_t* kf, const uint8_t* 
 #pragma unroll
             for (int h = 0; h < 4; h++)
                 o[t][dt] = mfma_f16_k32(__builtin_bit_cast(f16x8, a[h]), pt[t][h], o[t][dt]);
+    }
+    // each head's sum of the block's probabilities: a matrix-core step with an all-ones A
+    // operand (every row m of D gets the sum over the tokens of head n), which spares the
+    // vector unit 32 additions and a cross-lane sum per token and block
+    const f16x8 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f,
+                        (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+    for (int t = 0; t < TPW; t++) {
+        f32x4 ls = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int h = 0; h < 4; h++) ls = mfma_f16_k32(ones, pt[t][h], ls);
+        l_run[t] += ls[0];
     }
 }
 
