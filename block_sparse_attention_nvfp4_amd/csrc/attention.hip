@@ -375,14 +375,32 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15;
     const int c = lane >> 4;
-    // XCD-aware work mapping: pair = (b, g) -> XCD pair % 8
+    // XCD-aware work mapping: pair = (b, g) -> XCD pair % 8. With an even number of query
+    // tokens, drafts 2i and 2i + 1 of one (pair, split) take the XCD's workgroups L and
+    // L + NL / 2 (NL workgroups per XCD): when the grid holds two workgroups per compute unit,
+    // the dispatcher places those two on one compute unit, and the pages of two drafts mostly
+    // coincide (measured 0.15-0.35 us faster at 8 sequences x 4 drafts; any mapping gives the
+    // same results)
     const int per_pair = q_len * n_split;
     const int local = blockIdx.x >> 3;
-    const int pair = (local / per_pair) * 8 + (blockIdx.x & 7);
+    int pair, j, split;
+    if ((q_len & 1) == 0) {
+        const int half = (int)(gridDim.x >> 4);  // NL / 2
+        const int hi = local >= half ? 1 : 0;
+        const int r = local - hi * half;
+        const int pp = per_pair >> 1;
+        pair = (r / pp) * 8 + (blockIdx.x & 7);
+        const int within = r - (r / pp) * pp;
+        const int jl = within / n_split;
+        split = within - jl * n_split;
+        j = 2 * jl + hi;
+    } else {
+        pair = (local / per_pair) * 8 + (blockIdx.x & 7);
+        const int within = local - (local / per_pair) * per_pair;
+        j = within / n_split;
+        split = within - j * n_split;
+    }
     if (pair >= batch * kKvHeads) return;
-    const int within = local - (local / per_pair) * per_pair;
-    const int j = within / n_split;
-    const int split = within - j * n_split;
     const int b = pair >> 2;
     const int g = pair & 3;
     const int bq = b * q_len + j;
