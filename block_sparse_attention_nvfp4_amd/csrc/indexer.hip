@@ -352,6 +352,31 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
     const int n_blocks = nb_ctx > gb ? min(max_blocks, (nb_ctx - gb + gs - 1) / gs) : 0;
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     pid_all = (wg_blk0 + lane < n_blocks && pid_all >= 0 && pid_all < num_pages) ? pid_all : -1;
+    if (wg_blk0 >= n_blocks) {
+        // no block of this workgroup holds a key of the context (a short sequence in a batch
+        // sized for a longer one): every score of its blocks is -inf, and the workgroup ends
+        // after its insert items, freeing its compute unit a memory round trip sooner
+        const int rows_all = 4 * q_len;
+        for (int i = threadIdx.x; i < rows_all * kPagesPerWg; i += kWaves * 64) {
+            const int rn = i / kPagesPerWg, kb = i - rn * kPagesPerWg;
+            if (wg_blk0 + kb < wg_end)
+                scores[((int64_t)b * rows_all + rn) * max_blocks + wg_blk0 + kb] = -INFINITY;
+        }
+        if constexpr (FUSED) {
+            for (bool first = true; item < n_items; item += kWaves * gx, first = false) {
+                const f32x2 x = first ? ins_x
+                                      : *reinterpret_cast<const f32x2*>(
+                                            item_source(item, b, q_len, new_k, new_v, new_ik) + 2 * lane);
+                const int pos = T - q_len + item / 9;
+                const int64_t page = pos >= 0 ? table[pos >> 7] : -1;
+                uint32_t byte, scale;
+                quantize_pair(x[0], x[1], byte, scale);
+                store_item(item, page, pos, num_pages, byte, scale, k_pool_w, v_pool_w,
+                           const_cast<uint8_t*>(ik_pool), lane);
+            }
+        }
+        return;
+    }
     // the first insert item's position and block-table entry (set after the first page of the
     // first row tile is requested)
     int ins_pos = -1;
