@@ -349,9 +349,10 @@ __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c
 }
 
 // SELECT: the row's blocks are selected here from its block scores (wavefront 0 of every
-// workgroup of the row; the first split also writes them to block_ids) instead of being read
+// workgroup of the row, or with LONG, rows of up to kSelectLongMaxBlocks blocks, all four
+// wavefronts; the first split also writes them to block_ids) instead of being read
 // from block_ids.
-template <int BPW, bool SELECT>
+template <int BPW, bool SELECT, bool LONG = false>
 __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
     const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool, int64_t num_pages,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens, int batch,
@@ -367,7 +368,9 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
     __shared__ float sh_l[kWaves][kGroupHeads];
     __shared__ int sh_sel[SELECT ? kTopk : 1];
     static_assert(kSelectScratch * 8 <= kBlockBytes, "selection scratch must fit in a page buffer");
-    __shared__ int sh_tbl[SELECT ? kSelectFusedMaxBlocks : 1];  // the sequence's block table
+    __shared__ int sh_tbl[SELECT ? (LONG ? kSelectLongMaxBlocks : kSelectFusedMaxBlocks) : 1];  // the sequence's block table
+    __shared__ int sh_lid[LONG ? kWaves : 1][kTopk];
+    __shared__ uint32_t sh_lkey[LONG ? kWaves : 1][kTopk];
 
     const int lane = threadIdx.x & 63;
     // wavefront-uniform (a scalar value): the per-wavefront roles below are scalar branches, so
@@ -421,7 +424,75 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
     // load issued between page loads would make the in-order memory counter wait for every
     // page in flight.
     int id;
-    if constexpr (SELECT) {
+    if constexpr (SELECT && LONG) {
+        // rows of up to kSelectLongMaxBlocks blocks: every wavefront selects the best 15 of a
+        // quarter of the row (blocks 1024 wave + lane + 64 k) and copies a quarter of the
+        // block-table row; wavefront 0 then ranks the 60 candidates exactly (the top 15 of the
+        // row lie among the best 15 of their quarters)
+        constexpr int kThr = kWaves * 64;
+        constexpr int kPer = (kSelectLongMaxBlocks + kThr - 1) / kThr;
+        const int32_t* trow = block_table + (int64_t)b * max_blocks;
+        const float* srow = scores + (int64_t)rg * max_blocks;
+        float sv[16];
+#pragma unroll
+        for (int k = 0; k < 16; k++) sv[k] = srow[min(1024 * wave + lane + 64 * k, max_blocks - 1)];
+        int tv[kPer];
+#pragma unroll
+        for (int r = 0; r < kPer; r++) tv[r] = trow[min((int)threadIdx.x + r * kThr, max_blocks - 1)];
+        int t_sel = T_raw;
+        asm volatile("" : "+v"(t_sel));
+#pragma unroll
+        for (int r = 0; r < kPer; r++) sh_tbl[min((int)threadIdx.x + r * kThr, max_blocks - 1)] = tv[r];
+        const int n_el = eligible_blocks(clamp_ctx(t_sel, max_blocks) - q_len + j, max_blocks);
+        if (n_el > kTopk) {
+            const int m = n_el - 1;  // candidates 0..m-1 compete for 15 places
+            uint32_t key[16];
+#pragma unroll
+            for (int k = 0; k < 16; k++) {
+                const int i = 1024 * wave + lane + 64 * k;
+                key[k] = i < m ? order_key(sv[k]) : 0u;
+            }
+            const int base = 1024 * wave;
+            select_top<16>(key, lane, reinterpret_cast<uint64_t*>(&lds[wave][0][0]), sh_lid[wave],
+                           sh_lkey[wave], [base](int i) { return base + i; }, kTopk - 1);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            if (n_el > kTopk) {
+                // the 60 candidates in ascending block order (list w holds quarter w's blocks,
+                // ascending), each ranked against the others read back as LDS broadcasts
+                constexpr int kCand = kWaves * (kTopk - 1);
+                uint64_t* cand = reinterpret_cast<uint64_t*>(&lds[0][0][0]);
+                const int li = lane < kCand ? lane : 0;
+                const uint32_t ky = lane < kCand ? sh_lkey[li / (kTopk - 1)][li % (kTopk - 1)] : 0u;
+                const int cid = sh_lid[li / (kTopk - 1)][li % (kTopk - 1)];
+                const uint64_t mine = ky ? (((uint64_t)ky << 32) | (uint32_t)~(uint32_t)lane) : 0ull;
+                cand[lane] = mine;
+                __builtin_amdgcn_wave_barrier();
+                asm volatile("" ::: "memory");
+                int rank = 0;
+#pragma unroll
+                for (int t0 = 0; t0 < 64; t0 += 8) {
+                    uint64_t o[8];
+#pragma unroll
+                    for (int i = 0; i < 8; i++) o[i] = cand[t0 + i];
+#pragma unroll
+                    for (int i = 0; i < 8; i++) rank += (int)(o[i] > mine);
+                }
+                const bool sel = ky != 0u && rank < kTopk - 1;
+                const uint64_t smask = __ballot(sel);
+                if (sel) sh_sel[lanes_before(smask)] = cid;
+                const int n_sel = popc64(smask);
+                if (lane >= n_sel && lane < kTopk - 1) sh_sel[lane] = -1;
+                if (lane == 0) sh_sel[kTopk - 1] = n_el - 1;  // the forced block, the largest id
+            } else if (lane < kTopk) {
+                sh_sel[lane] = lane < n_el ? lane : -1;
+            }
+        }
+        __syncthreads();
+        if (split == 0 && wave == 0 && lane < kTopk) block_ids[(int64_t)rg * kTopk + lane] = sh_sel[lane];
+        id = lane < BPW ? sh_sel[(split * kWaves + wave) * BPW + lane] : -1;
+    } else if constexpr (SELECT) {
         if (wave == 0) {
             // the row's scores and the context length in one memory round trip, then the
             // selection, exactly as msa_block_topk makes it
@@ -1399,6 +1470,28 @@ hipError_t launch_attention_t(const uint8_t* k_pool, const uint8_t* v_pool, int6
     return hipGetLastError();
 }
 
+// Rows of kSelectFusedMaxBlocks + 1 .. kSelectLongMaxBlocks blocks with four splits (the
+// per-token kernel with one block per wavefront): the selection in the attention launch, shared
+// by the workgroup's four wavefronts.
+hipError_t launch_attention_long_select(const uint8_t* k_pool, const uint8_t* v_pool,
+                                        int64_t num_pages, const int32_t* block_table,
+                                        const int32_t* ctx_lens, int batch, int max_blocks,
+                                        int q_len, const uint16_t* q, int32_t* ids,
+                                        const float* scores, float softmax_scale, uint16_t* out,
+                                        void* workspace, hipStream_t stream) {
+    const int pairs = batch * kKvHeads;
+    const int pair_slots = 8 * ((pairs + 7) / 8);
+    const float scale_log2 = softmax_scale * 1.4426950408889634f;
+    int32_t* counters = static_cast<int32_t*>(workspace);
+    float* partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                               attn_counter_bytes(batch, q_len));
+    hipLaunchKernelGGL((attention_kernel<1, true, true>), dim3(pair_slots * q_len * kMaxSplits),
+                       dim3(kWaves * 64), 0, stream, k_pool, v_pool, num_pages, block_table,
+                       ctx_lens, batch, max_blocks, q_len, q, ids, scores, scale_log2, out,
+                       counters, partials);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_attention(const uint8_t* k_pool, const uint8_t* v_pool, int64_t num_pages,
@@ -1416,8 +1509,13 @@ hipError_t launch_select_attention(const uint8_t* k_pool, const uint8_t* v_pool,
                                    int max_blocks, int q_len, const float* scores, int32_t* ids,
                                    const uint16_t* q, float softmax_scale, uint16_t* out,
                                    void* workspace, hipStream_t stream) {
+    if (max_blocks > kSelectFusedMaxBlocks && max_blocks <= kSelectLongMaxBlocks &&
+        attn_num_splits(batch, q_len) == kMaxSplits && !use_union(batch, q_len, max_blocks, false))
+        return launch_attention_long_select(k_pool, v_pool, num_pages, block_table, ctx_lens, batch,
+                                            max_blocks, q_len, q, ids, scores, softmax_scale, out,
+                                            workspace, stream);
     if (max_blocks > kSelectFusedMaxBlocks) {
-        // long rows: the selection kernel for them, then the attention reading its ids
+        // longer rows: the selection kernel for them, then the attention reading its ids
         const hipError_t err = launch_topk(scores, ctx_lens, batch, max_blocks, q_len, ids, stream);
         if (err != hipSuccess) return err;
         return launch_attention(k_pool, v_pool, num_pages, block_table, ctx_lens, batch,

@@ -114,6 +114,9 @@ hipError_t launch_attention_union(const uint8_t* k_pool, const uint8_t* v_pool, 
 // Selection fused into the attention (one launch): rows of up to this many blocks, whose
 // selection one wavefront holds in 16 keys per lane; longer rows launch the two kernels.
 constexpr int kSelectFusedMaxBlocks = 64 * 16 + 1;
+// Rows of up to this many blocks keep the selection in the attention launch with its four
+// wavefronts sharing it (one quarter of the row each); longer rows launch the two kernels.
+constexpr int kSelectLongMaxBlocks = 4 * 64 * 16 + 1;
 hipError_t launch_select_attention(const uint8_t* k_pool, const uint8_t* v_pool, int64_t num_pages,
                                    const int32_t* block_table, const int32_t* ctx_lens, int batch,
                                    int max_blocks, int q_len, const float* scores, int32_t* ids,

@@ -361,10 +361,13 @@ int msa_sparse_attn_decode_shared_prefix(const msa_cache_t *cache, const msa_bat
  * each attention workgroup selects its row's blocks itself from the scores, so the selection
  * needs no launch of its own and its ids no round trip through memory ("MiniMax M3 on vLLM",
  * section "Decode indexer score kernel": the top-k boundary stays close to the scores). Rows of
- * more than 1,025 blocks (max_blocks > 1025) run the two steps as two launches, and so do
- * batches of 8 or more query tokens per sequence with at least 1,024 (token, group) rows
- * (prefill chunks), whose attention streams the union of 16 tokens' blocks once per
- * workgroup instead of once per token.
+ * 1,026 to 4,097 blocks keep one launch when the batch has fewer than 128 query tokens in all
+ * and does not take the speculative-verify kernel (the four wavefronts of a workgroup then
+ * share the selection, a quarter of the row each); longer rows, and those other batches with
+ * max_blocks > 1025, run the two steps as two launches, and so do batches of 8 or more query
+ * tokens per sequence with at least 1,024 (token, group) rows (prefill chunks), whose
+ * attention streams the union of 16 tokens' blocks once per workgroup instead of once per
+ * token.
  * Arguments and workspace as for the two calls. Errors: as for the two calls.
  */
 int msa_select_attn_decode(const msa_cache_t *cache, const msa_batch_t *batch,

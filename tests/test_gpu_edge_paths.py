@@ -9,7 +9,10 @@
 2. Selection rows of more than 4,097 blocks (contexts past 524,416 tokens, up to the 1M-token
    contexts of "MiniMax M3 on vLLM"): the workgroup radix select, both with the keys held in
    registers (up to 4,096 candidates) and re-read from memory, on constructed tie, signed-zero
-   and -inf rows, bit for bit against the oracle.
+   and -inf rows, bit for bit against the oracle. Rows of 1,026 to 4,097 blocks in the fused
+   selection + attention call, whose four wavefronts share the selection (a quarter of the row
+   each, then a rank among their 60 candidates): ids bit for bit against the oracle and
+   msa_block_topk, output bit for bit against msa_sparse_attn_decode on those ids.
 3. Pools whose bytes past every context length are 0xFF (E4M3 NaN scales): the attention must
    ignore them (a zero probability times a NaN value would still be NaN), as must the indexer.
 """
@@ -119,6 +122,51 @@ def test_radix_selection_of_long_rows(max_blocks):
                 want, _ = oracle.block_topk(scores[i, g].astype(np.float64), n)
                 assert np.array_equal(got[i, g], want), (path, max_blocks, n, g, got[i, g], want)
     assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.parametrize("max_blocks", [1026, 2500, 4097])
+def test_fused_selection_of_rows_up_to_4097_blocks(max_blocks):
+    import block_sparse_attention_nvfp4_amd as msa
+    rng = np.random.default_rng(11 + max_blocks)
+    pats = _patterns(max_blocks, rng)
+    # eligible counts on both sides of 1,025 (one wavefront's selection) and of each quarter
+    n_list = [16, 17, 1024, 1025, 1026, 1100, 2048, 2049, 4096, 4097]
+    n_list = sorted(set(n for n in n_list if n <= max_blocks))
+    assert len(n_list) * 4 < 512  # four splits: the path under test
+    rows = [pats[(i * 4 + g) % len(pats)] for i in range(len(n_list)) for g in range(4)]
+    scores = np.stack(rows).reshape(len(n_list), 4, max_blocks).astype(np.float32)
+    ctx = torch.tensor([128 * (n - 1) + 1 for n in n_list], dtype=torch.int32, device="cuda")
+    # four pages of seeded NVFP4 data, block i of every sequence on page i % 4
+    pages = 4
+    cache = msa.Cache.allocate(pages)
+    g = torch.Generator().manual_seed(5 + max_blocks)
+    slots = torch.arange(pages * 128, dtype=torch.int64, device="cuda")
+    kv = lambda: torch.randn((pages * 128, 4, 128), generator=g).cuda()
+    msa.msa_kv_insert_nvfp4(cache, slots, kv(), kv(), torch.randn((pages * 128, 128), generator=g).cuda())
+    table = (torch.arange(max_blocks, dtype=torch.int32, device="cuda") % pages).repeat(len(n_list), 1)
+    b = msa.Batch(table.contiguous(), ctx, 1)
+    s_dev = torch.from_numpy(scores).cuda()
+    q = torch.randn((len(n_list), 64, 128), generator=g).to(torch.bfloat16).cuda()
+    ids = torch.full((len(n_list), 4, 16), -7, dtype=torch.int32, device="cuda")
+    ids2 = torch.full_like(ids, -7)
+    out = torch.empty_like(q)
+    out2 = torch.empty_like(q)
+    ws_bytes = msa.msa_sparse_attn_workspace_bytes(b)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    _log(f"[fused long {max_blocks}] msa_block_topk + msa_sparse_attn_decode")
+    msa.msa_block_topk(s_dev, b, 16, ids)
+    msa.msa_sparse_attn_decode(cache, b, q, ids, 0.088, out, ws)
+    _log(f"[fused long {max_blocks}] msa_select_attn_decode")
+    msa.msa_select_attn_decode(cache, b, s_dev, 16, ids2, q, 0.088, out2, ws)
+    torch.cuda.synchronize()
+    got, got2 = ids.cpu().numpy(), ids2.cpu().numpy()
+    for i, n in enumerate(n_list):
+        for gr in range(4):
+            want, _ = oracle.block_topk(scores[i, gr].astype(np.float64), n)
+            assert np.array_equal(got[i, gr], want), ("topk", max_blocks, n, gr)
+            assert np.array_equal(got2[i, gr], want), ("fused", max_blocks, n, gr, got2[i, gr], want)
+    assert torch.isfinite(out.float()).all()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
 
 
 FILL_CASES = {
