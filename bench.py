@@ -227,7 +227,8 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the MSA decode path "
-              "here is single-GPU; sharding the indexer by pages is not built.", file=sys.stderr)
+              "here runs on a single device (its indexer shards run on one GPU; the exchange "
+              "between devices is not implemented).", file=sys.stderr)
         sys.exit(2)
 
     import torch
