@@ -49,6 +49,10 @@ CASES = {
     "union_q2": (3, dict(batch=17, ctx_lens=[2500 + 37 * i for i in range(17)], q_len=2)),
     "union_q3": (3, dict(batch=32, ctx_lens=[258 + 131 * i for i in range(32)], q_len=3)),
     "union_q4_one_split": (3, dict(batch=64, ctx_lens=[130 + 29 * i for i in range(64)])),
+    # rows of 1,026 to 4,097 blocks: the selection shared by the attention workgroup's four
+    # wavefronts, and indexer workgroups whose blocks all lie past a short sequence's context
+    "ragged_long": (4, dict(batch=3, ctx_lens=[140_001, 2_000, 70_000])),
+    "spec_long": (3, dict(batch=2, ctx_lens=[140_000, 131_203], q_len=4)),
 }
 
 
