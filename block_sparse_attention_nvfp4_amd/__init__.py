@@ -15,6 +15,8 @@ HIP stream into the C calls, with the same names:
     msa_block_topk_merge(cand_ids, cand_keys, batch, topk, block_ids)   # merge of all shards
     msa_sparse_attn_workspace_bytes(batch)
     msa_sparse_attn_decode(cache, batch, q, block_ids, softmax_scale, out, workspace)
+    msa_sparse_attn_decode_topk(cache, batch, q, block_ids, softmax_scale, out, workspace)
+                                             # rows of 1..64 ids (block_ids' last dimension)
     msa_select_attn_decode(cache, batch, block_scores, topk, block_ids, q, softmax_scale, out,
                            workspace)        # the last two in one launch
     msa_insert_indexer_score(cache, batch, k, v, ik, q_idx, block_scores)  # insert + indexer
@@ -57,7 +59,8 @@ EXPORTED = ("msa_page_bytes", "msa_kv_insert_nvfp4", "msa_indexer_score", "msa_i
             "msa_indexer_score_shared_prefix", "msa_indexer_score_shard",
             "msa_block_topk",
             "msa_block_topk_window", "msa_block_topk_local", "msa_block_topk_merge",
-            "msa_sparse_attn_workspace_bytes", "msa_sparse_attn_decode", "msa_select_attn_decode",
+            "msa_sparse_attn_workspace_bytes", "msa_sparse_attn_decode",
+            "msa_sparse_attn_decode_topk", "msa_select_attn_decode",
             "msa_sparse_attn_shared_prefix_workspace_bytes", "msa_sparse_attn_decode_shared_prefix",
             "msa_insert_indexer_score", "msa_decode_step", "msa_decode_step_noalloc",
             "msa_last_error", "msa_version",
@@ -116,6 +119,9 @@ def _load() -> ctypes.CDLL:
     L.msa_sparse_attn_decode.restype = ctypes.c_int
     L.msa_sparse_attn_decode.argtypes = [ctypes.POINTER(_Cache), ctypes.POINTER(_Batch), vp, vp,
                                          ctypes.c_float, vp, vp, sz, vp]
+    L.msa_sparse_attn_decode_topk.restype = ctypes.c_int
+    L.msa_sparse_attn_decode_topk.argtypes = [ctypes.POINTER(_Cache), ctypes.POINTER(_Batch), vp,
+                                              vp, i32, ctypes.c_float, vp, vp, sz, vp]
     L.msa_sparse_attn_shared_prefix_workspace_bytes.restype = sz
     L.msa_sparse_attn_shared_prefix_workspace_bytes.argtypes = [ctypes.POINTER(_Batch)]
     L.msa_sparse_attn_decode_shared_prefix.restype = ctypes.c_int
@@ -359,6 +365,27 @@ def msa_sparse_attn_decode(cache: Cache, batch: Batch, q: torch.Tensor, block_id
                                       _ptr(block_ids, torch.int32, "block_ids"),
                                       float(softmax_scale), _ptr(out, torch.bfloat16, "out"),
                                       ws_ptr, ws_bytes, _stream(stream)))
+
+
+def msa_sparse_attn_decode_topk(cache: Cache, batch: Batch, q: torch.Tensor,
+                                block_ids: torch.Tensor, softmax_scale: float, out: torch.Tensor,
+                                workspace: Optional[torch.Tensor], stream=None) -> None:
+    """Attention over rows of any selection size: block_ids is [batch*q_len][4][topk], and topk
+    is taken from its last dimension."""
+    if tuple(q.shape) != (batch.rows, Q_HEADS, HEAD_DIM) or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q and out: expected [batch*q_len][64][128]")
+    if block_ids.dim() != 3 or tuple(block_ids.shape[:2]) != (batch.rows, KV_HEADS):
+        raise ValueError("block_ids: expected [batch*q_len][4][topk]")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _ptr(workspace, workspace.dtype, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.msa_sparse_attn_decode_topk(ctypes.byref(cache._c), ctypes.byref(batch._c),
+                                           _ptr(q, torch.bfloat16, "q"),
+                                           _ptr(block_ids, torch.int32, "block_ids"),
+                                           int(block_ids.shape[2]), float(softmax_scale),
+                                           _ptr(out, torch.bfloat16, "out"), ws_ptr, ws_bytes,
+                                           _stream(stream)))
 
 
 def msa_sparse_attn_shared_prefix_workspace_bytes(batch: Batch) -> int:

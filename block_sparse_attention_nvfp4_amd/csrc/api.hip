@@ -314,6 +314,28 @@ int msa_sparse_attn_decode(const msa_cache_t* cache, const msa_batch_t* batch, c
                       fn);
 }
 
+int msa_sparse_attn_decode_topk(const msa_cache_t* cache, const msa_batch_t* batch,
+                                const uint16_t* q, const int32_t* block_ids, int32_t topk,
+                                float softmax_scale, uint16_t* out, void* workspace,
+                                size_t ws_bytes, void* stream) {
+    static const char* fn = "msa_sparse_attn_decode_topk";
+    int rc = check_cache(cache, fn, true, false);
+    if (rc) return rc;
+    if ((rc = check_batch(batch, fn))) return rc;
+    if (!q || !block_ids || !out)
+        return fail(MSA_ERR_INVALID_ARG, "%s: q, block_ids or out is NULL", fn);
+    if (topk < 1 || topk > msa::kMaxTopkIds)
+        return fail(MSA_ERR_UNSUPPORTED, "%s: topk=%d (1..%d are built)", fn, topk,
+                    msa::kMaxTopkIds);
+    if ((rc = check_workspace(batch, workspace, ws_bytes, fn))) return rc;
+    return hip_status(msa::launch_attention_topk(cache->k, cache->v, cache->num_pages,
+                                                 batch->block_table, batch->ctx_lens,
+                                                 batch->batch, batch->max_blocks, batch->q_len, q,
+                                                 block_ids, topk, softmax_scale, out, workspace,
+                                                 (hipStream_t)stream),
+                      fn);
+}
+
 size_t msa_sparse_attn_shared_prefix_workspace_bytes(const msa_batch_t* batch) {
     if (!batch || batch->batch < 1 || batch->q_len < 1) return 0;
     return msa::attn_shared_prefix_workspace_bytes(batch->batch, batch->q_len);

@@ -352,15 +352,22 @@ __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c
 // workgroup of the row, or with LONG, rows of up to kSelectLongMaxBlocks blocks, all four
 // wavefronts; the first split also writes them to block_ids) instead of being read
 // from block_ids.
-template <int BPW, bool SELECT, bool LONG = false>
+// VAR_IDS: rows of ids_per_row (1..64) ids instead of 16: each wavefront takes
+// ceil(ids_per_row / (4 NSPLIT)) consecutive slots (at most BPW), the selection sizes of the
+// window knobs ("MiniMax M3 on vLLM", section "MSA mechanism": the top-k count is a knob).
+template <int BPW, bool SELECT, bool LONG = false, int NSPLIT = kMaxSplits / BPW, bool VAR_IDS = false>
 __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
     const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool, int64_t num_pages,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens, int batch,
     int max_blocks, int q_len, const uint16_t* __restrict__ q, int32_t* __restrict__ block_ids,
     const float* __restrict__ scores, float scale_log2, uint16_t* __restrict__ out,
-    int32_t* __restrict__ counters, float* __restrict__ partials) {
+    int32_t* __restrict__ counters, float* __restrict__ partials, int ids_per_row) {
     constexpr int kBufs = BPW > 1 ? 2 : 1;
-    constexpr int n_split = kMaxSplits / BPW;  // workgroups per row group (BPW blocks per wavefront)
+    constexpr int n_split = NSPLIT;  // workgroups per row group
+    static_assert(VAR_IDS ? !SELECT : BPW * kWaves * NSPLIT == kTopk,
+                  "16 ids per row fill the slots exactly; other counts come from block_ids");
+    // blocks per wavefront (a constant unless the row length is a call argument)
+    const int bpw = VAR_IDS ? (ids_per_row + kWaves * NSPLIT - 1) / (kWaves * NSPLIT) : BPW;
     static_assert(kWaves * kBufs * kBlockBytes >= kWaves * kGroupHeads * kMergeStride * 4,
                   "merge area must fit in the page buffers");
     __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves][kBufs][kBlockBytes];
@@ -526,14 +533,20 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
         __syncthreads();
         id = lane < BPW ? sh_sel[(split * kWaves + wave) * BPW + lane] : -1;
     } else {
-        const int32_t* my_ids = block_ids + (int64_t)rg * kTopk + (split * kWaves + wave) * BPW;
-        id = lane < BPW ? my_ids[lane] : -1;
+        if constexpr (VAR_IDS) {
+            const int slot0 = (split * kWaves + wave) * bpw;
+            const int32_t* my_ids = block_ids + (int64_t)rg * ids_per_row + slot0;
+            id = (lane < bpw && slot0 + lane < ids_per_row) ? my_ids[lane] : -1;
+        } else {
+            const int32_t* my_ids = block_ids + (int64_t)rg * kTopk + (split * kWaves + wave) * BPW;
+            id = lane < BPW ? my_ids[lane] : -1;
+        }
         asm volatile("" : "+v"(id));
     }
     const int T = clamp_ctx(T_raw, max_blocks);
     const int p = T - q_len + j;
     int page = -1;
-    if (lane < BPW && id >= 0 && id < max_blocks && id * kBlock <= p) {
+    if (lane < bpw && id >= 0 && id < max_blocks && id * kBlock <= p) {
         const int pg = SELECT ? sh_tbl[id] : block_table[(int64_t)b * max_blocks + id];
         page = (pg >= 0 && pg < num_pages) ? pg : -1;
     }
@@ -573,9 +586,9 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
     const float logit_scale = fabsf(scale_log2) * (f16 ? q_unscale : 1.0f);
 
     // (left to the compiler: with several blocks per wavefront the unrolled body is too large)
-    for (int kb = 0; kb < BPW; kb++) {
+    for (int kb = 0; kb < bpw; kb++) {
         int nxt_id = -1;
-        if (kb + 1 < BPW) {
+        if (kb + 1 < bpw) {
             nxt_id = __builtin_amdgcn_readlane(blk_id, kb + 1);
             if (nxt_id >= 0) {
                 const int pg = __builtin_amdgcn_readlane(page, kb + 1);
@@ -1390,6 +1403,7 @@ static bool use_union(int batch, int q_len, int max_blocks, bool select) {
            max_blocks <= (select ? kSelectFusedMaxBlocks : kUnionAttnMaxBlocks);
 }
 
+
 hipError_t launch_attn_workspace_clear(void* workspace, int batch, int q_len, hipStream_t stream) {
     // the counters of whichever kernel runs sit at the start of the workspace
     size_t bytes = attn_num_splits(batch, q_len) > 1 ? attn_counter_bytes(batch, q_len) : 0;
@@ -1460,7 +1474,7 @@ hipError_t launch_attention_t(const uint8_t* k_pool, const uint8_t* v_pool, int6
 #define MSA_LAUNCH_ATTN(BPW_)                                                                    \
     hipLaunchKernelGGL((attention_kernel<BPW_, SELECT>), grid, block, 0, stream, k_pool, v_pool, \
                        num_pages, block_table, ctx_lens, batch, max_blocks, q_len, q, ids,       \
-                       scores, scale_log2, out, counters, partials)
+                       scores, scale_log2, out, counters, partials, kTopk)
     switch (ns) {
         case 1: MSA_LAUNCH_ATTN(4); break;
         case 2: MSA_LAUNCH_ATTN(2); break;
@@ -1488,11 +1502,45 @@ hipError_t launch_attention_long_select(const uint8_t* k_pool, const uint8_t* v_
     hipLaunchKernelGGL((attention_kernel<1, true, true>), dim3(pair_slots * q_len * kMaxSplits),
                        dim3(kWaves * 64), 0, stream, k_pool, v_pool, num_pages, block_table,
                        ctx_lens, batch, max_blocks, q_len, q, ids, scores, scale_log2, out,
-                       counters, partials);
+                       counters, partials, kTopk);
     return hipGetLastError();
 }
 
 }  // namespace
+
+// Rows of topk (1..64) ids: the per-token kernel whatever the batch shape, with the splits of
+// the 16-id calls and ceil(topk / (4 splits)) slots per wavefront.
+hipError_t launch_attention_topk(const uint8_t* k_pool, const uint8_t* v_pool, int64_t num_pages,
+                                 const int32_t* block_table, const int32_t* ctx_lens, int batch,
+                                 int max_blocks, int q_len, const uint16_t* q, const int32_t* ids,
+                                 int topk, float softmax_scale, uint16_t* out, void* workspace,
+                                 hipStream_t stream) {
+    const int ns = attn_num_splits(batch, q_len);
+    const int pairs = batch * kKvHeads;
+    const int pair_slots = 8 * ((pairs + 7) / 8);
+    const float scale_log2 = softmax_scale * 1.4426950408889634f;
+    const dim3 grid(pair_slots * q_len * ns), block(kWaves * 64);
+    int32_t* counters = nullptr;
+    float* partials = nullptr;
+    if (ns > 1) {
+        counters = static_cast<int32_t*>(workspace);
+        partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                            attn_counter_bytes(batch, q_len));
+    }
+    static_assert(kMaxTopkIds <= 16 * kWaves, "one split holds 16 slots per wavefront at most");
+#define MSA_LAUNCH_ATTN_VAR(NS_)                                                                 \
+    hipLaunchKernelGGL((attention_kernel<16, false, false, NS_, true>), grid, block, 0, stream,  \
+                       k_pool, v_pool, num_pages, block_table, ctx_lens, batch, max_blocks,      \
+                       q_len, q, const_cast<int32_t*>(ids), nullptr, scale_log2, out, counters,  \
+                       partials, topk)
+    switch (ns) {
+        case 1: MSA_LAUNCH_ATTN_VAR(1); break;
+        case 2: MSA_LAUNCH_ATTN_VAR(2); break;
+        default: MSA_LAUNCH_ATTN_VAR(4); break;
+    }
+#undef MSA_LAUNCH_ATTN_VAR
+    return hipGetLastError();
+}
 
 hipError_t launch_attention(const uint8_t* k_pool, const uint8_t* v_pool, int64_t num_pages,
                             const int32_t* block_table, const int32_t* ctx_lens, int batch,

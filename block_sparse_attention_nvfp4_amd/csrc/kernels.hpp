@@ -96,6 +96,13 @@ hipError_t launch_attention(const uint8_t* k_pool, const uint8_t* v_pool, int64_
                             int max_blocks, int q_len, const uint16_t* q, const int32_t* ids,
                             float softmax_scale, uint16_t* out, void* workspace,
                             hipStream_t stream);
+// The same over rows of topk (1..kMaxTopkIds) ids each; the workspace of launch_attention.
+constexpr int kMaxTopkIds = 64;  // the largest selection of the window knobs
+hipError_t launch_attention_topk(const uint8_t* k_pool, const uint8_t* v_pool, int64_t num_pages,
+                                 const int32_t* block_table, const int32_t* ctx_lens, int batch,
+                                 int max_blocks, int q_len, const uint16_t* q, const int32_t* ids,
+                                 int topk, float softmax_scale, uint16_t* out, void* workspace,
+                                 hipStream_t stream);
 
 // Attention for 2 to 4 query tokens per sequence over the union of their selected blocks
 // (attention_union.hip): rows of up to kUnionAttnMaxBlocks blocks; the selection is made in the

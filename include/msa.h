@@ -220,8 +220,8 @@ int msa_block_topk(const float *block_scores, const msa_batch_t *batch, int32_t 
  * ranges once), and the best others by (score descending, block index ascending) fill the rest
  * of the topk places.
  *   block_ids : device int32 [batch * q_len][4][topk], ascending, padded with -1.
- * With topk = 16, init_blocks = 0, local_blocks = 1 the result is msa_block_topk's. The
- * attention calls take 16 ids per row; other counts are for selection studies.
+ * With topk = 16, init_blocks = 0, local_blocks = 1 the result is msa_block_topk's. Rows of
+ * any topk feed msa_sparse_attn_decode_topk (16-id rows also every other attention call).
  * Scores must not be NaN. Errors: MSA_ERR_INVALID_ARG (NULL pointers, sizes < 1, init_blocks
  * or local_blocks < 0, init_blocks + local_blocks > topk), MSA_ERR_UNSUPPORTED (topk outside
  * 1..64, max_blocks > 4096).
@@ -323,6 +323,29 @@ size_t msa_sparse_attn_workspace_bytes(const msa_batch_t *batch);
 int msa_sparse_attn_decode(const msa_cache_t *cache, const msa_batch_t *batch, const uint16_t *q,
                            const int32_t *block_ids, float softmax_scale, uint16_t *out,
                            void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Sparse attention over rows of any selection size from 1 to 64 blocks, as
+ * msa_block_topk_window writes them ("MiniMax M3 on vLLM", section "MSA mechanism": the top-k
+ * count, the init blocks and the local blocks are configuration knobs; "vLLM day-0 support for
+ * MiniMax-M3.1-Flash", section "MSA primer": exact attention over whatever the selection kept).
+ * Arguments, results, workspace and errors as msa_sparse_attn_decode, with:
+ *   block_ids : device int32 [batch * q_len][4][topk]; every entry that is >= 0, < max_blocks
+ *               and holds a visible key is attended (-1 and other entries are skipped; a block
+ *               listed twice counts twice, as the formula then says).
+ *   topk      : 1..64. With topk = 16 the output is msa_sparse_attn_decode's bit for bit
+ *               wherever that call runs its per-token kernel (below 16 sequences or outside
+ *               2-4 query tokens per sequence, and below 8 query tokens per sequence or 1,024
+ *               rows), and within the attention tolerance of it elsewhere.
+ *   workspace : at least msa_sparse_attn_workspace_bytes(batch) bytes, the same contract.
+ * Every batch shape runs the per-token kernel (each wavefront streams ceil(topk / (4 splits))
+ * blocks in turn), not the union or token-tile kernels of the 16-id call.
+ * Errors: as msa_sparse_attn_decode; MSA_ERR_UNSUPPORTED for topk outside 1..64.
+ */
+int msa_sparse_attn_decode_topk(const msa_cache_t *cache, const msa_batch_t *batch,
+                                const uint16_t *q, const int32_t *block_ids, int32_t topk,
+                                float softmax_scale, uint16_t *out, void *workspace,
+                                size_t ws_bytes, void *stream);
 
 /*
  * Sparse attention for a batch whose requests share a prefix: every sequence's blocks

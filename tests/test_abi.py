@@ -113,6 +113,15 @@ def test_invalid_arguments_return_codes_without_launch(msa):
     assert "topk" in msa.msa_last_error()
     assert L.msa_block_topk(None, by(_batch()), 16, 1, None) == msa.MSA_ERR_INVALID_ARG
     assert L.msa_block_topk(1, by(_batch(mb=0)), 16, 1, None) == msa.MSA_ERR_INVALID_ARG
+    # attention over rows of 1..64 ids (args: cache batch q ids topk scale out ws ws_bytes stream)
+    at = L.msa_sparse_attn_decode_topk
+    for bad in (0, 65, -3):
+        assert at(by(_cache()), by(_batch()), 1, 1, bad, 0.1, 1, None, 0, None) == msa.MSA_ERR_UNSUPPORTED
+    assert "topk" in msa.msa_last_error()
+    assert at(by(_cache()), by(_batch()), None, 1, 16, 0.1, 1, None, 0, None) == msa.MSA_ERR_INVALID_ARG
+    assert at(by(_cache()), by(_batch()), 1, None, 16, 0.1, 1, None, 0, None) == msa.MSA_ERR_INVALID_ARG
+    assert at(by(_cache(k=None)), by(_batch()), 1, 1, 16, 0.1, 1, None, 0, None) == msa.MSA_ERR_INVALID_ARG
+    assert at(by(_cache()), by(_batch(q=0)), 1, 1, 16, 0.1, 1, None, 0, None) == msa.MSA_ERR_INVALID_ARG
     # selection with the window knobs (args: scores batch topk init local ids stream)
     win = L.msa_block_topk_window
     assert win(1, by(_batch(mb=8)), 0, 0, 1, 1, None) == msa.MSA_ERR_UNSUPPORTED

@@ -1,0 +1,111 @@
+"""Attention over selections of 1 to 64 blocks per row, against the oracle (needs an MI355X).
+
+"MiniMax M3 on vLLM", section "MSA mechanism", makes the number of kept blocks and the init and
+local windows configuration knobs; "vLLM day-0 support for MiniMax-M3.1-Flash", section "MSA
+primer", fixes what follows the selection: exact attention over the kept blocks. Here
+msa_block_topk_window's ids (bit for bit those of oracle.block_topk_variant on the same scores)
+drive msa_sparse_attn_decode_topk end to end, and its outputs are checked against the oracle's
+attention over those ids. The batch shapes take each split count of the per-token kernel
+(4 splits below 512 rows, 2 below 1,024, then 1), so a wavefront streams from 1 up to 16
+blocks in turn. With 16 ids per row the call must give msa_sparse_attn_decode's bits where that
+call runs the same per-token kernel.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import msa_inputs as mi
+import oracle
+from msa_testlib import DeviceWorkload, bf16_to_f64, check_attention, oracle_sequence
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# name: (config, workload overrides, topk, init_blocks, local_blocks, sequences checked
+# against the oracle (None: all))
+CASES = {
+    "k1_q4": (3, dict(batch=3, ctx_lens=[5000, 128 * 23 + 7, 2100], q_len=4, seed=17), 1, 0, 1, None),
+    "k8_q4": (3, dict(batch=3, ctx_lens=[5000, 128 * 23 + 7, 2100], q_len=4, seed=17), 8, 1, 1, None),
+    "k32_q4": (3, dict(batch=3, ctx_lens=[9000, 128 * 40 + 1, 2100], q_len=4, seed=19), 32, 2, 2, None),
+    "k64_q4": (3, dict(batch=2, ctx_lens=[10000, 128 * 70 + 5], q_len=4, seed=23), 64, 4, 1, None),
+    "k64_q1": (2, dict(batch=3, ctx_lens=[12000, 128 * 64, 700], q_len=1, seed=29), 64, 0, 1, None),
+    "k40_q3": (3, dict(batch=2, ctx_lens=[7000, 6000], q_len=3, seed=31), 40, 3, 2, None),
+    # 520 rows: two splits, 6 slots per wavefront
+    "k48_q5_2split": (3, dict(batch=26, ctx_lens=[9000, 8000] + [1100] * 24, q_len=5, seed=37),
+                      48, 2, 3, [0, 1, 25]),
+    # 1,040 rows: one split, 16 slots per wavefront
+    "k64_q5_1split": (3, dict(batch=52, ctx_lens=[9500, 8800] + [1000] * 50, q_len=5, seed=41),
+                      64, 0, 1, [0, 1, 51]),
+}
+
+
+def _setup(cfg, kw):
+    import block_sparse_attention_nvfp4_amd as msa
+    w = mi.make_workload(cfg, **kw)
+    d = DeviceWorkload(w)
+    msa.msa_kv_insert_nvfp4(d.cache, d.new_slots, d.new_k, d.new_v, d.new_ik)
+    rows = w.batch * w.q_len
+    scores = torch.empty((rows, 4, w.max_blocks), dtype=torch.float32, device="cuda")
+    msa.msa_indexer_score(d.cache, d.batch, d.q_idx, scores)
+    ws_bytes = msa.msa_sparse_attn_workspace_bytes(d.batch)
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device="cuda") if ws_bytes else None
+    return w, d, scores, ws
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_any_topk_selection_drives_the_attention(name):
+    import block_sparse_attention_nvfp4_amd as msa
+    cfg, kw, topk, init, local, check = CASES[name]
+    _log(f"topk attention case {name}: topk={topk} init={init} local={local}")
+    w, d, scores, ws = _setup(cfg, kw)
+    rows = w.batch * w.q_len
+    ids = torch.full((rows, 4, topk), -7, dtype=torch.int32, device="cuda")
+    msa.msa_block_topk_window(scores, d.batch, topk, init, local, ids)
+    out = torch.full((rows, 64, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    msa.msa_sparse_attn_decode_topk(d.cache, d.batch, d.q, ids, msa.default_softmax_scale(), out, ws)
+    torch.cuda.synchronize()
+    s_h, ids_h = scores.cpu().numpy(), ids.cpu().numpy()
+    got = bf16_to_f64(out)
+    assert np.isfinite(got).all()
+    for b in range(w.batch):
+        T = w.ctx_lens[b]
+        for j in range(w.q_len):
+            r = b * w.q_len + j
+            n = (T - w.q_len + j) // 128 + 1
+            for g in range(4):
+                want = oracle.block_topk_variant(s_h[r, g], n, topk, init, local)
+                assert list(ids_h[r, g]) == list(want), (r, g)
+    kept = (ids_h >= 0).sum(axis=2)
+    assert kept.max() == min(topk, max((t - 1) // 128 + 1 for t in w.ctx_lens))
+    for b in (range(w.batch) if check is None else check):
+        rr = slice(b * w.q_len, (b + 1) * w.q_len)
+        ref = oracle_sequence(w, b, attention_tokens=list(range(w.q_len)), ids_override=ids_h[rr])
+        check_attention(got[rr], ref["attention"])
+
+
+@pytest.mark.parametrize("name", ["k8_q4", "k48_q5_2split", "k64_q5_1split"])
+def test_sixteen_ids_match_the_fixed_size_call(name):
+    """topk = 16 through the sized call gives msa_sparse_attn_decode's bits (both run the
+    per-token kernel on these shapes: under 16 sequences or 5 query tokens per sequence)."""
+    import block_sparse_attention_nvfp4_amd as msa
+    cfg, kw, _, _, _, _ = CASES[name]
+    _log(f"topk attention 16 ids vs fixed call: {name}")
+    w, d, scores, ws = _setup(cfg, kw)
+    rows = w.batch * w.q_len
+    ids = torch.empty((rows, 4, 16), dtype=torch.int32, device="cuda")
+    msa.msa_block_topk(scores, d.batch, 16, ids)
+    scale = msa.default_softmax_scale()
+    a = torch.empty((rows, 64, 128), dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    msa.msa_sparse_attn_decode(d.cache, d.batch, d.q, ids, scale, a, ws)
+    msa.msa_sparse_attn_decode_topk(d.cache, d.batch, d.q, ids, scale, b, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(a.view(torch.int16).cpu().numpy(), b.view(torch.int16).cpu().numpy())
+
