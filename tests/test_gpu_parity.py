@@ -51,6 +51,10 @@ CASES = {
     "union_q4_one_split": (3, dict(batch=64, ctx_lens=[130 + 29 * i for i in range(64)])),
     # rows of 1,026 to 4,097 blocks: the selection shared by the attention workgroup's four
     # wavefronts, and indexer workgroups whose blocks all lie past a short sequence's context
+    # consecutive drafts whose positions lie in different blocks (127 | 128, 1151 | 1152,
+    # 383 | 384), and 6 drafts per sequence
+    "spec_pair_straddle": (3, dict(batch=3, ctx_lens=[131, 128 * 9 + 1, 3 * 128 + 3], q_len=4)),
+    "spec_q6": (3, dict(batch=2, ctx_lens=[3000, 5100], q_len=6)),
     "ragged_long": (4, dict(batch=3, ctx_lens=[140_001, 2_000, 70_000])),
     "spec_long": (3, dict(batch=2, ctx_lens=[140_000, 131_203], q_len=4)),
 }
