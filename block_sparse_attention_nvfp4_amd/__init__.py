@@ -24,6 +24,7 @@ HIP stream into the C calls, with the same names:
                     block_ids, out, workspace)   # the two launches above and below in one call
     msa_decode_step_noalloc(cache, batch, k, v, ik, q_idx, q, topk, softmax_scale, block_scores,
                             block_ids, out)     # the same with the library's static workspace
+    use_library(checked), msa_debug_checks()   # the checked build and its failed-check counts
 
 A non-zero status raises MSAError. There is no fallback: importing fails loudly when the
 library has not been built (python block_sparse_attention_nvfp4_amd/build.py).
@@ -39,6 +40,8 @@ import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmsa.so")
+# the same library built with the kernels' checks (include/msa_debug.h): use_library(True)
+CHECKED_LIB_PATH = os.path.join(HERE, "libmsa_checked.so")
 
 BLOCK = 128
 HEAD_DIM = 128
@@ -64,6 +67,8 @@ EXPORTED = ("msa_page_bytes", "msa_kv_insert_nvfp4", "msa_indexer_score", "msa_i
             "msa_sparse_attn_shared_prefix_workspace_bytes", "msa_sparse_attn_decode_shared_prefix",
             "msa_insert_indexer_score", "msa_decode_step", "msa_decode_step_noalloc",
             "msa_last_error", "msa_version",
+            # include/msa_debug.h (checked build diagnostics)
+            "msa_debug_checks",
             # include/msa_probe.h (measurement aid)
             "msa_probe_stream_read", "msa_probe_sink_words")
 
@@ -85,11 +90,11 @@ class _Batch(ctypes.Structure):
                 ("q_len", ctypes.c_int32)]
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with "
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
                           "`python block_sparse_attention_nvfp4_amd/build.py` (hipcc, gfx950)")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     L.msa_page_bytes.restype, L.msa_page_bytes.argtypes = sz, [ctypes.c_int]
     L.msa_kv_insert_nvfp4.restype = ctypes.c_int
@@ -144,10 +149,31 @@ def _load() -> ctypes.CDLL:
     L.msa_probe_sink_words.restype, L.msa_probe_sink_words.argtypes = sz, []
     L.msa_last_error.restype, L.msa_last_error.argtypes = ctypes.c_char_p, []
     L.msa_version.restype, L.msa_version.argtypes = ctypes.c_char_p, []
+    L.msa_debug_checks.restype = ctypes.c_int
+    L.msa_debug_checks.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_uint32)]
     return L
 
 
 lib = _load()
+_libs = {False: lib}
+
+
+def use_library(checked: bool) -> None:
+    """Route every call of this module to libmsa_checked.so (True) or libmsa.so (False). Both
+    are built from the same sources; the checked one also counts failed kernel checks, which
+    msa_debug_checks() returns."""
+    global lib
+    if checked not in _libs:
+        _libs[checked] = _load(CHECKED_LIB_PATH)
+    lib = _libs[checked]
+
+
+def msa_debug_checks():
+    """(failed checks, lowest failing site) on the current device since the previous call, both
+    reset; only the checked library counts (MSAError from libmsa.so)."""
+    count, site = ctypes.c_uint32(0), ctypes.c_uint32(0)
+    _check(lib.msa_debug_checks(ctypes.byref(count), ctypes.byref(site)))
+    return int(count.value), int(site.value)
 
 
 def _check(rc: int) -> None:

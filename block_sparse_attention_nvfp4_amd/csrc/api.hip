@@ -1,4 +1,4 @@
-// C entry points of libmsa.so (declared and documented in include/msa.h): host-side argument
+// C entry points of libmsa.so (declared and documented in include/msa.h and include/msa_debug.h): host-side argument
 // checks, then asynchronous launches on the caller's stream.
 #include <stdarg.h>
 #include <stdio.h>
@@ -6,6 +6,7 @@
 #include <mutex>
 
 #include "../../include/msa.h"
+#include "../../include/msa_debug.h"
 #include "kernels.hpp"
 
 namespace {
@@ -104,7 +105,35 @@ size_t msa_page_bytes(int which) {
 
 const char* msa_last_error(void) { return g_last_error; }
 
-const char* msa_version(void) { return "msa-mi355x 0.1 (gfx950)"; }
+const char* msa_version(void) {
+#ifdef MSA_CHECKED
+    return "msa-mi355x 0.1 (gfx950, checked)";
+#else
+    return "msa-mi355x 0.1 (gfx950)";
+#endif
+}
+
+int msa_debug_checks(uint32_t* count, uint32_t* site) {
+    static const char* fn = "msa_debug_checks";
+    if (!count || !site) return fail(MSA_ERR_INVALID_ARG, "%s: count or site is NULL", fn);
+#ifdef MSA_CHECKED
+    uint32_t n = 0, lowest = 0xFFFFFFFFu;
+    for (auto take : {msa::checks_take_attention, msa::checks_take_union, msa::checks_take_indexer,
+                      msa::checks_take_indexer_gemm, msa::checks_take_insert,
+                      msa::checks_take_topk}) {
+        const hipError_t e = take(&n, &lowest);
+        if (e != hipSuccess)
+            return fail(MSA_ERR_HIP, "%s: reading the check counters: %s", fn, hipGetErrorString(e));
+    }
+    *count = n;
+    *site = lowest == 0xFFFFFFFFu ? 0u : lowest;
+    return MSA_OK;
+#else
+    *count = 0;
+    *site = 0;
+    return fail(MSA_ERR_UNSUPPORTED, "%s: this library is built without the checks (use libmsa_checked.so)", fn);
+#endif
+}
 
 int msa_kv_insert_nvfp4(const msa_cache_t* cache, const int64_t* slots, const float* k,
                         const float* v, const float* ik, int32_t n, void* stream) {

@@ -545,6 +545,23 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
     }
     const int T = clamp_ctx(T_raw, max_blocks);
     const int p = T - q_len + j;
+    MSA_CHECK(threadIdx.x != 0 || (T_raw >= q_len && T_raw <= max_blocks * kBlock), kCheckCtxLen);
+    MSA_CHECK(!SELECT || max_blocks <= (LONG ? kSelectLongMaxBlocks : kSelectFusedMaxBlocks), kCheckLds);
+    MSA_CHECK(bq < batch * q_len && rg < batch * q_len * kKvHeads && split < n_split, kCheckOutput);
+#ifdef MSA_CHECKED
+    if constexpr (SELECT) {
+        // the row's ids: ascending within the eligible blocks, the block of the query token last
+        if (wave == 0 && lane < kTopk) {
+            const int n_el = eligible_blocks(p, max_blocks);
+            const int kept = min(kTopk, n_el);
+            const int v = sh_sel[lane];
+            MSA_CHECK(lane < kept ? (v >= 0 && v < n_el && (lane == 0 || v > sh_sel[lane - 1]) &&
+                                     (lane != kept - 1 || v == n_el - 1))
+                                  : v == -1,
+                      kCheckSelection);
+        }
+    }
+#endif
     int page = -1;
     if (lane < bpw && id >= 0 && id < max_blocks && id * kBlock <= p) {
         const int pg = SELECT ? sh_tbl[id] : block_table[(int64_t)b * max_blocks + id];
@@ -654,6 +671,9 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
         // counter counts finished wavefronts and is left at zero again for the next launch)
         const int64_t part_base = (int64_t)rg * n_split * kGroupHeads;
         float* pp = partials + ((part_base + (int64_t)split * kGroupHeads) + h) * kPartStride;
+        MSA_CHECK(((part_base + (int64_t)split * kGroupHeads) + h + 1) * kPartStride <=
+                      (int64_t)batch * q_len * kKvHeads * n_split * kGroupHeads * kPartStride,
+                  kCheckWorkspace);
         if (d0 == 0) store16_coherent(pp, f32x4{M, L, 0.f, 0.f});
         store16_coherent(pp + 4 + d0, f32x4{acc[0], acc[1], acc[2], acc[3]});
         store16_coherent(pp + 8 + d0, f32x4{acc[4], acc[5], acc[6], acc[7]});
@@ -965,6 +985,7 @@ __global__ __launch_bounds__(kTileWaves * 64) void attention_tile_kernel(
     }
     __syncthreads();
     const int nu = ucount;
+    MSA_CHECK(nu <= kTileTokens * kTopk && max_blocks <= kUnionMaxBlocks, kCheckLds);
     if ((int)threadIdx.x < nu) {
         const int pg = block_table[(int64_t)b * max_blocks + ulist[threadIdx.x]];
         upage[threadIdx.x] = (pg >= 0 && pg < num_pages) ? pg : -1;
@@ -1136,6 +1157,7 @@ __global__ __launch_bounds__(kTileWaves * 64) void shared_block_kernel(
     }
     __syncthreads();
     const int count = __builtin_amdgcn_readfirstlane(min(n_items, kSharedMaxRows));
+    MSA_CHECK(n_items <= kSharedMaxRows, kCheckLds);
     // sequence 0's table entry: the page every request holds for the block
     const int pg = __builtin_amdgcn_readfirstlane(block_table[blk]);
     if (count == 0 || pg < 0 || pg >= num_pages) return;  // the whole workgroup
@@ -1369,6 +1391,10 @@ __global__ __launch_bounds__(kCombineWaves * 64) void shared_combine_kernel(
 }
 
 }  // namespace
+
+#ifdef MSA_CHECKED
+MSA_DEFINE_CHECKS_READER(checks_take_attention)
+#endif
 
 int attn_num_splits(int batch, int q_len) {
     const long rows = (long)batch * q_len * kKvHeads;

@@ -410,6 +410,23 @@ __global__ __launch_bounds__(kUWaves * 64) void attention_union_kernel(
     }
     __syncthreads();
     const int U = sh_ucount;
+    MSA_CHECK(threadIdx.x != 0 || (T_raw >= QL && T_raw <= max_blocks * kBlock), kCheckCtxLen);
+    MSA_CHECK(U <= kUMaxUnion && max_blocks <= kWords * 64, kCheckLds);
+    MSA_CHECK(split < n_split && n_split <= kUMaxSplits && b < batch, kCheckWorkspace);
+#ifdef MSA_CHECKED
+    if constexpr (SELECT) {
+        // each draft's ids: ascending within its eligible blocks, the block of its token last
+        if (wave < QL && lane < kTopk) {
+            const int n_el = eligible_blocks(T - QL + wave, max_blocks);
+            const int kept = min(kTopk, n_el);
+            const int v = sh_sel[wave][lane];
+            MSA_CHECK(lane < kept ? (v >= 0 && v < n_el && (lane == 0 || v > sh_sel[wave][lane - 1]) &&
+                                     (lane != kept - 1 || v == n_el - 1))
+                                  : v == -1,
+                      kCheckSelection);
+        }
+    }
+#endif
     const int lo = (int)(((int64_t)split * U) / n_split);
     const int hi = (int)(((int64_t)(split + 1) * U) / n_split);
     // every load so far is complete, and the compiler knows it (none is waited for between the
@@ -623,6 +640,10 @@ __global__ __launch_bounds__(kUWaves * 64) void attention_union_kernel(
 }
 
 }  // namespace
+
+#ifdef MSA_CHECKED
+MSA_DEFINE_CHECKS_READER(checks_take_union)
+#endif
 
 int union_num_splits(int batch) {
     const int pairs = batch * kKvHeads;

@@ -180,6 +180,49 @@ __device__ __forceinline__ f32x4 mfma_f16_k16(const f16x4& a, const f16x4& b, co
     return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
+// ---------------------------------------------------------------- checked build
+// Compiled with -DMSA_CHECKED (libmsa_checked.so), the kernels check the values they read from
+// device memory against their contract (context lengths, page ids, block ids, slots: every
+// build clamps or skips values outside it) and the indexes they compute against the extents of
+// their arguments. A failed check adds 1 to this file's device counter and lowers its lowest
+// failing site (the site codes of include/msa_debug.h); the kernel goes on. msa_debug_checks
+// reads and resets the counters of every file. In the normal build a check compiles to nothing.
+#ifdef MSA_CHECKED
+static __device__ uint32_t g_checks[2] = {0u, 0xFFFFFFFFu};  // failures, lowest failing site
+__device__ __forceinline__ void check_site(bool ok, uint32_t site) {
+    if (!ok) {
+        atomicAdd(&g_checks[0], 1u);
+        atomicMin(&g_checks[1], site);
+    }
+}
+#define MSA_CHECK(ok, site) ::msa::check_site((ok), (site))
+// The host reader of this file's counters (one per .hip file with kernels): adds the failures
+// to *count, lowers *site, and resets both.
+#define MSA_DEFINE_CHECKS_READER(NAME)                                                   \
+    hipError_t NAME(uint32_t* count, uint32_t* site) {                                   \
+        uint32_t v[2];                                                                   \
+        hipError_t e = hipMemcpyFromSymbol(v, HIP_SYMBOL(g_checks), sizeof(v), 0,        \
+                                           hipMemcpyDeviceToHost);                       \
+        if (e != hipSuccess) return e;                                                   \
+        *count += v[0];                                                                  \
+        if (v[1] < *site) *site = v[1];                                                  \
+        const uint32_t init[2] = {0u, 0xFFFFFFFFu};                                      \
+        return hipMemcpyToSymbol(HIP_SYMBOL(g_checks), init, sizeof(init), 0,            \
+                                 hipMemcpyHostToDevice);                                 \
+    }
+#else
+#define MSA_CHECK(ok, site) ((void)0)
+#endif
+
+// Check sites (the codes of include/msa_debug.h): a value read from device memory outside its
+// contract, then invariants of the kernels' own index arithmetic.
+constexpr uint32_t kCheckCtxLen = 1;       // a context length outside q_len .. max_blocks * 128
+constexpr uint32_t kCheckSelection = 101;  // a selection not ascending, not within the eligible
+                                           // blocks, or without the block of the query token
+constexpr uint32_t kCheckWorkspace = 102;  // a split partial or counter past the call's workspace
+constexpr uint32_t kCheckLds = 103;        // an LDS list or table index past its array
+constexpr uint32_t kCheckOutput = 104;     // a score, id, cache or output index past its array
+
 __device__ __forceinline__ int clamp_ctx(int T, int max_blocks) {
     const int cap = max_blocks * kBlock;
     return T < 0 ? 0 : (T > cap ? cap : T);

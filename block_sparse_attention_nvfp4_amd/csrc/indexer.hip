@@ -344,6 +344,8 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
     asm volatile("" : "+v"(pid_all), "+v"(T_raw), "+v"(ins_x));
     // the same value in every lane
     const int T = __builtin_amdgcn_readfirstlane(clamp_ctx(T_raw, FUSED ? max_blocks : total_blocks));
+    MSA_CHECK(threadIdx.x != 0 || (T_raw >= q_len && T_raw <= (FUSED ? max_blocks : total_blocks) * kBlock),
+              kCheckCtxLen);
     const int rows = 4 * q_len;
     const int64_t row_base = (int64_t)b * rows;
     // blocks past the last query position hold no visible key and are never loaded (columns
@@ -393,6 +395,7 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
     };
     // load half h of page u of a tile into LDS buffer `buf`; false when the page is absent
     auto issue = [&](int u, int buf, int vis_end) {
+        MSA_CHECK(vis_end - 1 - u - wg_blk0 >= 0 && vis_end - 1 - u - wg_blk0 < kPagesPerWg, kCheckLds);
         const int pid = __builtin_amdgcn_readlane(pid_all, vis_end - 1 - u - wg_blk0);
         if (pid < 0) return false;
         half_to_lds(ik_pool + (int64_t)pid * kHeadPageBytes, h, lds[wave][buf], lane);
@@ -584,6 +587,10 @@ __global__ __launch_bounds__(kWaves * 64) void indexer_kernel(
 }
 
 }  // namespace
+
+#ifdef MSA_CHECKED
+MSA_DEFINE_CHECKS_READER(checks_take_indexer)
+#endif
 
 static int indexer_wgs(int batch, int max_blocks) {
     return (max_blocks + kPagesPerWg - 1) / kPagesPerWg * batch;

@@ -74,7 +74,9 @@ __global__ __launch_bounds__(kGWaves * 64, 2) void indexer_gemm_kernel(
     const int blk0 = blk_begin + blockIdx.x * kGWaves;  // this workgroup's first block
     const int blk = blk0 + wave;
     // (SHARED: a context past every block, so that nothing is masked)
-    const int T = SHARED ? max_blocks * kBlock : clamp_ctx(ctx_lens[b], total_blocks);
+    const int T_raw = SHARED ? max_blocks * kBlock : ctx_lens[b];
+    const int T = SHARED ? T_raw : clamp_ctx(T_raw, total_blocks);
+    MSA_CHECK(SHARED || threadIdx.x != 0 || (T_raw >= q_len && T_raw <= total_blocks * kBlock), kCheckCtxLen);
     const uint8_t* qseq = reinterpret_cast<const uint8_t*>(q_idx + (int64_t)b * rows * kDim);
 
     // stage loads: copies of 1 KB (tile tt, piece m), kCopies per wavefront; lane
@@ -184,6 +186,10 @@ __global__ __launch_bounds__(kGWaves * 64, 2) void indexer_gemm_kernel(
 }
 
 }  // namespace
+
+#ifdef MSA_CHECKED
+MSA_DEFINE_CHECKS_READER(checks_take_indexer_gemm)
+#endif
 
 namespace {
 

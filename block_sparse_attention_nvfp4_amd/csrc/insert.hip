@@ -54,6 +54,7 @@ __global__ __launch_bounds__(576) void insert_kernel(uint8_t* __restrict__ k_poo
         int t_raw = ctx_lens[b];
         asm volatile("" : "+v"(x), "+v"(t_raw));
         const int pos = clamp_ctx(t_raw, max_blocks) - q_len + (token - b * q_len);
+        MSA_CHECK(threadIdx.x != 0 || (t_raw >= q_len && t_raw <= max_blocks * kBlock), kCheckCtxLen);
         if (pos < 0) return;
         page = block_table[(int64_t)b * max_blocks + (pos >> 7)];
         t = pos & 127;
@@ -112,7 +113,9 @@ __global__ __launch_bounds__(576) void insert_run_kernel(
         base = ik;
         stride = kDim;
     }
-    const int T = clamp_ctx(ctx_lens[b], max_blocks);
+    const int T_raw = ctx_lens[b];
+    const int T = clamp_ctx(T_raw, max_blocks);
+    MSA_CHECK(threadIdx.x != 0 || (T_raw >= q_len && T_raw <= max_blocks * kBlock), kCheckCtxLen);
     const int p_first = T - q_len;                 // position of new token 0 (may be < 0)
     const int pos0 = ((p_first >> 3) + r) * kRun;  // this run's first position (floor of p / 8)
     const int lo = max(pos0, max(p_first, 0));
@@ -232,6 +235,10 @@ __global__ __launch_bounds__(576) void insert_slots_kernel(
 }
 
 }  // namespace
+
+#ifdef MSA_CHECKED
+MSA_DEFINE_CHECKS_READER(checks_take_insert)
+#endif
 
 hipError_t launch_insert(uint8_t* k_pool, uint8_t* v_pool, uint8_t* ik_pool, int64_t num_pages,
                          const int64_t* slots, const float* k, const float* v, const float* ik,

@@ -143,4 +143,15 @@ hipError_t launch_attention_shared_prefix(const uint8_t* k_pool, const uint8_t* 
                                           int prefix_blocks, float softmax_scale, uint16_t* out,
                                           void* workspace, hipStream_t stream);
 
+#ifdef MSA_CHECKED
+// The checked build's per-file readers of the failed-check counters (device_common.hpp): each
+// adds its failures to *count, lowers *site and resets its counters.
+hipError_t checks_take_attention(uint32_t* count, uint32_t* site);
+hipError_t checks_take_union(uint32_t* count, uint32_t* site);
+hipError_t checks_take_indexer(uint32_t* count, uint32_t* site);
+hipError_t checks_take_indexer_gemm(uint32_t* count, uint32_t* site);
+hipError_t checks_take_insert(uint32_t* count, uint32_t* site);
+hipError_t checks_take_topk(uint32_t* count, uint32_t* site);
+#endif
+
 }  // namespace msa

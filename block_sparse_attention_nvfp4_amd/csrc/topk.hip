@@ -119,7 +119,9 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     const int wave = tid >> 6;
     int32_t* out = ids + (int64_t)row * kTopk;
 
-    const int T = clamp_ctx(ctx_lens[b], max_blocks);
+    const int T_raw = ctx_lens[b];
+    const int T = clamp_ctx(T_raw, max_blocks);
+    MSA_CHECK(tid != 0 || (T_raw >= q_len && T_raw <= max_blocks * kBlock), kCheckCtxLen);
     const int p = T - q_len + j;
     if (p < 0) {
         if (tid < kTopk) out[tid] = -1;
@@ -246,6 +248,7 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void topk_wave_kernel(
 #pragma unroll
     for (int k = 0; k < KPL; k++) asm volatile("" : "+v"(v[k]));
     asm volatile("" : "+v"(T_raw));
+    MSA_CHECK(lane != 0 || (T_raw >= q_len && T_raw <= max_blocks * kBlock), kCheckCtxLen);
     const int p = clamp_ctx(T_raw, max_blocks) - q_len + j;
     select_row<KPL>(v, eligible_blocks(p, max_blocks), lane, cand[wave], ids + (int64_t)row * kTopk);
 }
@@ -269,6 +272,7 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void topk_window_kernel(
 #pragma unroll
     for (int k = 0; k < KPL; k++) asm volatile("" : "+v"(v[k]));
     asm volatile("" : "+v"(T_raw));
+    MSA_CHECK(lane != 0 || (T_raw >= q_len && T_raw <= max_blocks * kBlock), kCheckCtxLen);
     const int p = clamp_ctx(T_raw, max_blocks) - q_len + j;
     select_row_window<KPL>(v, eligible_blocks(p, max_blocks), lane, cand[wave],
                            ids + (int64_t)row * topk, topk, init, local);
@@ -303,6 +307,7 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void topk_local_kernel(
 #pragma unroll
     for (int k = 0; k < KPL; k++) asm volatile("" : "+v"(v[k]));
     asm volatile("" : "+v"(T_raw));
+    MSA_CHECK(lane != 0 || (T_raw >= q_len && T_raw <= max_blocks * kBlock), kCheckCtxLen);
     const int n = eligible_blocks(clamp_ctx(T_raw, max_blocks) - q_len + j, max_blocks);
     uint32_t key[KPL];
 #pragma unroll
@@ -374,6 +379,10 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void topk_merge_kernel(
 }
 
 }  // namespace
+
+#ifdef MSA_CHECKED
+MSA_DEFINE_CHECKS_READER(checks_take_topk)
+#endif
 
 hipError_t launch_topk_window(const float* scores, const int32_t* ctx_lens, int batch,
                               int max_blocks, int q_len, int topk, int init, int local,

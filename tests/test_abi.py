@@ -44,12 +44,31 @@ def test_header_declares_the_path(msa):
 
 
 def test_library_exports_every_declared_symbol(msa):
-    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
-    exported = set(re.findall(r"\bT (msa_[a-z0-9_]+)$", out, flags=re.M))
-    missing = set(declared_functions()) - exported
-    assert not missing, missing
+    for path in (LIB, msa.CHECKED_LIB_PATH):
+        out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                             check=True).stdout
+        exported = set(re.findall(r"\bT (msa_[a-z0-9_]+)$", out, flags=re.M))
+        missing = set(declared_functions()) - exported
+        assert not missing, (path, missing)
     for f in declared_functions():
         assert hasattr(msa.lib, f)
+
+
+def test_checked_library_and_its_diagnostics(msa):
+    """libmsa.so counts nothing (MSA_ERR_UNSUPPORTED); libmsa_checked.so is the same library
+    with the kernels' checks; NULL pointers are rejected before any GPU call in both."""
+    c, s = ctypes.c_uint32(7), ctypes.c_uint32(7)
+    assert msa.lib.msa_debug_checks(ctypes.byref(c), ctypes.byref(s)) == msa.MSA_ERR_UNSUPPORTED
+    assert (c.value, s.value) == (0, 0)
+    assert msa.lib.msa_debug_checks(None, ctypes.byref(s)) == msa.MSA_ERR_INVALID_ARG
+    try:
+        msa.use_library(True)
+        assert "checked" in msa.msa_version()
+        assert msa.lib.msa_debug_checks(ctypes.byref(c), None) == msa.MSA_ERR_INVALID_ARG
+        assert msa.lib.msa_block_topk(None, None, 16, None, None) == msa.MSA_ERR_INVALID_ARG
+    finally:
+        msa.use_library(False)
+    assert "checked" not in msa.msa_version()
 
 
 def test_constants_and_version(msa):
