@@ -23,7 +23,9 @@ Beside the headline line: "side" repeats the step on the batched workload (32 x 
 sequences at 128K with 4 query tokens (which takes the union attention kernel), each with its
 two launches against the HBM peak; "hbm_read_ceiling_gbs" is the GPU's measured streaming-read
 rate for a 76 MB and a 2 GiB working set; "prefill" times the chunked-prefill workload's calls
-against the matrix-core peak; "cpu_baseline" times the oracle on the host.
+against the matrix-core peak; "side" also holds the prefix-sharing workload (prefix64) and the
+headline workload with the window knobs of the selection (window64: top-64, init and local
+blocks, attention over 64 ids per row); "cpu_baseline" times the oracle on the host.
 
 Output: one JSON line (see the keys below). --gpus N > 1 exits: the path runs on one GPU.
 """
@@ -59,7 +61,7 @@ def parse():
     ap.add_argument("--only", default="", help="profiling aid: run a calibration copy of "
                     f"{COPY_BYTES >> 20} MiB, then only this call in a loop "
                     "(insert|indexer|insert_indexer|topk|attention|select_attention), and exit; "
-                    "'prefill' and 'prefix' run only that side measurement")
+                    "'prefill', 'prefix' and 'window' run only that side measurement")
     ap.add_argument("--workload", default="spec128k",
                     choices=("spec128k", "union32x128k", "batched32k", "ragged512k"),
                     help="decode workload of an --only run")
@@ -243,6 +245,9 @@ def main():
     if args.only == "prefix":
         print(json.dumps(prefix_side(args)), flush=True)
         return
+    if args.only == "window":
+        print(json.dumps(window_side(args)), flush=True)
+        return
     if args.only:
         ow = {"spec128k": w, "union32x128k": mi.make_workload(3, batch=32),
               "batched32k": mi.full_workload(2), "ragged512k": mi.full_workload(4)}[args.workload]
@@ -316,6 +321,9 @@ def main():
         torch.cuda.empty_cache()
         print("# side line prefix64", file=sys.stderr, flush=True)
         result["side"]["prefix64"] = prefix_side(args)
+        torch.cuda.empty_cache()
+        print("# side line window64", file=sys.stderr, flush=True)
+        result["side"]["window64"] = window_side(args)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
@@ -645,6 +653,90 @@ def prefix_side(args, L=4):
         "query_tokens_per_s": {k: round(B * q / (us[k] * 1e-6), 1) for k in paths},
         "attention_dequantized_blocks": {"per_request": per_row, "shared_prefix": uniq + per_row - int(shared.sum())},
         "shared_slots": int(shared.sum()),
+    }
+
+
+def window_side(args, topk=64, init=1, local=2, L=4):
+    """The headline workload (8 x 131,072 tokens, 4 query tokens) with the window knobs of the
+    selection: top-`topk` blocks with the first `init` and the last `local` blocks kept, then
+    attention over those rows of `topk` ids. The step as three launches (insert + indexer, the
+    window selection, the attention) on L rotated layers, every call also timed alone; the
+    attention's gather against the HBM peak (144 B per valid token of each distinct selected
+    (sequence, group, block), the scores, queries and outputs)."""
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_nvfp4_amd as msa
+    import msa_inputs as mi
+
+    dev = "cuda"
+    w = mi.full_workload(3)
+    B, q = w.batch, w.q_len
+    caches = layer_caches(w, L)
+    batch = msa.Batch(torch.from_numpy(w.block_table).to(dev),
+                      torch.tensor(w.ctx_lens, dtype=torch.int32, device=dev), q)
+    toks = [(b, w.ctx_lens[b] - q, w.ctx_lens[b]) for b in range(B)]
+    new_k = torch.cat([w.kv_rows("k", b, t0, t1, dev) for b, t0, t1 in toks])
+    new_v = torch.cat([w.kv_rows("v", b, t0, t1, dev) for b, t0, t1 in toks])
+    new_ik = torch.cat([w.ik_rows(b, t0, t1, dev) for b, t0, t1 in toks])
+    q_idx, qq = w.q_idx.to(dev), w.q.to(dev)
+    steps = [msa.DecodeStep(c, batch, dev) for c in caches]
+    ids = [torch.full((B * q, 4, topk), -1, dtype=torch.int32, device=dev) for _ in steps]
+    scale = msa.default_softmax_scale()
+    calls = {
+        "insert_indexer": lambda i, s: msa.msa_insert_indexer_score(s.cache, batch, new_k, new_v,
+                                                                    new_ik, q_idx, s.block_scores),
+        "topk_window": lambda i, s: msa.msa_block_topk_window(s.block_scores, batch, topk, init,
+                                                              local, ids[i]),
+        "attention_topk": lambda i, s: msa.msa_sparse_attn_decode_topk(s.cache, batch, qq, ids[i],
+                                                                       scale, s.out, s.workspace),
+    }
+    step = tuple(calls)
+    for i, s in enumerate(steps):
+        for name in step:
+            calls[name](i, s)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    graphs = {}
+    with torch.cuda.stream(stream):
+        for key, names in [("step", step)] + [(n, (n,)) for n in calls]:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i, s in enumerate(steps):
+                    for name in names:
+                        calls[name](i, s)
+            graphs[key] = g
+    torch.cuda.synchronize()
+    us = {}
+    with torch.cuda.stream(stream):
+        for key, g in graphs.items():
+            g.replay()
+            series = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(args.kernel_reps):
+                    g.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                series.append(e0.elapsed_time(e1) * 1e3 / (args.kernel_reps * L))
+            us[key] = round(sorted(series)[2], 3)
+    sel = ids[0].cpu().numpy().reshape(B, q, 4, topk)
+    gathered = 0
+    for b in range(B):
+        T = w.ctx_lens[b]
+        for g in range(4):
+            for blk in set(int(x) for x in sel[b, :, g].ravel() if x >= 0):
+                gathered += max(0, min(128, T - blk * 128))
+    attn_bytes = gathered * 144 + 2 * B * q * 64 * 128 * 2 + B * q * 4 * topk * 4
+    return {
+        "workload": f"spec128k with window selection: batch {B} x context {w.ctx_lens[0]} tokens, "
+                    f"{q} query tokens each, top-{topk} with init {init} and local {local} "
+                    f"blocks, {L} layers rotated",
+        "us": us,
+        "query_tokens_per_s": round(B * q / (us["step"] * 1e-6), 1),
+        "attention_gather": {"algorithmic_bytes": attn_bytes,
+                             "frac": round(attn_bytes / (us["attention_topk"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
     }
 
 

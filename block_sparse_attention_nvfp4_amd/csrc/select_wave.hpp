@@ -228,6 +228,47 @@ __device__ __forceinline__ void select_top(const uint32_t (&key)[KPL], int lane,
     }
 }
 
+// select_top for picks above 16 (the window knobs' top-k up to 64), where the lane-maxima bound
+// would leave far more than 64 candidates: t, the pick-th largest key, is found bit by bit from
+// the top (the largest value that at least `pick` keys reach, counted by ballots); then every key
+// above t and the first keys equal to t in position order (equal keys rank by the lower
+// position) are written in ascending position order. The same contract as select_top.
+template <int KPL, class IdOf>
+__device__ __forceinline__ void select_top_radix(const uint32_t (&key)[KPL], int lane,
+                                                 int32_t* out, uint32_t* key_out, IdOf id_of,
+                                                 int pick) {
+    uint32_t t = 0;  // stays 0 when fewer than `pick` keys are candidates (every candidate is >= 1)
+    for (int bit = 31; bit >= 0; bit--) {
+        const uint32_t c = t | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int k = 0; k < KPL; k++) cnt += popc64(__ballot(key[k] >= c));
+        if (cnt >= pick) t = c;
+    }
+    int above = 0;
+#pragma unroll
+    for (int k = 0; k < KPL; k++) above += popc64(__ballot(key[k] > t));
+    int take_eq = t == 0u ? 0 : pick - above;  // keys equal to t still to take
+    int at = 0;
+#pragma unroll
+    for (int k = 0; k < KPL; k++) {
+        const bool eq = t != 0u && key[k] == t;
+        const uint64_t eqm = __ballot(eq);
+        const bool sel = key[k] > t || (eq && lanes_before(eqm) < take_eq);
+        const uint64_t sm = __ballot(sel);
+        if (sel) {
+            out[at + lanes_before(sm)] = id_of(lane + 64 * k);
+            if (key_out) key_out[at + lanes_before(sm)] = key[k];
+        }
+        at += popc64(sm);
+        take_eq -= min(take_eq, popc64(eqm));
+    }
+    if (lane >= at && lane < pick) {
+        out[lane] = -1;
+        if (key_out) key_out[lane] = 0u;
+    }
+}
+
 // Select the row's blocks from its scores v (as load_row_scores holds them) and its n eligible
 // blocks: out[0..15] gets the selected block ids in ascending order, padded with -1. `cand` is
 // this wavefront's kSelectScratch entries of LDS; `out` may point to global memory or LDS.
@@ -270,8 +311,11 @@ __device__ __forceinline__ void select_row_window(const float (&v)[KPL], int n, 
         key[k] = (i >= lo && i < hi) ? order_key(v[k]) : 0u;
     }
     // the picks lie between the two forced ranges, so the ascending order is kept
-    select_top<KPL>(key, lane, cand, out + lo, nullptr, [](int i) { return i; },
-                    topk - lo - (n - hi));
+    const int pick = topk - lo - (n - hi);
+    if (pick > kTopk)
+        select_top_radix<KPL>(key, lane, out + lo, nullptr, [](int i) { return i; }, pick);
+    else
+        select_top<KPL>(key, lane, cand, out + lo, nullptr, [](int i) { return i; }, pick);
     if (lane < lo) out[lane] = lane;
     if (lane < n - hi) out[topk - (n - hi) + lane] = hi + lane;
 }
