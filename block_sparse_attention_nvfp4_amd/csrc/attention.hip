@@ -1474,7 +1474,7 @@ hipError_t launch_attention_t(const uint8_t* k_pool, const uint8_t* v_pool, int6
         // speculative verify: each (sequence, group) reads the union of its drafts' blocks once
         return launch_attention_union(k_pool, v_pool, num_pages, block_table, ctx_lens, batch,
                                       max_blocks, q_len, q, ids, SELECT ? scores : nullptr,
-                                      scale_log2, out, workspace, stream);
+                                      kTopk, scale_log2, out, workspace, stream);
     }
     if (ns == 1 && q_len >= kTileMinQ && max_blocks <= kUnionMaxBlocks) {
         // many tokens per sequence: token tiles over the union of their blocks (the selection,
@@ -1534,8 +1534,11 @@ hipError_t launch_attention_long_select(const uint8_t* k_pool, const uint8_t* v_
 
 }  // namespace
 
-// Rows of topk (1..64) ids: the per-token kernel whatever the batch shape, with the splits of
-// the 16-id calls and ceil(topk / (4 splits)) slots per wavefront.
+// Rows of topk (1..64) ids: rows of up to kTopk ids on the union kernel wherever the 16-id call
+// runs it, else the per-token kernel with the splits of the 16-id calls and
+// ceil(topk / (4 splits)) slots per wavefront. (On rows of 64 ids the union kernel, whose
+// splits each stream a long run of union blocks, is the slower one: 62 against 40 us per launch
+// at 8 sequences of 128K tokens with 4 query tokens.)
 hipError_t launch_attention_topk(const uint8_t* k_pool, const uint8_t* v_pool, int64_t num_pages,
                                  const int32_t* block_table, const int32_t* ctx_lens, int batch,
                                  int max_blocks, int q_len, const uint16_t* q, const int32_t* ids,
@@ -1545,6 +1548,10 @@ hipError_t launch_attention_topk(const uint8_t* k_pool, const uint8_t* v_pool, i
     const int pairs = batch * kKvHeads;
     const int pair_slots = 8 * ((pairs + 7) / 8);
     const float scale_log2 = softmax_scale * 1.4426950408889634f;
+    if (topk <= kTopk && use_union(batch, q_len, max_blocks, false))
+        return launch_attention_union(k_pool, v_pool, num_pages, block_table, ctx_lens, batch,
+                                      max_blocks, q_len, q, const_cast<int32_t*>(ids), nullptr,
+                                      topk, scale_log2, out, workspace, stream);
     const dim3 grid(pair_slots * q_len * ns), block(kWaves * 64);
     int32_t* counters = nullptr;
     float* partials = nullptr;

@@ -8,11 +8,13 @@
 // are flattened into query rows with their own causal positions; section "MiniMax sparse
 // attention backend": the decode kernel reads the selected pages and merges partial outputs.
 //
-// The draft tokens of one (sequence b, group g) pair select nearly the same 16 blocks. Here the
-// pair's query rows (QL tokens x 16 heads, QL row tiles of the matrix cores) are computed
-// together, over the union of the drafts' selections: each union block streams into LDS once and
-// is dequantized once for every draft. A draft that did not select a union block gets zero
-// probabilities for it, so each row's result is exactly the attention over its own selection.
+// The draft tokens of one (sequence b, group g) pair select nearly the same blocks (16 per row,
+// or up to 16 with the window knobs). Here the pair's query rows (QL tokens x 16 heads, QL row
+// tiles of the matrix cores) are computed together, over the union of the drafts' selections:
+// each union block streams into LDS once and is dequantized once for every draft. A draft that
+// did not select a union block gets zero probabilities for it, and one whose row lists a block
+// several times weights its keys that many times, so each row's result is exactly the attention
+// over its own selection.
 //
 // Work: n_split workgroups per pair take contiguous ranges of the union. A workgroup has eight
 // wavefronts, wavefront (w, h) = (token quarter, half of the row tiles): for every block it works
@@ -133,9 +135,10 @@ __device__ __forceinline__ void lds_read_entry(int& x, int& y, int& z, uint32_t 
 // One union block for one wavefront: its quarter w of the block's tokens for its RT row tiles
 // (tiles tile0 .. tile0 + RT - 1; a tile at or past QL is never selected). `buf` holds the
 // block's K and V pages; tok0 = first token of the block; p = position of each of its tiles'
-// drafts (lowest first); dm = drafts that selected the block, shifted so bit i is tile0 + i;
-// T = context length.
-template <int RT, bool F16>
+// drafts (lowest first); dm = how many times each draft's row lists the block, one byte per
+// draft, shifted so byte i is tile0 + i (0: not selected; at most 1 unless MULTI); T = context
+// length.
+template <int RT, bool F16, bool MULTI>
 __device__ __forceinline__ void union_attend_block(const uint8_t* buf, int w, int lane, int c,
                                                    int n, int tok0, int T, const int (&p)[RT],
                                                    int dm, const u32x4 (&qop)[RT][4],
@@ -190,7 +193,8 @@ __device__ __forceinline__ void union_attend_block(const uint8_t* buf, int w, in
     f16x8 pt[RT];
 #pragma unroll
     for (int i = 0; i < RT; i++) {
-        const bool sel = (dm >> i) & 1;  // (wavefront-uniform)
+        const int cnt = (dm >> (8 * i)) & 0xFF;  // (wavefront-uniform)
+        const bool sel = cnt != 0;
         float mb = -INFINITY;
 #pragma unroll
         for (int tt = 0; tt < 2; tt++)
@@ -215,6 +219,13 @@ __device__ __forceinline__ void union_attend_block(const uint8_t* buf, int w, in
                 sum += x;
                 pt[i][4 * tt + e] = (_Float16)x;
             }
+        if (MULTI && cnt > 1) {
+            // a block listed cnt times in the draft's row: each of its keys counts cnt times
+            const float mult = (float)cnt;
+            sum *= mult;
+#pragma unroll
+            for (int e = 0; e < 8; e++) pt[i][e] *= (_Float16)mult;
+        }
         l_run[i] += sum;  // this lane's tokens; the four lanes of a row add up at the end
     }
     // ---- O^T += V^T P^T: lane (n, c) holds dim 16 dt + n of tokens 32c + 8w + (0..7)
@@ -249,8 +260,9 @@ __device__ __forceinline__ void union_attend_block(const uint8_t* buf, int w, in
 }
 
 // The union blocks [lo, hi) of one split: double-buffered page copies, a workgroup barrier per
-// block, then this wavefront's part of each block (one instantiation per operand type).
-template <int RT, bool F16, class Issue, class Entry>
+// block, then this wavefront's part of each block (one instantiation per operand type; MULTI:
+// a row may list a block more than once).
+template <int RT, bool F16, bool MULTI, class Issue, class Entry>
 __device__ __forceinline__ void union_loop(uint8_t* pages, int lo, int hi, Issue issue, Entry entry,
                                            int w, int tile0, int lane, int c, int n, int T,
                                            const int (&p)[RT], const u32x4 (&qop)[RT][4],
@@ -266,8 +278,8 @@ __device__ __forceinline__ void union_loop(uint8_t* pages, int lo, int hi, Issue
         int id, pg, dm;
         entry(u, id, pg, dm);
         if (pg < 0) continue;  // (uniform)
-        union_attend_block<RT, F16>(pages + bi * kUBlockBytes, w, lane, c, n, id * kBlock, T, p,
-                                    dm >> tile0, qop, ls, m_run, l_run, o);
+        union_attend_block<RT, F16, MULTI>(pages + bi * kUBlockBytes, w, lane, c, n, id * kBlock, T, p,
+                                    dm >> (8 * tile0), qop, ls, m_run, l_run, o);
     }
 }
 
@@ -282,7 +294,7 @@ __global__ __launch_bounds__(kUWaves * 64) void attention_union_kernel(
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_lens, int batch,
     int max_blocks, int n_split, const uint16_t* __restrict__ q, int32_t* __restrict__ block_ids,
     const float* __restrict__ scores, float scale_log2, uint16_t* __restrict__ out,
-    int32_t* __restrict__ counters, uint8_t* __restrict__ partials) {
+    int32_t* __restrict__ counters, uint8_t* __restrict__ partials, int ids_per_row) {
     static_assert(QL >= 2 && QL <= kUMaxQL, "2 to 4 query tokens per sequence");
     constexpr int RT = (QL + kUHalves - 1) / kUHalves;  // row tiles per wavefront
     constexpr int kWords = ((SELECT ? kSelectFusedMaxBlocks : kUnionAttnMaxBlocks) + 63) / 64;
@@ -329,6 +341,7 @@ __global__ __launch_bounds__(kUWaves * 64) void attention_union_kernel(
     const int T_raw = ctx_lens[b];
     for (int i = threadIdx.x; i < kWords; i += kUWaves * 64) sh_bits[i] = 0ull;
     for (int i = threadIdx.x; i < QL * kWords; i += kUWaves * 64) (&sh_dbits[0][0])[i] = 0ull;
+    for (int i = threadIdx.x; i < kUMaxUnion; i += kUWaves * 64) sh_udm[i] = 0;
 
     // ---- each draft's selection: wavefront j (< QL) selects draft j's row; the others copy the
     // sequence's block-table row into LDS
@@ -354,14 +367,18 @@ __global__ __launch_bounds__(kUWaves * 64) void attention_union_kernel(
             for (int r = 0; r < kPer; r++) sh_tbl[min(t0 + r * kThr, max_blocks - 1)] = tv[r];
         }
     } else {
-        if (wave < QL && lane < kTopk)
-            sh_sel[wave][lane] = block_ids[((int64_t)(b * QL + wave) * kKvHeads + g) * kTopk + lane];
+        // draft j's row of ids_per_row (1 .. kTopk) ids
+        if (wave < QL && lane < kTopk) {
+            const int32_t* row = block_ids + ((int64_t)(b * QL + wave) * kKvHeads + g) * ids_per_row;
+            sh_sel[wave][lane] = lane < ids_per_row ? row[lane] : -1;
+        }
     }
     const int T = clamp_ctx(T_raw, max_blocks);
     __syncthreads();
 
     // ---- the union of the drafts' usable blocks (in range, holding a key visible to the draft),
-    // in ascending order, by wavefront 0: candidate l = entry l % 16 of draft l / 16
+    // in ascending order, by wavefront 0: candidate l = entry l % 16 of draft l / 16. Every union
+    // entry counts, per draft, how many times the draft's row lists it (one byte per draft).
     if (wave == 0) {
         const int jd = lane >> 4;
         int x = -1;
@@ -395,15 +412,15 @@ __global__ __launch_bounds__(kUWaves * 64) void attention_union_kernel(
         if (x >= 0) {
             const int wd = x >> 6;
             const uint64_t below = (1ull << (x & 63)) - 1ull;
+            const int r = sh_prefix[wd] + popc64(sh_bits[wd] & below);
+            atomicAdd(&sh_udm[r], 1 << (8 * jd));
             int dm = 0;
 #pragma unroll
             for (int j = 0; j < QL; j++) dm |= (int)((sh_dbits[j][wd] >> (x & 63)) & 1ull) << j;
             if ((dm & ((1 << jd) - 1)) == 0) {  // the first draft that holds x writes its entry
-                const int r = sh_prefix[wd] + popc64(sh_bits[wd] & below);
                 sh_ulist[r] = x;
                 const int pg = SELECT ? sh_tbl[x] : block_table[(int64_t)b * max_blocks + x];
                 sh_upage[r] = (pg >= 0 && pg < num_pages) ? pg : -1;
-                sh_udm[r] = dm;
             }
         }
         if (lane == 0) sh_ucount = base;
@@ -493,9 +510,9 @@ __global__ __launch_bounds__(kUWaves * 64) void attention_union_kernel(
         for (int dt = 0; dt < 8; dt++) o[i][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     if (f16)
-        union_loop<RT, true>(scratch, lo, hi, issue, entry, w, tile0, lane, c, n, T, p, qop, ls, m_run, l_run, o);
+        union_loop<RT, true, !SELECT>(scratch, lo, hi, issue, entry, w, tile0, lane, c, n, T, p, qop, ls, m_run, l_run, o);
     else
-        union_loop<RT, false>(scratch, lo, hi, issue, entry, w, tile0, lane, c, n, T, p, qop, ls, m_run, l_run, o);
+        union_loop<RT, false, !SELECT>(scratch, lo, hi, issue, entry, w, tile0, lane, c, n, T, p, qop, ls, m_run, l_run, o);
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __syncthreads();  // the page buffers are free: the merge below reuses them
 
@@ -666,8 +683,8 @@ size_t union_workspace_bytes(int batch, int q_len) {
 hipError_t launch_attention_union(const uint8_t* k_pool, const uint8_t* v_pool, int64_t num_pages,
                                   const int32_t* block_table, const int32_t* ctx_lens, int batch,
                                   int max_blocks, int q_len, const uint16_t* q, int32_t* ids,
-                                  const float* scores, float scale_log2, uint16_t* out,
-                                  void* workspace, hipStream_t stream) {
+                                  const float* scores, int ids_per_row, float scale_log2,
+                                  uint16_t* out, void* workspace, hipStream_t stream) {
     const int ns = union_num_splits(batch);
     const int pairs = batch * kKvHeads;
     const dim3 grid(8 * ((pairs + 7) / 8) * ns), block(kUWaves * 64);
@@ -680,7 +697,7 @@ hipError_t launch_attention_union(const uint8_t* k_pool, const uint8_t* v_pool, 
 #define MSA_LAUNCH_UNION(QL_, SEL_)                                                                  \
     hipLaunchKernelGGL((attention_union_kernel<QL_, SEL_>), grid, block, 0, stream, k_pool, v_pool, \
                        num_pages, block_table, ctx_lens, batch, max_blocks, ns, q, ids, scores,     \
-                       scale_log2, out, counters, partials)
+                       scale_log2, out, counters, partials, ids_per_row)
     const bool sel = scores != nullptr;
     switch (q_len) {
         case 2: if (sel) MSA_LAUNCH_UNION(2, true); else MSA_LAUNCH_UNION(2, false); break;

@@ -105,9 +105,10 @@ hipError_t launch_attention_topk(const uint8_t* k_pool, const uint8_t* v_pool, i
                                  hipStream_t stream);
 
 // Attention for 2 to 4 query tokens per sequence over the union of their selected blocks
-// (attention_union.hip): rows of up to kUnionAttnMaxBlocks blocks; the selection is made in the
-// same launch when `scores` is given (rows of up to kSelectFusedMaxBlocks blocks), else the ids
-// are read. scale_log2 = softmax scale x log2(e).
+// (attention_union.hip): rows of up to kUnionAttnMaxBlocks blocks; the selection (kTopk ids per
+// row) is made in the same launch when `scores` is given (rows of up to kSelectFusedMaxBlocks
+// blocks), else ids_per_row (1 .. kTopk) ids per row are read.
+// scale_log2 = softmax scale x log2(e).
 constexpr int kUnionAttnMaxBlocks = 8192;
 int union_num_splits(int batch);
 size_t union_counter_bytes(int batch);
@@ -115,8 +116,8 @@ size_t union_workspace_bytes(int batch, int q_len);
 hipError_t launch_attention_union(const uint8_t* k_pool, const uint8_t* v_pool, int64_t num_pages,
                                   const int32_t* block_table, const int32_t* ctx_lens, int batch,
                                   int max_blocks, int q_len, const uint16_t* q, int32_t* ids,
-                                  const float* scores, float scale_log2, uint16_t* out,
-                                  void* workspace, hipStream_t stream);
+                                  const float* scores, int ids_per_row, float scale_log2,
+                                  uint16_t* out, void* workspace, hipStream_t stream);
 
 // Selection fused into the attention (one launch): rows of up to this many blocks, whose
 // selection one wavefront holds in 16 keys per lane; longer rows launch the two kernels.

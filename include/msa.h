@@ -334,12 +334,13 @@ int msa_sparse_attn_decode(const msa_cache_t *cache, const msa_batch_t *batch, c
  *               and holds a visible key is attended (-1 and other entries are skipped; a block
  *               listed twice counts twice, as the formula then says).
  *   topk      : 1..64. With topk = 16 the output is msa_sparse_attn_decode's bit for bit
- *               wherever that call runs its per-token kernel (below 16 sequences or outside
- *               2-4 query tokens per sequence, and below 8 query tokens per sequence or 1,024
- *               rows), and within the attention tolerance of it elsewhere.
+ *               wherever that call runs its per-token or union kernel (below 8 query tokens
+ *               per sequence or 1,024 rows), and within the attention tolerance of it where
+ *               that call runs its token-tile kernel.
  *   workspace : at least msa_sparse_attn_workspace_bytes(batch) bytes, the same contract.
- * Every batch shape runs the per-token kernel (each wavefront streams ceil(topk / (4 splits))
- * blocks in turn), not the union or token-tile kernels of the 16-id call.
+ * Rows of up to 16 ids take the union kernel where the 16-id call does (2-4 query tokens per
+ * sequence, 16 sequences and more); every other shape runs the per-token kernel (each wavefront
+ * streams ceil(topk / (4 splits)) blocks in turn).
  * Errors: as msa_sparse_attn_decode; MSA_ERR_UNSUPPORTED for topk outside 1..64.
  */
 int msa_sparse_attn_decode_topk(const msa_cache_t *cache, const msa_batch_t *batch,

@@ -135,7 +135,8 @@ def oracle_sequence(w: mi.Workload, b: int, attention_tokens: Optional[Sequence[
         return res
     use_ids = ids if ids_override is None else ids_override
     tokens = list(attention_tokens)
-    blocks = sorted(set(int(x) for j in tokens for x in use_ids[j].ravel() if x >= 0))
+    # (ids past the context hold no key: the oracle's attention skips them)
+    blocks = sorted(set(int(x) for j in tokens for x in use_ids[j].ravel() if 0 <= x and x * BLOCK < T))
     kc = np.zeros((T, 4, 64), np.uint8)
     ks = np.zeros((T, 4, 8), np.uint8)
     vc = np.zeros_like(kc)
