@@ -353,8 +353,9 @@ __device__ __forceinline__ void attend_block(const uint8_t* buf, int lane, int c
 // wavefronts; the first split also writes them to block_ids) instead of being read
 // from block_ids.
 // VAR_IDS: rows of ids_per_row (1..64) ids instead of 16: each wavefront takes
-// ceil(ids_per_row / (4 NSPLIT)) consecutive slots (at most BPW), the selection sizes of the
-// window knobs ("MiniMax M3 on vLLM", section "MSA mechanism": the top-k count is a knob).
+// ceil(ids_per_row / (4 NSPLIT)) consecutive slots (up to 16; BPW then only sets the page
+// buffers: two for BPW > 1, else one), the selection sizes of the window knobs ("MiniMax M3 on
+// vLLM", section "MSA mechanism": the top-k count is a knob).
 template <int BPW, bool SELECT, bool LONG = false, int NSPLIT = kMaxSplits / BPW, bool VAR_IDS = false>
 __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
     const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool, int64_t num_pages,
@@ -603,11 +604,14 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
     const float logit_scale = fabsf(scale_log2) * (f16 ? q_unscale : 1.0f);
 
     // (left to the compiler: with several blocks per wavefront the unrolled body is too large)
+    // Two buffers: the next block's copies are issued before the current block is attended.
+    // One buffer (VAR_IDS rows with BPW = 1, which may still give a wavefront several blocks):
+    // they are issued once the current block's LDS reads have all returned.
     for (int kb = 0; kb < bpw; kb++) {
         int nxt_id = -1;
         if (kb + 1 < bpw) {
             nxt_id = __builtin_amdgcn_readlane(blk_id, kb + 1);
-            if (nxt_id >= 0) {
+            if (kBufs > 1 && nxt_id >= 0) {
                 const int pg = __builtin_amdgcn_readlane(page, kb + 1);
                 block_to_lds(kg + pg * kPageStride, vg + pg * kPageStride,
                              lds[wave][(kb + 1) % kBufs], lane);
@@ -617,7 +621,7 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
             // the current block's K page (its first 9 loads) has arrived
             uint8_t* buf = lds[wave][kb % kBufs];
             const int tok0 = cur_id * kBlock;
-            if (nxt_id >= 0) {
+            if (kBufs > 1 && nxt_id >= 0) {
                 asm volatile("s_waitcnt vmcnt(27)" ::: "memory");
                 if (f16) attend_block<true, true>(buf, lane, c, tok0, p, qop, logit_scale, m_run, l_run, o);
                 else attend_block<false, true>(buf, lane, c, tok0, p, qop, logit_scale, m_run, l_run, o);
@@ -626,6 +630,11 @@ __global__ __launch_bounds__(kWaves * 64) void attention_kernel(
                 if (f16) attend_block<true, false>(buf, lane, c, tok0, p, qop, logit_scale, m_run, l_run, o);
                 else attend_block<false, false>(buf, lane, c, tok0, p, qop, logit_scale, m_run, l_run, o);
             }
+        }
+        if (kBufs == 1 && nxt_id >= 0) {
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+            const int pg = __builtin_amdgcn_readlane(page, kb + 1);
+            block_to_lds(kg + pg * kPageStride, vg + pg * kPageStride, lds[wave][0], lane);
         }
         cur_id = nxt_id;
     }
@@ -1536,9 +1545,12 @@ hipError_t launch_attention_long_select(const uint8_t* k_pool, const uint8_t* v_
 
 // Rows of topk (1..64) ids: rows of up to kTopk ids on the union kernel wherever the 16-id call
 // runs it, else the per-token kernel with the splits of the 16-id calls and
-// ceil(topk / (4 splits)) slots per wavefront. (On rows of 64 ids the union kernel, whose
-// splits each stream a long run of union blocks, is the slower one: 62 against 40 us per launch
-// at 8 sequences of 128K tokens with 4 query tokens.)
+// ceil(topk / (4 splits)) slots per wavefront, streamed through one page buffer per wavefront:
+// 74 KB of LDS per workgroup, so two workgroups share a compute unit and hide each other's
+// copies, where two buffers (144 KB) would leave one workgroup per compute unit (at 64 ids,
+// 8 sequences of 128K tokens with 4 query tokens: 31.8 against 39.5 us per launch). (The union
+// kernel over rows of 64 ids, whose splits each stream a long run of union blocks, is slower
+// still there: 62 us.)
 hipError_t launch_attention_topk(const uint8_t* k_pool, const uint8_t* v_pool, int64_t num_pages,
                                  const int32_t* block_table, const int32_t* ctx_lens, int batch,
                                  int max_blocks, int q_len, const uint16_t* q, const int32_t* ids,
@@ -1562,7 +1574,7 @@ hipError_t launch_attention_topk(const uint8_t* k_pool, const uint8_t* v_pool, i
     }
     static_assert(kMaxTopkIds <= 16 * kWaves, "one split holds 16 slots per wavefront at most");
 #define MSA_LAUNCH_ATTN_VAR(NS_)                                                                 \
-    hipLaunchKernelGGL((attention_kernel<16, false, false, NS_, true>), grid, block, 0, stream,  \
+    hipLaunchKernelGGL((attention_kernel<1, false, false, NS_, true>), grid, block, 0, stream,   \
                        k_pool, v_pool, num_pages, block_table, ctx_lens, batch, max_blocks,      \
                        q_len, q, const_cast<int32_t*>(ids), nullptr, scale_log2, out, counters,  \
                        partials, topk)

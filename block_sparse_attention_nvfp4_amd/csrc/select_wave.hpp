@@ -229,26 +229,64 @@ __device__ __forceinline__ void select_top(const uint32_t (&key)[KPL], int lane,
 }
 
 // select_top for picks above 16 (the window knobs' top-k up to 64), where the lane-maxima bound
-// would leave far more than 64 candidates: t, the pick-th largest key, is found bit by bit from
-// the top (the largest value that at least `pick` keys reach, counted by ballots); then every key
-// above t and the first keys equal to t in position order (equal keys rank by the lower
-// position) are written in ascending position order. The same contract as select_top.
+// would leave far more than 64 candidates: t, the pick-th largest key (counted with
+// multiplicity, the zero keys of non-candidates included), is found one byte at a time from the
+// top: a 256-bin histogram in LDS (`hist`, 256 words of this wavefront's scratch) of the next
+// byte of the keys that share the bytes found so far, then the bin in which the pick-th largest
+// lies. Every key above t and the first keys equal to t in position order (equal keys rank by
+// the lower position) are then written in ascending position order; t = 0 (fewer than `pick`
+// candidates) takes every candidate. The same contract as select_top.
 template <int KPL, class IdOf>
 __device__ __forceinline__ void select_top_radix(const uint32_t (&key)[KPL], int lane,
-                                                 int32_t* out, uint32_t* key_out, IdOf id_of,
-                                                 int pick) {
-    uint32_t t = 0;  // stays 0 when fewer than `pick` keys are candidates (every candidate is >= 1)
-    for (int bit = 31; bit >= 0; bit--) {
-        const uint32_t c = t | (1u << bit);
-        int cnt = 0;
+                                                 uint32_t* hist, int32_t* out, uint32_t* key_out,
+                                                 IdOf id_of, int pick) {
+    uint32_t t = 0, known = 0;  // the bytes of t found so far, and their mask
+    int need = pick;            // rank of t among the keys that share those bytes
 #pragma unroll
-        for (int k = 0; k < KPL; k++) cnt += popc64(__ballot(key[k] >= c));
-        if (cnt >= pick) t = c;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) hist[lane + 64 * i] = 0u;
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int k = 0; k < KPL; k++)
+            if ((key[k] & known) == t) atomicAdd(&hist[(key[k] >> shift) & 0xFFu], 1u);
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+        // lane l holds bins 4l .. 4l + 3; keys in the bins of higher lanes come first
+        uint32_t cb[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) cb[i] = hist[4 * lane + i];
+        const int own = (int)(cb[0] + cb[1] + cb[2] + cb[3]);
+        int incl = own;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_down(incl, d, 64);
+            if (lane + d < 64) incl += y;
+        }
+        int cum = incl - own;  // keys in higher bins
+        int found = -1, rest = 0;
+#pragma unroll
+        for (int i = 3; i >= 0; i--) {
+            if (cum < need && cum + (int)cb[i] >= need) {
+                found = 4 * lane + i;
+                rest = need - cum;
+            }
+            cum += (int)cb[i];
+        }
+        // exactly one lane holds the bin (the keys that share the bytes found so far number at
+        // least `need`)
+        const int src = __builtin_ctzll(__ballot(found >= 0));
+        t |= (uint32_t)__builtin_amdgcn_readlane(found, src) << shift;
+        need = __builtin_amdgcn_readlane(rest, src);
+        known |= 0xFFu << shift;
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
     }
     int above = 0;
 #pragma unroll
     for (int k = 0; k < KPL; k++) above += popc64(__ballot(key[k] > t));
-    int take_eq = t == 0u ? 0 : pick - above;  // keys equal to t still to take
+    int take_eq = t == 0u ? 0 : pick - above;  // keys equal to t still to take (none: t = 0)
     int at = 0;
 #pragma unroll
     for (int k = 0; k < KPL; k++) {
@@ -313,7 +351,8 @@ __device__ __forceinline__ void select_row_window(const float (&v)[KPL], int n, 
     // the picks lie between the two forced ranges, so the ascending order is kept
     const int pick = topk - lo - (n - hi);
     if (pick > kTopk)
-        select_top_radix<KPL>(key, lane, out + lo, nullptr, [](int i) { return i; }, pick);
+        select_top_radix<KPL>(key, lane, reinterpret_cast<uint32_t*>(cand), out + lo, nullptr,
+                              [](int i) { return i; }, pick);
     else
         select_top<KPL>(key, lane, cand, out + lo, nullptr, [](int i) { return i; }, pick);
     if (lane < lo) out[lane] = lane;
