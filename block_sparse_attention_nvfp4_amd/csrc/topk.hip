@@ -254,14 +254,17 @@ __global__ __launch_bounds__(kRowsPerWg * 64) void topk_wave_kernel(
 }
 
 // ---------------------------------------------------------------- window knobs
+// One row per workgroup (a wavefront each): the byte histograms of select_top_radix are built
+// with LDS atomic adds, which rows sharing a compute unit would queue on its one LDS.
+constexpr int kWindowRowsPerWg = 1;
 template <int KPL>
-__global__ __launch_bounds__(kRowsPerWg * 64) void topk_window_kernel(
+__global__ __launch_bounds__(kWindowRowsPerWg * 64) void topk_window_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ ctx_lens, int max_blocks,
     int q_len, int rows, int topk, int init, int local, int32_t* __restrict__ ids) {
-    __shared__ uint64_t cand[kRowsPerWg][kSelectScratch];
+    __shared__ uint64_t cand[kWindowRowsPerWg][kSelectScratch];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int row = blockIdx.x * kRowsPerWg + wave;
+    const int row = blockIdx.x * kWindowRowsPerWg + wave;
     if (row >= rows) return;
     const int bq = row >> 2;
     const int b = bq / q_len;
@@ -388,7 +391,7 @@ hipError_t launch_topk_window(const float* scores, const int32_t* ctx_lens, int 
                               int max_blocks, int q_len, int topk, int init, int local,
                               int32_t* ids, hipStream_t stream) {
     const int rows = batch * q_len * kKvHeads;
-    const dim3 grid((rows + kRowsPerWg - 1) / kRowsPerWg), block(kRowsPerWg * 64);
+    const dim3 grid((rows + kWindowRowsPerWg - 1) / kWindowRowsPerWg), block(kWindowRowsPerWg * 64);
     if (max_blocks <= 64 * 16)
         hipLaunchKernelGGL(topk_window_kernel<16>, grid, block, 0, stream, scores, ctx_lens,
                            max_blocks, q_len, rows, topk, init, local, ids);
