@@ -28,7 +28,8 @@ def _log(msg):
 
 
 # every step mode on each: the decode kernels (per-token attention with 4 and 2 splits and the
-# fused selection, the union kernel, rows past 1,025 blocks), and the prefill kernels (score-GEMM
+# fused selection, the union kernel, rows past 1,025 and past 2,048 blocks), and the prefill
+# kernels (score-GEMM
 # indexer, token tiles over 1,024 rows, run insert)
 CASES = {
     "spec_q4": (3, dict(batch=2, ctx=6000)),
@@ -37,6 +38,7 @@ CASES = {
     "two_splits": (2, dict(batch=130, ctx=1500, q_len=1)),
     "union_q4": (3, dict(batch=16, ctx=2600)),
     "long_rows": (4, dict(batch=2, ctx_lens=[140_001, 2_000])),
+    "long_table": (4, dict(batch=2, ctx_lens=[2100 * 128 + 77, 2_000])),
     "prefill": (5, dict(batch=1, ctx=2048 + 256, q_len=256)),
 }
 

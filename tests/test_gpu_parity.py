@@ -41,6 +41,9 @@ CASES = {
     # partial last blocks, blocks past the shorter sequences, and 800 rows per sequence (two
     # row ranges, the second partial)
     "prefill_ragged": (5, dict(batch=3, ctx_lens=[40, 700, 3003], q_len=40)),
+    # rows of more than 2,048 blocks: a long sequence beside short ones (one of them past every
+    # indexer workgroup of its row but the first), the selection of rows past 1,025 blocks
+    "long_table": (4, dict(batch=3, ctx_lens=[2100 * 128 + 77, 3000, 129])),
     "prefill_q200": (5, dict(ctx_lens=[2048 + 200, 1500], q_len=200)),
     # 16 or more sequences with 2 to 4 draft tokens: the union kernel (each (sequence, group)
     # reads the union of its drafts' blocks once): 4 and 2 splits per pair, ragged lengths with
