@@ -236,6 +236,7 @@ __device__ __forceinline__ void select_top(const uint32_t (&key)[KPL], int lane,
 // lies. Every key above t and the first keys equal to t in position order (equal keys rank by
 // the lower position) are then written in ascending position order; t = 0 (fewer than `pick`
 // candidates) takes every candidate. The same contract as select_top.
+static_assert(kSelectScratch * 8 >= 256 * 4, "the byte histogram fits a wavefront's scratch");
 template <int KPL, class IdOf>
 __device__ __forceinline__ void select_top_radix(const uint32_t (&key)[KPL], int lane,
                                                  uint32_t* hist, int32_t* out, uint32_t* key_out,
