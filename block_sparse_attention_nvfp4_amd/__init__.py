@@ -65,7 +65,8 @@ EXPORTED = ("msa_page_bytes", "msa_kv_insert_nvfp4", "msa_indexer_score", "msa_i
             "msa_sparse_attn_workspace_bytes", "msa_sparse_attn_decode",
             "msa_sparse_attn_decode_topk", "msa_select_attn_decode",
             "msa_sparse_attn_shared_prefix_workspace_bytes", "msa_sparse_attn_decode_shared_prefix",
-            "msa_insert_indexer_score", "msa_decode_step", "msa_decode_step_noalloc",
+            "msa_insert_indexer_score", "msa_decode_step", "msa_decode_step_window",
+            "msa_decode_step_noalloc",
             "msa_last_error", "msa_version",
             # include/msa_debug.h (checked build diagnostics)
             "msa_debug_checks",
@@ -141,6 +142,10 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.msa_decode_step.restype = ctypes.c_int
     L.msa_decode_step.argtypes = [ctypes.POINTER(_Cache), ctypes.POINTER(_Batch), vp, vp, vp, vp,
                                   vp, i32, ctypes.c_float, vp, vp, vp, vp, sz, vp]
+    L.msa_decode_step_window.restype = ctypes.c_int
+    L.msa_decode_step_window.argtypes = [ctypes.POINTER(_Cache), ctypes.POINTER(_Batch), vp, vp,
+                                         vp, vp, vp, i32, i32, i32, ctypes.c_float, vp, vp, vp,
+                                         vp, sz, vp]
     L.msa_decode_step_noalloc.restype = ctypes.c_int
     L.msa_decode_step_noalloc.argtypes = [ctypes.POINTER(_Cache), ctypes.POINTER(_Batch), vp, vp,
                                           vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp]
@@ -497,6 +502,33 @@ def msa_decode_step(cache: Cache, batch: Batch, k: torch.Tensor, v: torch.Tensor
                                _ptr(block_ids, torch.int32, "block_ids"),
                                _ptr(out, torch.bfloat16, "out"), ws_ptr, ws_bytes,
                                _stream(stream)))
+
+
+def msa_decode_step_window(cache: Cache, batch: Batch, k: torch.Tensor, v: torch.Tensor,
+                           ik: torch.Tensor, q_idx: torch.Tensor, q: torch.Tensor, topk: int,
+                           init_blocks: int, local_blocks: int, softmax_scale: float,
+                           block_scores: torch.Tensor, block_ids: torch.Tensor, out: torch.Tensor,
+                           workspace: Optional[torch.Tensor], stream=None) -> None:
+    """The decode step with the window knobs: insert + indexer, msa_block_topk_window, then
+    attention over the topk ids per row."""
+    _check_step_shapes(batch, k=k, v=v, ik=ik, q_idx=q_idx, q=q, out=out,
+                       block_scores=block_scores)
+    if tuple(block_ids.shape) != (batch.rows, KV_HEADS, int(topk)):
+        raise ValueError("block_ids: expected [batch*q_len][4][topk]")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _ptr(workspace, workspace.dtype, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.msa_decode_step_window(ctypes.byref(cache._c), ctypes.byref(batch._c),
+                                      _ptr(k, torch.float32, "k"), _ptr(v, torch.float32, "v"),
+                                      _ptr(ik, torch.float32, "ik"),
+                                      _ptr(q_idx, torch.bfloat16, "q_idx"),
+                                      _ptr(q, torch.bfloat16, "q"), int(topk), int(init_blocks),
+                                      int(local_blocks), float(softmax_scale),
+                                      _ptr(block_scores, torch.float32, "block_scores"),
+                                      _ptr(block_ids, torch.int32, "block_ids"),
+                                      _ptr(out, torch.bfloat16, "out"), ws_ptr, ws_bytes,
+                                      _stream(stream)))
 
 
 def msa_decode_step_noalloc(cache: Cache, batch: Batch, k: torch.Tensor, v: torch.Tensor,

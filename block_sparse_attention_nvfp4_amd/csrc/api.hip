@@ -472,6 +472,48 @@ int msa_decode_step(const msa_cache_t* cache, const msa_batch_t* batch, const fl
                       fn);
 }
 
+int msa_decode_step_window(const msa_cache_t* cache, const msa_batch_t* batch, const float* k,
+                           const float* v, const float* ik, const uint16_t* q_idx,
+                           const uint16_t* q, int32_t topk, int32_t init_blocks,
+                           int32_t local_blocks, float softmax_scale, float* block_scores,
+                           int32_t* block_ids, uint16_t* out, void* workspace, size_t ws_bytes,
+                           void* stream) {
+    static const char* fn = "msa_decode_step_window";
+    int rc = check_insert_indexer(cache, batch, k, v, ik, q_idx, block_scores, fn);
+    if (rc) return rc;
+    if (!q || !block_ids || !out)
+        return fail(MSA_ERR_INVALID_ARG, "%s: q, block_ids or out is NULL", fn);
+    if (topk < 1 || topk > msa::kMaxTopkIds)
+        return fail(MSA_ERR_UNSUPPORTED, "%s: topk=%d (1..%d are built)", fn, topk,
+                    msa::kMaxTopkIds);
+    if (init_blocks < 0 || local_blocks < 0 || init_blocks + local_blocks > topk)
+        return fail(MSA_ERR_INVALID_ARG,
+                    "%s: init_blocks=%d and local_blocks=%d must be >= 0 and sum to at most topk=%d",
+                    fn, init_blocks, local_blocks, topk);
+    if (batch->max_blocks > msa::kWindowMaxBlocks)
+        return fail(MSA_ERR_UNSUPPORTED, "%s: max_blocks=%d (up to %d are built)", fn,
+                    batch->max_blocks, msa::kWindowMaxBlocks);
+    if ((rc = check_workspace(batch, workspace, ws_bytes, fn))) return rc;
+    const hipStream_t s = (hipStream_t)stream;
+    rc = hip_status(msa::launch_insert_indexer(cache->k, cache->v, cache->ik, cache->num_pages,
+                                               batch->block_table, batch->ctx_lens, batch->batch,
+                                               batch->max_blocks, batch->q_len, k, v, ik, q_idx,
+                                               block_scores, s),
+                    fn);
+    if (rc) return rc;
+    rc = hip_status(msa::launch_topk_window(block_scores, batch->ctx_lens, batch->batch,
+                                            batch->max_blocks, batch->q_len, topk, init_blocks,
+                                            local_blocks, block_ids, s),
+                    fn);
+    if (rc) return rc;
+    return hip_status(msa::launch_attention_topk(cache->k, cache->v, cache->num_pages,
+                                                 batch->block_table, batch->ctx_lens,
+                                                 batch->batch, batch->max_blocks, batch->q_len, q,
+                                                 block_ids, topk, softmax_scale, out, workspace,
+                                                 s),
+                      fn);
+}
+
 int msa_decode_step_noalloc(const msa_cache_t* cache, const msa_batch_t* batch, const float* k,
                             const float* v, const float* ik, const uint16_t* q_idx,
                             const uint16_t* q, int32_t topk, float softmax_scale,

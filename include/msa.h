@@ -445,6 +445,28 @@ int msa_decode_step(const msa_cache_t *cache, const msa_batch_t *batch, const fl
                     uint16_t *out, void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * One whole decode step with the selection's window knobs ("MiniMax M3 on vLLM", section "MSA
+ * mechanism": the number of kept blocks and the init and local windows are configuration
+ * knobs), in three launches: the effect of
+ *   msa_insert_indexer_score(cache, batch, k, v, ik, q_idx, block_scores)
+ *   msa_block_topk_window(block_scores, batch, topk, init_blocks, local_blocks, block_ids)
+ *   msa_sparse_attn_decode_topk(cache, batch, q, block_ids, topk, softmax_scale, out,
+ *                               workspace, ws_bytes)
+ * on one stream, with those calls' results bit for bit. Arguments as for msa_decode_step, with:
+ *   topk, init_blocks, local_blocks : as msa_block_topk_window takes them (topk 1..64,
+ *          init_blocks + local_blocks <= topk); block_ids is [batch * q_len][4][topk].
+ * Errors: MSA_ERR_INVALID_ARG (a NULL pointer, sizes < 1, knobs out of range),
+ * MSA_ERR_UNSUPPORTED (topk outside 1..64, rows longer than msa_block_topk_window builds),
+ * MSA_ERR_WORKSPACE.
+ */
+int msa_decode_step_window(const msa_cache_t *cache, const msa_batch_t *batch, const float *k,
+                           const float *v, const float *ik, const uint16_t *q_idx,
+                           const uint16_t *q, int32_t topk, int32_t init_blocks,
+                           int32_t local_blocks, float softmax_scale, float *block_scores,
+                           int32_t *block_ids, uint16_t *out, void *workspace, size_t ws_bytes,
+                           void *stream);
+
+/*
  * msa_decode_step for callers that cannot allocate device memory: code under HIP graph capture,
  * tight serving loops, and harnesses that forbid hipMalloc. The same two launches and results,
  * bit for bit, as msa_decode_step with a workspace, preceded by one small kernel that zeroes the

@@ -221,6 +221,24 @@ def test_invalid_arguments_return_codes_without_launch(msa):
     assert call(batch=by(_batch(q=0))) == msa.MSA_ERR_INVALID_ARG
     assert call(a10=None, a11=0) == msa.MSA_ERR_WORKSPACE
     assert call(a10=257) == msa.MSA_ERR_WORKSPACE
+    # the step with the window knobs: k v ik q_idx q topk init local scale scores ids out ws bytes
+    sw = L.msa_decode_step_window
+    wargs = [1, 1, 1, 1, 1, 64, 1, 2, 0.1, 1, 1, 1, 256, need, None]
+    def wcall(cache=None, batch=small, **over):
+        a = list(wargs)
+        for i, val in over.items():
+            a[int(i[1:])] = val
+        return sw(by(cache or _cache()), batch, *a)
+    for bad in (0, 65):
+        assert wcall(a5=bad) == msa.MSA_ERR_UNSUPPORTED
+    assert "topk" in msa.msa_last_error()
+    for init, local in ((-1, 1), (0, -1), (40, 30)):
+        assert wcall(a6=init, a7=local) == msa.MSA_ERR_INVALID_ARG, (init, local)
+    assert wcall(batch=by(_batch(mb=5000))) == msa.MSA_ERR_UNSUPPORTED
+    for i in (0, 1, 2, 3, 4, 9, 10, 11):
+        assert wcall(**{f"a{i}": None}) == msa.MSA_ERR_INVALID_ARG, i
+    assert wcall(cache=_cache(ik=None)) == msa.MSA_ERR_INVALID_ARG
+    assert wcall(a12=None, a13=0) == msa.MSA_ERR_WORKSPACE
     ii = L.msa_insert_indexer_score
     for i in range(5):
         a = [1] * 5

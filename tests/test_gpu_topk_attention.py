@@ -208,3 +208,38 @@ def test_window64_at_full_size():
         ref = oracle_sequence(w, b, attention_tokens=list(range(w.q_len)), ids_override=ids_h[rr])
         d_max, _ = check_attention(got[rr], ref["attention"])
         _log(f"  sequence {b}: attention worst |d| {d_max:.3e}")
+
+
+@pytest.mark.parametrize("name", ["k64_q4", "k40_q3", "k8_q3_union16"])
+def test_window_step_matches_the_three_calls(name):
+    """msa_decode_step_window gives, bit for bit, the block scores, ids, outputs and cache bytes
+    of msa_insert_indexer_score, msa_block_topk_window and msa_sparse_attn_decode_topk called
+    one after the other on the same inputs."""
+    import block_sparse_attention_nvfp4_amd as msa
+    cfg, kw, topk, init, local, _ = CASES[name]
+    _log(f"window step vs the three calls: {name}")
+    w = mi.make_workload(cfg, **kw)
+    g = DeviceWorkload(w, snapshot=True)
+    rows = w.batch * w.q_len
+    ws_bytes = msa.msa_sparse_attn_workspace_bytes(g.batch)
+    scale = msa.default_softmax_scale()
+    res = []
+    for fused in (False, True):
+        g.restore_prefix()
+        ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+        scores = torch.full((rows, 4, w.max_blocks), float("nan"), dtype=torch.float32, device="cuda")
+        ids = torch.full((rows, 4, topk), -7, dtype=torch.int32, device="cuda")
+        out = torch.full((rows, 64, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+        if fused:
+            msa.msa_decode_step_window(g.cache, g.batch, g.new_k, g.new_v, g.new_ik, g.q_idx, g.q,
+                                       topk, init, local, scale, scores, ids, out, ws)
+        else:
+            msa.msa_insert_indexer_score(g.cache, g.batch, g.new_k, g.new_v, g.new_ik, g.q_idx,
+                                         scores)
+            msa.msa_block_topk_window(scores, g.batch, topk, init, local, ids)
+            msa.msa_sparse_attn_decode_topk(g.cache, g.batch, g.q, ids, scale, out, ws)
+        torch.cuda.synchronize()
+        res.append([t.clone() for t in (scores, ids, out, g.cache.k, g.cache.v, g.cache.ik)])
+    assert torch.isfinite(res[1][2].float()).all()
+    for i, (a, b) in enumerate(zip(*res)):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), (name, i)
