@@ -659,10 +659,10 @@ def prefix_side(args, L=4):
 def window_side(args, topk=64, init=1, local=2, L=4):
     """The headline workload (8 x 131,072 tokens, 4 query tokens) with the window knobs of the
     selection: top-`topk` blocks with the first `init` and the last `local` blocks kept, then
-    attention over those rows of `topk` ids. The step as three launches (insert + indexer, the
-    window selection, the attention) on L rotated layers, every call also timed alone; the
-    attention's gather against the HBM peak (144 B per valid token of each distinct selected
-    (sequence, group, block), the scores, queries and outputs)."""
+    attention over those rows of `topk` ids. The step as msa_decode_step_window (three launches:
+    insert + indexer, the window selection, the attention) on L rotated layers, every call also
+    timed alone; the attention's gather against the HBM peak (144 B per valid token of each
+    distinct selected (sequence, group, block), the scores, queries and outputs)."""
     import numpy as np
     import torch
 
@@ -684,6 +684,9 @@ def window_side(args, topk=64, init=1, local=2, L=4):
     ids = [torch.full((B * q, 4, topk), -1, dtype=torch.int32, device=dev) for _ in steps]
     scale = msa.default_softmax_scale()
     calls = {
+        "step": lambda i, s: msa.msa_decode_step_window(s.cache, batch, new_k, new_v, new_ik, q_idx,
+                                                        qq, topk, init, local, scale,
+                                                        s.block_scores, ids[i], s.out, s.workspace),
         "insert_indexer": lambda i, s: msa.msa_insert_indexer_score(s.cache, batch, new_k, new_v,
                                                                     new_ik, q_idx, s.block_scores),
         "topk_window": lambda i, s: msa.msa_block_topk_window(s.block_scores, batch, topk, init,
@@ -691,15 +694,13 @@ def window_side(args, topk=64, init=1, local=2, L=4):
         "attention_topk": lambda i, s: msa.msa_sparse_attn_decode_topk(s.cache, batch, qq, ids[i],
                                                                        scale, s.out, s.workspace),
     }
-    step = tuple(calls)
     for i, s in enumerate(steps):
-        for name in step:
-            calls[name](i, s)
+        calls["step"](i, s)
     torch.cuda.synchronize()
     stream = torch.cuda.Stream()
     graphs = {}
     with torch.cuda.stream(stream):
-        for key, names in [("step", step)] + [(n, (n,)) for n in calls]:
+        for key, names in [(n, (n,)) for n in calls]:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=stream):
                 for i, s in enumerate(steps):
